@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs and the workload shapes.
+
+This module draws random numbers and describes shapes.  It holds none of the
+path's arithmetic (no quantiser, no scoring, no selection, no attention), so
+the test suite can feed the same inputs to the HIP library and to the CPU
+checker.  Every tensor comes from a torch.Generator seeded from
+(workload seed, layer, role); on a GPU device the draw uses that device's
+generator, so a check on the CPU copies the drawn inputs to the host.
+
+Value recipes (the pages' workloads are long-context decode/prefill of the
+DeepSeek-V4.1-Flash CSA2 layers; no dataset is involved):
+  * latent KV rows and window rows: float32 N(0, 1), d_qk channels;
+  * indexer queries and keys: integers uniform in [-4, 4] stored as E4M3
+    bytes (exact, via torch's float8_e4m3fn cast of small integers);
+  * indexer head weights: float32 N(0, 1);
+  * attention queries: float32 N(0, 1);
+  * every sequence has the full context (ctx_len = N) and a full window.
+"""
+
+from dataclasses import dataclass, field
+
+import torch
+
+ROLE = {
+    "kv": 1, "k_idx": 2, "q_idx": 3, "w": 4, "q": 5, "swa": 6, "sink": 7,
+}
+
+
+def _gen(seed, layer, role, device):
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(layer) * 10_007 + ROLE[role]) & 0x7FFF_FFFF_FFFF)
+    return g
+
+
+def normal_f32(shape, seed, layer, role, device="cpu"):
+    g = _gen(seed, layer, role, device)
+    return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+
+def int_e4m3(shape, seed, layer, role, lo=-4, hi=4, device="cpu"):
+    """E4M3 bytes of integers drawn uniformly from [lo, hi] (exactly representable)."""
+    g = _gen(seed, layer, role, device)
+    v = torch.randint(lo, hi + 1, shape, generator=g, device=device, dtype=torch.int32)
+    return v.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    B: int            # sequences
+    N: int            # context tokens per sequence
+    H: int            # attention query heads
+    d_qk: int         # latent row width (nope + rope)
+    d_v: int          # value width (first d_v channels of the row)
+    H_I: int          # indexer heads
+    D_I: int          # indexer head dim
+    K: int            # Top-K
+    W: int = 128      # sliding window
+    Tq: int = 1       # query tokens per sequence
+    layers: list = field(default_factory=lambda: ["full"])
+    pool_block: int = 0
+    pool_nblocks: int = 0
+    softmax_scale: float = 0.0
+
+    def __post_init__(self):
+        if self.softmax_scale == 0.0:
+            self.softmax_scale = 1.0 / (576.0 ** 0.5)
+
+
+# The five measured/parity workloads.
+WORKLOADS = {
+    "tiny": Workload("tiny: B1 x 4096 ctx, Full, 16 heads, indexer 4x64, top-256", 0,
+                     B=1, N=4096, H=16, d_qk=576, d_v=512, H_I=4, D_I=64, K=256),
+    "decode64k": Workload("decode: B64 x 64K ctx, Full, 64 heads, indexer 8x128, top-2048", 1,
+                          B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048),
+    "group128k": Workload("group: B16 x 128K ctx, Full -> Reindex -> Reuse, top-2048", 2,
+                          B=16, N=131072, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048,
+                          layers=["full", "reindex", "reuse"]),
+    "hier1m": Workload("hierarchical: B4 x 1M ctx, Full + 9 pool layers, pool 2048x8, top-2048", 3,
+                       B=4, N=1 << 20, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048,
+                       layers=["full"] + ["pool"] * 9, pool_block=8, pool_nblocks=2048),
+    "prefill256k": Workload("prefill: B1, 4096 new tokens on 256K ctx, causal, top-2048", 4,
+                            B=1, N=262144 + 4096, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048,
+                            Tq=4096),
+    # The pages' own shapes: 512-wide K=V row, indexer 32 x 128, top-512.
+    "pages512": Workload("pages' shape: B2 x 8192 ctx, d 512 (K=V), indexer 32x128, top-512", 5,
+                         B=2, N=8192, H=64, d_qk=512, d_v=512, H_I=32, D_I=128, K=512,
+                         softmax_scale=1.0 / (512.0 ** 0.5)),
+}
+
+
+def decode_layer_inputs(wl, layer, device="cpu", seqs=None):
+    """Per-layer query-side inputs of a decode workload (fresh for every layer).
+
+    Returns dict: q_idx [B][Tq][H_I][D_I] u8, w [B][Tq][H_I] f32,
+    q [B][Tq][H][d_qk] f32, swa_x [B][W][d_qk] f32 (window rows before
+    quantisation).  `seqs` restricts to a subset of sequences (same values as
+    in the full draw).
+    """
+    B, Tq = wl.B, wl.Tq
+    d = {
+        "q_idx": int_e4m3((B, Tq, wl.H_I, wl.D_I), wl.seed, layer, "q_idx", device=device),
+        "w": normal_f32((B, Tq, wl.H_I), wl.seed, layer, "w", device=device),
+        "q": normal_f32((B, Tq, wl.H, wl.d_qk), wl.seed, layer, "q", device=device),
+        "swa_x": normal_f32((B, wl.W + Tq - 1, wl.d_qk), wl.seed, layer, "swa", device=device),
+    }
+    if seqs is not None:
+        d = {k: v[seqs] for k, v in d.items()}
+    return d
+
+
+def shared_cache_inputs(wl, device="cpu"):
+    """Shared caches of a workload: kv_x [B][N][d_qk] f32 rows, k_idx [B][N][D_I] u8."""
+    return {
+        "kv_x": normal_f32((wl.B, wl.N, wl.d_qk), wl.seed, 0, "kv", device=device),
+        "k_idx": int_e4m3((wl.B, wl.N, wl.D_I), wl.seed, 0, "k_idx", device=device),
+    }

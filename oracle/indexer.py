@@ -1,0 +1,74 @@
+"""Lightning-style indexer scores (oracle; test infrastructure).
+
+[map] "Checked in its code", row "Indexer-selected sparse attention": a
+dedicated indexer with its own heads and head dim scores past tokens and each
+query attends only to the indexer's top-k tokens, following the DeepSeek
+Sparse Attention lightning-indexer pattern; [facts] token selection: 32 heads
+x 128, top-512, and the indexer K cache holds one key row of index_head_dim
+per token, shared by all indexer heads.
+
+The pages print no formula.  Reading: the published lightning-indexer form
+    I(t, j) = sum_h  w[t, h] * ReLU( q[t, h, :] . k[j, :] )
+with per-query, per-head float32 weights w.  To make the result a single
+well-defined float32 value, the sum is evaluated in a fixed order:
+    d_h = q_h . k_j            exact (float64 holds every E4M3 product and
+                                the sum of up to 2^10 of them exactly)
+    r_h = float32(max(d_h, 0))
+    s   = +0.0f; for h = 0, 1, ..., H-1:  s = fl32(s + fl32(w_h * r_h))
+with every float32 operation rounded to nearest even and no fused
+multiply-add.  NumPy float32 array arithmetic performs exactly these
+roundings.
+
+Visibility: token j is visible to a query at position p of sequence b when
+j < ctx_len[b] and (no positions given, or j <= p).  Invisible tokens get
+score -inf here and are never selected.
+
+Parity: pinned by brute-force pure-Python loops on tiny inputs, by an int64
+recomputation of the dots, and by dyadic weights (k/64) that make every
+partial sum exact so the result must equal the real-number sum
+(tests/test_oracle_indexer.py).
+"""
+
+import numpy as np
+
+from .formats import e4m3fn_decode
+
+
+def head_dots(q_bytes, k_bytes):
+    """Exact dots d[h, j] = q_h . k_j for E4M3 bytes q [H][D], k [N][D] -> float64 [H][N]."""
+    q = e4m3fn_decode(np.asarray(q_bytes, dtype=np.uint8))
+    k = e4m3fn_decode(np.asarray(k_bytes, dtype=np.uint8))
+    return q @ k.T
+
+
+def combine_heads(d, w):
+    """Fixed-order float32 head sum of w_h * ReLU(d_h); d float64 [H][N], w float32 [H] -> float32 [N]."""
+    w = np.asarray(w, dtype=np.float32)
+    r = np.maximum(d, 0.0).astype(np.float32)
+    s = np.zeros(d.shape[1], dtype=np.float32)
+    for h in range(d.shape[0]):
+        s = (s + (w[h] * r[h]).astype(np.float32)).astype(np.float32)
+    return s
+
+
+def index_scores(q_bytes, w, k_bytes, n_visible):
+    """Scores of the first n_visible keys for one query row.
+
+    q_bytes [H][D] u8 (E4M3), w [H] f32, k_bytes [N][D] u8 (E4M3).
+    Returns float32 [N] with -inf at positions >= n_visible.
+    """
+    k_bytes = np.asarray(k_bytes)
+    n = k_bytes.shape[0]
+    nv = max(0, min(int(n_visible), n))
+    s = np.full(n, -np.inf, dtype=np.float32)
+    if nv > 0:
+        s[:nv] = combine_heads(head_dots(q_bytes, k_bytes[:nv]), w)
+    return s
+
+
+def visible_count(ctx_len, q_pos=None):
+    """Length of the visible prefix for a query: min(ctx_len, q_pos + 1)."""
+    n = int(ctx_len)
+    if q_pos is not None:
+        n = min(n, int(q_pos) + 1)
+    return max(n, 0)

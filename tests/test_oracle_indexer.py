@@ -1,0 +1,77 @@
+"""Pins for oracle.indexer: exact dots, fixed-order float32 head sum, visibility."""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle import indexer as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ints_to_e4m3(v):
+    return torch.tensor(np.asarray(v, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_head_dots_equal_int64_dots():
+    rng = np.random.default_rng(0)
+    qi = rng.integers(-4, 5, (8, 128))
+    ki = rng.integers(-4, 5, (700, 128))
+    d = I.head_dots(_ints_to_e4m3(qi), _ints_to_e4m3(ki))
+    want = qi.astype(np.int64) @ ki.astype(np.int64).T
+    assert np.array_equal(d, want.astype(np.float64))
+
+
+def test_head_dots_exact_for_general_e4m3():
+    # Arbitrary finite E4M3 values: float64 must hold the exact rational dot.
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 256, (3, 32))
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    kc = rng.integers(0, 256, (5, 32))
+    kc[(kc & 0x7F) == 0x7F] = 0x38
+    d = I.head_dots(codes.astype(np.uint8), kc.astype(np.uint8))
+    qv = torch.tensor(codes.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    kv = torch.tensor(kc.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    for h in range(3):
+        for j in range(5):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qv[h], kv[j]))
+            assert Fraction(d[h, j]) == exact
+
+
+def test_head_sum_order_golden():
+    for line in open(os.path.join(GOLDEN, "indexer_order.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        w, d, want = [p.split() for p in line.split(";")]
+        w = np.array([float(x) for x in w], dtype=np.float32)
+        d = np.array([[float(x)] for x in d], dtype=np.float64)
+        got = I.combine_heads(d, w)
+        assert got.dtype == np.float32
+        assert got[0] == np.float32(float(want[0])), (line, got)
+
+
+def test_dyadic_weights_give_the_exact_real_sum():
+    rng = np.random.default_rng(2)
+    qi = rng.integers(-4, 5, (8, 128))
+    ki = rng.integers(-4, 5, (300, 128))
+    w = (rng.integers(-64, 65, 8) / 64.0).astype(np.float32)
+    s = I.index_scores(_ints_to_e4m3(qi), w, _ints_to_e4m3(ki), 300)
+    for j in range(300):
+        exact = sum(Fraction(float(w[h])) * max(int(qi[h] @ ki[j]), 0) for h in range(8))
+        assert Fraction(float(s[j])) == exact
+
+
+def test_visibility_prefix():
+    rng = np.random.default_rng(3)
+    q = _ints_to_e4m3(rng.integers(-4, 5, (4, 64)))
+    k = _ints_to_e4m3(rng.integers(-4, 5, (50, 64)))
+    w = rng.standard_normal(4).astype(np.float32)
+    s = I.index_scores(q, w, k, 37)
+    assert np.all(np.isneginf(s[37:])) and np.all(np.isfinite(s[:37]))
+    full = I.index_scores(q, w, k, 50)
+    assert np.array_equal(s[:37], full[:37])
+    assert I.visible_count(100, None) == 100
+    assert I.visible_count(100, 41) == 42
+    assert I.visible_count(30, 41) == 30
