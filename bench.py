@@ -1,0 +1,293 @@
+"""CSA2 hot-path benchmark on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the hot path over one batch of synthetic input with
+every cache resident in HBM:
+  decode64k   (default) one Full-mode decode layer: indexer scores + exact
+              Top-K over all 64K tokens of 64 sequences, then sparse FP4 +
+              FP8-window attention of 64 heads;
+  tiny        the same at 1 x 4096 (a parity-sized case);
+  group128k   Full -> Reindex -> Reuse layers over 16 x 128K;
+  hier1m      Full layer with the 2048 x 8 candidate pool + 9 pool layers, 4 x 1M;
+  prefill256k one causal chunk of 4096 queries on a 256K cache.
+Prints one JSON line: decode queries/s, algorithmic HBM GB/s, the roofline
+of the dominant kernel (HIP events around each library launch inside the
+timed region) and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% peak), 64K–1M ctx"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode64k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=0, help="sequences timed for the CPU baseline (0 = auto)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (for counter calibration) and exit")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------ byte model ---
+
+def layer_bytes(wl, kind, pool_cap=0):
+    """Algorithmic HBM bytes per query row of one layer (what the method must move)."""
+    d, K, W, H = wl.d_qk, wl.K, wl.W, wl.H
+    row = d // 2 + d // 16            # FP4 main row: codes + E4M3 scales
+    swa = d + d // 32                 # window row: E4M3 values + E8M0 scales
+    attn = K * row + W * swa + 4 * H * d + 4 * H * wl.d_v
+    idx_q = wl.H_I * wl.D_I + 4 * wl.H_I
+    if kind in ("full", "reindex"):
+        b = wl.D_I * wl.N + idx_q + 8 * K + attn
+        if wl.pool_block:
+            b += 4 * wl.pool_nblocks * wl.pool_block        # pool write
+        return b
+    if kind == "reuse":
+        return 4 * K + attn
+    if kind == "pool":
+        return wl.D_I * pool_cap + 4 * pool_cap + idx_q + 8 * K + attn
+    raise ValueError(kind)
+
+
+# ------------------------------------------------------------- workloads ---
+
+class Case:
+    """Resident inputs and the step function of one workload."""
+
+    def __init__(self, wl, dev):
+        import torch
+        import fp4_kv_cache_index_amd as csa2
+        from fp4_kv_cache_index_amd import inputs
+        self.wl, self.dev, self.csa2, self.torch = wl, dev, csa2, torch
+        B, N, d = wl.B, wl.N, wl.d_qk
+        # Shared caches: FP4 main rows in the pages' interleaved entry layout.
+        self.cache = torch.empty(B, N, d // 2 + d // 16, dtype=torch.uint8, device=dev)
+        self.codes, self.scales = self.cache[..., : d // 2], self.cache[..., d // 2:]
+        for b in range(B):   # quantise one sequence at a time (bounded temporary)
+            x = inputs.kv_rows_seq(wl, b, device=dev)
+            csa2.kv_fp4_quantize(x, codes=self.codes[b], scales=self.scales[b])
+            del x
+        self.k_idx = inputs.int_e4m3((B, N, wl.D_I), wl.seed, 0, "k_idx", device=dev)
+        self.ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
+        self.swa_len = torch.full((B,), wl.W, dtype=torch.int32, device=dev)
+        self.layers = []
+        for li, kind in enumerate(wl.layers):
+            lay = inputs.decode_layer_inputs(wl, li, device=dev)
+            sv, ss = csa2.swa_fp8_quantize(lay["swa_x"])
+            ent = {"kind": kind, "q_idx": lay["q_idx"], "w": lay["w"], "sv": sv, "ss": ss,
+                   "q": lay["q"] if wl.Tq > 1 else lay["q"][:, 0].contiguous()}
+            self.layers.append(ent)
+        if wl.Tq > 1:
+            base = N - wl.Tq
+            self.q_pos = (torch.arange(wl.Tq, dtype=torch.int32, device=dev) + base).repeat(B, 1).contiguous()
+            self.swa_pos0 = torch.full((B,), base - wl.W + 1, dtype=torch.int32, device=dev)
+        else:
+            self.q_pos = None
+        # Workspaces and outputs, allocated once.
+        rows = B * wl.Tq
+        pb, nb = (wl.pool_block, wl.pool_nblocks) if wl.pool_block else (0, 0)
+        self.ws_idx = self._ws(csa2.csa2_index_score_topk_workspace_size(B, wl.Tq, N, wl.K, pb, nb))
+        self.ws_attn = self._ws(csa2.csa2_sparse_attn_prefill_workspace_size(B, wl.Tq, wl.H, wl.d_v, wl.K, wl.W)
+                                if wl.Tq > 1 else csa2.csa2_sparse_attn_decode_workspace_size(B, wl.H, wl.d_v, wl.K,
+                                                                                            wl.W))
+        self.pool_cap = nb * pb
+        self.ws_pool = self._ws(csa2.csa2_hier_pool_topk_workspace_size(B, 1, self.pool_cap, wl.K)) if pb else None
+        self.topk = [torch.empty(B, wl.Tq, wl.K, dtype=torch.int32, device=dev) for _ in wl.layers]
+        self.out = torch.empty(rows * wl.H * wl.d_v, dtype=torch.float32, device=dev)
+        if pb:
+            self.pool_idx = torch.empty(B, 1, self.pool_cap, dtype=torch.int32, device=dev)
+            self.pool_len = torch.empty(B, 1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    def _ws(self, n):
+        t = self.torch.empty(int(n) + 256, dtype=self.torch.uint8, device=self.dev)
+        off = (-t.data_ptr()) % 256
+        return t[off:off + int(n)]
+
+    def step(self):
+        wl, csa2 = self.wl, self.csa2
+        prev = None
+        for li, L in enumerate(self.layers):
+            kind = L["kind"]
+            if kind in ("full", "reindex"):
+                extra = {}
+                if wl.pool_block and li == 0:
+                    extra = dict(pool_block=wl.pool_block, pool_nblocks=wl.pool_nblocks,
+                                 out={"topk_idx": self.topk[li], "pool_idx": self.pool_idx, "pool_len": self.pool_len})
+                else:
+                    extra = dict(out={"topk_idx": self.topk[li]})
+                csa2.csa2_index_score_topk(L["q_idx"], L["w"], self.k_idx, self.ctx, wl.K, q_pos=self.q_pos,
+                                           workspace=self.ws_idx, **extra)
+                idx = self.topk[li]
+            elif kind == "pool":
+                csa2.csa2_hier_pool_topk(L["q_idx"], L["w"], self.k_idx, self.pool_idx, self.pool_len, wl.K,
+                                         workspace=self.ws_pool, out={"topk_idx": self.topk[li]})
+                idx = self.topk[li]
+            elif kind == "reuse":
+                idx = prev
+            else:
+                raise ValueError(kind)
+            if wl.Tq > 1:
+                out = self.out.view(wl.B, wl.Tq, wl.H, wl.d_v)
+                csa2.csa2_sparse_attn_prefill(L["q"], self.codes, self.scales, idx, self.ctx, self.q_pos, L["sv"],
+                                              L["ss"], self.swa_pos0, wl.W, wl.softmax_scale, d_v=wl.d_v,
+                                              workspace=self.ws_attn, out=out)
+            else:
+                out = self.out.view(wl.B, wl.H, wl.d_v)
+                csa2.csa2_sparse_attn_decode(L["q"], self.codes, self.scales, idx[:, 0], self.ctx, L["sv"], L["ss"],
+                                             self.swa_len, wl.softmax_scale, d_v=wl.d_v, workspace=self.ws_attn,
+                                             out=out)
+            prev = idx
+
+    def step_bytes(self):
+        wl = self.wl
+        per_row = sum(layer_bytes(wl, L["kind"], self.pool_cap) for L in self.layers)
+        return per_row * wl.B * wl.Tq
+
+
+# ----------------------------------------------------------- CPU oracle ---
+
+def cpu_baseline(case, n_seq):
+    """Time the oracle's step (scores + Top-K + attention) on n_seq sequences of
+    the first layer; cache quantisation of the rows it reads is set-up."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import indexer as I
+    from oracle import quant as Q
+    from oracle.topk import topk_select
+    from fp4_kv_cache_index_amd import inputs
+    wl = case.wl
+    L = case.layers[0]
+    h = lambda t: t.detach().cpu().numpy()
+    t_tot = 0.0
+    rows = 0
+    for b in range(n_seq):
+        k_idx = h(case.k_idx[b])
+        kv_x = h(inputs.kv_rows_seq(wl, b, device=case.dev))
+        qi, w, q = h(L["q_idx"][b]), h(L["w"][b]), h(L["q"][b])
+        swa_x = h(inputs.decode_layer_inputs(wl, 0, device=case.dev)["swa_x"][b])
+        for t in range(wl.Tq if wl.Tq == 1 else 1):
+            t0 = time.perf_counter()
+            s = I.index_scores(qi[t], w[t], k_idx, wl.N)
+            idx, _ = topk_select(s, wl.N, wl.K)
+            t1 = time.perf_counter()
+            # set-up: the oracle's own cache rows for the selected ids and the window
+            sel = idx[idx >= 0]
+            codes = np.zeros((wl.N, wl.d_qk // 2), np.uint8)
+            scales = np.zeros((wl.N, wl.d_qk // 16), np.uint8)
+            codes[sel], scales[sel] = Q.fp4_quantize(kv_x[sel])
+            v8, s8 = Q.mxfp8_quantize(swa_x[: wl.W])
+            t2 = time.perf_counter()
+            A.sparse_attn_decode_row(q if q.ndim == 2 else q[t], codes, scales, idx, wl.N, v8, s8, wl.W, wl.d_qk,
+                                     wl.d_v, wl.softmax_scale)
+            t3 = time.perf_counter()
+            t_tot += (t1 - t0) + (t3 - t2)
+            rows += 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    return {"value": rows / t_tot, "unit": "queries/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{rows} query row(s) of layer 0 of {wl.name} (scores + Top-K + attention; "
+                      f"host has {os.cpu_count()} logical CPUs, BLAS threads {blas})",
+            "seconds": round(t_tot, 3)}
+
+
+# ------------------------------------------------------------------ main ---
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp4_kv_cache_index_amd as csa2
+    from fp4_kv_cache_index_amd import inputs
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+    wl = inputs.WORKLOADS[args.workload]
+    print(f"[bench] building inputs for {wl.name}", file=sys.stderr, flush=True)
+    case = Case(wl, dev)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        case.step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with csa2.KernelTrace(capacity=64 * args.steps * max(1, len(wl.layers))) as tr:
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            case.step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    launches = tr.durations_ms()
+    tr.close()
+    per_kernel = {}
+    for name, t in launches:
+        s = per_kernel.setdefault(name, [0.0, 0])
+        s[0] += t
+        s[1] += 1
+    qps = wl.B * wl.Tq / (ms * 1e-3)
+    step_bytes = case.step_bytes()
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    # Dominant kernel: the indexer scan over the key cache.
+    dom = "index_score"
+    dom_ms = per_kernel[dom][0] / per_kernel[dom][1] if dom in per_kernel else float("nan")
+    n_scan_layers = sum(1 for L in case.layers if L["kind"] in ("full", "reindex"))
+    scan_bytes = (wl.D_I * wl.N + wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B * wl.Tq if wl.Tq == 1 else \
+        wl.D_I * wl.N * wl.B + (wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B * wl.Tq
+    achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+            "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_seq = args.cpu_sample or (1 if wl.N >= (1 << 20) else 2)
+        print(f"[bench] CPU oracle on {n_seq} sequence(s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, n_seq)
+    line = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8+fp16 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.N, "query_tokens": wl.Tq,
+                   "heads": wl.H, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "window": wl.W,
+                   "layers": wl.layers, "parallelism": "single GPU"},
+        "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "step_bytes": step_bytes,
+        "kernels_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in per_kernel.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

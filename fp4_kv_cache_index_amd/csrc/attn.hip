@@ -1,0 +1,357 @@
+// Sparse MLA attention over the Top-K FP4 main-KV rows plus the FP8 window.
+//
+// What it computes (DeepSeek-V4.1-Flash techniques map, "Checked in its
+// code": multi-head latent attention with a single latent KV head and a
+// learnable per-head sink logit in the sparse-MLA softmax denominator; fact
+// sheet: one shared K=V entry per token, a 128-token window per layer; blog,
+// CSA2 paragraph: attention runs over the indexer's Top-K entries of the FP4
+// main cache): for each query row and head h, softmax over the selected
+// entries (and the sink) of scale * q_h . k_e, applied to v_e = the first
+// d_v channels of the same row.
+//
+// gfx950 mapping.  A workgroup holds one query row (all H heads, one wave per
+// 16 heads) and a contiguous split of its entry list (Top-K rows, then the
+// window rows).  Per chunk of 32 entries it gathers the rows by index
+// (coalesced: consecutive lanes read consecutive 8-byte code groups of a
+// row), dequantises them into LDS as fp16 -- exact, since E2M1 x E4M3 has at
+// most 6 significant bits within [2^-10, 2688] -- and runs
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16 (q rounded to fp16 once),
+//   online softmax in fp32 (exp2 domain),
+//   O  += P V     on the same instruction, P taken straight from the S^T
+//                 accumulators (their lane layout is the A-operand layout of
+//                 P once the k index is permuted identically for V).
+// Splits write unnormalised partial (O, m, l); a combine kernel merges them
+// with the log-sum-exp rule and adds the sink.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+
+constexpr int kChunk = 32;           // entries per LDS chunk
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int DQK>
+struct AttnShape {
+  static constexpr int G16 = DQK / 16;          // 16-channel groups per row
+  static constexpr int KQ = DQK / 32;           // MFMA k-steps for S = K Q^T
+  static constexpr int PITCH = DQK + 8;         // fp16 row pitch in LDS (bank spread)
+};
+
+__device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  v8h r;
+  r[0] = (_Float16)a.x; r[1] = (_Float16)a.y; r[2] = (_Float16)a.z; r[3] = (_Float16)a.w;
+  r[4] = (_Float16)b.x; r[5] = (_Float16)b.y; r[6] = (_Float16)b.z; r[7] = (_Float16)b.w;
+  return r;
+}
+
+constexpr int kMaxSpan = 1024;      // entries per split (ids staged in LDS)
+constexpr int kAttnThreads = 256;   // 4 waves; wave w owns heads 16w .. 16w+15
+
+template <int DQK, int DV>
+__global__ void __launch_bounds__(kAttnThreads)
+sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
+                         float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using S = AttnShape<DQK>;
+  constexpr int NT = DV / 16;                   // output tiles per wave
+  constexpr int TPT = (kChunk * S::G16 + kAttnThreads - 1) / kAttnThreads;
+  __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * S::PITCH];
+  __shared__ int32_t eid[kMaxSpan];             // main: token id; window: window row; -1 = skip
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int64_t row = blockIdx.y;
+  const int split = blockIdx.x;
+  const int64_t b = row / a.Tq;
+  const int H = a.H;
+  const int K = a.k_top;
+  const int E = K + a.W;
+  const int e_begin = split * span;
+  int e_end = e_begin + span;
+  if (e_end > E) e_end = E;
+
+  const int64_t ctx = a.ctx_len[b];
+  int64_t swa_r0 = 0, n_swa = 0;
+  if (prefill) {
+    int64_t p = a.q_pos[row];
+    int64_t p0 = a.swa_pos0[b];
+    int64_t lo = p - a.W + 1 > p0 ? p - a.W + 1 : p0;
+    int64_t hi = p < p0 + a.swa_rows - 1 ? p : p0 + a.swa_rows - 1;
+    swa_r0 = lo - p0;
+    n_swa = hi >= lo ? hi - lo + 1 : 0;
+  } else if (a.W > 0) {
+    int64_t sl = a.swa_len[b];
+    n_swa = sl < 0 ? 0 : (sl > a.W ? a.W : sl);
+  }
+  const int32_t* idx_row = a.topk_idx + row * (int64_t)K;
+  for (int e = e_begin + threadIdx.x; e < e_end; e += kAttnThreads) {
+    int32_t v = -1;
+    if (e < K) {
+      int64_t id = idx_row[e];
+      if (id >= 0 && id < ctx) v = (int32_t)id;
+    } else {
+      int64_t wv = e - K;
+      if (wv < n_swa) v = (int32_t)(swa_r0 + wv);
+    }
+    eid[e - e_begin] = v;
+  }
+
+  // q fragments of this wave's 16 heads: lane holds head 16*wave + c16,
+  // dims 32*i + 8*g .. +8 of k-step i (the B operand of S^T = K Q^T).
+  const bool active = 16 * wave < H;
+  const int head_b = 16 * wave + c16;
+  v8h qf[S::KQ];
+  if (active) {
+    const float* qrow = a.q + (row * H + head_b) * (int64_t)DQK;
+#pragma unroll
+    for (int i = 0; i < S::KQ; ++i) qf[i] = load_f32x8_as_f16(qrow + 32 * i + 8 * g);
+  }
+  const float sl2 = a.softmax_scale * kLog2e;
+  const uint8_t* codes_b = a.kv_codes + b * a.c_bstride;
+  const uint8_t* scales_b = a.kv_scales + b * a.s_bstride;
+  const uint8_t* sv_b = a.swa_vals ? a.swa_vals + b * a.sv_bstride : nullptr;
+  const uint8_t* ss_b = a.swa_scales ? a.swa_scales + b * a.ss_bstride : nullptr;
+
+  v4f o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+  __syncthreads();
+
+  for (int c0 = e_begin; c0 < e_end; c0 += kChunk) {
+    // ---- gather: task = (entry, 16-channel group), group fastest; all of a
+    // thread's loads are issued before any conversion.
+    uint32_t raw[TPT][4];
+    uint32_t sraw[TPT];
+    int kind[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int task = threadIdx.x + u * kAttnThreads;
+      kind[u] = 0;
+      if (task < kChunk * S::G16) {
+        const int e = task / S::G16;
+        const int gq = task - e * S::G16;
+        const int ce = c0 + e;
+        const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
+        if (id >= 0 && ce < K) {
+          const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 8 * gq);
+          raw[u][0] = cp[0];
+          raw[u][1] = cp[1];
+          sraw[u] = scales_b[(int64_t)id * a.s_rstride + gq];
+          kind[u] = 1;
+        } else if (id >= 0) {
+          const uint32_t* vp = reinterpret_cast<const uint32_t*>(sv_b + (int64_t)id * a.sv_rstride + 16 * gq);
+          raw[u][0] = vp[0]; raw[u][1] = vp[1]; raw[u][2] = vp[2]; raw[u][3] = vp[3];
+          sraw[u] = ss_b[(int64_t)id * a.ss_rstride + (gq >> 1)];
+          kind[u] = 2;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int task = threadIdx.x + u * kAttnThreads;
+      if (task >= kChunk * S::G16) break;
+      const int e = task / S::G16;
+      const int gq = task - e * S::G16;
+      uint32_t hv[8];
+      if (kind[u] == 1) {
+        _Float16 sh = (_Float16)e4m3_to_f32(sraw[u]);
+        v2h s2 = {sh, sh};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t byte = (raw[u][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          uint32_t lo = byte & 0xFu, hi = byte >> 4;
+          uint32_t bits = e2m1_mag_to_f16_bits(lo & 7u) | ((lo & 8u) << 12) |
+                          ((e2m1_mag_to_f16_bits(hi & 7u) | ((hi & 8u) << 12)) << 16);
+          v2h v = __builtin_bit_cast(v2h, bits);
+          v = v * s2;   // exact: at most 6 significant bits, within fp16 range
+          hv[i] = __builtin_bit_cast(uint32_t, v);
+        }
+      } else if (kind[u] == 2) {
+        float sc = e8m0_to_f32(sraw[u]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t wv = raw[u][i >> 1] >> (16 * (i & 1));
+          v2h v;
+          v[0] = (_Float16)(e4m3_to_f32(wv & 0xFFu) * sc);
+          v[1] = (_Float16)(e4m3_to_f32((wv >> 8) & 0xFFu) * sc);
+          hv[i] = __builtin_bit_cast(uint32_t, v);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = 0u;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(kt + e * S::PITCH + 16 * gq);
+      dst[0] = uint4{hv[0], hv[1], hv[2], hv[3]};
+      dst[1] = uint4{hv[4], hv[5], hv[6], hv[7]};
+    }
+    __syncthreads();
+    if (active) {
+      // ---- S^T = K Q^T for 2 tiles of 16 entries
+      v4f st[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        const _Float16* krow = kt + (16 * t + c16) * S::PITCH + 8 * g;
+#pragma unroll
+        for (int i = 0; i < S::KQ; ++i) {
+          v8h ka = *reinterpret_cast<const v8h*>(krow + 32 * i);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[i], acc, 0, 0, 0);
+        }
+        st[t] = acc;   // st[t][r] = S^T[entry 16t + 4g + r][head c16]
+      }
+      // ---- online softmax (log2 domain), per head = lane & 15
+      float z[8];
+      float cmax = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int ce = c0 + 16 * t + 4 * g + r;
+          bool ok = ce < e_end && eid[ce - e_begin] >= 0;
+          float v = ok ? st[t][r] * sl2 : -__builtin_inff();
+          z[4 * t + r] = v;
+          cmax = fmaxf(cmax, v);
+        }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m_run, cmax);
+      float alpha = 1.0f;
+      float psum = 0.0f;
+      v8h pa;
+      if (m_new == -__builtin_inff()) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pa[i] = (_Float16)0.0f;
+      } else {
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float p = __builtin_amdgcn_exp2f(z[i] - m_new);
+          psum += p;
+          pa[i] = (_Float16)p;
+        }
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // ---- rescale O rows (heads 4g + r) and accumulate P V
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
+      const _Float16* vb = kt + c16;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        v4f acc = o[n];
+        acc[0] *= al[0]; acc[1] *= al[1]; acc[2] *= al[2]; acc[3] *= al[3];
+        v8h vf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          int e = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
+          vf[j] = vb[e * S::PITCH + 16 * n];
+        }
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // ---- partial results: l summed over the 4 lane groups of a head
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const int64_t pbase = (row * splits + split) * (int64_t)H;
+  if (g == 0) {
+    part_ml[(pbase + head_b) * 2 + 0] = m_run;
+    part_ml[(pbase + head_b) * 2 + 1] = l_tot;
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int h = 16 * wave + 4 * g + r;
+      part_o[(pbase + h) * DV + 16 * n + c16] = o[n][r];
+    }
+}
+
+// Merge split partials: out = sum_s O_s 2^(m_s - M) / L, L = sum_s l_s 2^(m_s - M)
+// (+ 2^(sink*log2e - M)), lse = (M + log2 L) ln 2.
+template <int DV>
+__global__ void __launch_bounds__(128)
+sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H,
+                           const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse) {
+  const int64_t rh = blockIdx.x;            // row * H + h
+  const int h = (int)(rh % H);
+  const int64_t row = rh / H;
+  float M = -__builtin_inff();
+  const float sk = sink ? sink[h] * kLog2e : -__builtin_inff();
+  for (int s = 0; s < splits; ++s) {
+    float m = part_ml[((row * splits + s) * H + h) * 2];
+    M = fmaxf(M, m);
+  }
+  M = fmaxf(M, sk);
+  float L = 0.0f;
+  float acc[DV / 128];
+#pragma unroll
+  for (int i = 0; i < DV / 128; ++i) acc[i] = 0.0f;
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < splits; ++s) {
+      const int64_t pi = (row * splits + s) * H + h;
+      float m = part_ml[pi * 2];
+      if (m == -__builtin_inff()) continue;
+      float wgt = __builtin_amdgcn_exp2f(m - M);
+      L += part_ml[pi * 2 + 1] * wgt;
+#pragma unroll
+      for (int i = 0; i < DV / 128; ++i) acc[i] += part_o[pi * DV + threadIdx.x + 128 * i] * wgt;
+    }
+    if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int i = 0; i < DV / 128; ++i) out[rh * DV + threadIdx.x + 128 * i] = acc[i] * inv;
+  if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+}
+
+int attn_num_splits(int64_t rows, int k_top, int W) {
+  int E = k_top + W;
+  int max_splits = (E + 63) / 64;
+  int min_splits = (E + kMaxSpan - 1) / kMaxSpan;
+  int64_t want = (2LL * device_cu_count() + rows - 1) / rows;
+  int s = (int)(want < 1 ? 1 : (want > max_splits ? max_splits : want));
+  if (s < min_splits) s = min_splits;
+  return s < 1 ? 1 : s;
+}
+
+size_t attn_ws_bytes(int64_t rows, int H, int d_v, int splits) {
+  size_t po = sizeof(float) * (size_t)rows * splits * H * d_v;
+  size_t pm = sizeof(float) * (size_t)rows * splits * H * 2;
+  return ((po + 255) & ~(size_t)255) + ((pm + 255) & ~(size_t)255);
+}
+
+template <int DQK, int DV>
+static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.Tq;
+  const int splits = attn_num_splits(rows, a.k_top, a.W);
+  const int E = a.k_top + a.W;
+  int span = (E + splits - 1) / splits;
+  span = (span + kChunk - 1) / kChunk * kChunk;
+  const int real_splits = (E + span - 1) / span;
+  size_t po = sizeof(float) * (size_t)rows * real_splits * a.H * DV;
+  float* part_o = (float*)ws;
+  float* part_ml = (float*)((char*)ws + ((po + 255) & ~(size_t)255));
+  CSA2_LAUNCH("sparse_attn_split", (sparse_attn_split_kernel<DQK, DV>), dim3(real_splits, (unsigned)rows),
+              dim3(kAttnThreads), 0, s, a, prefill ? 1 : 0, real_splits, span, part_o, part_ml);
+  CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV>), dim3((unsigned)(rows * a.H)), dim3(128), 0,
+              s, part_o, part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, bool prefill, void* ws, hipStream_t s) {
+  if (a.d_qk == 576 && a.d_v == 512) return launch_attn_t<576, 512>(a, prefill, ws, s);
+  if (a.d_qk == 512 && a.d_v == 512) return launch_attn_t<512, 512>(a, prefill, ws, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace csa2

@@ -1,0 +1,131 @@
+// Internal (host-side) interface between the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// Kernel launch with the optional per-thread trace (events around the launch).
+struct Trace {
+  hipEvent_t* events = nullptr;
+  const char** names = nullptr;
+  int capacity = 0;
+  int count = 0;
+  bool active = false;
+};
+Trace& thread_trace();
+
+void trace_before(hipStream_t s, const char* name);
+void trace_after(hipStream_t s);
+
+#define CSA2_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                             \
+    ::csa2::trace_before((stream), (name));                                       \
+    hipLaunchKernelGGL(kernel, (grid), (block), (shmem), (stream), __VA_ARGS__);   \
+    ::csa2::trace_after((stream));                                                 \
+  } while (0)
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// ----------------------------------------------------------- quantisers ---
+hipError_t launch_kv_fp4_quantize(const float* x, int64_t n_rows, int d, int64_t x_stride,
+                                  uint8_t* codes, int64_t c_stride, uint8_t* scales, int64_t s_stride,
+                                  hipStream_t s);
+hipError_t launch_swa_fp8_quantize(const float* x, int64_t n_rows, int d, int64_t x_stride,
+                                   uint8_t* vals, int64_t v_stride, uint8_t* scales, int64_t s_stride,
+                                   hipStream_t s);
+
+// --------------------------------------------------------- radix select ---
+// Per-row exact Top-K over u32 keys (larger is better, key 0 = absent) of
+// the first n_valid[row] positions, ties to the lower position, emitted in
+// ascending position order.  Workspace: select_ws_bytes(rows, tiles).
+constexpr int kSelTile = 4096;      // positions per workgroup in the select passes
+constexpr int kDigit1Bits = 12, kDigit2Bits = 12, kDigit3Bits = 8;
+
+struct SelectRowCtl {               // per-row control block (64 bytes)
+  uint32_t arrive[6];               // last-workgroup counters of the passes
+  uint32_t mode;                    // 0 = refine, 1 = take every valid position
+  uint32_t prefix;                  // resolved key prefix so far
+  uint32_t need;                    // how many still to take at/below prefix
+  uint32_t thr;                     // final threshold key T
+  uint32_t need_eq;                 // ties at T to take (lowest positions)
+  uint32_t total;                   // number of positions emitted
+  uint32_t pad[4];
+};
+
+struct SelectWs {
+  SelectRowCtl* ctl;                // [rows]
+  uint32_t* hist1;                  // [rows][4096]
+  uint32_t* hist2;                  // [rows][4096]
+  uint32_t* hist3;                  // [rows][256]
+  uint32_t* tile_gt;                // [rows][tiles]
+  uint32_t* tile_eq;                // [rows][tiles]
+};
+size_t select_ws_bytes(int64_t rows, int64_t tiles);
+SelectWs select_ws_carve(void* base, int64_t rows, int64_t tiles);
+
+// Output modes of the emit pass.
+struct SelectOut {
+  int32_t* idx;                     // [rows][k] (row stride k)
+  float* score;                     // nullable [rows][k]
+  const int32_t* map;               // nullable [rows][map_stride]: emitted id = map[pos]
+  int64_t map_stride;
+  // Pool expansion: when expand > 0 each selected position c (a block)
+  // expands to ids c*expand + u (u < expand, id < expand_limit[row]) at
+  // output slots slot*expand + u; pool_len[row] receives the valid count.
+  int expand;
+  const int32_t* expand_limit;      // [rows] visible token count
+  int32_t* pool_len;                // [rows]
+};
+
+// Clears the control blocks and histograms of `rows` rows.
+hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s);
+// Pass 1 over stored keys (when the producer did not build histogram 1).
+hipError_t select_hist1(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
+                        int64_t rows, int64_t n_max, int k, hipStream_t s);
+// Passes 2..5: refine the threshold and emit the selection.
+hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
+                         int64_t rows, int64_t n_max, int k, const SelectOut& out, hipStream_t s);
+
+// Device-side: resolve digit 1 in the last workgroup of a producer pass.
+// (Declared here for the scoring kernels, defined in select.hip.)
+
+// ------------------------------------------------------------- scoring ---
+struct ScoreArgs {
+  const uint8_t* q_idx; const float* w;
+  const uint8_t* k_idx; int64_t k_bstride, k_rstride;
+  const int32_t* ctx_len; const int32_t* q_pos;
+  int B, Tq, H_I, D_I; int64_t n_max; int k_top;
+  int pool_block, pool_nblocks;
+};
+hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                              const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
+                              const SelectWs* blk, hipStream_t s);
+hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                             int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int32_t* n_valid,
+                             const SelectWs& ws, hipStream_t s);
+
+// ----------------------------------------------------------- attention ---
+struct AttnArgs {
+  const float* q;
+  const uint8_t* kv_codes; int64_t c_bstride, c_rstride;
+  const uint8_t* kv_scales; int64_t s_bstride, s_rstride;
+  const int32_t* topk_idx; int k_top; const int32_t* ctx_len;
+  const int32_t* q_pos;                                  // prefill only (nullable)
+  const uint8_t* swa_vals; int64_t sv_bstride, sv_rstride;
+  const uint8_t* swa_scales; int64_t ss_bstride, ss_rstride;
+  const int32_t* swa_len;                                // decode only
+  const int32_t* swa_pos0; int swa_rows;                 // prefill only
+  int W; const float* sink;
+  int B, Tq, H, d_qk, d_v; float softmax_scale;
+  float* out; float* lse;
+};
+int attn_num_splits(int64_t rows, int k_top, int W);
+size_t attn_ws_bytes(int64_t rows, int H, int d_v, int splits);
+hipError_t launch_sparse_attn(const AttnArgs& a, bool prefill, void* ws, hipStream_t s);
+
+}  // namespace csa2

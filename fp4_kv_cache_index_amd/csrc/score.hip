@@ -1,0 +1,283 @@
+// Indexer scoring: the lightning-style indexer of the DeepSeek-V4.1-Flash
+// techniques map ("Checked in its code", indexer-selected sparse attention):
+// every indexer head h of the query scores each visible key row k_j, and the
+// per-token score is  s_j = sum_h w_h * ReLU(q_h . k_j).  The key cache holds
+// one row of index_head_dim per token (fact sheet, kv_groups: indexer K).
+//
+// gfx950 mapping.  The scan is an HBM stream of the key rows (D_I bytes per
+// token).  The dots run on the FP8 matrix cores (v_mfma_f32_16x16x32_fp8_fp8):
+// A = the query heads (16 rows, padded), B = 16 key rows, K = 32 bytes per
+// instruction.  With integer-valued E4M3 inputs every product and partial sum
+// is an integer below 2^24, so the fp32 accumulation is exact and the order
+// inside the instruction does not matter.  Each lane loads one contiguous
+// D_I/4-byte slice of a key row; the A operand uses the same slice of each
+// query head, so the k-permutation is identical on both sides.  The 16x16
+// results pass through LDS so that every lane owns one token, applies ReLU
+// and the weights, and adds the heads in ascending order with float32
+// roundings and no FMA.  The epilogue also builds the radix-select
+// histogram of the top 12 key bits in LDS, writes the score keys, and (for
+// the hierarchical pool) the per-block maxima and their histogram.
+#include "common.h"
+#include "internal.h"
+#include "select_dev.h"
+
+namespace csa2 {
+
+constexpr int kScanTile = 4096;       // tokens per workgroup of the flat scan
+constexpr int kPoolTile = 512;        // pool positions per workgroup (later layers)
+constexpr int kScanWaves = 4;
+
+template <int CH>
+struct Frag {
+  uint32_t w[CH / 4];
+};
+
+template <int CH>
+__device__ __forceinline__ void load_frag(Frag<CH>& f, const uint8_t* p, bool ok) {
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < CH / 4; ++i) f.w[i] = 0u;
+    return;
+  }
+  if constexpr (CH % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < CH / 16; ++i) {
+      v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i);
+      f.w[4 * i] = v[0]; f.w[4 * i + 1] = v[1]; f.w[4 * i + 2] = v[2]; f.w[4 * i + 3] = v[3];
+    }
+  } else {
+    v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    f.w[0] = v[0]; f.w[1] = v[1];
+  }
+}
+
+__device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+
+// GATHER = false: tokens j = tile positions of the row (flat scan).
+// GATHER = true : position p maps to token pool_idx[row][p] (pool layers).
+template <int DI, int HB, bool GATHER>
+__global__ void __launch_bounds__(256)
+index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+                   const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
+                   const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
+                   const int32_t* __restrict__ pool_idx, const int32_t* __restrict__ pool_len, int pool_cap,
+                   int Tq, int H_I, int64_t n_max, int k_top, int tile,
+                   uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
+                   SelectWs tok,
+                   int pool_block, int nblocks, uint32_t* __restrict__ bkeys, int64_t bkey_stride,
+                   int32_t* __restrict__ nb_valid_out, SelectWs blk) {
+  constexpr int CH = DI / 4;           // bytes of a key row per lane
+  constexpr int KS = DI / 32;          // MFMA k-steps
+  constexpr int HMAX = 16 * HB;
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t bhist[4096];
+  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][64 * HMAX];
+  __shared__ float wsh[HMAX];
+  __shared__ uint32_t flag;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  const int64_t b = row / Tq;
+  const bool pool = pool_block > 0;
+
+  int64_t nv;
+  if (GATHER) {
+    int64_t pl = pool_len[row];
+    nv = pl < 0 ? 0 : (pl > pool_cap ? pool_cap : pl);
+  } else {
+    int64_t c = ctx_len[b];
+    if (q_pos) {
+      int64_t qp = (int64_t)q_pos[row] + 1;
+      if (qp < c) c = qp;
+    }
+    nv = c < 0 ? 0 : (c > n_max ? n_max : c);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    n_valid_out[row] = (int32_t)nv;
+    if (pool) nb_valid_out[row] = (int32_t)((nv + pool_block - 1) / pool_block);
+  }
+
+  for (int i = threadIdx.x; i < 4096; i += 256) {
+    hist[i] = 0u;
+    if (pool) bhist[i] = 0u;
+  }
+  if (threadIdx.x < HMAX) wsh[threadIdx.x] = threadIdx.x < H_I ? w[row * H_I + threadIdx.x] : 0.0f;
+
+  // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
+  const int c16 = lane & 15, g = lane >> 4;
+  long qa[HB][KS];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    int h = c16 + 16 * hb;
+    Frag<CH> f;
+    load_frag<CH>(f, q_idx + (row * H_I + h) * DI + g * CH, h < H_I);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qa[hb][i] = as_long(f.w[2 * i], f.w[2 * i + 1]);
+  }
+  __syncthreads();
+
+  const int64_t tile0 = (int64_t)blockIdx.x * tile;
+  const int pitch = (H_I + 3) & ~3;
+  float* my = dots[wave];
+  const uint8_t* kb = k_idx + b * k_bstride;
+  const int32_t* prow = GATHER ? pool_idx + row * (int64_t)pool_cap : nullptr;
+
+  // Each wave owns tile/4 consecutive positions, 64 per iteration.
+  const int64_t wbase = tile0 + (int64_t)wave * (tile / kScanWaves);
+  int64_t wend = wbase + tile / kScanWaves;
+  if (wend > nv) wend = nv;
+
+  auto frag_ptr = [&](int64_t pos, bool& ok) -> const uint8_t* {
+    ok = pos < wend;
+    int64_t tokid = pos;
+    if (GATHER && ok) tokid = prow[pos];
+    return kb + (ok ? tokid : 0) * k_rstride + g * CH;
+  };
+
+  Frag<CH> cur[4], nxt[4];
+  if (wbase < wend) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bool ok;
+      const uint8_t* p = frag_ptr(wbase + 16 * s + c16, ok);
+      load_frag<CH>(cur[s], p, ok);
+    }
+  }
+  for (int64_t it = wbase; it < wend; it += 64) {
+    const bool more = it + 64 < wend;
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bool ok;
+        const uint8_t* p = frag_ptr(it + 64 + 16 * s + c16, ok);
+        load_frag<CH>(nxt[s], p, ok);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KS; ++i)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[hb][i], as_long(cur[s].w[2 * i], cur[s].w[2 * i + 1]),
+                                                           acc, 0, 0, 0);
+        // acc[r] = dot(head 16*hb + 4*g + r, token 16*s + c16)
+        int h0 = 16 * hb + 4 * g;
+        if (h0 < H_I) *reinterpret_cast<v4f*>(my + (16 * s + c16) * pitch + h0) = acc;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // Lane owns token it + lane.
+    const int64_t j = it + lane;
+    const bool vis = j < wend;
+    float sc = 0.0f;
+    const float* src = my + lane * pitch;
+    for (int h = 0; h < H_I; ++h) {
+      float d = src[h];
+      float r = d > 0.0f ? d : 0.0f;
+      sc = __fadd_rn(sc, __fmul_rn(wsh[h], r));
+    }
+    uint32_t key = vis ? score_key(sc) : 0u;
+    if (vis) {
+      keys[row * key_stride + j] = key;
+      atomicAdd(&hist[key >> 20], 1u);
+    }
+    if (pool) {
+      uint32_t m = key;
+      for (int off = 1; off < pool_block; off <<= 1) {
+        uint32_t o = __shfl_xor(m, off, 64);
+        m = m > o ? m : o;
+      }
+      if (vis && (j % pool_block) == 0) {
+        bkeys[row * bkey_stride + j / pool_block] = m;
+        atomicAdd(&bhist[m >> 20], 1u);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) cur[s] = nxt[s];
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = tok.hist1 + row * 4096;
+  for (int i = threadIdx.x; i < 4096; i += 256)
+    if (hist[i]) atomic_add_agent(gh + i, hist[i]);
+  uint32_t* gbh = pool ? blk.hist1 + row * 4096 : nullptr;
+  if (pool)
+    for (int i = threadIdx.x; i < 4096; i += 256)
+      if (bhist[i]) atomic_add_agent(gbh + i, bhist[i]);
+  if (arrive_last(&tok.ctl[row].arrive[0], gridDim.x, &flag)) {
+    select_resolve1(&tok.ctl[row], gh, (uint32_t)k_top);
+    __syncthreads();
+    if (pool) select_resolve1(&blk.ctl[row], gbh, (uint32_t)nblocks);
+  }
+}
+
+template <int DI, int HB>
+static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                                const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
+                                const SelectWs* blk, hipStream_t s) {
+  int64_t rows = (int64_t)a.B * a.Tq;
+  int64_t tiles = (a.n_max + kScanTile - 1) / kScanTile;
+  if (tiles < 1) tiles = 1;
+  SelectWs bw = blk ? *blk : tok;
+  CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false>), dim3((unsigned)tiles, (unsigned)rows),
+              dim3(256), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
+              (const int32_t*)nullptr, (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, kScanTile, keys, key_stride,
+              n_valid, tok, a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
+  return hipGetLastError();
+}
+
+template <int DI, int HB>
+static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                                int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                                int B, int Tq, int H_I, int k_top, uint32_t* keys, int32_t* n_valid,
+                                const SelectWs& ws, hipStream_t s) {
+  int64_t rows = (int64_t)B * Tq;
+  int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
+  if (tiles < 1) tiles = 1;
+  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
+              0, s, q_idx, w, k_idx, k_bstride, k_rstride, (const int32_t*)nullptr, (const int32_t*)nullptr,
+              pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, (int64_t)pool_cap, n_valid, ws,
+              0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
+  return hipGetLastError();
+}
+
+#define CSA2_DISPATCH_DI_HB(DI_, HB_, CALL)                                       \
+  do {                                                                           \
+    int hb__ = (HB_) <= 16 ? 1 : 2;                                              \
+    switch (DI_) {                                                               \
+      case 32: return hb__ == 1 ? CALL(32, 1) : CALL(32, 2);                      \
+      case 64: return hb__ == 1 ? CALL(64, 1) : CALL(64, 2);                      \
+      case 128: return hb__ == 1 ? CALL(128, 1) : CALL(128, 2);                   \
+      case 256: return hb__ == 1 ? CALL(256, 1) : CALL(256, 2);                   \
+      default: return hipErrorInvalidValue;                                       \
+    }                                                                            \
+  } while (0)
+
+hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                              const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
+                              const SelectWs* blk, hipStream_t s) {
+#define CALL_SCAN(D, H) launch_scan_t<D, H>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
+  CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_SCAN);
+#undef CALL_SCAN
+}
+
+hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
+                             int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int32_t* n_valid,
+                             const SelectWs& ws, hipStream_t s) {
+#define CALL_POOL(D, H) \
+  launch_pool_t<D, H>(q_idx, w, k_idx, k_bstride, k_rstride, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
+                      n_valid, ws, s)
+  CSA2_DISPATCH_DI_HB(D_I, H_I, CALL_POOL);
+#undef CALL_POOL
+}
+
+}  // namespace csa2

@@ -116,3 +116,26 @@ def shared_cache_inputs(wl, device="cpu"):
         "kv_x": normal_f32((wl.B, wl.N, wl.d_qk), wl.seed, 0, "kv", device=device),
         "k_idx": int_e4m3((wl.B, wl.N, wl.D_I), wl.seed, 0, "k_idx", device=device),
     }
+
+
+def random_index_lists(B, K, N, seed, layer=0, device="cpu", n_invalid=0):
+    """Random Top-K-shaped index lists [B][K] int32: distinct ids < N, with the
+    last n_invalid slots of each row replaced by -1 and out-of-range ids."""
+    g = _gen(seed, layer, "q", device)
+    out = torch.empty(B, K, dtype=torch.int32, device=device)
+    for b in range(B):
+        perm = torch.randperm(N, generator=g, device=device)[:K]
+        out[b, : len(perm)] = perm.to(torch.int32)
+        if len(perm) < K:
+            out[b, len(perm):] = -1
+    if n_invalid:
+        bad = torch.full((B, n_invalid), -1, dtype=torch.int32, device=device)
+        bad[:, ::2] = N + 7
+        out[:, K - n_invalid:] = bad
+    return out
+
+
+def kv_rows_seq(wl, b, device="cpu"):
+    """float32 N(0, 1) latent rows [N][d_qk] of sequence b (drawn per sequence so
+    that very long caches can be built and checked one sequence at a time)."""
+    return normal_f32((wl.N, wl.d_qk), wl.seed * 7919 + b, 0, "kv", device=device)

@@ -1,0 +1,191 @@
+"""GPU parity of the sparse attention (decode and prefill) against the float64 oracle.
+
+Tolerance: for every (query row, head), max|o - o_ref| / max|o_ref| <= 2e-3,
+and |lse - lse_ref| <= 2e-3.  Derivation: K/V rows enter the fp16 matrix
+cores exactly; q and P are rounded to fp16 once (relative 2^-11), which moves
+each logit by about scale * |q| |k| * 2^-11 ~ 5e-4 for unit-variance rows and
+each weight by the same relative amount; fp32 accumulation adds < 1e-6.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_index_amd as csa2
+from fp4_kv_cache_index_amd import inputs
+from oracle import attention as A
+from oracle import quant as Q
+from tests.gpu_util import ATTN_TOL, LSE_TOL, announce, gpu, np_, require_gpu, rowwise_rel_err
+
+
+def _make_caches(B, N, d_qk, W, seed, interleaved=True):
+    kv_x = inputs.normal_f32((B, N, d_qk), seed, 0, "kv", device="cuda")
+    if interleaved:
+        cache = torch.empty((B, N, d_qk // 2 + d_qk // 16), dtype=torch.uint8, device="cuda")
+        codes, scales = cache[..., : d_qk // 2], cache[..., d_qk // 2:]
+        csa2.kv_fp4_quantize(kv_x, codes=codes, scales=scales)
+    else:
+        codes, scales = csa2.kv_fp4_quantize(kv_x)
+    swa_x = inputs.normal_f32((B, W, d_qk), seed, 1, "swa", device="cuda")
+    sv, ss = csa2.swa_fp8_quantize(swa_x) if W > 0 else (None, None)
+    return kv_x, codes, scales, swa_x, sv, ss
+
+
+def _oracle_decode(q, kv_x, idx, ctx, swa_x, swa_len, d_qk, d_v, scale, sink=None):
+    B = q.shape[0]
+    outs, lses = [], []
+    for b in range(B):
+        codes, scales = Q.fp4_quantize(kv_x[b])
+        if swa_x is not None:
+            sv, ss = Q.mxfp8_quantize(swa_x[b])
+        else:
+            sv = ss = None
+        o, l = A.sparse_attn_decode_row(q[b], codes, scales, idx[b], ctx[b], sv, ss,
+                                        0 if swa_len is None else swa_len[b], d_qk, d_v, scale, sink)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def _check(out, lse, want_o, want_l):
+    err = rowwise_rel_err(np_(out), want_o)
+    assert err <= ATTN_TOL, err
+    wl, gl = want_l, np_(lse)
+    fin = np.isfinite(wl)
+    assert np.array_equal(fin, np.isfinite(gl))
+    assert np.max(np.abs(gl[fin] - wl[fin]), initial=0.0) <= LSE_TOL
+    return err
+
+
+@gpu
+def test_tiny_config_decode_attention():
+    require_gpu()
+    wl = inputs.WORKLOADS["tiny"]
+    announce("attn decode tiny H16 K256 W128")
+    kv_x, codes, scales, swa_x, sv, ss = _make_caches(wl.B, wl.N, wl.d_qk, wl.W, wl.seed)
+    q = inputs.normal_f32((wl.B, wl.H, wl.d_qk), wl.seed, 0, "q", device="cuda")
+    idx = inputs.random_index_lists(wl.B, wl.K, wl.N, wl.seed, device="cuda")
+    ctx = torch.full((wl.B,), wl.N, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((wl.B,), wl.W, dtype=torch.int32, device="cuda")
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, sv, ss, swa_len, wl.softmax_scale,
+                                            want_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = _oracle_decode(np_(q), np_(kv_x), np_(idx), np_(ctx), np_(swa_x), np_(swa_len),
+                                    wl.d_qk, wl.d_v, wl.softmax_scale)
+    _check(out, lse, want_o, want_l)
+
+
+@gpu
+@pytest.mark.parametrize("d_qk,H,K,W,n_invalid", [(576, 64, 2048, 128, 0), (576, 64, 300, 50, 40),
+                                                  (512, 64, 512, 128, 7), (576, 32, 64, 0, 3),
+                                                  (512, 16, 33, 1, 0)])
+def test_decode_shapes_invalid_entries_and_ragged_windows(d_qk, H, K, W, n_invalid):
+    require_gpu()
+    announce(f"attn decode d_qk={d_qk} H={H} K={K} W={W} invalid={n_invalid}")
+    B, N = 3, 5000
+    kv_x, codes, scales, swa_x, sv, ss = _make_caches(B, N, d_qk, W, 21, interleaved=(d_qk == 576))
+    q = inputs.normal_f32((B, H, d_qk), 21, 2, "q", device="cuda")
+    idx = inputs.random_index_lists(B, K, N, 21, device="cuda", n_invalid=n_invalid)
+    ctx = torch.tensor([N, N - 1000, 4000], dtype=torch.int32, device="cuda")
+    swa_len = torch.tensor([W, max(W - 3, 0), min(W, 1)], dtype=torch.int32, device="cuda") if W else None
+    scale = 1.0 / np.sqrt(d_qk)
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, sv, ss, swa_len, scale, want_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = _oracle_decode(np_(q), np_(kv_x), np_(idx), np_(ctx), None if W == 0 else np_(swa_x),
+                                    None if W == 0 else np_(swa_len), d_qk, 512, scale)
+    _check(out, lse, want_o, want_l)
+
+
+@gpu
+def test_topk_covering_context_is_dense_attention_and_sink():
+    require_gpu()
+    announce("attn decode K >= N (dense) with sink")
+    B, N, d_qk, H, W = 2, 700, 576, 64, 128
+    kv_x, codes, scales, swa_x, sv, ss = _make_caches(B, N, d_qk, W, 22)
+    q = inputs.normal_f32((B, H, d_qk), 22, 2, "q", device="cuda")
+    idx = torch.arange(N, dtype=torch.int32, device="cuda").repeat(B, 1)
+    idx = torch.cat([idx, torch.full((B, 68), -1, dtype=torch.int32, device="cuda")], dim=1).contiguous()
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((B,), W, dtype=torch.int32, device="cuda")
+    sink = inputs.normal_f32((H,), 22, 3, "sink", device="cuda") * 3.0
+    sink[0] = float("-inf")
+    scale = 1.0 / np.sqrt(576.0)
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, sv, ss, swa_len, scale, sink=sink,
+                                            want_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = _oracle_decode(np_(q), np_(kv_x), np_(idx), np_(ctx), np_(swa_x), np_(swa_len), d_qk, 512,
+                                    scale, sink=np_(sink))
+    _check(out, lse, want_o, want_l)
+
+
+@gpu
+def test_empty_entry_sets():
+    require_gpu()
+    announce("attn decode empty entry sets")
+    B, N, d_qk, H = 2, 100, 576, 16
+    kv_x, codes, scales, _, _, _ = _make_caches(B, N, d_qk, 0, 23)
+    q = inputs.normal_f32((B, H, d_qk), 23, 2, "q", device="cuda")
+    idx = torch.full((B, 64), -1, dtype=torch.int32, device="cuda")
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    sink = torch.full((H,), 0.25, dtype=torch.float32, device="cuda")
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, None, None, None, 0.05, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, None, None, None, 0.05, sink=sink,
+                                            want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.allclose(lse, torch.full_like(lse, 0.25))
+
+
+@gpu
+def test_prefill_attention_causal_windows():
+    require_gpu()
+    announce("attn prefill B2 Tq=9 K=256 W=128")
+    B, Tq, N0, d_qk, H, K, W = 2, 9, 3000, 576, 64, 256, 128
+    N = N0 + Tq
+    kv_x, codes, scales, _, _, _ = _make_caches(B, N, d_qk, 0, 24)
+    S = W - 1 + Tq
+    swa_x = inputs.normal_f32((B, S, d_qk), 24, 1, "swa", device="cuda")
+    sv, ss = csa2.swa_fp8_quantize(swa_x)
+    q = inputs.normal_f32((B, Tq, H, d_qk), 24, 2, "q", device="cuda")
+    idx = inputs.random_index_lists(B * Tq, K, N0, 24, device="cuda", n_invalid=5).reshape(B, Tq, K).contiguous()
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    q_pos = (torch.arange(Tq, dtype=torch.int32, device="cuda") + N0).repeat(B, 1).contiguous()
+    swa_pos0 = torch.tensor([N0 - W + 1, N0 - W + 1], dtype=torch.int32, device="cuda")
+    scale = 1.0 / np.sqrt(576.0)
+    out, lse = csa2.csa2_sparse_attn_prefill(q, codes, scales, idx, ctx, q_pos, sv, ss, swa_pos0, W, scale,
+                                             want_lse=True)
+    torch.cuda.synchronize()
+    kvh, svh, ssh = np_(kv_x), np_(sv), np_(ss)
+    want_o = np.zeros((B, Tq, H, 512))
+    want_l = np.zeros((B, Tq, H))
+    for b in range(B):
+        c, s = Q.fp4_quantize(kvh[b])
+        v8, s8 = Q.mxfp8_quantize(np_(swa_x[b]))
+        for t in range(Tq):
+            want_o[b, t], want_l[b, t] = A.sparse_attn_prefill_row(np_(q[b, t]), c, s, np_(idx[b, t]), N,
+                                                                   np_(q_pos)[b, t], v8, s8, np_(swa_pos0)[b], W,
+                                                                   d_qk, 512, scale)
+    _check(out, lse, want_o, want_l)
+
+
+@gpu
+def test_decode64k_attention_sampled_rows():
+    """The 64 x 2048 (+128 window) attention of the benchmark configuration;
+    rows 0 and 63 checked against the oracle."""
+    require_gpu()
+    wl = inputs.WORKLOADS["decode64k"]
+    announce("attn decode decode64k full batch, rows 0/63 sampled")
+    B, N = wl.B, 8192   # cache rows beyond the selected ids never enter attention
+    kv_x, codes, scales, swa_x, sv, ss = _make_caches(B, N, wl.d_qk, wl.W, wl.seed)
+    q = inputs.normal_f32((B, wl.H, wl.d_qk), wl.seed, 0, "q", device="cuda")
+    idx = inputs.random_index_lists(B, wl.K, N, wl.seed, device="cuda")
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((B,), wl.W, dtype=torch.int32, device="cuda")
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, sv, ss, swa_len, wl.softmax_scale,
+                                            want_lse=True)
+    torch.cuda.synchronize()
+    rows = [0, B - 1]
+    want_o, want_l = _oracle_decode(np_(q[rows]), np_(kv_x[rows]), np_(idx[rows]), np_(ctx[rows]),
+                                    np_(swa_x[rows]), np_(swa_len[rows]), wl.d_qk, wl.d_v, wl.softmax_scale)
+    _check(out[rows], lse[rows], want_o, want_l)
