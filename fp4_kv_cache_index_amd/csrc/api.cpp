@@ -92,13 +92,13 @@ static int attn_common_check(const float* q, const uint8_t* kv_codes, int64_t c_
   if (!q || !kv_codes || !kv_scales || !topk_idx || !ctx_len || !out) return CSA2_EINVAL;
   if (B < 0 || k_top < 0 || W < 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return CSA2_EINVAL;
   if (d_qk % 16 != 0 || d_v > d_qk || d_v % 16 != 0) return CSA2_EINVAL;
-  if (!aligned4(kv_codes) || !aligned4(kv_scales) || !aligned4(q)) return CSA2_EINVAL;
-  if ((c_bstride | c_rstride | s_bstride | s_rstride) & 3) return CSA2_EINVAL;
+  // Code rows are read as 32-bit words; scale bytes are read one at a time.
+  if (!aligned4(kv_codes) || !aligned4(q)) return CSA2_EINVAL;
+  if ((c_bstride | c_rstride) & 3) return CSA2_EINVAL;
   if (c_rstride < d_qk / 2 || s_rstride < d_qk / 16 || c_bstride < 0 || s_bstride < 0) return CSA2_EINVAL;
   if (W > 0) {
     if (!swa_vals || !swa_scales) return CSA2_EINVAL;
-    if (!aligned4(swa_vals) || !aligned4(swa_scales)) return CSA2_EINVAL;
-    if ((sv_bstride | sv_rstride | ss_bstride | ss_rstride) & 3) return CSA2_EINVAL;
+    if (!aligned4(swa_vals) || ((sv_bstride | sv_rstride) & 3)) return CSA2_EINVAL;
     if (sv_rstride < d_qk || ss_rstride < d_qk / 32 || sv_bstride < 0 || ss_bstride < 0) return CSA2_EINVAL;
     if (d_qk % 32 != 0) return CSA2_EINVAL;
   }

@@ -26,9 +26,10 @@
  *     library never allocates, frees or synchronises; all work is enqueued on
  *     `stream` (a hipStream_t; NULL = the null stream).  Results are valid
  *     once the stream reaches that point.
- *   - Row-major layouts.  Cache strides are in BYTES and must be multiples of
- *     4, as must cache base pointers; this admits both the pages' interleaved
- *     entry (codes then scales in one row) and separate code/scale arrays.
+ *   - Row-major layouts.  Cache strides are in BYTES.  Code / value arrays
+ *     (and their strides) must be 4-byte aligned; scale arrays may have any
+ *     stride.  This admits both the pages' interleaved entry (codes then
+ *     scales in one row) and separate code/scale arrays.
  *   - Host-side validation of shapes, strides and pointers only; the data is
  *     not inspected.  NaN/Inf inputs are outside the contract.
  *   - Workspace: `ws` must hold at least the matching *_workspace_size()

@@ -85,14 +85,18 @@ def e2m1_nearest_code(absx, scale):
     """Magnitude code (0..7) of the E2M1 value v minimising |absx - v*scale|.
 
     This is the E2M1 value nearest the real quotient absx/scale, found without
-    forming the quotient: v*scale is exact in float64 (at most 6 significant
-    bits) and absx is a float32, so each distance is exact whenever the two
-    are within 2^28 of each other in magnitude, which covers every case where
-    two candidates are close to tying.  Ties go to the even code; quotients
-    beyond 6 saturate to code 7 (6.0).  scale must be > 0.
+    forming the quotient.  A quotient above 6 saturates to code 7 (6.0); that
+    test, absx > 6*scale, is exact.  Below it absx <= 6*scale, v*scale is
+    exact in float64 (at most 6 significant bits) and absx is a float32, so
+    the distances are exact whenever absx is within 2^28 of the candidates,
+    which covers every case where two candidates come close to tying; ties go
+    to the even code.  scale must be > 0.
     """
     a = np.asarray(absx, dtype=np.float64)
     s = np.asarray(scale, dtype=np.float64)
+    a, s = np.broadcast_arrays(a, s)
+    sat = a > 6.0 * s
+    a = np.where(sat, 6.0 * s, a)
     mags = e2m1_decode(np.arange(8))
     dist = np.abs(a[..., None] - mags * s[..., None])  # [..., 8]
     best = dist.min(axis=-1, keepdims=True)
@@ -103,4 +107,4 @@ def e2m1_nearest_code(absx, scale):
     pick_even = cand & even
     has_even = pick_even.any(axis=-1, keepdims=True)
     cand = np.where(has_even, pick_even, cand)
-    return np.argmax(cand, axis=-1).astype(np.int64)
+    return np.where(sat, 7, np.argmax(cand, axis=-1)).astype(np.int64)

@@ -94,3 +94,13 @@ def test_e2m1_nearest_code_exact_on_ties_and_neighbours():
     got = F.e2m1_nearest_code(np.array(xs), np.array(ss))
     want = np.array([_nearest_e2m1_exact(x, s) for x, s in zip(xs, ss)])
     assert np.array_equal(got, want)
+
+
+def test_e2m1_nearest_code_saturates_huge_quotients():
+    # Quotients far beyond 6 (where float64 distances to every candidate round
+    # to the same value) must still pick 6.0, the nearest magnitude.
+    scales = F.e4m3fn_decode(np.array([1, 8, 0x38, 0x7E]))
+    xs = np.array([3e38, 1e30, 6.5e10, 1e8], dtype=np.float32)
+    for s in scales:
+        for x in xs:
+            assert F.e2m1_nearest_code(np.array([x]), np.array([s]))[0] == _nearest_e2m1_exact(float(x), float(s)) == 7

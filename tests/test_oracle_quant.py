@@ -132,3 +132,15 @@ def test_mxfp8_saturates_top_of_binade():
     x[0, 0] = np.float32(500.0)  # floor(log2) = 8 -> exponent 0 -> 500 saturates to 448
     v, s = Q.mxfp8_quantize(x)
     assert s[0, 0] == 127 and v[0, 0] == 0x7E
+
+
+def test_fp4_huge_and_tiny_groups():
+    # amax/6 saturates the scale at 448; the huge elements saturate to +-6.
+    x = np.array([[3e38, -3e38] + [1.0] * 14], dtype=np.float32)
+    codes, sc = Q.fp4_quantize(x)
+    assert sc.tolist() == [[0x7E]]
+    assert codes[0].tolist() == [0xF7] + [0] * 7
+    # float32 subnormals and values whose scale rounds to zero give all-zero codes.
+    x = np.array([[1e-40] * 8 + [-3e-39] * 8, [2.0 ** -12] * 16], dtype=np.float32)
+    codes, sc = Q.fp4_quantize(x)
+    assert sc.tolist() == [[0], [0]] and np.all(codes == 0)
