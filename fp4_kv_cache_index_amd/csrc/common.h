@@ -94,19 +94,23 @@ __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
 }
 
 // "Last workgroup" election: every workgroup of a group calls this once after
-// publishing its contribution; exactly one (the last to arrive) gets true and
-// then observes every other workgroup's writes.  No workgroup waits.
+// publishing its contribution with agent-scope atomics (RMW or atomic
+// stores); exactly one workgroup -- the last to arrive -- gets true, and its
+// agent-scope loads then observe every other workgroup's contribution.  No
+// workgroup waits for another.  Each thread first waits for its own memory
+// operations to be acknowledged (they are performed at the agent coherence
+// point by then), so the counter increment that follows the barrier is
+// ordered after all of them without a release fence; a release fence here
+// would write back the whole L2 of the XCD once per workgroup.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* lds_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    uint32_t prev = atomic_add_agent_acq_rel(counter, 1u);
+    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = (prev == expected - 1u) ? 1u : 0u;
   }
   __syncthreads();
-  bool last = *lds_flag != 0u;
-  if (last) __threadfence();
-  return last;
+  return *lds_flag != 0u;
 }
 
 }  // namespace csa2

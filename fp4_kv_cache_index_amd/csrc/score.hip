@@ -32,18 +32,28 @@ struct Frag {
   uint32_t w[CH / 4];
 };
 
-template <int CH>
+// A lane's share of a DI-byte row: for DI >= 64, DI/64 chunks of 16 bytes,
+// chunk j at byte 64*j + 16*g (so the four lane groups of one load
+// instruction cover whole 64-byte segments of 16 rows); for DI = 32 one
+// 8-byte piece at 8*g.  Piece i (8 bytes) of the fragment feeds MFMA k-step i;
+// the query fragments use the same map, so products pair up.
+template <int DI>
+__device__ __forceinline__ const uint8_t* frag_base(const uint8_t* row, int g) {
+  return row + (DI >= 64 ? 16 * g : 8 * g);
+}
+
+template <int CH, int DI>
 __device__ __forceinline__ void load_frag(Frag<CH>& f, const uint8_t* p, bool ok) {
   if (!ok) {
 #pragma unroll
     for (int i = 0; i < CH / 4; ++i) f.w[i] = 0u;
     return;
   }
-  if constexpr (CH % 16 == 0) {
+  if constexpr (DI >= 64) {
 #pragma unroll
-    for (int i = 0; i < CH / 16; ++i) {
-      v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i);
-      f.w[4 * i] = v[0]; f.w[4 * i + 1] = v[1]; f.w[4 * i + 2] = v[2]; f.w[4 * i + 3] = v[3];
+    for (int j = 0; j < DI / 64; ++j) {
+      v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + 64 * j));
+      f.w[4 * j] = v[0]; f.w[4 * j + 1] = v[1]; f.w[4 * j + 2] = v[2]; f.w[4 * j + 3] = v[3];
     }
   } else {
     v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
@@ -57,7 +67,7 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 
 // GATHER = false: tokens j = tile positions of the row (flat scan).
 // GATHER = true : position p maps to token pool_idx[row][p] (pool layers).
-template <int DI, int HB, bool GATHER>
+template <int DI, int HB, bool GATHER, bool POOL>
 __global__ void __launch_bounds__(256)
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
@@ -72,7 +82,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   constexpr int KS = DI / 32;          // MFMA k-steps
   constexpr int HMAX = 16 * HB;
   __shared__ uint32_t hist[4096];
-  __shared__ uint32_t bhist[4096];
+  __shared__ uint32_t bhist[POOL ? 4096 : 1];
   __shared__ __attribute__((aligned(16))) float dots[kScanWaves][64 * HMAX];
   __shared__ float wsh[HMAX];
   __shared__ uint32_t flag;
@@ -80,7 +90,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;
   const int64_t b = row / Tq;
-  const bool pool = pool_block > 0;
+  constexpr bool pool = POOL;
 
   int64_t nv;
   if (GATHER) {
@@ -112,7 +122,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   for (int hb = 0; hb < HB; ++hb) {
     int h = c16 + 16 * hb;
     Frag<CH> f;
-    load_frag<CH>(f, q_idx + (row * H_I + h) * DI + g * CH, h < H_I);
+    load_frag<CH, DI>(f, frag_base<DI>(q_idx + (row * H_I + h) * DI, g), h < H_I);
 #pragma unroll
     for (int i = 0; i < KS; ++i) qa[hb][i] = as_long(f.w[2 * i], f.w[2 * i + 1]);
   }
@@ -133,7 +143,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     ok = pos < wend;
     int64_t tokid = pos;
     if (GATHER && ok) tokid = prow[pos];
-    return kb + (ok ? tokid : 0) * k_rstride + g * CH;
+    return frag_base<DI>(kb + (ok ? tokid : 0) * k_rstride, g);
   };
 
   Frag<CH> cur[4], nxt[4];
@@ -142,7 +152,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     for (int s = 0; s < 4; ++s) {
       bool ok;
       const uint8_t* p = frag_ptr(wbase + 16 * s + c16, ok);
-      load_frag<CH>(cur[s], p, ok);
+      load_frag<CH, DI>(cur[s], p, ok);
     }
   }
   for (int64_t it = wbase; it < wend; it += 64) {
@@ -152,7 +162,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
       for (int s = 0; s < 4; ++s) {
         bool ok;
         const uint8_t* p = frag_ptr(it + 64 + 16 * s + c16, ok);
-        load_frag<CH>(nxt[s], p, ok);
+        load_frag<CH, DI>(nxt[s], p, ok);
       }
     }
 #pragma unroll
@@ -224,13 +234,26 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
   int64_t rows = (int64_t)a.B * a.Tq;
-  int64_t tiles = (a.n_max + kScanTile - 1) / kScanTile;
+  // Largest tile (fewest histogram flushes) that still gives >= 4 workgroups
+  // per compute unit; at least 1024 tokens.
+  int tile = kScanTile;
+  const int64_t want = 4LL * device_cu_count();
+  while (tile > 1024 && rows * ((a.n_max + tile - 1) / tile) < want) tile >>= 1;
+  int64_t tiles = (a.n_max + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
   SelectWs bw = blk ? *blk : tok;
-  CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false>), dim3((unsigned)tiles, (unsigned)rows),
-              dim3(256), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
-              (const int32_t*)nullptr, (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, kScanTile, keys, key_stride,
-              n_valid, tok, a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
+  dim3 grid((unsigned)tiles, (unsigned)rows);
+  if (a.pool_block > 0) {
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true>), grid, dim3(256), 0, s, a.q_idx, a.w,
+                a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
+                (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok,
+                a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
+  } else {
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false>), grid, dim3(256), 0, s, a.q_idx, a.w,
+                a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
+                (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok, 0,
+                0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, bw);
+  }
   return hipGetLastError();
 }
 
@@ -242,7 +265,7 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
   int64_t rows = (int64_t)B * Tq;
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
+  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
               0, s, q_idx, w, k_idx, k_bstride, k_rstride, (const int32_t*)nullptr, (const int32_t*)nullptr,
               pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, (int64_t)pool_cap, n_valid, ws,
               0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);

@@ -160,8 +160,8 @@ select_count_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_
   if ((threadIdx.x & 63) == 0) { sgt[threadIdx.x >> 6] = gt; seq[threadIdx.x >> 6] = eq; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    ws.tile_gt[row * tiles + blockIdx.x] = sgt[0] + sgt[1] + sgt[2] + sgt[3];
-    ws.tile_eq[row * tiles + blockIdx.x] = seq[0] + seq[1] + seq[2] + seq[3];
+    store_agent(ws.tile_gt + row * tiles + blockIdx.x, sgt[0] + sgt[1] + sgt[2] + sgt[3]);
+    store_agent(ws.tile_eq + row * tiles + blockIdx.x, seq[0] + seq[1] + seq[2] + seq[3]);
   }
   if (!arrive_last(&ctl->arrive[3], (uint32_t)tiles, &flag)) return;
   // Exclusive scan over tiles, 256 at a time with a running carry.
