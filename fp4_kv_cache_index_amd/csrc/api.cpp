@@ -215,7 +215,7 @@ size_t csa2_hier_pool_topk_workspace_size(int32_t B, int32_t Tq, int32_t pool_ca
   int64_t rows = (int64_t)B * Tq;
   int64_t tiles = (pool_cap + kSelTile - 1) / kSelTile;
   if (tiles < 1) tiles = 1;
-  return al256(sizeof(uint32_t) * rows * (pool_cap > 0 ? pool_cap : 1)) + al256(sizeof(int32_t) * rows) +
+  return al256(sizeof(uint32_t) * rows * round_up(pool_cap > 0 ? pool_cap : 1, 64)) + al256(sizeof(int32_t) * rows) +
          al256(select_ws_bytes(rows, tiles));
 }
 
@@ -236,7 +236,7 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
   if (ws_bytes < need) return CSA2_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   int64_t rows = (int64_t)B * Tq;
-  int64_t cap = pool_cap > 0 ? pool_cap : 1;
+  int64_t cap = round_up(pool_cap > 0 ? pool_cap : 1, 64);   // key row stride
   int64_t tiles = (pool_cap + kSelTile - 1) / kSelTile;
   if (tiles < 1) tiles = 1;
   char* base = (char*)ws;
@@ -248,10 +248,10 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
   hipError_t e = select_clear(sw, rows, s);
   if (e == hipSuccess)
     e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B, Tq, H_I,
-                          D_I, k_top, keys, n_valid, sw, s);
+                          D_I, k_top, keys, cap, n_valid, sw, s);
   if (e == hipSuccess) {
     SelectOut out{topk_idx, topk_score, pool_idx, pool_cap, 0, nullptr, nullptr};
-    e = select_finish(sw, keys, pool_cap, n_valid, rows, pool_cap, k_top, out, s);
+    e = select_finish(sw, keys, cap, n_valid, rows, pool_cap, k_top, out, s);
   }
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }

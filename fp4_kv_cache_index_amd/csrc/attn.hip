@@ -13,8 +13,11 @@
 // 16 heads) and a contiguous split of its entry list (Top-K rows, then the
 // window rows).  Per chunk of 32 entries it gathers the rows by index
 // (coalesced: consecutive lanes read consecutive 8-byte code groups of a
-// row), dequantises them into LDS as fp16 -- exact, since E2M1 x E4M3 has at
-// most 6 significant bits within [2^-10, 2688] -- and runs
+// row), dequantises them into LDS as fp16 with the gfx950 scaled converts
+// (v_cvt_scalef32_pk_f16_fp4 / _fp8, which apply the power-of-two part of
+// their scale; the E4M3 scale of a main row is applied as an fp16 multiply)
+// -- exact, since E2M1 x E4M3 has at most 6 significant bits within
+// [2^-10, 2688] -- and runs
 //   S^T = K Q^T   on v_mfma_f32_16x16x32_f16 (q rounded to fp16 once),
 //   online softmax in fp32 (exp2 domain),
 //   O  += P V     on the same instruction, P taken straight from the S^T
@@ -49,16 +52,26 @@ __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
 
 constexpr int kMaxSpan = 1024;      // entries per split (ids staged in LDS)
 constexpr int kAttnThreads = 256;   // 4 waves; wave w owns heads 16w .. 16w+15
+constexpr int kVtPitch = kChunk + 4;  // fp16 per V^T row (18 dwords: spreads banks)
+
+// Raw bytes of one gather task: two entries (2*ep, 2*ep+1) of one 16-channel group.
+struct RawTask {
+  uint32_t w[2][4];   // main: 8 code bytes in w[k][0..1]; window: 16 value bytes
+  uint32_t sc[2];     // scale byte (E4M3 for main rows, E8M0 for window rows)
+  uint32_t kind;      // 2 bits per entry: 0 skip, 1 main, 2 window
+};
 
 template <int DQK, int DV>
 __global__ void __launch_bounds__(kAttnThreads)
 sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
                          float* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = AttnShape<DQK>;
-  constexpr int NT = DV / 16;                   // output tiles per wave
-  constexpr int TPT = (kChunk * S::G16 + kAttnThreads - 1) / kAttnThreads;
-  __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * S::PITCH];
-  __shared__ int32_t eid[kMaxSpan];             // main: token id; window: window row; -1 = skip
+  constexpr int NT = DV / 16;                         // output tiles per wave
+  constexpr int NTASK = (kChunk / 2) * S::G16;        // (entry pair, group) tasks per chunk
+  constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
+  __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * S::PITCH];   // K rows, row-major
+  __shared__ __attribute__((aligned(16))) _Float16 vt[DV * kVtPitch];       // V transposed
+  __shared__ int32_t eid[kMaxSpan];   // main: token id; window: window row; -1 = skip
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
@@ -113,82 +126,109 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   const uint8_t* scales_b = a.kv_scales + b * a.s_bstride;
   const uint8_t* sv_b = a.swa_vals ? a.swa_vals + b * a.sv_bstride : nullptr;
   const uint8_t* ss_b = a.swa_scales ? a.swa_scales + b * a.ss_bstride : nullptr;
+  __syncthreads();
+
+  // ---- gather: task = (entry pair ep, 16-channel group gq), ep fastest so
+  // that a wave's V^T stores hit consecutive words.
+  RawTask raw[TPT];
+  auto gather = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int task = threadIdx.x + u * kAttnThreads;
+      raw[u].kind = 0;
+      if (task < NTASK) {
+        const int ep = task & 15, gq = task >> 4;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int ce = c0 + 2 * ep + k;
+          const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
+          if (id >= 0 && ce < K) {
+            const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 8 * gq);
+            raw[u].w[k][0] = cp[0];
+            raw[u].w[k][1] = cp[1];
+            raw[u].sc[k] = scales_b[(int64_t)id * a.s_rstride + gq];
+            raw[u].kind |= 1u << (2 * k);
+          } else if (id >= 0) {
+            const uint32_t* vp = reinterpret_cast<const uint32_t*>(sv_b + (int64_t)id * a.sv_rstride + 16 * gq);
+            raw[u].w[k][0] = vp[0]; raw[u].w[k][1] = vp[1]; raw[u].w[k][2] = vp[2]; raw[u].w[k][3] = vp[3];
+            raw[u].sc[k] = ss_b[(int64_t)id * a.ss_rstride + (gq >> 1)];
+            raw[u].kind |= 2u << (2 * k);
+          }
+        }
+      }
+    }
+  };
+  // ---- dequantise the staged bytes into K rows and V^T columns.
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int task = threadIdx.x + u * kAttnThreads;
+      if (task >= NTASK) break;
+      const int ep = task & 15, gq = task >> 4;
+      uint32_t hv[2][8];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t kind = (raw[u].kind >> (2 * k)) & 3u;
+        if (kind == 1u) {
+          // E2M1 -> fp16 in hardware (scale 1), then the E4M3 scale as an fp16
+          // multiply; both steps are exact (at most 6 significant bits).
+          _Float16 sh = (_Float16)e4m3_to_f32(raw[u].sc[k]);
+          v2h s2 = {sh, sh};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t word = raw[u].w[k][i >> 2];
+            v2h v;
+            switch (i & 3) {
+              case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0); break;
+              case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1); break;
+              case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2); break;
+              default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3); break;
+            }
+            v = v * s2;
+            hv[k][i] = __builtin_bit_cast(uint32_t, v);
+          }
+        } else if (kind == 2u) {
+          // E4M3 -> fp16 scaled by the E8M0 power of two, in one instruction.
+          const float sc = e8m0_to_f32(raw[u].sc[k]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t word = raw[u].w[k][i >> 1];
+            v2h v = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, true)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, false);
+            hv[k][i] = __builtin_bit_cast(uint32_t, v);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) hv[k][i] = 0u;
+        }
+        uint4* dst = reinterpret_cast<uint4*>(kt + (2 * ep + k) * S::PITCH + 16 * gq);
+        dst[0] = uint4{hv[k][0], hv[k][1], hv[k][2], hv[k][3]};
+        dst[1] = uint4{hv[k][4], hv[k][5], hv[k][6], hv[k][7]};
+      }
+      if (16 * gq < DV) {
+        uint32_t* vcol = reinterpret_cast<uint32_t*>(vt + (16 * gq) * kVtPitch + 2 * ep);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)   // (entry 2ep, entry 2ep+1) halves of channel 16gq + c
+          vcol[c * (kVtPitch / 2)] = __builtin_amdgcn_perm(hv[1][c >> 1], hv[0][c >> 1],
+                                                           (c & 1) ? 0x07060302u : 0x05040100u);
+      }
+    }
+  };
 
   v4f o[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
-  __syncthreads();
 
+  if (e_begin < e_end) {
+    gather(e_begin);
+    store();
+  }
+  __syncthreads();
   for (int c0 = e_begin; c0 < e_end; c0 += kChunk) {
-    // ---- gather: task = (entry, 16-channel group), group fastest; all of a
-    // thread's loads are issued before any conversion.
-    uint32_t raw[TPT][4];
-    uint32_t sraw[TPT];
-    int kind[TPT];
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int task = threadIdx.x + u * kAttnThreads;
-      kind[u] = 0;
-      if (task < kChunk * S::G16) {
-        const int e = task / S::G16;
-        const int gq = task - e * S::G16;
-        const int ce = c0 + e;
-        const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
-        if (id >= 0 && ce < K) {
-          const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 8 * gq);
-          raw[u][0] = cp[0];
-          raw[u][1] = cp[1];
-          sraw[u] = scales_b[(int64_t)id * a.s_rstride + gq];
-          kind[u] = 1;
-        } else if (id >= 0) {
-          const uint32_t* vp = reinterpret_cast<const uint32_t*>(sv_b + (int64_t)id * a.sv_rstride + 16 * gq);
-          raw[u][0] = vp[0]; raw[u][1] = vp[1]; raw[u][2] = vp[2]; raw[u][3] = vp[3];
-          sraw[u] = ss_b[(int64_t)id * a.ss_rstride + (gq >> 1)];
-          kind[u] = 2;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const int task = threadIdx.x + u * kAttnThreads;
-      if (task >= kChunk * S::G16) break;
-      const int e = task / S::G16;
-      const int gq = task - e * S::G16;
-      uint32_t hv[8];
-      if (kind[u] == 1) {
-        _Float16 sh = (_Float16)e4m3_to_f32(sraw[u]);
-        v2h s2 = {sh, sh};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t byte = (raw[u][i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          uint32_t lo = byte & 0xFu, hi = byte >> 4;
-          uint32_t bits = e2m1_mag_to_f16_bits(lo & 7u) | ((lo & 8u) << 12) |
-                          ((e2m1_mag_to_f16_bits(hi & 7u) | ((hi & 8u) << 12)) << 16);
-          v2h v = __builtin_bit_cast(v2h, bits);
-          v = v * s2;   // exact: at most 6 significant bits, within fp16 range
-          hv[i] = __builtin_bit_cast(uint32_t, v);
-        }
-      } else if (kind[u] == 2) {
-        float sc = e8m0_to_f32(sraw[u]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t wv = raw[u][i >> 1] >> (16 * (i & 1));
-          v2h v;
-          v[0] = (_Float16)(e4m3_to_f32(wv & 0xFFu) * sc);
-          v[1] = (_Float16)(e4m3_to_f32((wv >> 8) & 0xFFu) * sc);
-          hv[i] = __builtin_bit_cast(uint32_t, v);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hv[i] = 0u;
-      }
-      uint4* dst = reinterpret_cast<uint4*>(kt + e * S::PITCH + 16 * gq);
-      dst[0] = uint4{hv[0], hv[1], hv[2], hv[3]};
-      dst[1] = uint4{hv[4], hv[5], hv[6], hv[7]};
-    }
-    __syncthreads();
+    const bool has_next = c0 + kChunk < e_end;
+    if (has_next) gather(c0 + kChunk);   // in flight during this chunk's math
     if (active) {
       // ---- S^T = K Q^T for 2 tiles of 16 entries
       v4f st[2];
@@ -236,24 +276,30 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      // ---- rescale O rows (heads 4g + r) and accumulate P V
-      float al[4];
+      // ---- rescale O rows (heads 4g + r) when some head's max moved
+      if (!__all(alpha == 1.0f)) {
+        float al[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
-      const _Float16* vb = kt + c16;
+        for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          o[n][0] *= al[0]; o[n][1] *= al[1]; o[n][2] *= al[2]; o[n][3] *= al[3];
+        }
+      }
+      // ---- O += P V; B operand = V^T row (dim), entries 4g..4g+3 and 16+4g..16+4g+3
+      const _Float16* vrow = vt + c16 * kVtPitch + 4 * g;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        v4f acc = o[n];
-        acc[0] *= al[0]; acc[1] *= al[1]; acc[2] *= al[2]; acc[3] *= al[3];
-        v8h vf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int e = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-          vf[j] = vb[e * S::PITCH + 16 * n];
-        }
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf, acc, 0, 0, 0);
+        const _Float16* vp = vrow + (16 * n) * kVtPitch;
+        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+        v4h lo = *reinterpret_cast<const v4h*>(vp);
+        v4h hi = *reinterpret_cast<const v4h*>(vp + 16);
+        v8h vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf, o[n], 0, 0, 0);
       }
     }
+    __syncthreads();
+    if (has_next) store();
     __syncthreads();
   }
 
@@ -315,10 +361,11 @@ sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __rest
 }
 
 int attn_num_splits(int64_t rows, int k_top, int W) {
+  // One resident workgroup per compute unit (LDS and registers allow one).
   int E = k_top + W;
   int max_splits = (E + 63) / 64;
   int min_splits = (E + kMaxSpan - 1) / kMaxSpan;
-  int64_t want = (2LL * device_cu_count() + rows - 1) / rows;
+  int64_t want = ((int64_t)device_cu_count() + rows - 1) / rows;
   int s = (int)(want < 1 ? 1 : (want > max_splits ? max_splits : want));
   if (s < min_splits) s = min_splits;
   return s < 1 ? 1 : s;

@@ -43,7 +43,6 @@ hipError_t launch_swa_fp8_quantize(const float* x, int64_t n_rows, int d, int64_
 // the first n_valid[row] positions, ties to the lower position, emitted in
 // ascending position order.  Workspace: select_ws_bytes(rows, tiles).
 constexpr int kSelTile = 4096;      // positions per workgroup in the select passes
-constexpr int kDigit1Bits = 12, kDigit2Bits = 12, kDigit3Bits = 8;
 
 struct SelectRowCtl {               // per-row control block (64 bytes)
   uint32_t arrive[6];               // last-workgroup counters of the passes
@@ -90,9 +89,6 @@ hipError_t select_hist1(const SelectWs& ws, const uint32_t* keys, int64_t key_st
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
                          int64_t rows, int64_t n_max, int k, const SelectOut& out, hipStream_t s);
 
-// Device-side: resolve digit 1 in the last workgroup of a producer pass.
-// (Declared here for the scoring kernels, defined in select.hip.)
-
 // ------------------------------------------------------------- scoring ---
 struct ScoreArgs {
   const uint8_t* q_idx; const float* w;
@@ -106,8 +102,8 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
                               const SelectWs* blk, hipStream_t s);
 hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                              int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
-                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int32_t* n_valid,
-                             const SelectWs& ws, hipStream_t s);
+                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
+                             int32_t* n_valid, const SelectWs& ws, hipStream_t s);
 
 // ----------------------------------------------------------- attention ---
 struct AttnArgs {

@@ -260,14 +260,14 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
 template <int DI, int HB>
 static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                                 int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
-                                int B, int Tq, int H_I, int k_top, uint32_t* keys, int32_t* n_valid,
-                                const SelectWs& ws, hipStream_t s) {
+                                int B, int Tq, int H_I, int k_top, uint32_t* keys, int64_t key_stride,
+                                int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
   int64_t rows = (int64_t)B * Tq;
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
   CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
               0, s, q_idx, w, k_idx, k_bstride, k_rstride, (const int32_t*)nullptr, (const int32_t*)nullptr,
-              pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, (int64_t)pool_cap, n_valid, ws,
+              pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, key_stride, n_valid, ws,
               0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
   return hipGetLastError();
 }
@@ -294,11 +294,11 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
 
 hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                              int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
-                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int32_t* n_valid,
-                             const SelectWs& ws, hipStream_t s) {
+                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
+                             int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
 #define CALL_POOL(D, H) \
   launch_pool_t<D, H>(q_idx, w, k_idx, k_bstride, k_rstride, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
-                      n_valid, ws, s)
+                      key_stride, n_valid, ws, s)
   CSA2_DISPATCH_DI_HB(D_I, H_I, CALL_POOL);
 #undef CALL_POOL
 }

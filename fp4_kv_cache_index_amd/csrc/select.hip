@@ -45,6 +45,22 @@ SelectWs select_ws_carve(void* base, int64_t rows, int64_t tiles) {
   return w;
 }
 
+// The 16 keys a thread handles in the unordered passes: positions
+// base + 4*(tid + 256*i) + (0..3), i = 0..3, loaded as four 16-byte vectors
+// (coalesced across the workgroup) before any of them is used.  Positions at
+// or past nv read as 0 (absent).  Rows are padded to a multiple of 64 keys, so
+// a vector that starts below nv stays inside the row.
+__device__ __forceinline__ void load_tile_keys(const uint32_t* kr, int64_t base, int64_t nv, uint32_t (&k)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t p = base + 4 * ((int64_t)threadIdx.x + 256 * i);
+    v4u v = {0u, 0u, 0u, 0u};
+    if (p < nv) v = *reinterpret_cast<const v4u*>(kr + p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[4 * i + j] = (p + j < nv) ? v[j] : 0u;
+  }
+}
+
 // ------------------------------------------------------------- kernels ---
 
 __global__ void select_clear_kernel(uint32_t* p, int64_t n_words) {
@@ -64,9 +80,11 @@ select_hist1_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_
   const int64_t nv = n_valid[row];
   for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
   __syncthreads();
-  const uint32_t* kr = keys + row * key_stride;
-  int64_t end = base + kSelTile < nv ? base + kSelTile : nv;
-  for (int64_t j = base + threadIdx.x; j < end; j += 256) atomicAdd(&hist[kr[j] >> 20], 1u);
+  uint32_t kk[16];
+  load_tile_keys(keys + row * key_stride, base, nv, kk);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (kk[i]) atomicAdd(&hist[kk[i] >> 20], 1u);
   __syncthreads();
   uint32_t* gh = ws.hist1 + row * 4096;
   for (int i = threadIdx.x; i < 4096; i += 256)
@@ -96,12 +114,11 @@ select_refine_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key
     const int64_t nv = n_valid[row];
     for (int i = threadIdx.x; i < BINS; i += 256) hist[i] = 0u;
     __syncthreads();
-    const uint32_t* kr = keys + row * key_stride;
-    int64_t end = base + kSelTile < nv ? base + kSelTile : nv;
-    for (int64_t j = base + threadIdx.x; j < end; j += 256) {
-      uint32_t key = kr[j];
-      if ((key >> SHIFT) == prefix) atomicAdd(&hist[(key >> DSHIFT) & (BINS - 1)], 1u);
-    }
+    uint32_t kk[16];
+    load_tile_keys(keys + row * key_stride, base, nv, kk);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (kk[i] && (kk[i] >> SHIFT) == prefix) atomicAdd(&hist[(kk[i] >> DSHIFT) & (BINS - 1)], 1u);
     __syncthreads();
     for (int i = threadIdx.x; i < BINS; i += 256)
       if (hist[i]) atomic_add_agent(gh + i, hist[i]);
@@ -143,13 +160,13 @@ select_count_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_
   const uint32_t thr = ctl->thr;
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
   const int64_t nv = n_valid[row];
-  const uint32_t* kr = keys + row * key_stride;
-  int64_t end = base + kSelTile < nv ? base + kSelTile : nv;
+  uint32_t kk[16];
+  load_tile_keys(keys + row * key_stride, base, nv, kk);
   uint32_t gt = 0, eq = 0;
-  for (int64_t j = base + threadIdx.x; j < end; j += 256) {
-    uint32_t key = kr[j];
-    gt += key > thr;
-    eq += key == thr;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    gt += kk[i] != 0u && kk[i] > thr;
+    eq += kk[i] != 0u && kk[i] == thr;
   }
   // workgroup sums
   for (int off = 32; off > 0; off >>= 1) {
@@ -227,7 +244,12 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   const uint32_t* kr = keys + row * key_stride;
   uint32_t kk[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) kk[i] = (p0 + i < nv) ? kr[p0 + i] : 0u;
+  for (int i = 0; i < PER / 4; ++i) {
+    v4u v = {0u, 0u, 0u, 0u};
+    if (p0 + 4 * i < nv) v = *reinterpret_cast<const v4u*>(kr + p0 + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kk[4 * i + j] = (p0 + 4 * i + j < nv) ? v[j] : 0u;
+  }
   uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
