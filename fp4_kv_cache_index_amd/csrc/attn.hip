@@ -9,9 +9,10 @@
 // entries (and the sink) of scale * q_h . k_e, applied to v_e = the first
 // d_v channels of the same row.
 //
-// gfx950 mapping.  A workgroup holds one query row (all H heads, one wave per
-// 16 heads) and a contiguous split of its entry list (Top-K rows, then the
-// window rows).  Per chunk of 32 entries it gathers the rows by index
+// gfx950 mapping.  A workgroup holds one query row and a contiguous split of
+// its entry list (Top-K rows, then the window rows).  Its 8 waves (two per
+// SIMD) each own 16 heads and half of the 512 output dims, which keeps the
+// fp32 O accumulators at 64 registers per lane.  Per chunk of 32 entries it gathers the rows by index
 // (coalesced: consecutive lanes read consecutive 8-byte code groups of a
 // row), dequantises them into LDS as fp16 with the gfx950 scaled converts
 // (v_cvt_scalef32_pk_f16_fp4 / _fp8, which apply the power-of-two part of
@@ -51,7 +52,7 @@ __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
 }
 
 constexpr int kMaxSpan = 1024;      // entries per split (ids staged in LDS)
-constexpr int kAttnThreads = 256;   // 4 waves; wave w owns heads 16w .. 16w+15
+constexpr int kAttnThreads = 512;   // 8 waves; wave w: heads 16*(w&3).., output dims 256*(w>>2)..
 constexpr int kVtPitch = kChunk + 4;  // fp16 per V^T row (18 dwords: spreads banks)
 
 // Raw bytes of one gather task: two entries (2*ep, 2*ep+1) of one 16-channel group.
@@ -66,7 +67,7 @@ __global__ void __launch_bounds__(kAttnThreads)
 sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
                          float* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = AttnShape<DQK>;
-  constexpr int NT = DV / 16;                         // output tiles per wave
+  constexpr int NT = DV / 32;                         // output tiles per wave (half the dims)
   constexpr int NTASK = (kChunk / 2) * S::G16;        // (entry pair, group) tasks per chunk
   constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
   __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * S::PITCH];   // K rows, row-major
@@ -113,8 +114,9 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 
   // q fragments of this wave's 16 heads: lane holds head 16*wave + c16,
   // dims 32*i + 8*g .. +8 of k-step i (the B operand of S^T = K Q^T).
-  const bool active = 16 * wave < H;
-  const int head_b = 16 * wave + c16;
+  const int hg = wave & 3, dh = wave >> 2;
+  const bool active = 16 * hg < H;
+  const int head_b = 16 * hg + c16;
   v8h qf[S::KQ];
   if (active) {
     const float* qrow = a.q + (row * H + head_b) * (int64_t)DQK;
@@ -230,18 +232,28 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const bool has_next = c0 + kChunk < e_end;
     if (has_next) gather(c0 + kChunk);   // in flight during this chunk's math
     if (active) {
-      // ---- S^T = K Q^T for 2 tiles of 16 entries
-      v4f st[2];
+      // ---- S^T = K Q^T for 2 tiles of 16 entries (chains interleaved, reads batched)
+      v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+      const _Float16* krow0 = kt + c16 * S::PITCH + 8 * g;
+      const _Float16* krow1 = krow0 + 16 * S::PITCH;
+      constexpr int BATCH = 6;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const _Float16* krow = kt + (16 * t + c16) * S::PITCH + 8 * g;
+      for (int i0 = 0; i0 < S::KQ; i0 += BATCH) {
+        v8h ka[BATCH], kb[BATCH];
 #pragma unroll
-        for (int i = 0; i < S::KQ; ++i) {
-          v8h ka = *reinterpret_cast<const v8h*>(krow + 32 * i);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[i], acc, 0, 0, 0);
+        for (int j = 0; j < BATCH; ++j) {
+          if (i0 + j < S::KQ) {
+            ka[j] = *reinterpret_cast<const v8h*>(krow0 + 32 * (i0 + j));
+            kb[j] = *reinterpret_cast<const v8h*>(krow1 + 32 * (i0 + j));
+          }
         }
-        st[t] = acc;   // st[t][r] = S^T[entry 16t + 4g + r][head c16]
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          if (i0 + j < S::KQ) {
+            st[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[j], qf[i0 + j], st[0], 0, 0, 0);
+            st[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[j], qf[i0 + j], st[1], 0, 0, 0);
+          }
+        }
       }
       // ---- online softmax (log2 domain), per head = lane & 15
       float z[8];
@@ -286,16 +298,22 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           o[n][0] *= al[0]; o[n][1] *= al[1]; o[n][2] *= al[2]; o[n][3] *= al[3];
         }
       }
-      // ---- O += P V; B operand = V^T row (dim), entries 4g..4g+3 and 16+4g..16+4g+3
-      const _Float16* vrow = vt + c16 * kVtPitch + 4 * g;
+      // ---- O += P V over dims 256*dh ..; B operand = V^T row, entries 4g..4g+3 and 16+4g..16+4g+3
+      const _Float16* vrow = vt + (256 * dh + c16) * kVtPitch + 4 * g;
+      typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+      constexpr int VB = 8;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const _Float16* vp = vrow + (16 * n) * kVtPitch;
-        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-        v4h lo = *reinterpret_cast<const v4h*>(vp);
-        v4h hi = *reinterpret_cast<const v4h*>(vp + 16);
-        v8h vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf, o[n], 0, 0, 0);
+      for (int n0 = 0; n0 < NT; n0 += VB) {
+        v8h vf[VB];
+#pragma unroll
+        for (int j = 0; j < VB; ++j) {
+          const _Float16* vp = vrow + (16 * (n0 + j)) * kVtPitch;
+          v4h lo = *reinterpret_cast<const v4h*>(vp);
+          v4h hi = *reinterpret_cast<const v4h*>(vp + 16);
+          vf[j] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < VB; ++j) o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[j], o[n0 + j], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -309,7 +327,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   const int64_t pbase = (row * splits + split) * (int64_t)H;
-  if (g == 0) {
+  if (g == 0 && dh == 0) {
     part_ml[(pbase + head_b) * 2 + 0] = m_run;
     part_ml[(pbase + head_b) * 2 + 1] = l_tot;
   }
@@ -317,8 +335,8 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int h = 16 * wave + 4 * g + r;
-      part_o[(pbase + h) * DV + 16 * n + c16] = o[n][r];
+      int h = 16 * hg + 4 * g + r;
+      part_o[(pbase + h) * DV + 256 * dh + 16 * n + c16] = o[n][r];
     }
 }
 
