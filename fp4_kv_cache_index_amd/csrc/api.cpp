@@ -51,7 +51,7 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 // ----------------------------------------------------- index score topk ---
 
 struct ScoreLayout {
-  int64_t rows, n_stride, tiles, nb_max, nb_stride, nb_tiles;
+  int64_t rows, n_stride, nb_max, nb_stride;
   size_t off_keys, off_nvalid, off_tok, off_bkeys, off_nbvalid, off_blk, total;
 };
 
@@ -59,20 +59,16 @@ static ScoreLayout score_layout(int64_t B, int64_t Tq, int64_t n_max, int32_t po
   ScoreLayout L{};
   L.rows = B * Tq;
   L.n_stride = round_up(n_max > 0 ? n_max : 1, 64);
-  L.tiles = (n_max + kSelTile - 1) / kSelTile;
-  if (L.tiles < 1) L.tiles = 1;
   size_t o = 0;
   L.off_keys = o; o += al256(sizeof(uint32_t) * L.rows * L.n_stride);
   L.off_nvalid = o; o += al256(sizeof(int32_t) * L.rows);
-  L.off_tok = o; o += al256(select_ws_bytes(L.rows, L.tiles));
+  L.off_tok = o; o += al256(select_ws_bytes(L.rows, n_max));
   if (pool_block > 0) {
     L.nb_max = (n_max + pool_block - 1) / pool_block;
     L.nb_stride = round_up(L.nb_max > 0 ? L.nb_max : 1, 64);
-    L.nb_tiles = (L.nb_max + kSelTile - 1) / kSelTile;
-    if (L.nb_tiles < 1) L.nb_tiles = 1;
     L.off_bkeys = o; o += al256(sizeof(uint32_t) * L.rows * L.nb_stride);
     L.off_nbvalid = o; o += al256(sizeof(int32_t) * L.rows);
-    L.off_blk = o; o += al256(select_ws_bytes(L.rows, L.nb_tiles));
+    L.off_blk = o; o += al256(select_ws_bytes(L.rows, L.nb_max));
   }
   L.total = o;
   return L;
@@ -174,7 +170,7 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
     if (!pool_len || pool_nblocks <= 0 || !pool_block_ok(pool_block)) return CSA2_EINVAL;
   }
   if (!d_idx_ok(D_I) || H_I > 32) return CSA2_EUNSUPPORTED;
-  if (n_max > INT32_MAX || (int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
+  if (n_max > (int64_t)kSelTile * kMaxSelTiles || (int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
   if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;  // 16-byte slices per lane
   if ((k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
   ScoreLayout L = score_layout(B, Tq, n_max, pool ? pool_block : 0);
@@ -183,14 +179,14 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
   char* base = (char*)ws;
   uint32_t* keys = (uint32_t*)(base + L.off_keys);
   int32_t* n_valid = (int32_t*)(base + L.off_nvalid);
-  SelectWs tok = select_ws_carve(base + L.off_tok, L.rows, L.tiles);
+  SelectWs tok = select_ws_carve(base + L.off_tok, L.rows, n_max);
   SelectWs blk{};
   uint32_t* bkeys = nullptr;
   int32_t* nb_valid = nullptr;
   if (pool) {
     bkeys = (uint32_t*)(base + L.off_bkeys);
     nb_valid = (int32_t*)(base + L.off_nbvalid);
-    blk = select_ws_carve(base + L.off_blk, L.rows, L.nb_tiles);
+    blk = select_ws_carve(base + L.off_blk, L.rows, L.nb_max);
   }
   ScoreArgs a{q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max, k_top,
               pool ? pool_block : 0, pool ? pool_nblocks : 0};
@@ -200,11 +196,11 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
     e = launch_index_score(a, keys, L.n_stride, n_valid, tok, bkeys, L.nb_stride, nb_valid, pool ? &blk : nullptr, s);
   if (e == hipSuccess) {
     SelectOut out{topk_idx, topk_score, nullptr, 0, 0, nullptr, nullptr};
-    e = select_finish(tok, keys, L.n_stride, n_valid, L.rows, n_max, k_top, out, s);
+    e = select_finish(tok, keys, L.n_stride, n_valid, L.rows, k_top, out, s);
   }
   if (e == hipSuccess && pool) {
     SelectOut out{pool_idx, nullptr, nullptr, 0, pool_block, n_valid, pool_len};
-    e = select_finish(blk, bkeys, L.nb_stride, nb_valid, L.rows, L.nb_max, pool_nblocks, out, s);
+    e = select_finish(blk, bkeys, L.nb_stride, nb_valid, L.rows, pool_nblocks, out, s);
   }
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }
@@ -213,10 +209,8 @@ size_t csa2_hier_pool_topk_workspace_size(int32_t B, int32_t Tq, int32_t pool_ca
   (void)k_top;
   if (B < 0 || Tq < 0 || pool_cap < 0) return 0;
   int64_t rows = (int64_t)B * Tq;
-  int64_t tiles = (pool_cap + kSelTile - 1) / kSelTile;
-  if (tiles < 1) tiles = 1;
   return al256(sizeof(uint32_t) * rows * round_up(pool_cap > 0 ? pool_cap : 1, 64)) + al256(sizeof(int32_t) * rows) +
-         al256(select_ws_bytes(rows, tiles));
+         al256(select_ws_bytes(rows, pool_cap));
 }
 
 int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_batch_stride,
@@ -231,27 +225,25 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
   if (((uintptr_t)ws & 255u) != 0) return CSA2_EINVAL;
   if (!d_idx_ok(D_I) || H_I > 32) return CSA2_EUNSUPPORTED;
   if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;
-  if ((int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
+  if ((int64_t)B * Tq > 65535 || pool_cap > kSelTile * kMaxSelTiles) return CSA2_EUNSUPPORTED;
   size_t need = csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top);
   if (ws_bytes < need) return CSA2_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   int64_t rows = (int64_t)B * Tq;
   int64_t cap = round_up(pool_cap > 0 ? pool_cap : 1, 64);   // key row stride
-  int64_t tiles = (pool_cap + kSelTile - 1) / kSelTile;
-  if (tiles < 1) tiles = 1;
   char* base = (char*)ws;
   uint32_t* keys = (uint32_t*)base;
   base += al256(sizeof(uint32_t) * rows * cap);
   int32_t* n_valid = (int32_t*)base;
   base += al256(sizeof(int32_t) * rows);
-  SelectWs sw = select_ws_carve(base, rows, tiles);
+  SelectWs sw = select_ws_carve(base, rows, pool_cap);
   hipError_t e = select_clear(sw, rows, s);
   if (e == hipSuccess)
     e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B, Tq, H_I,
                           D_I, k_top, keys, cap, n_valid, sw, s);
   if (e == hipSuccess) {
     SelectOut out{topk_idx, topk_score, pool_idx, pool_cap, 0, nullptr, nullptr};
-    e = select_finish(sw, keys, cap, n_valid, rows, pool_cap, k_top, out, s);
+    e = select_finish(sw, keys, cap, n_valid, rows, k_top, out, s);
   }
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }

@@ -41,53 +41,50 @@ hipError_t launch_swa_fp8_quantize(const float* x, int64_t n_rows, int d, int64_
 // --------------------------------------------------------- radix select ---
 // Per-row exact Top-K over u32 keys (larger is better, key 0 = absent) of
 // the first n_valid[row] positions, ties to the lower position, emitted in
-// ascending position order.  Workspace: select_ws_bytes(rows, tiles).
-constexpr int kSelTile = 4096;      // positions per workgroup in the select passes
+// ascending position order.  The producer of the keys also builds `hist1`,
+// the per-row histogram of the top 12 key bits (after select_clear).
+constexpr int kSelTile = 4096;       // positions per workgroup in the select passes
+constexpr int kMaxSelTiles = 1024;   // positions per row <= kSelTile * kMaxSelTiles
 
-struct SelectRowCtl {               // per-row control block (64 bytes)
-  uint32_t arrive[6];               // last-workgroup counters of the passes
-  uint32_t mode;                    // 0 = refine, 1 = take every valid position
-  uint32_t prefix;                  // resolved key prefix so far
-  uint32_t need;                    // how many still to take at/below prefix
-  uint32_t thr;                     // final threshold key T
-  uint32_t need_eq;                 // ties at T to take (lowest positions)
-  uint32_t total;                   // number of positions emitted
-  uint32_t pad[4];
+struct SelectRowCtl {                // per-row control block (64 bytes)
+  uint32_t cand_count;               // candidates appended by the collect pass
+  uint32_t thr;                      // final threshold key T
+  uint32_t need_eq;                  // ties at T to take (lowest positions)
+  uint32_t total;                    // number of positions emitted
+  uint32_t pad[12];
 };
 
 struct SelectWs {
-  SelectRowCtl* ctl;                // [rows]
-  uint32_t* hist1;                  // [rows][4096]
-  uint32_t* hist2;                  // [rows][4096]
-  uint32_t* hist3;                  // [rows][256]
-  uint32_t* tile_gt;                // [rows][tiles]
-  uint32_t* tile_eq;                // [rows][tiles]
+  SelectRowCtl* ctl;                 // [rows]
+  uint32_t* hist1;                   // [rows][4096]
+  uint32_t* cand;                    // [rows][cand_cap] of (key, position)
+  uint32_t* tile_gt;                 // [rows][tiles] keys above the threshold bucket
+  uint32_t* tile_off;                // [rows][tiles] output offset of the tile
+  uint32_t* tile_eqb;                // [rows][tiles] threshold ties before the tile
+  int64_t cand_cap, tiles;
 };
-size_t select_ws_bytes(int64_t rows, int64_t tiles);
-SelectWs select_ws_carve(void* base, int64_t rows, int64_t tiles);
+size_t select_ws_bytes(int64_t rows, int64_t n_max);
+SelectWs select_ws_carve(void* base, int64_t rows, int64_t n_max);
 
 // Output modes of the emit pass.
 struct SelectOut {
-  int32_t* idx;                     // [rows][k] (row stride k)
-  float* score;                     // nullable [rows][k]
-  const int32_t* map;               // nullable [rows][map_stride]: emitted id = map[pos]
+  int32_t* idx;                      // [rows][k] (row stride k)
+  float* score;                      // nullable [rows][k]
+  const int32_t* map;                // nullable [rows][map_stride]: emitted id = map[pos]
   int64_t map_stride;
   // Pool expansion: when expand > 0 each selected position c (a block)
   // expands to ids c*expand + u (u < expand, id < expand_limit[row]) at
   // output slots slot*expand + u; pool_len[row] receives the valid count.
   int expand;
-  const int32_t* expand_limit;      // [rows] visible token count
-  int32_t* pool_len;                // [rows]
+  const int32_t* expand_limit;       // [rows] visible token count
+  int32_t* pool_len;                 // [rows]
 };
 
-// Clears the control blocks and histograms of `rows` rows.
+// Clears the control blocks and first-digit histograms of `rows` rows.
 hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s);
-// Pass 1 over stored keys (when the producer did not build histogram 1).
-hipError_t select_hist1(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
-                        int64_t rows, int64_t n_max, int k, hipStream_t s);
-// Passes 2..5: refine the threshold and emit the selection.
+// collect + finalize + emit, after the producer has written keys and hist1.
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
-                         int64_t rows, int64_t n_max, int k, const SelectOut& out, hipStream_t s);
+                         int64_t rows, int k, const SelectOut& out, hipStream_t s);
 
 // ------------------------------------------------------------- scoring ---
 struct ScoreArgs {

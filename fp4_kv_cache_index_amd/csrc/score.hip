@@ -23,9 +23,19 @@
 
 namespace csa2 {
 
-constexpr int kScanTile = 4096;       // tokens per workgroup of the flat scan
+#ifndef CSA2_SCAN_TILE
+#define CSA2_SCAN_TILE 4096
+#endif
+constexpr int kScanTile = CSA2_SCAN_TILE;   // max tokens per workgroup of the flat scan
 constexpr int kPoolTile = 512;        // pool positions per workgroup (later layers)
 constexpr int kScanWaves = 4;
+// 16-token MFMA groups per wave iteration (bytes in flight per wave =
+// 2 * 16 * groups * D_I); fewer for 32 indexer heads to bound the LDS tile.
+#ifndef CSA2_SCAN_GROUPS
+#define CSA2_SCAN_GROUPS 4
+#endif
+template <int HB>
+constexpr int kScanGroups = HB == 1 ? CSA2_SCAN_GROUPS : 4;
 
 template <int CH>
 struct Frag {
@@ -83,9 +93,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   constexpr int HMAX = 16 * HB;
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t bhist[POOL ? 4096 : 1];
-  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][64 * HMAX];
+  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HMAX];
   __shared__ float wsh[HMAX];
-  __shared__ uint32_t flag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;
@@ -114,6 +123,10 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     if (pool) bhist[i] = 0u;
   }
   if (threadIdx.x < HMAX) wsh[threadIdx.x] = threadIdx.x < H_I ? w[row * H_I + threadIdx.x] : 0.0f;
+  __syncthreads();
+  float wv[HMAX];   // head weights (0 past H_I), wave-uniform
+#pragma unroll
+  for (int h = 0; h < HMAX; ++h) wv[h] = wsh[h];
 
   // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
   const int c16 = lane & 15, g = lane >> 4;
@@ -134,7 +147,10 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   const uint8_t* kb = k_idx + b * k_bstride;
   const int32_t* prow = GATHER ? pool_idx + row * (int64_t)pool_cap : nullptr;
 
-  // Each wave owns tile/4 consecutive positions, 64 per iteration.
+  // Each wave owns tile/4 consecutive positions, SG*16 per iteration; the
+  // next iteration's key rows are in flight while this one is scored.
+  constexpr int SG = kScanGroups<HB>;
+  constexpr int IT = 16 * SG;
   const int64_t wbase = tile0 + (int64_t)wave * (tile / kScanWaves);
   int64_t wend = wbase + tile / kScanWaves;
   if (wend > nv) wend = nv;
@@ -146,33 +162,26 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     return frag_base<DI>(kb + (ok ? tokid : 0) * k_rstride, g);
   };
 
-  Frag<CH> cur[4], nxt[4];
-  if (wbase < wend) {
+  // Two fragment buffers used in ping-pong: while one batch of IT tokens is
+  // scored, the other batch's loads are in flight.
+  Frag<CH> fa[SG], fb[SG];
+  auto load_batch = [&](Frag<CH>(&f)[SG], int64_t base) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < SG; ++s) {
       bool ok;
-      const uint8_t* p = frag_ptr(wbase + 16 * s + c16, ok);
-      load_frag<CH, DI>(cur[s], p, ok);
+      const uint8_t* p = frag_ptr(base + 16 * s + c16, ok);
+      load_frag<CH, DI>(f[s], p, ok);
     }
-  }
-  for (int64_t it = wbase; it < wend; it += 64) {
-    const bool more = it + 64 < wend;
-    if (more) {
+  };
+  auto score_batch = [&](const Frag<CH>(&f)[SG], int64_t it) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bool ok;
-        const uint8_t* p = frag_ptr(it + 64 + 16 * s + c16, ok);
-        load_frag<CH, DI>(nxt[s], p, ok);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < SG; ++s) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < KS; ++i)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[hb][i], as_long(cur[s].w[2 * i], cur[s].w[2 * i + 1]),
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[hb][i], as_long(f[s].w[2 * i], f[s].w[2 * i + 1]),
                                                            acc, 0, 0, 0);
         // acc[r] = dot(head 16*hb + 4*g + r, token 16*s + c16)
         int h0 = 16 * hb + 4 * g;
@@ -181,38 +190,53 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    // Lane owns token it + lane.
-    const int64_t j = it + lane;
-    const bool vis = j < wend;
-    float sc = 0.0f;
-    const float* src = my + lane * pitch;
-    for (int h = 0; h < H_I; ++h) {
-      float d = src[h];
-      float r = d > 0.0f ? d : 0.0f;
-      sc = __fadd_rn(sc, __fmul_rn(wsh[h], r));
-    }
-    uint32_t key = vis ? score_key(sc) : 0u;
-    if (vis) {
-      keys[row * key_stride + j] = key;
-      atomicAdd(&hist[key >> 20], 1u);
-    }
-    if (pool) {
-      uint32_t m = key;
-      for (int off = 1; off < pool_block; off <<= 1) {
-        uint32_t o = __shfl_xor(m, off, 64);
-        m = m > o ? m : o;
+#pragma unroll
+    for (int u = 0; u < SG / 4; ++u) {
+      // Lane owns token it + 64u + lane.
+      const int64_t j = it + 64 * u + lane;
+      const bool vis = j < wend;
+      float sc = 0.0f;
+      const float* src = my + (64 * u + lane) * pitch;
+#pragma unroll
+      for (int h4 = 0; h4 < HMAX; h4 += 4) {
+        if (h4 < pitch) {
+          const v4f d4 = *reinterpret_cast<const v4f*>(src + h4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // heads past H_I have weight 0: adding +0 leaves the sum unchanged
+            float r = d4[e] > 0.0f ? d4[e] : 0.0f;
+            sc = __fadd_rn(sc, __fmul_rn(wv[h4 + e], r));
+          }
+        }
       }
-      if (vis && (j % pool_block) == 0) {
-        bkeys[row * bkey_stride + j / pool_block] = m;
-        atomicAdd(&bhist[m >> 20], 1u);
+      uint32_t key = vis ? score_key(sc) : 0u;
+      if (vis) {
+        keys[row * key_stride + j] = key;
+        atomicAdd(&hist[key >> 20], 1u);
+      }
+      if (pool) {
+        uint32_t m = key;
+        for (int off = 1; off < pool_block; off <<= 1) {
+          uint32_t o = __shfl_xor(m, off, 64);
+          m = m > o ? m : o;
+        }
+        if (vis && (j % pool_block) == 0) {
+          bkeys[row * bkey_stride + j / pool_block] = m;
+          atomicAdd(&bhist[m >> 20], 1u);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) cur[s] = nxt[s];
-    }
+  };
+
+  if (wbase < wend) load_batch(fa, wbase);
+  for (int64_t it = wbase; it < wend; it += 2 * IT) {
+    const bool has_b = it + IT < wend;
+    if (has_b) load_batch(fb, it + IT);
+    score_batch(fa, it);
+    if (it + 2 * IT < wend) load_batch(fa, it + 2 * IT);
+    if (has_b) score_batch(fb, it + IT);
   }
   __syncthreads();
   uint32_t* gh = tok.hist1 + row * 4096;
@@ -222,11 +246,6 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   if (pool)
     for (int i = threadIdx.x; i < 4096; i += 256)
       if (bhist[i]) atomic_add_agent(gbh + i, bhist[i]);
-  if (arrive_last(&tok.ctl[row].arrive[0], gridDim.x, &flag)) {
-    select_resolve1(&tok.ctl[row], gh, (uint32_t)k_top);
-    __syncthreads();
-    if (pool) select_resolve1(&blk.ctl[row], gbh, (uint32_t)nblocks);
-  }
 }
 
 template <int DI, int HB>

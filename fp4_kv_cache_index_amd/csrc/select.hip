@@ -7,13 +7,17 @@
 //
 // With T the k-th largest key and need_eq the number of keys equal to T that
 // belong to the selection, the selection is {key > T} plus the need_eq
-// lowest positions with key == T.  T is found digit by digit (12 + 12 + 8
-// bits) from histograms; each pass is a grid of workgroups over fixed tiles
-// of a row, and the last workgroup of a row to finish (counter election, no
-// waiting) resolves the digit for that row.  A final count pass gives every
-// tile its output offset, and the emit pass writes indices in order.  Rows
-// whose visible count is <= k, or whose threshold bucket is taken whole,
-// skip the remaining digit passes.
+// lowest positions with key == T.  The producer (the scoring kernel) writes
+// the keys and a histogram of their top 12 bits.  Then:
+//   collect  -- every workgroup resolves the threshold bucket from the
+//               histogram itself, counts its tile's keys above the bucket and
+//               appends the bucket's keys as (key, position) candidates;
+//   finalize -- one workgroup per row finds T and need_eq among the
+//               candidates (two more radix digits in LDS), then each tile's
+//               output offset and the -1 padding;
+//   emit     -- every tile writes its selected positions in ascending order.
+// No workgroup waits for or elects another; kernel boundaries order the
+// passes.  The key array is read twice after it is written.
 #include "common.h"
 #include "internal.h"
 #include "select_dev.h"
@@ -22,26 +26,34 @@ namespace csa2 {
 
 static __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t select_ws_bytes(int64_t rows, int64_t tiles) {
+static int64_t sel_tiles(int64_t n_max) {
+  int64_t t = (n_max + kSelTile - 1) / kSelTile;
+  return t < 1 ? 1 : t;
+}
+static int64_t sel_cap(int64_t n_max) { return ((n_max > 0 ? n_max : 1) + 63) / 64 * 64; }
+
+size_t select_ws_bytes(int64_t rows, int64_t n_max) {
+  const int64_t tiles = sel_tiles(n_max), cap = sel_cap(n_max);
   size_t b = 0;
   b += align256(sizeof(SelectRowCtl) * rows);
   b += align256(sizeof(uint32_t) * 4096 * rows);
-  b += align256(sizeof(uint32_t) * 4096 * rows);
-  b += align256(sizeof(uint32_t) * 256 * rows);
-  b += align256(sizeof(uint32_t) * tiles * rows);
-  b += align256(sizeof(uint32_t) * tiles * rows);
+  b += align256(sizeof(uint32_t) * 2 * cap * rows);
+  b += 3 * align256(sizeof(uint32_t) * tiles * rows);
   return b;
 }
 
-SelectWs select_ws_carve(void* base, int64_t rows, int64_t tiles) {
+SelectWs select_ws_carve(void* base, int64_t rows, int64_t n_max) {
+  const int64_t tiles = sel_tiles(n_max), cap = sel_cap(n_max);
   char* p = (char*)base;
   SelectWs w;
   w.ctl = (SelectRowCtl*)p; p += align256(sizeof(SelectRowCtl) * rows);
   w.hist1 = (uint32_t*)p; p += align256(sizeof(uint32_t) * 4096 * rows);
-  w.hist2 = (uint32_t*)p; p += align256(sizeof(uint32_t) * 4096 * rows);
-  w.hist3 = (uint32_t*)p; p += align256(sizeof(uint32_t) * 256 * rows);
+  w.cand = (uint32_t*)p; p += align256(sizeof(uint32_t) * 2 * cap * rows);
   w.tile_gt = (uint32_t*)p; p += align256(sizeof(uint32_t) * tiles * rows);
-  w.tile_eq = (uint32_t*)p;
+  w.tile_off = (uint32_t*)p; p += align256(sizeof(uint32_t) * tiles * rows);
+  w.tile_eqb = (uint32_t*)p;
+  w.cand_cap = cap;
+  w.tiles = tiles;
   return w;
 }
 
@@ -69,146 +81,134 @@ __global__ void select_clear_kernel(uint32_t* p, int64_t n_words) {
     p[i] = 0u;
 }
 
-// Pass 1 over stored keys: histogram of the top 12 bits.
+// collect: counts above the threshold bucket per tile; appends the bucket.
 __global__ void __launch_bounds__(256)
-select_hist1_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
-                    const int32_t* __restrict__ n_valid, int k) {
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t flag;
+select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
+                      const int32_t* __restrict__ n_valid, int k) {
+  __shared__ uint32_t red[4], res[4];
+  __shared__ uint32_t slot0;
   const int64_t row = blockIdx.y;
-  const int64_t base = (int64_t)blockIdx.x * kSelTile;
+  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
   const int64_t nv = n_valid[row];
-  for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
-  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kSelTile;
   uint32_t kk[16];
   load_tile_keys(keys + row * key_stride, base, nv, kk);
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (kk[i]) atomicAdd(&hist[kk[i] >> 20], 1u);
-  __syncthreads();
-  uint32_t* gh = ws.hist1 + row * 4096;
-  for (int i = threadIdx.x; i < 4096; i += 256)
-    if (hist[i]) atomic_add_agent(gh + i, hist[i]);
-  if (arrive_last(&ws.ctl[row].arrive[0], gridDim.x, &flag)) select_resolve1(&ws.ctl[row], gh, (uint32_t)k);
-}
-
-// Pass 2 (DIGIT = 2) and pass 3 (DIGIT = 3): refine the threshold.
-template <int DIGIT>
-__global__ void __launch_bounds__(256)
-select_refine_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
-                     const int32_t* __restrict__ n_valid) {
-  constexpr int BINS = DIGIT == 2 ? 4096 : 256;
-  constexpr int SHIFT = DIGIT == 2 ? 20 : 8;         // prefix = key >> SHIFT
-  constexpr int DSHIFT = DIGIT == 2 ? 8 : 0;         // digit = (key >> DSHIFT) & (BINS-1)
-  __shared__ uint32_t hist[BINS];
-  __shared__ uint32_t flag;
-  __shared__ uint32_t red[4];
-  __shared__ uint32_t res[3];
-  const int64_t row = blockIdx.y;
-  SelectRowCtl* ctl = &ws.ctl[row];
-  const uint32_t mode = ctl->mode;
-  uint32_t* gh = (DIGIT == 2 ? ws.hist2 + row * 4096 : ws.hist3 + row * 256);
-  if (mode == 0u) {
-    const uint32_t prefix = ctl->prefix;
-    const int64_t base = (int64_t)blockIdx.x * kSelTile;
-    const int64_t nv = n_valid[row];
-    for (int i = threadIdx.x; i < BINS; i += 256) hist[i] = 0u;
-    __syncthreads();
-    uint32_t kk[16];
-    load_tile_keys(keys + row * key_stride, base, nv, kk);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (kk[i] && (kk[i] >> SHIFT) == prefix) atomicAdd(&hist[(kk[i] >> DSHIFT) & (BINS - 1)], 1u);
-    __syncthreads();
-    for (int i = threadIdx.x; i < BINS; i += 256)
-      if (hist[i]) atomic_add_agent(gh + i, hist[i]);
-  }
-  if (!arrive_last(&ctl->arrive[DIGIT - 1], gridDim.x, &flag)) return;
-  if (mode != 0u) return;
-  const uint32_t need = ctl->need;
-  resolve_digit<BINS>(gh, need, red, res);
-  if (threadIdx.x == 0) {
-    uint32_t d = res[0], above = res[1], cnt = res[2];
-    uint32_t prefix = (ctl->prefix << (DIGIT == 2 ? 12 : 8)) | d;
-    uint32_t n2 = need - above;
-    if (DIGIT == 3) {
-      ctl->thr = prefix;
-      ctl->need_eq = n2;
-      ctl->mode = 2u;
-    } else if (n2 == cnt) {
-      ctl->thr = (prefix << 8) - 1u;
-      ctl->need_eq = 0u;
-      ctl->mode = 2u;
-    } else {
-      ctl->prefix = prefix;
-      ctl->need = n2;
-    }
-  }
-}
-
-// Pass 4: per-tile counts of keys above and at the threshold; the last
-// workgroup turns them into output offsets and writes the -1 padding.
-__global__ void __launch_bounds__(256)
-select_count_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
-                    const int32_t* __restrict__ n_valid, int k, SelectOut out) {
-  __shared__ uint32_t flag;
-  __shared__ uint32_t red[4];
-  __shared__ uint32_t carry[2];
-  const int64_t row = blockIdx.y;
-  const int64_t tiles = gridDim.x;
-  SelectRowCtl* ctl = &ws.ctl[row];
-  const uint32_t thr = ctl->thr;
-  const int64_t base = (int64_t)blockIdx.x * kSelTile;
-  const int64_t nv = n_valid[row];
-  uint32_t kk[16];
-  load_tile_keys(keys + row * key_stride, base, nv, kk);
-  uint32_t gt = 0, eq = 0;
+  uint32_t gt = 0, nc = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    gt += kk[i] != 0u && kk[i] > thr;
-    eq += kk[i] != 0u && kk[i] == thr;
+    const bool valid = kk[i] != 0u;
+    const uint32_t bkt = kk[i] >> 20;
+    if (L.mode == 1u) gt += valid;
+    else if (L.mode == 2u) gt += valid && bkt >= L.d;
+    else {
+      gt += valid && bkt > L.d;
+      nc += valid && bkt == L.d;
+    }
   }
-  // workgroup sums
-  for (int off = 32; off > 0; off >>= 1) {
-    gt += __shfl_xor(gt, off, 64);
-    eq += __shfl_xor(eq, off, 64);
-  }
-  __shared__ uint32_t sgt[4], seq[4];
-  if ((threadIdx.x & 63) == 0) { sgt[threadIdx.x >> 6] = gt; seq[threadIdx.x >> 6] = eq; }
+  const uint32_t g_incl = block_prefix_sum_256(gt, red);
+  if (threadIdx.x == 255) ws.tile_gt[row * ws.tiles + blockIdx.x] = g_incl;
+  if (L.mode != 0u) return;
+  const uint32_t c_incl = block_prefix_sum_256(nc, red);
+  if (threadIdx.x == 255) slot0 = c_incl ? atomicAdd(&ws.ctl[row].cand_count, c_incl) : 0u;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    store_agent(ws.tile_gt + row * tiles + blockIdx.x, sgt[0] + sgt[1] + sgt[2] + sgt[3]);
-    store_agent(ws.tile_eq + row * tiles + blockIdx.x, seq[0] + seq[1] + seq[2] + seq[3]);
+  if (nc == 0u) return;
+  uint32_t slot = slot0 + c_incl - nc;
+  uint32_t* cr = ws.cand + row * 2 * ws.cand_cap;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (kk[i] != 0u && (kk[i] >> 20) == L.d) {
+      const int64_t pos = base + 4 * ((int64_t)threadIdx.x + 256 * (i >> 2)) + (i & 3);
+      cr[2 * slot] = kk[i];
+      cr[2 * slot + 1] = (uint32_t)pos;
+      ++slot;
+    }
   }
-  if (!arrive_last(&ctl->arrive[3], (uint32_t)tiles, &flag)) return;
-  // Exclusive scan over tiles, 256 at a time with a running carry.
-  const uint32_t need_eq = ctl->need_eq;
+}
+
+// finalize: one workgroup per row.
+__global__ void __launch_bounds__(256)
+select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t tsel[kMaxSelTiles], teq[kMaxSelTiles];
+  __shared__ uint32_t red[4], res[4];
+  __shared__ uint32_t carry[2];
+  const int64_t row = blockIdx.x;
+  const int64_t tiles = ws.tiles;
+  SelectRowCtl* ctl = &ws.ctl[row];
+  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
+  uint32_t thr, need_eq, total;
+  const uint32_t* cr = ws.cand + row * 2 * ws.cand_cap;
+  const uint32_t nc = L.mode == 0u ? ctl->cand_count : 0u;
+  if (L.mode == 1u) {
+    thr = 0u; need_eq = 0u; total = L.total;
+  } else if (L.mode == 2u) {
+    thr = (L.d << 20) - 1u; need_eq = 0u; total = (uint32_t)k;
+  } else {
+    total = (uint32_t)k;
+    const uint32_t need = (uint32_t)k - L.above;
+    for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t c = threadIdx.x; c < nc; c += 256) atomicAdd(&hist[(cr[2 * c] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    const Digit A = resolve_digit<4096>(hist, need, red, res);
+    const uint32_t need2 = need - A.above;
+    if (need2 == A.cnt) {
+      thr = (((L.d << 12) | A.d) << 8) - 1u;
+      need_eq = 0u;
+    } else {
+      for (int i = threadIdx.x; i < 256; i += 256) hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t c = threadIdx.x; c < nc; c += 256) {
+        const uint32_t key = cr[2 * c];
+        if (((key >> 8) & 0xFFFu) == A.d) atomicAdd(&hist[key & 0xFFu], 1u);
+      }
+      __syncthreads();
+      const Digit Bd = resolve_digit<256>(hist, need2, red, res);
+      thr = (L.d << 20) | (A.d << 8) | Bd.d;
+      need_eq = need2 - Bd.above;
+    }
+  }
+  // Selected candidates and ties per tile.
+  for (int64_t t = threadIdx.x; t < tiles; t += 256) {
+    tsel[t] = 0u;
+    teq[t] = 0u;
+  }
+  __syncthreads();
+  for (uint32_t c = threadIdx.x; c < nc; c += 256) {
+    const uint32_t key = cr[2 * c], tile = cr[2 * c + 1] / kSelTile;
+    if (key > thr) atomicAdd(&tsel[tile], 1u);
+    else if (key == thr) atomicAdd(&teq[tile], 1u);
+  }
   if (threadIdx.x == 0) { carry[0] = 0u; carry[1] = 0u; }
   __syncthreads();
+  // Exclusive scan over tiles, 256 at a time with a running carry.
   for (int64_t t0 = 0; t0 < tiles; t0 += 256) {
-    int64_t t = t0 + threadIdx.x;
+    const int64_t t = t0 + threadIdx.x;
     uint32_t g = 0, e = 0;
     if (t < tiles) {
-      g = load_agent(ws.tile_gt + row * tiles + t);
-      e = load_agent(ws.tile_eq + row * tiles + t);
+      g = ws.tile_gt[row * tiles + t] + tsel[t];
+      e = teq[t];
     }
-    uint32_t c_out = carry[0], c_eq = carry[1];
-    uint32_t e_incl = block_prefix_sum_256(e, red);
-    uint32_t eq_before = c_eq + e_incl - e;
+    const uint32_t c_out = carry[0], c_eq = carry[1];
+    const uint32_t e_incl = block_prefix_sum_256(e, red);
+    const uint32_t eq_before = c_eq + e_incl - e;
     uint32_t take = 0;
     if (need_eq > eq_before) take = (need_eq - eq_before) < e ? (need_eq - eq_before) : e;
-    uint32_t sel = g + take;
-    uint32_t s_incl = block_prefix_sum_256(sel, red);
+    const uint32_t sel = g + take;
+    const uint32_t s_incl = block_prefix_sum_256(sel, red);
     if (t < tiles) {
-      ws.tile_gt[row * tiles + t] = c_out + s_incl - sel;   // output offset of this tile
-      ws.tile_eq[row * tiles + t] = eq_before;              // ties before this tile
+      ws.tile_off[row * tiles + t] = c_out + s_incl - sel;
+      ws.tile_eqb[row * tiles + t] = eq_before;
     }
     __syncthreads();
     if (threadIdx.x == 255) { carry[0] = c_out + s_incl; carry[1] = c_eq + e_incl; }
     __syncthreads();
   }
-  const uint32_t total = carry[0];
-  if (threadIdx.x == 0) ctl->total = total;
+  if (threadIdx.x == 0) {
+    ctl->thr = thr;
+    ctl->need_eq = need_eq;
+    ctl->total = total;
+  }
   // Padding.
   if (out.expand == 0) {
     int32_t* oi = out.idx + row * (int64_t)k;
@@ -225,18 +225,18 @@ select_count_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_
   }
 }
 
-// Pass 5: emit the selected positions of each tile in ascending order.
+// emit: the selected positions of each tile, in ascending order.
 __global__ void __launch_bounds__(256)
 select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
                    const int32_t* __restrict__ n_valid, int k, SelectOut out) {
   constexpr int PER = kSelTile / 256;  // consecutive positions per thread
   __shared__ uint32_t red[4];
   const int64_t row = blockIdx.y;
-  const int64_t tiles = gridDim.x;
+  const int64_t tiles = ws.tiles;
   const SelectRowCtl* ctl = &ws.ctl[row];
   const uint32_t thr = ctl->thr, need_eq = ctl->need_eq;
-  const uint32_t off0 = ws.tile_gt[row * tiles + blockIdx.x];
-  const uint32_t eqb0 = ws.tile_eq[row * tiles + blockIdx.x];
+  const uint32_t off0 = ws.tile_off[row * tiles + blockIdx.x];
+  const uint32_t eqb0 = ws.tile_eqb[row * tiles + blockIdx.x];
   const int64_t nv = n_valid[row];
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
   if (base >= nv) return;
@@ -300,32 +300,20 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
 // ---------------------------------------------------------------- host ---
 
 hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s) {
-  // ctl, hist1, hist2 and hist3 are carved contiguously.
-  int64_t words = (int64_t)((char*)(ws.hist3 + 256 * rows) - (char*)ws.ctl) / 4;
-  int64_t grid = (words + 255) / 256;
-  if (grid > 4096) grid = 4096;
+  // ctl and hist1 are carved contiguously.
+  int64_t words = (int64_t)((char*)(ws.hist1 + 4096 * rows) - (char*)ws.ctl) / 4;
+  int64_t grid = (words + 1023) / 1024;
+  if (grid > 2048) grid = 2048;
   CSA2_LAUNCH("select_clear", select_clear_kernel, dim3((unsigned)grid), dim3(256), 0, s, (uint32_t*)ws.ctl,
               words);
   return hipGetLastError();
 }
 
-hipError_t select_hist1(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
-                        int64_t rows, int64_t n_max, int k, hipStream_t s) {
-  int64_t tiles = (n_max + kSelTile - 1) / kSelTile;
-  if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("select_hist1", select_hist1_kernel, dim3((unsigned)tiles, (unsigned)rows), dim3(256), 0, s, ws,
-              keys, key_stride, n_valid, k);
-  return hipGetLastError();
-}
-
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
-                         int64_t rows, int64_t n_max, int k, const SelectOut& out, hipStream_t s) {
-  int64_t tiles = (n_max + kSelTile - 1) / kSelTile;
-  if (tiles < 1) tiles = 1;
-  dim3 grid((unsigned)tiles, (unsigned)rows);
-  CSA2_LAUNCH("select_refine2", select_refine_kernel<2>, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid);
-  CSA2_LAUNCH("select_refine3", select_refine_kernel<3>, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid);
-  CSA2_LAUNCH("select_count", select_count_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k, out);
+                         int64_t rows, int k, const SelectOut& out, hipStream_t s) {
+  dim3 grid((unsigned)ws.tiles, (unsigned)rows);
+  CSA2_LAUNCH("select_collect", select_collect_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k);
+  CSA2_LAUNCH("select_finalize", select_finalize_kernel, dim3((unsigned)rows), dim3(256), 0, s, ws, k, out);
   CSA2_LAUNCH("select_emit", select_emit_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k, out);
   return hipGetLastError();
 }

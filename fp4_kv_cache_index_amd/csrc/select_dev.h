@@ -1,13 +1,11 @@
-// Device-side pieces of the radix select shared by the select passes and by
-// the producers (scoring kernels) that build the first histogram themselves.
+// Device-side helpers of the radix select: workgroup scans and the
+// resolution of a radix digit from a histogram.
 #pragma once
 
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
-
-// ------------------------------------------------------------ helpers ---
 
 // Inclusive suffix sum over the 256 threads of a workgroup (thread t gets
 // the sum of v over threads t..255).  `red` is LDS scratch of 4 words.
@@ -42,17 +40,22 @@ __device__ __forceinline__ uint32_t block_prefix_sum_256(uint32_t v, uint32_t* r
   return v + add;
 }
 
-// Given a global histogram of BINS bins and need >= 1 (<= total), find the
-// digit d with  sum_{e>d} h[e] < need <= sum_{e>=d} h[e].  Returns (d, above,
-// count of d) in res[0..2].  Run by all 256 threads of the workgroup.
+// Digit of a BINS-bin histogram (global or shared memory) at which the
+// running count from the top reaches `need` (1 <= need <= total):
+//   sum_{e>d} h[e] < need <= sum_{e>=d} h[e].
+// Every thread returns the same (d, above = sum_{e>d} h[e], h[d]).
+struct Digit {
+  uint32_t d, above, cnt;
+};
+
 template <int BINS>
-__device__ void resolve_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res) {
+__device__ Digit resolve_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res) {
   constexpr int BPT = BINS / 256;
   uint32_t h[BPT];
   uint32_t sum = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    h[i] = load_agent(hist + threadIdx.x * BPT + i);
+    h[i] = hist[threadIdx.x * BPT + i];
     sum += h[i];
   }
   uint32_t incl = block_suffix_sum_256(sum, red);
@@ -70,45 +73,35 @@ __device__ void resolve_digit(const uint32_t* hist, uint32_t need, uint32_t* red
     }
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t row_total_from_hist(const uint32_t* hist, uint32_t* red) {
-  uint32_t sum = 0;
-  for (int i = 0; i < 16; ++i) sum += load_agent(hist + threadIdx.x * 16 + i);
-  uint32_t incl = block_suffix_sum_256(sum, red);
-  __shared__ uint32_t tot;
-  if (threadIdx.x == 0) tot = incl;
+  Digit r{res[0], res[1], res[2]};
   __syncthreads();
-  return tot;
+  return r;
 }
 
-// Digit-1 resolution, run by the last workgroup of a row's first pass
-// (producers that build histogram 1 call this too).
-__device__ __forceinline__ void select_resolve1(SelectRowCtl* ctl, const uint32_t* hist1, uint32_t k) {
-  __shared__ uint32_t red[4];
-  __shared__ uint32_t res[3];
-  uint32_t total = row_total_from_hist(hist1, red);
-  if (total <= k) {
-    if (threadIdx.x == 0) {
-      ctl->mode = 1u; ctl->thr = 0u; ctl->need_eq = 0u; ctl->total = total;
-    }
-    return;
-  }
-  resolve_digit<4096>(hist1, k, red, res);
-  if (threadIdx.x == 0) {
-    uint32_t d = res[0], above = res[1], cnt = res[2];
-    uint32_t need = k - above;
-    ctl->mode = 0u;
-    ctl->prefix = d;
-    ctl->need = need;
-    ctl->total = k;
-    if (need == cnt) {              // the whole bucket is taken
-      ctl->mode = 2u;
-      ctl->thr = (d << 20) - 1u;
-      ctl->need_eq = 0u;
-    }
-  }
-}
+// First-digit state of a row, derived from its complete 12-bit histogram.
+struct Level1 {
+  uint32_t total;   // valid positions of the row
+  uint32_t mode;    // 0: refine inside bucket d; 1: take every valid position;
+                    // 2: take buckets >= d whole (threshold thr1 = (d << 20) - 1)
+  uint32_t d, above, cnt;
+};
 
+__device__ __forceinline__ Level1 resolve_level1(const uint32_t* hist1, uint32_t k, uint32_t* red, uint32_t* res) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += hist1[threadIdx.x * 16 + i];
+  uint32_t incl = block_suffix_sum_256(sum, red);
+  if (threadIdx.x == 0) res[3] = incl;
+  __syncthreads();
+  Level1 L{res[3], 1u, 0u, 0u, 0u};
+  __syncthreads();
+  if (L.total <= k) return L;
+  Digit dg = resolve_digit<4096>(hist1, k, red, res);
+  L.d = dg.d;
+  L.above = dg.above;
+  L.cnt = dg.cnt;
+  L.mode = (k - dg.above == dg.cnt) ? 2u : 0u;
+  return L;
+}
 
 }  // namespace csa2
