@@ -13,8 +13,8 @@
 //               histogram itself, counts its tile's keys above the bucket and
 //               appends the bucket's keys as (key, position) candidates;
 //   finalize -- one workgroup per row finds T and need_eq among the
-//               candidates (two more radix digits in LDS), then each tile's
-//               output offset and the -1 padding;
+//               candidates (two more radix digits, in LDS), every tile's
+//               output offset, the -1 padding and the pool length;
 //   emit     -- every tile writes its selected positions in ascending order.
 // No workgroup waits for or elects another; kernel boundaries order the
 // passes.  The key array is read twice after it is written.
@@ -88,11 +88,11 @@ select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t ke
   __shared__ uint32_t red[4], res[4];
   __shared__ uint32_t slot0;
   const int64_t row = blockIdx.y;
-  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
   const int64_t nv = n_valid[row];
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
   uint32_t kk[16];
-  load_tile_keys(keys + row * key_stride, base, nv, kk);
+  load_tile_keys(keys + row * key_stride, base, nv, kk);   // in flight during the resolution
+  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
   uint32_t gt = 0, nc = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -125,20 +125,51 @@ select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t ke
   }
 }
 
-// finalize: one workgroup per row.
+__device__ __forceinline__ uint32_t block_sum_256(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const uint32_t t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+constexpr int kCandLds = 4096;   // candidates staged in LDS by the finalize pass
+
+// finalize (one workgroup per row): the exact threshold T and tie count from
+// the candidates (staged in LDS when they fit), every tile's output offset
+// and the ties before it, the -1 padding and the pool length.
 __global__ void __launch_bounds__(256)
-select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
+select_finalize_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
+                       const int32_t* __restrict__ n_valid, int k, SelectOut out) {
   __shared__ uint32_t hist[4096];
+  __shared__ uint32_t ck[kCandLds], cp[kCandLds];
   __shared__ uint32_t tsel[kMaxSelTiles], teq[kMaxSelTiles];
   __shared__ uint32_t red[4], res[4];
   __shared__ uint32_t carry[2];
   const int64_t row = blockIdx.x;
   const int64_t tiles = ws.tiles;
-  SelectRowCtl* ctl = &ws.ctl[row];
+  const int64_t nv = n_valid[row];
   const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
-  uint32_t thr, need_eq, total;
+  const uint32_t nc = L.mode == 0u ? ws.ctl[row].cand_count : 0u;
   const uint32_t* cr = ws.cand + row * 2 * ws.cand_cap;
-  const uint32_t nc = L.mode == 0u ? ctl->cand_count : 0u;
+  const bool in_lds = nc <= (uint32_t)kCandLds;
+  if (in_lds) {
+    for (uint32_t c = threadIdx.x; c < nc; c += 256) {
+      ck[c] = cr[2 * c];
+      cp[c] = cr[2 * c + 1];
+    }
+  }
+  for (int64_t t = threadIdx.x; t < tiles; t += 256) {
+    tsel[t] = 0u;
+    teq[t] = 0u;
+  }
+  __syncthreads();
+  auto cand_key = [&](uint32_t c) { return in_lds ? ck[c] : cr[2 * c]; };
+  auto cand_pos = [&](uint32_t c) { return in_lds ? cp[c] : cr[2 * c + 1]; };
+  uint32_t thr, need_eq, total;
   if (L.mode == 1u) {
     thr = 0u; need_eq = 0u; total = L.total;
   } else if (L.mode == 2u) {
@@ -148,7 +179,7 @@ select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
     const uint32_t need = (uint32_t)k - L.above;
     for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0u;
     __syncthreads();
-    for (uint32_t c = threadIdx.x; c < nc; c += 256) atomicAdd(&hist[(cr[2 * c] >> 8) & 0xFFFu], 1u);
+    for (uint32_t c = threadIdx.x; c < nc; c += 256) atomicAdd(&hist[(cand_key(c) >> 8) & 0xFFFu], 1u);
     __syncthreads();
     const Digit A = resolve_digit<4096>(hist, need, red, res);
     const uint32_t need2 = need - A.above;
@@ -159,7 +190,7 @@ select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
       for (int i = threadIdx.x; i < 256; i += 256) hist[i] = 0u;
       __syncthreads();
       for (uint32_t c = threadIdx.x; c < nc; c += 256) {
-        const uint32_t key = cr[2 * c];
+        const uint32_t key = cand_key(c);
         if (((key >> 8) & 0xFFFu) == A.d) atomicAdd(&hist[key & 0xFFu], 1u);
       }
       __syncthreads();
@@ -169,18 +200,17 @@ select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
     }
   }
   // Selected candidates and ties per tile.
-  for (int64_t t = threadIdx.x; t < tiles; t += 256) {
-    tsel[t] = 0u;
-    teq[t] = 0u;
-  }
-  __syncthreads();
+  uint32_t eq_all = 0;
   for (uint32_t c = threadIdx.x; c < nc; c += 256) {
-    const uint32_t key = cr[2 * c], tile = cr[2 * c + 1] / kSelTile;
+    const uint32_t key = cand_key(c), tile = cand_pos(c) / kSelTile;
     if (key > thr) atomicAdd(&tsel[tile], 1u);
-    else if (key == thr) atomicAdd(&teq[tile], 1u);
+    else if (key == thr) {
+      atomicAdd(&teq[tile], 1u);
+      ++eq_all;
+    }
   }
   if (threadIdx.x == 0) { carry[0] = 0u; carry[1] = 0u; }
-  __syncthreads();
+  eq_all = block_sum_256(eq_all, red);
   // Exclusive scan over tiles, 256 at a time with a running carry.
   for (int64_t t0 = 0; t0 < tiles; t0 += 256) {
     const int64_t t = t0 + threadIdx.x;
@@ -205,9 +235,9 @@ select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    ctl->thr = thr;
-    ctl->need_eq = need_eq;
-    ctl->total = total;
+    ws.ctl[row].thr = thr;
+    ws.ctl[row].need_eq = need_eq;
+    ws.ctl[row].total = total;
   }
   // Padding.
   if (out.expand == 0) {
@@ -221,7 +251,17 @@ select_finalize_kernel(SelectWs ws, int k, SelectOut out) {
     const int64_t cap = (int64_t)k * out.expand;
     int32_t* oi = out.idx + row * cap;
     for (int64_t i = (int64_t)total * out.expand + threadIdx.x; i < cap; i += 256) oi[i] = -1;
-    if (threadIdx.x == 0) out.pool_len[row] = (int32_t)(total * out.expand);
+    if (threadIdx.x == 0) {
+      // Only the last block of the row can be partial; it is selected when
+      // it is above T, or at T with every tie taken (it is the last tie).
+      int32_t len = (int32_t)(total * out.expand);
+      if (nv > 0) {
+        const uint32_t klast = keys[row * key_stride + nv - 1];
+        const bool sel_last = L.mode == 1u || klast > thr || (klast == thr && eq_all <= need_eq);
+        if (sel_last) len -= (int32_t)(nv * out.expand - out.expand_limit[row]);
+      }
+      out.pool_len[row] = len;
+    }
   }
 }
 
@@ -233,10 +273,6 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   __shared__ uint32_t red[4];
   const int64_t row = blockIdx.y;
   const int64_t tiles = ws.tiles;
-  const SelectRowCtl* ctl = &ws.ctl[row];
-  const uint32_t thr = ctl->thr, need_eq = ctl->need_eq;
-  const uint32_t off0 = ws.tile_off[row * tiles + blockIdx.x];
-  const uint32_t eqb0 = ws.tile_eqb[row * tiles + blockIdx.x];
   const int64_t nv = n_valid[row];
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
   if (base >= nv) return;
@@ -250,6 +286,9 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
 #pragma unroll
     for (int j = 0; j < 4; ++j) kk[4 * i + j] = (p0 + 4 * i + j < nv) ? v[j] : 0u;
   }
+  const uint32_t thr = ws.ctl[row].thr, need_eq = ws.ctl[row].need_eq;
+  const uint32_t off0 = ws.tile_off[row * tiles + blockIdx.x];
+  const uint32_t eqb0 = ws.tile_eqb[row * tiles + blockIdx.x];
   uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -284,14 +323,10 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
     } else {
       const int64_t cap = (int64_t)k * out.expand;
       const int32_t lim = out.expand_limit[row];
-      int32_t invalid = 0;
       for (int u = 0; u < out.expand; ++u) {
         int64_t id = pos * out.expand + u;
-        bool ok = id < lim;
-        out.idx[row * cap + (int64_t)slot * out.expand + u] = ok ? (int32_t)id : -1;
-        invalid += !ok;
+        out.idx[row * cap + (int64_t)slot * out.expand + u] = id < lim ? (int32_t)id : -1;
       }
-      if (invalid) atomicSub(&out.pool_len[row], invalid);
     }
     ++slot;
   }
@@ -313,7 +348,8 @@ hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_s
                          int64_t rows, int k, const SelectOut& out, hipStream_t s) {
   dim3 grid((unsigned)ws.tiles, (unsigned)rows);
   CSA2_LAUNCH("select_collect", select_collect_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k);
-  CSA2_LAUNCH("select_finalize", select_finalize_kernel, dim3((unsigned)rows), dim3(256), 0, s, ws, k, out);
+  CSA2_LAUNCH("select_finalize", select_finalize_kernel, dim3((unsigned)rows), dim3(256), 0, s, ws, keys, key_stride,
+              n_valid, k, out);
   CSA2_LAUNCH("select_emit", select_emit_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k, out);
   return hipGetLastError();
 }

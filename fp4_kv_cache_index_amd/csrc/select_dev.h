@@ -48,16 +48,12 @@ struct Digit {
   uint32_t d, above, cnt;
 };
 
-template <int BINS>
-__device__ Digit resolve_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res) {
-  constexpr int BPT = BINS / 256;
-  uint32_t h[BPT];
+// Resolution from per-thread bin counts h[0..BPT) of bins tid*BPT + i.
+template <int BPT>
+__device__ Digit resolve_digit_regs(const uint32_t (&h)[BPT], uint32_t need, uint32_t* red, uint32_t* res) {
   uint32_t sum = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = hist[threadIdx.x * BPT + i];
-    sum += h[i];
-  }
+  for (int i = 0; i < BPT; ++i) sum += h[i];
   uint32_t incl = block_suffix_sum_256(sum, red);
   uint32_t excl = incl - sum;
   if (excl < need && need <= incl) {
@@ -78,6 +74,15 @@ __device__ Digit resolve_digit(const uint32_t* hist, uint32_t need, uint32_t* re
   return r;
 }
 
+template <int BINS>
+__device__ Digit resolve_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res) {
+  constexpr int BPT = BINS / 256;
+  uint32_t h[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) h[i] = hist[threadIdx.x * BPT + i];
+  return resolve_digit_regs<BPT>(h, need, red, res);
+}
+
 // First-digit state of a row, derived from its complete 12-bit histogram.
 struct Level1 {
   uint32_t total;   // valid positions of the row
@@ -87,20 +92,39 @@ struct Level1 {
 };
 
 __device__ __forceinline__ Level1 resolve_level1(const uint32_t* hist1, uint32_t k, uint32_t* red, uint32_t* res) {
+  uint32_t h[16];
   uint32_t sum = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) sum += hist1[threadIdx.x * 16 + i];
+  for (int i = 0; i < 16; ++i) {
+    h[i] = hist1[threadIdx.x * 16 + i];
+    sum += h[i];
+  }
+  // Total: thread 0's inclusive suffix sum.
   uint32_t incl = block_suffix_sum_256(sum, red);
   if (threadIdx.x == 0) res[3] = incl;
   __syncthreads();
   Level1 L{res[3], 1u, 0u, 0u, 0u};
   __syncthreads();
   if (L.total <= k) return L;
-  Digit dg = resolve_digit<4096>(hist1, k, red, res);
-  L.d = dg.d;
-  L.above = dg.above;
-  L.cnt = dg.cnt;
-  L.mode = (k - dg.above == dg.cnt) ? 2u : 0u;
+  const uint32_t excl = incl - sum;
+  if (excl < k && k <= incl) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      if (run + h[i] >= k && run < k) {
+        res[0] = threadIdx.x * 16 + i;
+        res[1] = run;
+        res[2] = h[i];
+      }
+      run += h[i];
+    }
+  }
+  __syncthreads();
+  L.d = res[0];
+  L.above = res[1];
+  L.cnt = res[2];
+  __syncthreads();
+  L.mode = (k - L.above == L.cnt) ? 2u : 0u;
   return L;
 }
 
