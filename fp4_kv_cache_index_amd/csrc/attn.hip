@@ -11,16 +11,18 @@
 //
 // gfx950 mapping.  A workgroup holds one query row and a contiguous split of
 // its entry list (Top-K rows, then the window rows).  Its 8 waves (two per
-// SIMD) each own 16 heads and half of the 512 output dims, which keeps the
-// fp32 O accumulators at 64 registers per lane.  Per chunk of 32 entries it gathers the rows by index
-// (coalesced: consecutive lanes read consecutive 8-byte code groups of a
-// row), dequantises them into LDS as fp16 with the gfx950 scaled converts
-// (v_cvt_scalef32_pk_f16_fp4 / _fp8, which apply the power-of-two part of
-// their scale; the E4M3 scale of a main row is applied as an fp16 multiply)
-// -- exact, since E2M1 x E4M3 has at most 6 significant bits within
-// [2^-10, 2688] -- and runs
-//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16 (q rounded to fp16 once),
-//   online softmax in fp32 (exp2 domain),
+// SIMD) form 4 head groups of 16 heads; the two waves of a head group own
+// one half each of the 64 entries of a chunk for S and one half each of the
+// 512 output dims for O (64 fp32 accumulator registers per lane).  Per chunk
+// of 64 entries it gathers the rows by index, dequantises them into LDS as
+// fp16 with the gfx950 scaled converts (v_cvt_scalef32_pk_f16_fp4 / _fp8,
+// which apply the power-of-two part of their scale; the E4M3 scale of a main
+// row is applied as an fp16 multiply) -- exact, since E2M1 x E4M3 has at most
+// 6 significant bits within [2^-10, 2688] -- and runs
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16 (q rounded to fp16 once), each
+//                 wave for its 32 entries,
+//   online softmax in fp32 (exp2 domain); the wave pair exchanges row maxima
+//                 and its P fragments through LDS,
 //   O  += P V     on the same instruction, P taken straight from the S^T
 //                 accumulators (their lane layout is the A-operand layout of
 //                 P once the k index is permuted identically for V).
@@ -31,7 +33,7 @@
 
 namespace csa2 {
 
-constexpr int kChunk = 32;           // entries per LDS chunk
+constexpr int kChunk = 64;           // entries per LDS chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -53,7 +55,7 @@ __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
 
 constexpr int kMaxSpan = 1024;      // entries per split (ids staged in LDS)
 constexpr int kAttnThreads = 512;   // 8 waves; wave w: heads 16*(w&3).., output dims 256*(w>>2)..
-constexpr int kVtPitch = kChunk + 4;  // fp16 per V^T row (18 dwords: spreads banks)
+constexpr int kVtPitch = kChunk + 4;  // fp16 per V^T row (34 dwords: spreads banks)
 
 // Raw bytes of one gather task: two entries (2*ep, 2*ep+1) of one 16-channel group.
 struct RawTask {
@@ -69,10 +71,13 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   using S = AttnShape<DQK>;
   constexpr int NT = DV / 32;                         // output tiles per wave (half the dims)
   constexpr int NTASK = (kChunk / 2) * S::G16;        // (entry pair, group) tasks per chunk
+  constexpr int NEP = kChunk / 2;                     // entry pairs per chunk
   constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
   __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * S::PITCH];   // K rows, row-major
   __shared__ __attribute__((aligned(16))) _Float16 vt[DV * kVtPitch];       // V transposed
   __shared__ int32_t eid[kMaxSpan];   // main: token id; window: window row; -1 = skip
+  __shared__ float pmx[2][64];        // per-head partial maxima / sums of the two dim halves
+  __shared__ __attribute__((aligned(16))) v8h pex[8][64];   // P fragments exchanged between wave pairs
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
@@ -139,7 +144,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       const int task = threadIdx.x + u * kAttnThreads;
       raw[u].kind = 0;
       if (task < NTASK) {
-        const int ep = task & 15, gq = task >> 4;
+        const int ep = task % NEP, gq = task / NEP;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int ce = c0 + 2 * ep + k;
@@ -166,7 +171,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
       if (task >= NTASK) break;
-      const int ep = task & 15, gq = task >> 4;
+      const int ep = task % NEP, gq = task / NEP;
       uint32_t hv[2][8];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -231,10 +236,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   for (int c0 = e_begin; c0 < e_end; c0 += kChunk) {
     const bool has_next = c0 + kChunk < e_end;
     if (has_next) gather(c0 + kChunk);   // in flight during this chunk's math
+    // ---- S^T = K Q^T for this wave's 2 tiles of 16 entries: entries 32*dh ..
+    float z[8];
+    float cmax = -__builtin_inff();
     if (active) {
-      // ---- S^T = K Q^T for 2 tiles of 16 entries (chains interleaved, reads batched)
       v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-      const _Float16* krow0 = kt + c16 * S::PITCH + 8 * g;
+      const _Float16* krow0 = kt + (32 * dh + c16) * S::PITCH + 8 * g;
       const _Float16* krow1 = krow0 + 16 * S::PITCH;
       constexpr int BATCH = 6;
 #pragma unroll
@@ -255,14 +262,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           }
         }
       }
-      // ---- online softmax (log2 domain), per head = lane & 15
-      float z[8];
-      float cmax = -__builtin_inff();
+      // st[t][r] = S^T[entry 32dh + 16t + 4g + r][head c16]
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          int ce = c0 + 16 * t + 4 * g + r;
+          int ce = c0 + 32 * dh + 16 * t + 4 * g + r;
           bool ok = ce < e_end && eid[ce - e_begin] >= 0;
           float v = ok ? st[t][r] * sl2 : -__builtin_inff();
           z[4 * t + r] = v;
@@ -270,8 +275,13 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      if (g == 0) pmx[dh][16 * hg + c16] = cmax;
+    }
+    __syncthreads();
+    float alpha = 1.0f;
+    if (active) {
+      cmax = fmaxf(cmax, pmx[dh ^ 1][16 * hg + c16]);   // max over the whole 64-entry chunk
       const float m_new = fmaxf(m_run, cmax);
-      float alpha = 1.0f;
       float psum = 0.0f;
       v8h pa;
       if (m_new == -__builtin_inff()) {
@@ -288,7 +298,13 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      // ---- rescale O rows (heads 4g + r) when some head's max moved
+      pex[wave][lane] = pa;
+    }
+    __syncthreads();
+    if (active) {
+      // P for entries 0..31 (k-step 0) comes from dim half 0, 32..63 from half 1.
+      const v8h p_own = pex[wave][lane], p_oth = pex[wave ^ 4][lane];
+      const v8h p0 = dh == 0 ? p_own : p_oth, p1 = dh == 0 ? p_oth : p_own;
       if (!__all(alpha == 1.0f)) {
         float al[4];
 #pragma unroll
@@ -298,22 +314,28 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           o[n][0] *= al[0]; o[n][1] *= al[1]; o[n][2] *= al[2]; o[n][3] *= al[3];
         }
       }
-      // ---- O += P V over dims 256*dh ..; B operand = V^T row, entries 4g..4g+3 and 16+4g..16+4g+3
+      // ---- O += P V over dims 256*dh ..; k-step j: entries 32j + {4g..4g+3, 16+4g..16+4g+3}
       const _Float16* vrow = vt + (256 * dh + c16) * kVtPitch + 4 * g;
       typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-      constexpr int VB = 8;
+      constexpr int VB = 4;
 #pragma unroll
       for (int n0 = 0; n0 < NT; n0 += VB) {
-        v8h vf[VB];
+        v8h vf[VB][2];
 #pragma unroll
-        for (int j = 0; j < VB; ++j) {
-          const _Float16* vp = vrow + (16 * (n0 + j)) * kVtPitch;
-          v4h lo = *reinterpret_cast<const v4h*>(vp);
-          v4h hi = *reinterpret_cast<const v4h*>(vp + 16);
-          vf[j] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int jn = 0; jn < VB; ++jn) {
+          const _Float16* vp = vrow + (16 * (n0 + jn)) * kVtPitch;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            v4h lo = *reinterpret_cast<const v4h*>(vp + 32 * j);
+            v4h hi = *reinterpret_cast<const v4h*>(vp + 32 * j + 16);
+            vf[jn][j] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
         }
 #pragma unroll
-        for (int j = 0; j < VB; ++j) o[n0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vf[j], o[n0 + j], 0, 0, 0);
+        for (int jn = 0; jn < VB; ++jn) {
+          o[n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p0, vf[jn][0], o[n0 + jn], 0, 0, 0);
+          o[n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p1, vf[jn][1], o[n0 + jn], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
@@ -321,11 +343,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     __syncthreads();
   }
 
-  if (!active) return;
-  // ---- partial results: l summed over the 4 lane groups of a head
+  // ---- partial results: l summed over the 4 lane groups and both dim halves
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  if (active && g == 0) pmx[dh][16 * hg + c16] = l_tot;
+  __syncthreads();
+  if (!active) return;
+  l_tot += pmx[dh ^ 1][16 * hg + c16];
   const int64_t pbase = (row * splits + split) * (int64_t)H;
   if (g == 0 && dh == 0) {
     part_ml[(pbase + head_b) * 2 + 0] = m_run;
