@@ -43,6 +43,33 @@ def parse():
     return p.parse_args()
 
 
+# ------------------------------------------------------- counter traffic ---
+
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when that summary is missing or the kernel's sources
+    have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_decode64k_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ": " in line and not line.startswith(("|", "#", "`")):
+            k, v = line.split(": ", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in kv["kernel_source_files"].split():
+            with open(os.path.join(ROOT, "fp4_kv_cache_index_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != kv["kernel_source_sha256"]:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------ byte model ---
 
 def layer_bytes(wl, kind, pool_cap=0):
@@ -268,7 +295,8 @@ def main():
         wl.D_I * wl.N * wl.B + (wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B * wl.Tq
     achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": counter_traffic(dom) if wl.name == "decode64k" else None, "kernel": dom,
             "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     cpu = None
     if not args.no_cpu_baseline:
