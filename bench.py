@@ -189,9 +189,11 @@ class Case:
 
 # ----------------------------------------------------------- CPU oracle ---
 
-def cpu_baseline(case, n_seq):
-    """Time the oracle's step (scores + Top-K + attention) on n_seq sequences of
-    the first layer; cache quantisation of the rows it reads is set-up."""
+def cpu_baseline(case, n_seq, budget_s=10.0):
+    """Time the oracle's step (scores + Top-K + attention) on at least n_seq
+    sequences of the first layer, continuing while less than budget_s seconds
+    of oracle work have accumulated (bounded by the batch); cache quantisation
+    of the rows it reads is set-up and not timed."""
     import numpy as np
     from oracle import attention as A
     from oracle import indexer as I
@@ -203,11 +205,14 @@ def cpu_baseline(case, n_seq):
     h = lambda t: t.detach().cpu().numpy()
     t_tot = 0.0
     rows = 0
-    for b in range(n_seq):
+    swa_all = h(inputs.decode_layer_inputs(wl, 0, device=case.dev)["swa_x"])
+    for b in range(wl.B):
+        if b >= n_seq and t_tot >= budget_s:
+            break
         k_idx = h(case.k_idx[b])
         kv_x = h(inputs.kv_rows_seq(wl, b, device=case.dev))
         qi, w, q = h(L["q_idx"][b]), h(L["w"][b]), h(L["q"][b])
-        swa_x = h(inputs.decode_layer_inputs(wl, 0, device=case.dev)["swa_x"][b])
+        swa_x = swa_all[b]
         for t in range(wl.Tq if wl.Tq == 1 else 1):
             t0 = time.perf_counter()
             s = I.index_scores(qi[t], w[t], k_idx, wl.N)
@@ -231,7 +236,8 @@ def cpu_baseline(case, n_seq):
     except Exception:  # noqa: BLE001
         blas = 1
     return {"value": rows / t_tot, "unit": "queries/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{rows} query row(s) of layer 0 of {wl.name} (scores + Top-K + attention; "
+            "sample": f"{rows} query row(s) of layer 0 of {wl.name} (scores + Top-K + attention, "
+                      f"{t_tot:.1f} s of oracle work; "
                       f"host has {os.cpu_count()} logical CPUs, BLAS threads {blas})",
             "seconds": round(t_tot, 3)}
 
