@@ -1,0 +1,194 @@
+"""GPU parity at the full sizes of the multi-layer and prefill workloads.
+
+Each test builds the whole workload on the GPU in the launch shapes the
+benchmark uses (one interleaved 324-byte FP4 cache, shared indexer keys,
+fresh per-layer queries) and checks sampled sequences / query rows against the
+oracle: Top-K indices and pools bit for bit, attention per (row, head) within
+2e-3 of the float64 oracle.
+
+  * group128k: Full -> Reindex -> Reuse over 16 x 128K (the Reindex layer
+    shares the Full layer's KV and indexer keys with fresh queries; the Reuse
+    layer attends with copied indices, which must give the same bits as
+    attending with the Reindex layer's own index buffer);
+  * hier1m: 4 x 1M, a Full layer building the 2048 x 8 candidate pool and nine
+    pool-restricted layers;
+  * prefill256k: 4096 causal queries appended to a 262,144-token context.
+"""
+
+import numpy as np
+import torch
+
+import fp4_kv_cache_index_amd as csa2
+from fp4_kv_cache_index_amd import inputs
+from oracle import attention as A
+from oracle import indexer as I
+from oracle import pool as P
+from oracle import quant as Q
+from oracle.topk import topk_select
+from tests.gpu_util import ATTN_TOL, LSE_TOL, announce, gpu, np_, require_gpu, rowwise_rel_err
+
+
+def _build_cache(wl):
+    d = wl.d_qk
+    cache = torch.empty(wl.B, wl.N, d // 2 + d // 16, dtype=torch.uint8, device="cuda")
+    codes, scales = cache[..., : d // 2], cache[..., d // 2:]
+    for b in range(wl.B):
+        x = inputs.kv_rows_seq(wl, b, device="cuda")
+        csa2.kv_fp4_quantize(x, codes=codes[b], scales=scales[b])
+        del x
+    k_idx = inputs.int_e4m3((wl.B, wl.N, wl.D_I), wl.seed, 0, "k_idx", device="cuda")
+    return codes, scales, k_idx
+
+
+def _compact_rows(wl, b, ids):
+    """Oracle FP4 rows of the distinct valid ids of sequence b, with the ids
+    renumbered 0..n-1 (attention depends only on the rows, not their ids)."""
+    ids = np.asarray(ids).reshape(-1)
+    uniq = np.unique(ids[ids >= 0])
+    x = np_(inputs.kv_rows_seq(wl, b, device="cuda")[torch.from_numpy(uniq).long().cuda()])
+    codes, scales = Q.fp4_quantize(x)
+    remap = {int(t): i for i, t in enumerate(uniq)}
+    return codes, scales, remap, len(uniq)
+
+
+def _renumber(idx, remap):
+    return np.array([remap[int(t)] if t >= 0 else -1 for t in np.asarray(idx)], dtype=np.int64)
+
+
+def _check_attn(got_o, got_l, want_o, want_l):
+    err = rowwise_rel_err(got_o, want_o)
+    assert err <= ATTN_TOL, err
+    fin = np.isfinite(want_l)
+    assert np.array_equal(fin, np.isfinite(got_l))
+    assert np.max(np.abs(got_l[fin] - want_l[fin]), initial=0.0) <= LSE_TOL
+
+
+def _oracle_decode_attn(wl, b, q_b, idx_b, swa_x_b):
+    codes, scales, remap, n = _compact_rows(wl, b, idx_b)
+    v8, s8 = Q.mxfp8_quantize(swa_x_b[: wl.W])
+    return A.sparse_attn_decode_row(q_b, codes, scales, _renumber(idx_b, remap), n, v8, s8, wl.W, wl.d_qk,
+                                    wl.d_v, wl.softmax_scale)
+
+
+@gpu
+def test_group128k_full_reindex_reuse():
+    require_gpu()
+    wl = inputs.WORKLOADS["group128k"]
+    announce("group128k B16 x 128K: Full -> Reindex -> Reuse, sequences 0 and 15 sampled")
+    codes, scales, k_idx = _build_cache(wl)
+    ctx = torch.full((wl.B,), wl.N, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((wl.B,), wl.W, dtype=torch.int32, device="cuda")
+    lays = [inputs.decode_layer_inputs(wl, li, device="cuda") for li in range(3)]
+    topk, outs, lses = [], [], []
+    for li, kind in enumerate(wl.layers):
+        L = lays[li]
+        if kind in ("full", "reindex"):
+            idx = csa2.csa2_index_score_topk(L["q_idx"], L["w"], k_idx, ctx, wl.K)["topk_idx"][:, 0].contiguous()
+        else:
+            idx = topk[-1].clone()      # Reuse: the indices are copied from the layer before
+        sv, ss = csa2.swa_fp8_quantize(L["swa_x"])
+        o, l = csa2.csa2_sparse_attn_decode(L["q"][:, 0].contiguous(), codes, scales, idx, ctx, sv, ss, swa_len,
+                                            wl.softmax_scale, want_lse=True)
+        topk.append(idx)
+        outs.append(o)
+        lses.append(l)
+    # Reuse with the copied indices == attention with the Reindex layer's own buffer, bit for bit.
+    L2 = lays[2]
+    sv2, ss2 = csa2.swa_fp8_quantize(L2["swa_x"])
+    o_same, l_same = csa2.csa2_sparse_attn_decode(L2["q"][:, 0].contiguous(), codes, scales, topk[1], ctx, sv2, ss2,
+                                                  swa_len, wl.softmax_scale, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_same, outs[2]) and torch.equal(l_same, lses[2])
+    assert not torch.equal(topk[0], topk[1])   # Reindex really re-selected
+    kh = None
+    for b in (0, wl.B - 1):
+        kh = np_(k_idx[b])
+        for li in range(3):
+            L = lays[li]
+            if li < 2:
+                s = I.index_scores(np_(L["q_idx"][b, 0]), np_(L["w"][b, 0]), kh, wl.N)
+                want_i, _ = topk_select(s, wl.N, wl.K)
+                assert np.array_equal(np_(topk[li][b]), want_i), (li, b)
+            want_o, want_l = _oracle_decode_attn(wl, b, np_(L["q"][b, 0]), np_(topk[li][b]), np_(L["swa_x"][b]))
+            _check_attn(np_(outs[li][b]), np_(lses[li][b]), want_o, want_l)
+
+
+@gpu
+def test_hier1m_pool_and_nine_pool_layers():
+    require_gpu()
+    wl = inputs.WORKLOADS["hier1m"]
+    announce("hier1m B4 x 1M: Full with pool 2048x8 + 9 pool layers, sequences 0 and 3 sampled")
+    codes, scales, k_idx = _build_cache(wl)
+    ctx = torch.full((wl.B,), wl.N, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((wl.B,), wl.W, dtype=torch.int32, device="cuda")
+    lays = [inputs.decode_layer_inputs(wl, li, device="cuda") for li in range(len(wl.layers))]
+    r0 = csa2.csa2_index_score_topk(lays[0]["q_idx"], lays[0]["w"], k_idx, ctx, wl.K,
+                                    pool_block=wl.pool_block, pool_nblocks=wl.pool_nblocks)
+    topk = [r0["topk_idx"]]
+    for li in range(1, len(wl.layers)):
+        L = lays[li]
+        topk.append(csa2.csa2_hier_pool_topk(L["q_idx"], L["w"], k_idx, r0["pool_idx"], r0["pool_len"],
+                                             wl.K)["topk_idx"])
+    checked_layers = (0, 1, 9)
+    outs = {}
+    for li in checked_layers:
+        L = lays[li]
+        sv, ss = csa2.swa_fp8_quantize(L["swa_x"])
+        outs[li] = csa2.csa2_sparse_attn_decode(L["q"][:, 0].contiguous(), codes, scales,
+                                                topk[li][:, 0].contiguous(), ctx, sv, ss, swa_len,
+                                                wl.softmax_scale, want_lse=True)
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        kh = np_(k_idx[b])
+        s0 = I.index_scores(np_(lays[0]["q_idx"][b, 0]), np_(lays[0]["w"][b, 0]), kh, wl.N)
+        pool, plen = P.hier_pool(s0, wl.N, wl.pool_block, wl.pool_nblocks)
+        assert int(np_(r0["pool_len"])[b, 0]) == plen == wl.pool_block * wl.pool_nblocks
+        assert np.array_equal(np_(r0["pool_idx"])[b, 0], pool)
+        flat, _ = topk_select(s0, wl.N, wl.K)
+        assert np.array_equal(np_(topk[0])[b, 0], flat)
+        assert set(flat.tolist()) <= set(pool.tolist())
+        for li in range(1, len(wl.layers)):
+            L = lays[li]
+            want_i, _ = P.pool_topk(np_(L["q_idx"][b, 0]), np_(L["w"][b, 0]), kh, pool, plen, wl.K)
+            assert np.array_equal(np_(topk[li])[b, 0], want_i), (li, b)
+        for li in checked_layers:
+            L = lays[li]
+            want_o, want_l = _oracle_decode_attn(wl, b, np_(L["q"][b, 0]), np_(topk[li])[b, 0], np_(L["swa_x"][b]))
+            o, l = outs[li]
+            _check_attn(np_(o[b]), np_(l[b]), want_o, want_l)
+
+
+@gpu
+def test_prefill256k_sampled_queries():
+    require_gpu()
+    wl = inputs.WORKLOADS["prefill256k"]
+    announce("prefill256k: 4096 causal queries on 266,240 tokens, query rows 0, 1, 2047, 4095 sampled")
+    codes, scales, k_idx = _build_cache(wl)
+    base = wl.N - wl.Tq
+    ctx = torch.full((wl.B,), wl.N, dtype=torch.int32, device="cuda")
+    q_pos = (torch.arange(wl.Tq, dtype=torch.int32, device="cuda") + base).repeat(wl.B, 1).contiguous()
+    swa_pos0 = torch.full((wl.B,), base - wl.W + 1, dtype=torch.int32, device="cuda")
+    L = inputs.decode_layer_inputs(wl, 0, device="cuda")
+    res = csa2.csa2_index_score_topk(L["q_idx"], L["w"], k_idx, ctx, wl.K, q_pos=q_pos)
+    sv, ss = csa2.swa_fp8_quantize(L["swa_x"])
+    out, lse = csa2.csa2_sparse_attn_prefill(L["q"], codes, scales, res["topk_idx"], ctx, q_pos, sv, ss, swa_pos0,
+                                             wl.W, wl.softmax_scale, want_lse=True)
+    torch.cuda.synchronize()
+    got = np_(res["topk_idx"])[0]
+    assert np.all(np.diff(got, axis=1) > 0)
+    assert np.all(got <= np_(q_pos)[0][:, None])
+    kh = np_(k_idx[0])
+    swa_h = np_(L["swa_x"][0])
+    v8, s8 = Q.mxfp8_quantize(swa_h)
+    for t in (0, 1, wl.Tq // 2 - 1, wl.Tq - 1):
+        p = int(np_(q_pos)[0, t])
+        nv = I.visible_count(wl.N, p)
+        s = I.index_scores(np_(L["q_idx"][0, t]), np_(L["w"][0, t]), kh, nv)
+        want_i, _ = topk_select(s, nv, wl.K)
+        assert np.array_equal(got[t], want_i), t
+        c, sc, remap, n = _compact_rows(wl, 0, want_i)
+        # Renumbered ids keep their order; the causal limit is already applied by the selection.
+        want_o, want_l = A.sparse_attn_prefill_row(np_(L["q"][0, t]), c, sc, _renumber(want_i, remap), n, p,
+                                                   v8, s8, int(np_(swa_pos0)[0]), wl.W, wl.d_qk, wl.d_v,
+                                                   wl.softmax_scale)
+        _check_attn(np_(out[0, t]), np_(lse[0, t]), want_o, want_l)
