@@ -291,6 +291,224 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Prefill chunk: many queries of one sequence against the same keys, so the
+// scores form a dense product [queries x heads] x [D_I] . [D_I] x [keys] and
+// run on the gfx950 FP8 matrix cores at full rate
+// (v_mfma_scale_f32_16x16x128_f8f6f4, unit E8M0 scales).  A workgroup holds
+// QW = 4*QG queries of one sequence and a tile of keys; its 8 waves split the
+// tile into 16-key chunks.  For 4 queries, MFMA number hg takes A rows
+// (query 4qg + r/4, head 4hg + r%4), so in the result lane l holds
+// query 4qg + l/16, heads 4hg..4hg+3 of key l%16: all heads of one
+// (query, key) pair end up in one lane, which adds them in ascending order
+// with float32 roundings and no FMA (padding heads carry weight 0).  Each
+// lane loads bytes [16g, 16g+16) and [64+16g, 64+16g+16) of each 128-byte
+// k-step for both operands, so the k-permutation matches on both sides.
+// The epilogue writes the score keys and builds per-query 12-bit histograms
+// in LDS, two queries per 32-bit word (counts stay below 2^16 per tile).
+constexpr int kPrefillWaves = 8;
+
+template <int DI>
+__device__ __forceinline__ void load_k128(uint32_t (&f)[DI / 16], const uint8_t* row, int g, bool ok) {
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < DI / 16; ++i) f[i] = 0u;
+    return;
+  }
+#pragma unroll
+  for (int ks = 0; ks < DI / 128; ++ks) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      v4u v = *reinterpret_cast<const v4u*>(row + 128 * ks + 64 * hf + 16 * g);
+      f[8 * ks + 4 * hf + 0] = v[0]; f[8 * ks + 4 * hf + 1] = v[1];
+      f[8 * ks + 4 * hf + 2] = v[2]; f[8 * ks + 4 * hf + 3] = v[3];
+    }
+  }
+}
+
+template <int DI, int HG, int QG>
+__global__ void __launch_bounds__(64 * kPrefillWaves)
+index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+                     const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
+                     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
+                     int Tq, int H_I, int64_t n_max, int key_tile, int qtiles,
+                     uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
+                     SelectWs tok) {
+  constexpr int KS = DI / 128;          // MFMA k-steps
+  constexpr int FW = DI / 16;           // fragment words per lane
+  constexpr int QW = 4 * QG;            // queries per workgroup
+  constexpr int HP = 4 * HG;            // heads incl. padding
+  constexpr int NT = 64 * kPrefillWaves;
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  __shared__ uint32_t hist[(QW / 2) * 4096];
+  __shared__ int32_t nvs[QW];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int64_t b = blockIdx.y / qtiles;
+  const int t0 = (int)(blockIdx.y % qtiles) * QW;
+  const int64_t row0 = b * Tq + t0;
+
+  if (threadIdx.x < QW) {
+    const int t = t0 + threadIdx.x;
+    int64_t nv = 0;
+    if (t < Tq) {
+      nv = ctx_len[b];
+      if (q_pos) {
+        int64_t qp = (int64_t)q_pos[row0 + threadIdx.x] + 1;
+        if (qp < nv) nv = qp;
+      }
+      nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+      if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
+    }
+    nvs[threadIdx.x] = (int32_t)nv;
+  }
+  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  __syncthreads();
+  int max_nv = 0;
+#pragma unroll
+  for (int i = 0; i < QW; ++i) max_nv = nvs[i] > max_nv ? nvs[i] : max_nv;
+  const int64_t k0 = (int64_t)blockIdx.x * key_tile;
+  int64_t k1 = k0 + key_tile;
+  if (k1 > max_nv) k1 = max_nv;
+  if (k0 >= k1) return;   // uniform: nothing visible in this tile
+
+  // A fragments: row c16 = (query 4qg + c16/4, head 4hg + c16%4).
+  v8i qa[QG][HG][KS];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const int t = t0 + 4 * qg + (c16 >> 2), h = 4 * hg + (c16 & 3);
+      uint32_t f[FW];
+      load_k128<DI>(f, q_idx + ((b * Tq + t) * H_I + h) * (int64_t)DI, g, t < Tq && h < H_I);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[qg][hg][ks] = v8i{(int)f[8 * ks], (int)f[8 * ks + 1], (int)f[8 * ks + 2], (int)f[8 * ks + 3],
+                             (int)f[8 * ks + 4], (int)f[8 * ks + 5], (int)f[8 * ks + 6], (int)f[8 * ks + 7]};
+    }
+  }
+  // Epilogue state of this lane: query 4qg + g of each group.
+  float wv[QG][HP];
+  int32_t nvq[QG];
+  uint32_t* krow[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int ql = 4 * qg + g, t = t0 + ql;
+#pragma unroll
+    for (int h = 0; h < HP; ++h) wv[qg][h] = (t < Tq && h < H_I) ? w[(b * Tq + t) * H_I + h] : 0.0f;
+    nvq[qg] = nvs[ql];
+    krow[qg] = keys + (row0 + ql) * key_stride;
+  }
+
+  const uint8_t* kb = k_idx + b * k_bstride;
+  const int nchunks = (int)((k1 - k0 + 15) >> 4);
+  uint32_t fa[FW], fb[FW];
+  auto load_chunk = [&](uint32_t (&f)[FW], int c) {
+    const int64_t j = k0 + 16 * (int64_t)c + c16;
+    load_k128<DI>(f, kb + (j < k1 ? j : k0) * k_rstride, g, j < k1);
+  };
+  auto score_chunk = [&](const uint32_t (&f)[FW], int c) {
+    const int64_t j = k0 + 16 * (int64_t)c + c16;
+    v8i kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = v8i{(int)f[8 * ks], (int)f[8 * ks + 1], (int)f[8 * ks + 2], (int)f[8 * ks + 3],
+                   (int)f[8 * ks + 4], (int)f[8 * ks + 5], (int)f[8 * ks + 6], (int)f[8 * ks + 7]};
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      v4f acc[HG];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        acc[hg] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[qg][hg][ks], kf[ks], acc[hg], 0, 0, 0, 127,
+                                                                     0, 127);
+      }
+      // acc[hg][i] = dot(query 4qg + g, head 4hg + i; key j)
+      float sc = 0.0f;
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float r = acc[hg][i] > 0.0f ? acc[hg][i] : 0.0f;
+          sc = __fadd_rn(sc, __fmul_rn(wv[qg][4 * hg + i], r));
+        }
+      if (j < nvq[qg]) {
+        const uint32_t key = score_key(sc);
+        __builtin_nontemporal_store(key, krow[qg] + j);
+        const int ql = 4 * qg + g;
+        atomicAdd(&hist[(ql >> 1) * 4096 + (key >> 20)], 1u << (16 * (ql & 1)));
+      }
+    }
+  };
+  int c = wave;
+  if (c < nchunks) load_chunk(fa, c);
+  for (; c < nchunks; c += 2 * kPrefillWaves) {
+    const int cb = c + kPrefillWaves;
+    if (cb < nchunks) load_chunk(fb, cb);
+    score_chunk(fa, c);
+    if (cb + kPrefillWaves < nchunks) load_chunk(fa, cb + kPrefillWaves);
+    if (cb < nchunks) score_chunk(fb, cb);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
+    const uint32_t v = hist[i];
+    if (!v) continue;
+    const int p = i >> 12, bin = i & 4095;
+    if (v & 0xFFFFu) atomic_add_agent(tok.hist1 + (row0 + 2 * p) * 4096 + bin, v & 0xFFFFu);
+    if (v >> 16) atomic_add_agent(tok.hist1 + (row0 + 2 * p + 1) * 4096 + bin, v >> 16);
+  }
+}
+
+template <int DI, int HG>
+static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                                   const SelectWs& tok, hipStream_t s) {
+  constexpr int QG = (HG * (DI / 128) <= 2) ? 4 : (HG * (DI / 128) <= 4 ? 2 : 1);
+  constexpr int QW = 4 * QG;
+  const int qtiles = (a.Tq + QW - 1) / QW;
+  const int64_t qrows = (int64_t)a.B * qtiles;
+  // Key tiles: at most 8192 keys (per-tile counts stay below 2^16), smaller
+  // while the grid would not cover the compute units twice.
+  int key_tile = 8192;
+  const int64_t want = 2LL * device_cu_count();
+  while (key_tile > 512 && qrows * ((a.n_max + key_tile - 1) / key_tile) < want) key_tile >>= 1;
+  int64_t tiles = (a.n_max + key_tile - 1) / key_tile;
+  if (tiles < 1) tiles = 1;
+  if (qrows > 65535) return hipErrorInvalidValue;
+  CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG>), dim3((unsigned)tiles, (unsigned)qrows),
+              dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
+              a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok);
+  return hipGetLastError();
+}
+
+static bool prefill_gemm_applies(const ScoreArgs& a) {
+  return a.Tq >= 16 && a.pool_block == 0 && (a.D_I == 128 || a.D_I == 256) && a.H_I <= 32;
+}
+
+static hipError_t launch_prefill(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                                 const SelectWs& tok, hipStream_t s) {
+  const int hg = (a.H_I + 3) / 4;
+  const int HGp = hg <= 1 ? 1 : (hg <= 2 ? 2 : (hg <= 4 ? 4 : 8));
+#define CALL_PF(D, H) launch_prefill_t<D, H>(a, keys, key_stride, n_valid, tok, s)
+  if (a.D_I == 128) {
+    switch (HGp) {
+      case 1: return CALL_PF(128, 1);
+      case 2: return CALL_PF(128, 2);
+      case 4: return CALL_PF(128, 4);
+      default: return CALL_PF(128, 8);
+    }
+  }
+  switch (HGp) {
+    case 1: return CALL_PF(256, 1);
+    case 2: return CALL_PF(256, 2);
+    case 4: return CALL_PF(256, 4);
+    default: return CALL_PF(256, 8);
+  }
+#undef CALL_PF
+}
+
 #define CSA2_DISPATCH_DI_HB(DI_, HB_, CALL)                                       \
   do {                                                                           \
     int hb__ = (HB_) <= 16 ? 1 : 2;                                              \
@@ -306,6 +524,7 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
 hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                               const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                               const SelectWs* blk, hipStream_t s) {
+  if (prefill_gemm_applies(a)) return launch_prefill(a, keys, key_stride, n_valid, tok, s);
 #define CALL_SCAN(D, H) launch_scan_t<D, H>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
   CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_SCAN);
 #undef CALL_SCAN

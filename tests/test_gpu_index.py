@@ -103,6 +103,28 @@ def test_causal_rows_with_q_pos():
 
 
 @gpu
+@pytest.mark.parametrize("H_I,D_I,Tq,K", [(8, 128, 40, 512), (3, 128, 17, 100), (32, 128, 20, 300),
+                                         (8, 256, 33, 256), (13, 256, 16, 64), (8, 128, 70, 2048)])
+def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K):
+    """Chunks of 16 or more queries per sequence take the matrix-core product
+    path; causal positions, a context shorter than some positions, a partial
+    last query tile and K above the visible count all appear."""
+    require_gpu()
+    announce(f"index_score_topk prefill chunk H_I={H_I} D_I={D_I} Tq={Tq} K={K}")
+    B, N = 3, 2 * 8192 + 1234
+    k_idx = inputs.int_e4m3((B, N, D_I), 31, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 31, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 31, 1, "w", device="cuda")
+    ctx = torch.tensor([N, N - 700, 5000], dtype=torch.int32, device="cuda")
+    base = torch.tensor([N - Tq, N - Tq - 900, 4000], dtype=torch.int64)
+    steps = torch.arange(Tq, dtype=torch.int64) * 37
+    q_pos = (base[:, None] + steps[None, :]).clamp(max=N - 1)
+    q_pos[0, :3] = torch.tensor([0, 5, K // 2])          # tiny visible prefixes
+    q_pos = q_pos.to(torch.int32).cuda().contiguous()
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos)
+
+
+@gpu
 @pytest.mark.parametrize("block,nblocks,K", [(8, 64, 256), (8, 2048, 2048), (4, 100, 64), (1, 300, 300), (16, 40, 128)])
 def test_hierarchical_pool_and_pool_topk(block, nblocks, K):
     require_gpu()
