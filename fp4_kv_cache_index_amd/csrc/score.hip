@@ -462,6 +462,130 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
   }
 }
 
+// Variant for D_I = 128 and at most 8 indexer heads: the product is taken
+// transposed, A = 16 keys of a chunk, B = one head of the workgroup's 16
+// queries, one MFMA per head.  Lane l then holds, for query l%16, the dots of
+// keys 4g..4g+3 (g = l/16) with every head in its own accumulator, so the
+// head sum stays inside the lane and the four consecutive keys of one query
+// leave in a single 16-byte store.
+template <int PD>
+__global__ void __launch_bounds__(64 * kPrefillWaves)
+index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+                        const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
+                        const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
+                        int Tq, int H_I, int64_t n_max, int key_tile, int qtiles,
+                        uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
+                        SelectWs tok) {
+  constexpr int DI = 128, FW = 8, QW = 16, HP = 8;
+  constexpr int NT = 64 * kPrefillWaves;
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  __shared__ uint32_t hist[(QW / 2) * 4096];
+  __shared__ int32_t nvs[QW];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int64_t b = blockIdx.y / qtiles;
+  const int t0 = (int)(blockIdx.y % qtiles) * QW;
+  const int64_t row0 = b * Tq + t0;
+
+  if (threadIdx.x < QW) {
+    const int t = t0 + threadIdx.x;
+    int64_t nv = 0;
+    if (t < Tq) {
+      nv = ctx_len[b];
+      if (q_pos) {
+        int64_t qp = (int64_t)q_pos[row0 + threadIdx.x] + 1;
+        if (qp < nv) nv = qp;
+      }
+      nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+      if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
+    }
+    nvs[threadIdx.x] = (int32_t)nv;
+  }
+  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  __syncthreads();
+  int max_nv = 0;
+#pragma unroll
+  for (int i = 0; i < QW; ++i) max_nv = nvs[i] > max_nv ? nvs[i] : max_nv;
+  const int64_t k0 = (int64_t)blockIdx.x * key_tile;
+  int64_t k1 = k0 + key_tile;
+  if (k1 > max_nv) k1 = max_nv;
+  if (k0 >= k1) return;   // uniform: nothing visible in this tile
+
+  // B fragments: column c16 = query t0 + c16, one per head.
+  const int t = t0 + c16;
+  const bool tok_q = t < Tq;
+  v8i qb[HP];
+  float wv[HP];
+#pragma unroll
+  for (int h = 0; h < HP; ++h) {
+    uint32_t f[FW];
+    load_k128<DI>(f, q_idx + ((b * Tq + t) * H_I + h) * (int64_t)DI, g, tok_q && h < H_I);
+    qb[h] = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], (int)f[4], (int)f[5], (int)f[6], (int)f[7]};
+    wv[h] = (tok_q && h < H_I) ? w[(b * Tq + t) * H_I + h] : 0.0f;
+  }
+  const int32_t nvq = nvs[c16];
+  uint32_t* krow = keys + (row0 + c16) * key_stride;
+  const int pair = c16 >> 1, shift = 16 * (c16 & 1);
+
+  const uint8_t* kb = k_idx + b * k_bstride;
+  const int nchunks = (int)((k1 - k0 + 15) >> 4);
+  uint32_t fk[PD][FW];
+  auto load_chunk = [&](uint32_t (&f)[FW], int c) {
+    const int64_t j = k0 + 16 * (int64_t)c + c16;
+    load_k128<DI>(f, kb + (j < k1 ? j : k0) * k_rstride, g, j < k1);
+  };
+  auto score_chunk = [&](const uint32_t (&f)[FW], int c) {
+    const v8i ka = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], (int)f[4], (int)f[5], (int)f[6], (int)f[7]};
+    v4f acc[HP];
+#pragma unroll
+    for (int h = 0; h < HP; ++h)
+      acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[h], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127,
+                                                                0, 127);
+    // acc[h][r] = dot(key j0 + 4g + r, query c16, head h)
+    const int64_t j0 = k0 + 16 * (int64_t)c + 4 * g;
+    uint32_t kk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int h = 0; h < HP; ++h) {
+        const float x = acc[h][r] > 0.0f ? acc[h][r] : 0.0f;
+        sc = __fadd_rn(sc, __fmul_rn(wv[h], x));
+      }
+      const bool vis = j0 + r < nvq;
+      kk[r] = vis ? score_key(sc) : 0u;
+      if (vis) atomicAdd(&hist[pair * 4096 + (kk[r] >> 20)], 1u << shift);
+    }
+    // Positions up to the next multiple of 16 lie inside the row's key
+    // stride; entries past the visible count are never read.
+    if (tok_q) *reinterpret_cast<v4u*>(krow + j0) = v4u{kk[0], kk[1], kk[2], kk[3]};
+  };
+  // Chunks c = wave, wave + 8, ...; PD chunks in flight per wave.
+  int c = wave;
+#pragma unroll
+  for (int d = 0; d < PD; ++d)
+    if (c + d * kPrefillWaves < nchunks) load_chunk(fk[d], c + d * kPrefillWaves);
+  for (; c < nchunks; c += PD * kPrefillWaves) {
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+      const int cd = c + d * kPrefillWaves;
+      if (cd < nchunks) {
+        score_chunk(fk[d], cd);
+        if (cd + PD * kPrefillWaves < nchunks) load_chunk(fk[d], cd + PD * kPrefillWaves);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
+    const uint32_t v = hist[i];
+    if (!v) continue;
+    const int p = i >> 12, bin = i & 4095;
+    if (v & 0xFFFFu) atomic_add_agent(tok.hist1 + (row0 + 2 * p) * 4096 + bin, v & 0xFFFFu);
+    if (v >> 16) atomic_add_agent(tok.hist1 + (row0 + 2 * p + 1) * 4096 + bin, v >> 16);
+  }
+}
+
 template <int DI, int HG>
 static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                                    const SelectWs& tok, hipStream_t s) {
@@ -477,9 +601,15 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
   int64_t tiles = (a.n_max + key_tile - 1) / key_tile;
   if (tiles < 1) tiles = 1;
   if (qrows > 65535) return hipErrorInvalidValue;
-  CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG>), dim3((unsigned)tiles, (unsigned)qrows),
-              dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
-              a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok);
+  if (DI == 128 && HG <= 2) {
+    CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3>), dim3((unsigned)tiles, (unsigned)qrows),
+                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
+                a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok);
+  } else {
+    CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG>), dim3((unsigned)tiles, (unsigned)qrows),
+                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len,
+                a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok);
+  }
   return hipGetLastError();
 }
 
