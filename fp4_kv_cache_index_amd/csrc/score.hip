@@ -479,7 +479,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   constexpr int DI = 128, FW = 8, QW = 16, HP = 8;
   constexpr int NT = 64 * kPrefillWaves;
   typedef int v8i __attribute__((ext_vector_type(8)));
-  __shared__ uint32_t hist[(QW / 2) * 4096];
+  __shared__ uint32_t hist[(QW / 2) * 4096 + 1];   // last word: bin of invisible keys
   __shared__ int32_t nvs[QW];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -502,7 +502,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     }
     nvs[threadIdx.x] = (int32_t)nv;
   }
-  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  for (int i = threadIdx.x; i <= (QW / 2) * 4096; i += NT) hist[i] = 0u;
   __syncthreads();
   int max_nv = 0;
 #pragma unroll
@@ -526,14 +526,24 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   }
   const int32_t nvq = nvs[c16];
   uint32_t* krow = keys + (row0 + c16) * key_stride;
-  const int pair = c16 >> 1, shift = 16 * (c16 & 1);
+  const uint32_t hbase = (uint32_t)(c16 >> 1) * 4096u, add = 1u << (16 * (c16 & 1));
+  constexpr uint32_t kTrash = (QW / 2) * 4096;
 
+  // Positions fit in 32 bits (n_max <= 2^22).  Every load is issued
+  // unconditionally from a clamped in-range row so that the compiler can
+  // count the loads in flight instead of draining them all at each chunk.
+  const int ik0 = (int)k0, ik1 = (int)k1;
   const uint8_t* kb = k_idx + b * k_bstride;
-  const int nchunks = (int)((k1 - k0 + 15) >> 4);
+  const int nchunks = (ik1 - ik0 + 15) >> 4;
   uint32_t fk[PD][FW];
   auto load_chunk = [&](uint32_t (&f)[FW], int c) {
-    const int64_t j = k0 + 16 * (int64_t)c + c16;
-    load_k128<DI>(f, kb + (j < k1 ? j : k0) * k_rstride, g, j < k1);
+    int j = ik0 + 16 * c + c16;
+    j = j < ik1 ? j : ik1 - 1;
+    const uint8_t* p = kb + (int64_t)j * k_rstride + 16 * g;
+    const v4u lo = *reinterpret_cast<const v4u*>(p);
+    const v4u hi = *reinterpret_cast<const v4u*>(p + 64);
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
   };
   auto score_chunk = [&](const uint32_t (&f)[FW], int c) {
     const v8i ka = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], (int)f[4], (int)f[5], (int)f[6], (int)f[7]};
@@ -542,20 +552,26 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     for (int h = 0; h < HP; ++h)
       acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[h], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127,
                                                                 0, 127);
-    // acc[h][r] = dot(key j0 + 4g + r, query c16, head h)
-    const int64_t j0 = k0 + 16 * (int64_t)c + 4 * g;
+    // acc[h][r] = dot(key j0 + r, query c16, head h)
+    const int j0 = ik0 + 16 * c + 4 * g;
     uint32_t kk[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float sc = 0.0f;
 #pragma unroll
       for (int h = 0; h < HP; ++h) {
-        const float x = acc[h][r] > 0.0f ? acc[h][r] : 0.0f;
+        // ReLU on the bit pattern: negative floats (and -0) are negative integers.
+        const int xi = __float_as_int(acc[h][r]);
+        const float x = __int_as_float(xi > 0 ? xi : 0);
         sc = __fadd_rn(sc, __fmul_rn(wv[h], x));
       }
+      // The sum starts at +0 and rounds to nearest, so it is never -0: the
+      // order-preserving key needs no zero canonicalisation here.
+      const uint32_t u = __float_as_uint(sc);
+      const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
       const bool vis = j0 + r < nvq;
-      kk[r] = vis ? score_key(sc) : 0u;
-      if (vis) atomicAdd(&hist[pair * 4096 + (kk[r] >> 20)], 1u << shift);
+      kk[r] = vis ? key : 0u;
+      atomicAdd(&hist[vis ? hbase + (key >> 20) : kTrash], add);
     }
     // Positions up to the next multiple of 16 lie inside the row's key
     // stride; entries past the visible count are never read.
@@ -564,16 +580,13 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   // Chunks c = wave, wave + 8, ...; PD chunks in flight per wave.
   int c = wave;
 #pragma unroll
-  for (int d = 0; d < PD; ++d)
-    if (c + d * kPrefillWaves < nchunks) load_chunk(fk[d], c + d * kPrefillWaves);
+  for (int d = 0; d < PD; ++d) load_chunk(fk[d], c + d * kPrefillWaves);
   for (; c < nchunks; c += PD * kPrefillWaves) {
 #pragma unroll
     for (int d = 0; d < PD; ++d) {
       const int cd = c + d * kPrefillWaves;
-      if (cd < nchunks) {
-        score_chunk(fk[d], cd);
-        if (cd + PD * kPrefillWaves < nchunks) load_chunk(fk[d], cd + PD * kPrefillWaves);
-      }
+      if (cd < nchunks) score_chunk(fk[d], cd);
+      load_chunk(fk[d], cd + PD * kPrefillWaves);
     }
   }
   __syncthreads();
