@@ -12,8 +12,9 @@ every cache resident in HBM:
   hier1m      Full layer with the 2048 x 8 candidate pool + 9 pool layers, 4 x 1M;
   prefill256k one causal chunk of 4096 queries on a 256K cache.
 Prints one JSON line: decode queries/s, algorithmic HBM GB/s, the roofline
-of the dominant kernel (HIP events around each library launch inside the
-timed region) and the CPU oracle timed on a bounded sample.
+of the dominant kernel (HIP events around each of its launches inside the
+timed region; no other launch is bracketed there), a per-kernel breakdown
+from a separate traced pass, and the CPU oracle timed on a bounded sample.
 """
 
 import argparse
@@ -27,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0      # dense FP8 matrix-core peak of MI355X
 METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% peak), 64K–1M ctx"
 
 
@@ -184,7 +186,12 @@ class Case:
     def step_bytes(self):
         wl = self.wl
         per_row = sum(layer_bytes(wl, L["kind"], self.pool_cap) for L in self.layers)
-        return per_row * wl.B * wl.Tq
+        total = per_row * wl.B * wl.Tq
+        if wl.Tq > 1:
+            # A prefill chunk streams the key cache once for all its queries.
+            n_scan = sum(1 for L in self.layers if L["kind"] in ("full", "reindex"))
+            total -= n_scan * wl.D_I * wl.N * wl.B * (wl.Tq - 1)
+        return total
 
 
 # ----------------------------------------------------------- CPU oracle ---
@@ -275,7 +282,14 @@ def main():
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with csa2.KernelTrace(capacity=64 * args.steps * max(1, len(wl.layers))) as tr:
+    # Dominant kernel: the indexer scan over the key cache (decode) or the
+    # dense FP8 scoring product (prefill chunk).  Inside the timed region only
+    # its launches are bracketed by HIP events, so the step time carries two
+    # event records per scoring launch and nothing else.
+    prefill = wl.Tq > 1
+    dom = "index_prefill" if prefill else "index_score"
+    n_scan_layers = sum(1 for L in case.layers if L["kind"] in ("full", "reindex"))
+    with csa2.KernelTrace(capacity=4 * args.steps * max(1, len(wl.layers)), only=dom) as tr:
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(args.steps):
@@ -283,27 +297,39 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    launches = tr.durations_ms()
+    dom_launches = [t for name, t in tr.durations_ms() if name == dom]
     tr.close()
+    dom_ms = sum(dom_launches) / len(dom_launches) if dom_launches else float("nan")
+    # Per-kernel breakdown from a separate traced pass (every launch bracketed).
+    n_bd = min(args.steps, 5)
+    with csa2.KernelTrace(capacity=64 * n_bd * max(1, len(wl.layers))) as tr:
+        for _ in range(n_bd):
+            case.step()
+        torch.cuda.synchronize()
     per_kernel = {}
-    for name, t in launches:
+    for name, t in tr.durations_ms():
         s = per_kernel.setdefault(name, [0.0, 0])
         s[0] += t
         s[1] += 1
+    tr.close()
     qps = wl.B * wl.Tq / (ms * 1e-3)
     step_bytes = case.step_bytes()
     gbps = step_bytes / (ms * 1e-3) / 1e9
-    # Dominant kernel: the indexer scan over the key cache.
-    dom = "index_score"
-    dom_ms = per_kernel[dom][0] / per_kernel[dom][1] if dom in per_kernel else float("nan")
-    n_scan_layers = sum(1 for L in case.layers if L["kind"] in ("full", "reindex"))
-    scan_bytes = (wl.D_I * wl.N + wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B * wl.Tq if wl.Tq == 1 else \
-        wl.D_I * wl.N * wl.B + (wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B * wl.Tq
-    achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": counter_traffic(dom) if wl.name == "decode64k" else None, "kernel": dom,
-            "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
+    if prefill:
+        base = wl.N - wl.Tq
+        pairs = wl.B * (wl.Tq * base + wl.Tq * (wl.Tq + 1) // 2)     # causal (query, key) pairs
+        flops = 2 * wl.H_I * wl.D_I * pairs
+        achieved = flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
+    else:
+        scan_bytes = (wl.D_I * wl.N + wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B
+        achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": counter_traffic(dom) if wl.name == "decode64k" else None, "kernel": dom,
+                "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     cpu = None
     if not args.no_cpu_baseline:
         n_seq = args.cpu_sample or (1 if wl.N >= (1 << 20) else 2)
@@ -317,7 +343,7 @@ def main():
                    "heads": wl.H, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "window": wl.W,
                    "layers": wl.layers, "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "step_bytes": step_bytes,
-        "kernels_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in per_kernel.items()},
+        "kernels_ms_per_step": {k: round(v[0] / n_bd, 5) for k, v in per_kernel.items()},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line))

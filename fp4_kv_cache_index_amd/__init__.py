@@ -49,6 +49,7 @@ _SIGS = {
                                                 c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
                                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "csa2_trace_attach": (ctypes.c_int, [ctypes.POINTER(c_void_p), ctypes.POINTER(ctypes.c_char_p), c_int32]),
+    "csa2_trace_only": (ctypes.c_int, [ctypes.c_char_p]),
     "csa2_trace_detach": (ctypes.c_int, [ctypes.POINTER(c_int32)]),
 }
 EXPORTS = tuple(_SIGS)
@@ -340,10 +341,13 @@ class KernelTrace:
 
     with KernelTrace(capacity) as tr: ...launch...; then tr.durations_ms()
     returns [(kernel name, ms)] after the stream has been synchronised.
+    only="name" records just the launches of that kernel (two events per
+    launch instead of two per library launch).
     """
 
-    def __init__(self, capacity=4096):
+    def __init__(self, capacity=4096, only=None):
         self.capacity = capacity
+        self.only = only
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), c_void_p, c_void_p]
@@ -359,6 +363,8 @@ class KernelTrace:
 
     def __enter__(self):
         _check(lib().csa2_trace_attach(self.events, self.names, self.capacity), "csa2_trace_attach")
+        if self.only is not None:
+            _check(lib().csa2_trace_only(self.only.encode()), "csa2_trace_only")
         return self
 
     def __exit__(self, *exc):

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cstring>
 
 #include "../../include/csa2.h"
 #include "internal.h"
@@ -19,6 +20,8 @@ Trace& thread_trace() {
 void trace_before(hipStream_t s, const char* name) {
   Trace& t = thread_trace();
   if (!t.active) return;
+  t.skipping = t.only[0] != 0 && std::strcmp(name, t.only) != 0;
+  if (t.skipping) return;
   if (t.count < t.capacity) {
     hipEventRecord(t.events[2 * t.count], s);
     if (t.names) t.names[t.count] = name;
@@ -27,7 +30,7 @@ void trace_before(hipStream_t s, const char* name) {
 
 void trace_after(hipStream_t s) {
   Trace& t = thread_trace();
-  if (!t.active) return;
+  if (!t.active || t.skipping) return;
   if (t.count < t.capacity) hipEventRecord(t.events[2 * t.count + 1], s);
   ++t.count;
 }
@@ -322,6 +325,15 @@ int csa2_trace_attach(void** events, const char** names, int32_t capacity) {
   t.capacity = capacity;
   t.count = 0;
   t.active = true;
+  return CSA2_OK;
+}
+
+int csa2_trace_only(const char* kernel_name) {
+  Trace& t = thread_trace();
+  if (!t.active) return CSA2_EINVAL;
+  if (kernel_name && std::strlen(kernel_name) >= sizeof(t.only)) return CSA2_EINVAL;
+  std::memset(t.only, 0, sizeof(t.only));
+  if (kernel_name) std::strcpy(t.only, kernel_name);
   return CSA2_OK;
 }
 

@@ -14,6 +14,8 @@ struct Trace {
   int capacity = 0;
   int count = 0;
   bool active = false;
+  char only[64] = {0};      // non-empty: trace only launches of this kernel name
+  bool skipping = false;    // the current launch is not traced
 };
 Trace& thread_trace();
 

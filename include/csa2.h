@@ -225,6 +225,13 @@ int csa2_sparse_attn_prefill(const float* q,
  * *n_launches (nullable) and stops recording.
  */
 int csa2_trace_attach(void** events, const char** names, int32_t capacity);
+/*
+ * Restrict the attached trace of the calling thread to launches whose static
+ * kernel name equals kernel_name (at most 63 characters; NULL = every
+ * launch again); other launches are neither recorded nor counted.  Returns
+ * CSA2_EINVAL when no trace is attached or the name is too long.
+ */
+int csa2_trace_only(const char* kernel_name);
 int csa2_trace_detach(int32_t* n_launches);
 
 #ifdef __cplusplus

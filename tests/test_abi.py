@@ -78,6 +78,13 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.csa2_trace_attach(None, None, 0) == 0
     n = ctypes.c_int32(-1)
     assert lib.csa2_trace_detach(ctypes.byref(n)) == 0 and n.value == 0
+    # the name filter needs an attached trace and a name below 64 characters
+    assert lib.csa2_trace_only(b"index_score") == 1
+    assert lib.csa2_trace_attach(None, None, 0) == 0
+    assert lib.csa2_trace_only(b"x" * 64) == 1
+    assert lib.csa2_trace_only(b"index_score") == 0
+    assert lib.csa2_trace_only(None) == 0
+    assert lib.csa2_trace_detach(ctypes.byref(n)) == 0 and n.value == 0
 
 
 def test_workspace_sizes_are_monotone():
