@@ -77,7 +77,7 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 
 // GATHER = false: tokens j = tile positions of the row (flat scan).
 // GATHER = true : position p maps to token pool_idx[row][p] (pool layers).
-template <int DI, int HB, bool GATHER, bool POOL>
+template <int DI, int HB, bool GATHER, bool POOL, bool H8>
 __global__ void __launch_bounds__(256)
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
@@ -91,9 +91,20 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   constexpr int CH = DI / 4;           // bytes of a key row per lane
   constexpr int KS = DI / 32;          // MFMA k-steps
   constexpr int HMAX = 16 * HB;
-  __shared__ uint32_t hist[4096];
+  // Heads kept per token: 8 when the indexer has at most 8 heads, else all
+  // 16*HB MFMA rows (padding heads have zero queries and weight 0).
+  constexpr int HP = H8 ? 8 : HMAX;
+  // Top-12-bit histogram, two 16-bit bins per word (a tile holds at most
+  // 4096 positions); the last word takes positions past the visible count.
+  __shared__ uint32_t hist[2049];
+  // Flat scan: the tile's keys are staged here and leave in one coalesced
+  // burst at the end (interleaving small key stores with the key-row stream
+  // costs more than the LDS round trip).
+  constexpr bool kStage = !GATHER && !POOL;
+  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? kScanTile : 1];
+  __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
   __shared__ uint32_t bhist[POOL ? 4096 : 1];
-  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HMAX];
+  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HP];
   __shared__ float wsh[HMAX];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -119,14 +130,15 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
 
   for (int i = threadIdx.x; i < 4096; i += 256) {
-    hist[i] = 0u;
+    if (i <= 2048) hist[i] = 0u;
     if (pool) bhist[i] = 0u;
   }
   if (threadIdx.x < HMAX) wsh[threadIdx.x] = threadIdx.x < H_I ? w[row * H_I + threadIdx.x] : 0.0f;
   __syncthreads();
-  float wv[HMAX];   // head weights (0 past H_I), wave-uniform
+  float wv[HP];   // head weights (0 past H_I), wave-uniform: scalar registers
 #pragma unroll
-  for (int h = 0; h < HMAX; ++h) wv[h] = wsh[h];
+  for (int h = 0; h < HP; ++h)
+    wv[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsh[h])));
 
   // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
   const int c16 = lane & 15, g = lane >> 4;
@@ -142,24 +154,34 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   __syncthreads();
 
   const int64_t tile0 = (int64_t)blockIdx.x * tile;
-  const int pitch = (H_I + 3) & ~3;
+  constexpr int pitch = HP;
   float* my = dots[wave];
   const uint8_t* kb = k_idx + b * k_bstride;
-  const int32_t* prow = GATHER ? pool_idx + row * (int64_t)pool_cap : nullptr;
+  if (GATHER) {   // pool token ids of the tile, read from LDS by the loads below
+    const int32_t* prow = pool_idx + row * (int64_t)pool_cap;
+    for (int i = threadIdx.x; i < tile; i += 256) {
+      const int64_t p = tile0 + i;
+      ptok[i] = p < nv ? prow[p] : 0;
+    }
+    __syncthreads();
+  }
 
   // Each wave owns tile/4 consecutive positions, SG*16 per iteration; the
-  // next iteration's key rows are in flight while this one is scored.
+  // next iteration's key rows are in flight while this one is scored.  Loads
+  // are issued unconditionally (positions past the wave's range read the
+  // last row of the range again and are never scored) so that waiting for
+  // one batch never waits for the batch behind it.
   constexpr int SG = kScanGroups<HB>;
   constexpr int IT = 16 * SG;
   const int64_t wbase = tile0 + (int64_t)wave * (tile / kScanWaves);
   int64_t wend = wbase + tile / kScanWaves;
   if (wend > nv) wend = nv;
+  const int64_t wlast = wend - 1;
 
-  auto frag_ptr = [&](int64_t pos, bool& ok) -> const uint8_t* {
-    ok = pos < wend;
-    int64_t tokid = pos;
-    if (GATHER && ok) tokid = prow[pos];
-    return frag_base<DI>(kb + (ok ? tokid : 0) * k_rstride, g);
+  auto frag_ptr = [&](int64_t pos) -> const uint8_t* {
+    const int64_t p = pos < wend ? pos : wlast;
+    const int64_t tokid = GATHER ? (int64_t)ptok[p - tile0] : p;
+    return frag_base<DI>(kb + tokid * k_rstride, g);
   };
 
   // Two fragment buffers used in ping-pong: while one batch of IT tokens is
@@ -167,11 +189,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   Frag<CH> fa[SG], fb[SG];
   auto load_batch = [&](Frag<CH>(&f)[SG], int64_t base) {
 #pragma unroll
-    for (int s = 0; s < SG; ++s) {
-      bool ok;
-      const uint8_t* p = frag_ptr(base + 16 * s + c16, ok);
-      load_frag<CH, DI>(f[s], p, ok);
-    }
+    for (int s = 0; s < SG; ++s) load_frag<CH, DI>(f[s], frag_ptr(base + 16 * s + c16), true);
   };
   auto score_batch = [&](const Frag<CH>(&f)[SG], int64_t it) {
 #pragma unroll
@@ -184,8 +202,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
           acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[hb][i], as_long(f[s].w[2 * i], f[s].w[2 * i + 1]),
                                                            acc, 0, 0, 0);
         // acc[r] = dot(head 16*hb + 4*g + r, token 16*s + c16)
-        int h0 = 16 * hb + 4 * g;
-        if (h0 < H_I) *reinterpret_cast<v4f*>(my + (16 * s + c16) * pitch + h0) = acc;
+        const int h0 = 16 * hb + 4 * g;
+        if (h0 < HP) *reinterpret_cast<v4f*>(my + (16 * s + c16) * pitch + h0) = acc;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -198,22 +216,22 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
       float sc = 0.0f;
       const float* src = my + (64 * u + lane) * pitch;
 #pragma unroll
-      for (int h4 = 0; h4 < HMAX; h4 += 4) {
-        if (h4 < pitch) {
-          const v4f d4 = *reinterpret_cast<const v4f*>(src + h4);
+      for (int h4 = 0; h4 < HP; h4 += 4) {
+        const v4f d4 = *reinterpret_cast<const v4f*>(src + h4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // heads past H_I have weight 0: adding +0 leaves the sum unchanged
-            float r = d4[e] > 0.0f ? d4[e] : 0.0f;
-            sc = __fadd_rn(sc, __fmul_rn(wv[h4 + e], r));
-          }
+        for (int e = 0; e < 4; ++e) {
+          // heads past H_I have weight 0: adding +0 leaves the sum unchanged
+          float r = d4[e] > 0.0f ? d4[e] : 0.0f;
+          sc = __fadd_rn(sc, __fmul_rn(wv[h4 + e], r));
         }
       }
+      // Positions up to the next multiple of 64 lie inside the row's key
+      // stride and belong to no other wave; past the visible count they are
+      // never read.
       uint32_t key = vis ? score_key(sc) : 0u;
-      if (vis) {
-        keys[row * key_stride + j] = key;
-        atomicAdd(&hist[key >> 20], 1u);
-      }
+      if (kStage) kst[j - tile0] = key;
+      else keys[row * key_stride + j] = key;
+      atomicAdd(&hist[vis ? key >> 21 : 2048u], 1u << (16 * ((key >> 20) & 1u)));
       if (pool) {
         uint32_t m = key;
         for (int off = 1; off < pool_block; off <<= 1) {
@@ -230,25 +248,39 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  if (wbase < wend) load_batch(fa, wbase);
-  for (int64_t it = wbase; it < wend; it += 2 * IT) {
-    const bool has_b = it + IT < wend;
-    if (has_b) load_batch(fb, it + IT);
-    score_batch(fa, it);
-    if (it + 2 * IT < wend) load_batch(fa, it + 2 * IT);
-    if (has_b) score_batch(fb, it + IT);
+  const int nb = wend > wbase ? (int)((wend - wbase + IT - 1) / IT) : 0;
+  if (nb > 0) {
+    load_batch(fa, wbase);
+    load_batch(fb, wbase + IT);
+  }
+  for (int ib = 0; ib < nb; ib += 2) {
+    score_batch(fa, wbase + (int64_t)ib * IT);
+    load_batch(fa, wbase + (int64_t)(ib + 2) * IT);
+    if (ib + 1 < nb) score_batch(fb, wbase + (int64_t)(ib + 1) * IT);
+    load_batch(fb, wbase + (int64_t)(ib + 3) * IT);
   }
   __syncthreads();
+  if (kStage) {
+    int64_t tend = tile0 + tile;
+    if (tend > nv) tend = nv;
+    // Whole 64-position groups: they stay inside the row's key stride.
+    const int64_t tn = tend > tile0 ? ((tend - tile0 + 63) & ~63LL) : 0;
+    for (int64_t i = 4 * threadIdx.x; i < tn; i += 4 * 256)
+      *reinterpret_cast<v4u*>(keys + row * key_stride + tile0 + i) = *reinterpret_cast<const v4u*>(&kst[i]);
+  }
   uint32_t* gh = tok.hist1 + row * 4096;
-  for (int i = threadIdx.x; i < 4096; i += 256)
-    if (hist[i]) atomic_add_agent(gh + i, hist[i]);
+  for (int i = threadIdx.x; i < 2048; i += 256) {
+    const uint32_t v = hist[i];
+    if (v & 0xFFFFu) atomic_add_agent(gh + 2 * i, v & 0xFFFFu);
+    if (v >> 16) atomic_add_agent(gh + 2 * i + 1, v >> 16);
+  }
   uint32_t* gbh = pool ? blk.hist1 + row * 4096 : nullptr;
   if (pool)
     for (int i = threadIdx.x; i < 4096; i += 256)
       if (bhist[i]) atomic_add_agent(gbh + i, bhist[i]);
 }
 
-template <int DI, int HB>
+template <int DI, int HB, bool H8>
 static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
@@ -263,12 +295,12 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
   SelectWs bw = blk ? *blk : tok;
   dim3 grid((unsigned)tiles, (unsigned)rows);
   if (a.pool_block > 0) {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true>), grid, dim3(256), 0, s, a.q_idx, a.w,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8>), grid, dim3(256), 0, s, a.q_idx, a.w,
                 a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok,
                 a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
   } else {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false>), grid, dim3(256), 0, s, a.q_idx, a.w,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8>), grid, dim3(256), 0, s, a.q_idx, a.w,
                 a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok, 0,
                 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, bw);
@@ -276,7 +308,7 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
   return hipGetLastError();
 }
 
-template <int DI, int HB>
+template <int DI, int HB, bool H8>
 static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                                 int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
                                 int B, int Tq, int H_I, int k_top, uint32_t* keys, int64_t key_stride,
@@ -284,7 +316,7 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
   int64_t rows = (int64_t)B * Tq;
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
+  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
               0, s, q_idx, w, k_idx, k_bstride, k_rstride, (const int32_t*)nullptr, (const int32_t*)nullptr,
               pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, key_stride, n_valid, ws,
               0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
@@ -654,12 +686,12 @@ static hipError_t launch_prefill(const ScoreArgs& a, uint32_t* keys, int64_t key
 
 #define CSA2_DISPATCH_DI_HB(DI_, HB_, CALL)                                       \
   do {                                                                           \
-    int hb__ = (HB_) <= 16 ? 1 : 2;                                              \
+    int hb__ = (HB_) <= 8 ? 0 : ((HB_) <= 16 ? 1 : 2);                           \
     switch (DI_) {                                                               \
-      case 32: return hb__ == 1 ? CALL(32, 1) : CALL(32, 2);                      \
-      case 64: return hb__ == 1 ? CALL(64, 1) : CALL(64, 2);                      \
-      case 128: return hb__ == 1 ? CALL(128, 1) : CALL(128, 2);                   \
-      case 256: return hb__ == 1 ? CALL(256, 1) : CALL(256, 2);                   \
+      case 32: return hb__ == 0 ? CALL(32, 1, true) : hb__ == 1 ? CALL(32, 1, false) : CALL(32, 2, false);      \
+      case 64: return hb__ == 0 ? CALL(64, 1, true) : hb__ == 1 ? CALL(64, 1, false) : CALL(64, 2, false);      \
+      case 128: return hb__ == 0 ? CALL(128, 1, true) : hb__ == 1 ? CALL(128, 1, false) : CALL(128, 2, false);  \
+      case 256: return hb__ == 0 ? CALL(256, 1, true) : hb__ == 1 ? CALL(256, 1, false) : CALL(256, 2, false);  \
       default: return hipErrorInvalidValue;                                       \
     }                                                                            \
   } while (0)
@@ -668,7 +700,7 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
                               const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                               const SelectWs* blk, hipStream_t s) {
   if (prefill_gemm_applies(a)) return launch_prefill(a, keys, key_stride, n_valid, tok, s);
-#define CALL_SCAN(D, H) launch_scan_t<D, H>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
+#define CALL_SCAN(D, H, E) launch_scan_t<D, H, E>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
   CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_SCAN);
 #undef CALL_SCAN
 }
@@ -677,8 +709,8 @@ hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t
                              int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
                              int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
                              int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
-#define CALL_POOL(D, H) \
-  launch_pool_t<D, H>(q_idx, w, k_idx, k_bstride, k_rstride, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
+#define CALL_POOL(D, H, E) \
+  launch_pool_t<D, H, E>(q_idx, w, k_idx, k_bstride, k_rstride, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
                       key_stride, n_valid, ws, s)
   CSA2_DISPATCH_DI_HB(D_I, H_I, CALL_POOL);
 #undef CALL_POOL
