@@ -13,19 +13,23 @@
 // its entry list (Top-K rows, then the window rows).  Its 8 waves (two per
 // SIMD) form 4 head groups of 16 heads; the two waves of a head group own
 // one half each of the 64 entries of a chunk for S and one half each of the
-// 512 output dims for O (64 fp32 accumulator registers per lane).  Per chunk
-// of 64 entries it gathers the rows by index, dequantises them into LDS as
-// fp16 with the gfx950 scaled converts (v_cvt_scalef32_pk_f16_fp4 / _fp8,
-// which apply the power-of-two part of their scale; the E4M3 scale of a main
-// row is applied as an fp16 multiply) -- exact, since E2M1 x E4M3 has at most
-// 6 significant bits within [2^-10, 2688] -- and runs
+// 512 output dims for O (64 fp32 accumulator registers per lane).  Chunks of
+// 64 entries are double-buffered in LDS as fp16 rows: while a chunk is
+// consumed, the next one is dequantised into the other buffer and the rows
+// of the one after it are in flight.  The rows are gathered by index and
+// dequantised with the gfx950 scaled converts (v_cvt_scalef32_pk_f16_fp4 /
+// _fp8, which apply the power-of-two part of their scale; the E4M3 scale of
+// a main row is applied as an fp16 multiply) -- exact, since E2M1 x E4M3 has
+// at most 6 significant bits within [2^-10, 2688] -- and then
 //   S^T = K Q^T   on v_mfma_f32_16x16x32_f16 (q rounded to fp16 once), each
 //                 wave for its 32 entries,
 //   online softmax in fp32 (exp2 domain); the wave pair exchanges row maxima
 //                 and its P fragments through LDS,
 //   O  += P V     on the same instruction, P taken straight from the S^T
 //                 accumulators (their lane layout is the A-operand layout of
-//                 P once the k index is permuted identically for V).
+//                 P once the k index is permuted identically for V), and V
+//                 read from the same fp16 rows with the LDS transpose read
+//                 (ds_read_b64_tr_b16), so no transposed copy is stored.
 // Splits write unnormalised partial (O, m, l); a combine kernel merges them
 // with the log-sum-exp rule and adds the sink.
 #include "common.h"
@@ -41,7 +45,7 @@ template <int DQK>
 struct AttnShape {
   static constexpr int G16 = DQK / 16;          // 16-channel groups per row
   static constexpr int KQ = DQK / 32;           // MFMA k-steps for S = K Q^T
-  static constexpr int PITCH = DQK + 8;         // fp16 row pitch in LDS (bank spread)
+  static constexpr int PITCH = DQK + 16;         // fp16 row pitch in LDS (bank spread)
 };
 
 __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
@@ -53,9 +57,8 @@ __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
   return r;
 }
 
-constexpr int kMaxSpan = 1024;      // entries per split (ids staged in LDS)
+constexpr int kMaxSpan = 640;       // entries per split (ids staged in LDS)
 constexpr int kAttnThreads = 512;   // 8 waves; wave w: heads 16*(w&3).., output dims 256*(w>>2)..
-constexpr int kVtPitch = kChunk + 4;  // fp16 per V^T row (34 dwords: spreads banks)
 
 // Raw bytes of one gather task: two entries (2*ep, 2*ep+1) of one 16-channel group.
 struct RawTask {
@@ -73,8 +76,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   constexpr int NTASK = (kChunk / 2) * S::G16;        // (entry pair, group) tasks per chunk
   constexpr int NEP = kChunk / 2;                     // entry pairs per chunk
   constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
-  __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * S::PITCH];   // K rows, row-major
-  __shared__ __attribute__((aligned(16))) _Float16 vt[DV * kVtPitch];       // V transposed
+  __shared__ __attribute__((aligned(16))) _Float16 kbuf[2][kChunk * S::PITCH];   // K rows, row-major, 2 chunks
   __shared__ int32_t eid[kMaxSpan];   // main: token id; window: window row; -1 = skip
   __shared__ float pmx[2][64];        // per-head partial maxima / sums of the two dim halves
   __shared__ __attribute__((aligned(16))) v8h pex[8][64];   // P fragments exchanged between wave pairs
@@ -166,7 +168,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     }
   };
   // ---- dequantise the staged bytes into K rows and V^T columns.
-  auto store = [&]() {
+  auto store = [&](_Float16* kt) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
@@ -212,13 +214,6 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         dst[0] = uint4{hv[k][0], hv[k][1], hv[k][2], hv[k][3]};
         dst[1] = uint4{hv[k][4], hv[k][5], hv[k][6], hv[k][7]};
       }
-      if (16 * gq < DV) {
-        uint32_t* vcol = reinterpret_cast<uint32_t*>(vt + (16 * gq) * kVtPitch + 2 * ep);
-#pragma unroll
-        for (int c = 0; c < 16; ++c)   // (entry 2ep, entry 2ep+1) halves of channel 16gq + c
-          vcol[c * (kVtPitch / 2)] = __builtin_amdgcn_perm(hv[1][c >> 1], hv[0][c >> 1],
-                                                           (c & 1) ? 0x07060302u : 0x05040100u);
-      }
     }
   };
 
@@ -230,12 +225,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 
   if (e_begin < e_end) {
     gather(e_begin);
-    store();
+    store(kbuf[0]);
   }
   __syncthreads();
-  for (int c0 = e_begin; c0 < e_end; c0 += kChunk) {
+  if (e_begin + kChunk < e_end) gather(e_begin + kChunk);
+  int cur = 0;
+  for (int c0 = e_begin; c0 < e_end; c0 += kChunk, cur ^= 1) {
     const bool has_next = c0 + kChunk < e_end;
-    if (has_next) gather(c0 + kChunk);   // in flight during this chunk's math
+    const _Float16* kt = kbuf[cur];
     // ---- S^T = K Q^T for this wave's 2 tiles of 16 entries: entries 32*dh ..
     float z[8];
     float cmax = -__builtin_inff();
@@ -314,21 +311,26 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           o[n][0] *= al[0]; o[n][1] *= al[1]; o[n][2] *= al[2]; o[n][3] *= al[3];
         }
       }
-      // ---- O += P V over dims 256*dh ..; k-step j: entries 32j + {4g..4g+3, 16+4g..16+4g+3}
-      const _Float16* vrow = vt + (256 * dh + c16) * kVtPitch + 4 * g;
-      typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+      // ---- O += P V over dims 256*dh ..; k-step j: entries 32j + {4g..4g+3, 16+4g..16+4g+3}.
+      // V is read from the row-major K rows with the LDS transpose read: in each
+      // 16-lane group, source lane s names entry (.. + s/4), dims 4(s%4)..+3, and
+      // lane i receives dim i of those four entries.
+      const int s16 = lane & 15;
+      const _Float16* vbase = kt + (4 * g + (s16 >> 2)) * S::PITCH + 256 * dh + 4 * (s16 & 3);
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
       constexpr int VB = 4;
 #pragma unroll
       for (int n0 = 0; n0 < NT; n0 += VB) {
         v8h vf[VB][2];
 #pragma unroll
         for (int jn = 0; jn < VB; ++jn) {
-          const _Float16* vp = vrow + (16 * (n0 + jn)) * kVtPitch;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            v4h lo = *reinterpret_cast<const v4h*>(vp + 32 * j);
-            v4h hi = *reinterpret_cast<const v4h*>(vp + 32 * j + 16);
-            vf[jn][j] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const _Float16* vp = vbase + 32 * j * S::PITCH + 16 * (n0 + jn);
+            v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vp));
+            v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vp + 16 * S::PITCH));
+            vf[jn][j] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
         }
 #pragma unroll
@@ -338,8 +340,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         }
       }
     }
-    __syncthreads();
-    if (has_next) store();
+    // Next chunk into the other buffer (last read one iteration ago), then
+    // the loads of the chunk after it.
+    if (has_next) {
+      store(kbuf[cur ^ 1]);
+      if (c0 + 2 * kChunk < e_end) gather(c0 + 2 * kChunk);
+    }
     __syncthreads();
   }
 
