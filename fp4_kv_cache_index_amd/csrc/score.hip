@@ -104,7 +104,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? kScanTile : 1];
   __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
   __shared__ uint32_t bhist[POOL ? 4096 : 1];
-  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HP];
+  // per wave: the batch's dots, then one 4-float trash slot per lane (whole-line path)
+  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HP + 256];
   __shared__ float wsh[HMAX];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -140,8 +141,27 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   for (int h = 0; h < HP; ++h)
     wv[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsh[h])));
 
+  // Whole-line loads (D_I = 128, one head block): every token of a group of
+  // 8 takes two B columns -- 2m holds bytes 32g..32g+15 of its row, 2m+1
+  // bytes 32g+16..32g+31 (lane group g) -- so the 8 lanes of a token read its
+  // whole 128-byte row in one instruction.  Two MFMA pairs with the matching
+  // halves of the query rows give the two partial dots, which one adjacent-
+  // lane exchange joins (exact: integers below 2^24).
+  constexpr bool FULL = (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
   // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
   const int c16 = lane & 15, g = lane >> 4;
+  long qh[2][2];   // FULL: [parity e][step s] = bytes 32g + 16e + 8s .. +8
+  if (FULL) {
+    const bool hv = c16 < H_I;
+    const uint8_t* qp = q_idx + (row * H_I + (hv ? c16 : 0)) * DI + 32 * g;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const v2u v = hv ? *reinterpret_cast<const v2u*>(qp + 16 * e + 8 * st) : v2u{0u, 0u};
+        qh[e][st] = as_long(v[0], v[1]);
+      }
+  }
   long qa[HB][KS];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
@@ -183,15 +203,53 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     const int64_t tokid = GATHER ? (int64_t)ptok[p - tile0] : p;
     return frag_base<DI>(kb + tokid * k_rstride, g);
   };
+  auto full_ptr = [&](int64_t pos) -> const uint8_t* {
+    const int64_t p = pos < wend ? pos : wlast;
+    const int64_t tokid = GATHER ? (int64_t)ptok[p - tile0] : p;
+    return kb + tokid * k_rstride + 16 * (2 * g + (c16 & 1));
+  };
 
   // Two fragment buffers used in ping-pong: while one batch of IT tokens is
   // scored, the other batch's loads are in flight.
   Frag<CH> fa[SG], fb[SG];
   auto load_batch = [&](Frag<CH>(&f)[SG], int64_t base) {
+    if constexpr (FULL) {
+      // 8 groups of 8 tokens; group u = 2s + half lands in f[s].w[4*half ..]
 #pragma unroll
-    for (int s = 0; s < SG; ++s) load_frag<CH, DI>(f[s], frag_ptr(base + 16 * s + c16), true);
+      for (int u = 0; u < 2 * SG; ++u) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(full_ptr(base + 8 * u + (c16 >> 1))));
+        f[u >> 1].w[4 * (u & 1) + 0] = v[0]; f[u >> 1].w[4 * (u & 1) + 1] = v[1];
+        f[u >> 1].w[4 * (u & 1) + 2] = v[2]; f[u >> 1].w[4 * (u & 1) + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < SG; ++s) load_frag<CH, DI>(f[s], frag_ptr(base + 16 * s + c16), true);
+    }
   };
   auto score_batch = [&](const Frag<CH>(&f)[SG], int64_t it) {
+    if constexpr (FULL) {
+#pragma unroll
+      for (int u = 0; u < 2 * SG; ++u) {
+        const uint32_t* w4 = &f[u >> 1].w[4 * (u & 1)];
+        const long lo = as_long(w4[0], w4[1]), hi = as_long(w4[2], w4[3]);
+        v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[0][0], lo, a0, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[0][1], hi, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[1][0], lo, a1, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[1][1], hi, a1, 0, 0, 0);
+        // even column 2m: a0 here plus a1 of the odd column 2m+1 (lane + 1).
+        // (__shfl_xor: the DPP builtins applied to elements of an MFMA result
+        // were folded into a single element by this compiler.)
+        v4f d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] = a0[r] + __shfl_xor(a1[r], 1, 64);
+        // d[r] = dot(head 4g + r, token 8u + m) on the even lanes; the other
+        // lanes write their own trash slot (no branch around the loads' waits)
+        const bool keep = (c16 & 1) == 0 && 4 * g < HP;
+        const int at = keep ? (8 * u + (c16 >> 1)) * pitch + 4 * g : 16 * SG * HP + 4 * lane;
+        *reinterpret_cast<v4f*>(my + at) = d;
+      }
+    } else {
 #pragma unroll
     for (int s = 0; s < SG; ++s) {
 #pragma unroll
@@ -205,6 +263,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
         const int h0 = 16 * hb + 4 * g;
         if (h0 < HP) *reinterpret_cast<v4f*>(my + (16 * s + c16) * pitch + h0) = acc;
       }
+    }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
