@@ -56,6 +56,8 @@ struct SelectRowCtl {                // per-row control block (64 bytes)
   uint32_t pad[12];
 };
 
+constexpr int kTileList = 512;       // positions listed per tile by the collect pass
+
 struct SelectWs {
   SelectRowCtl* ctl;                 // [rows]
   uint32_t* hist1;                   // [rows][4096]
@@ -63,6 +65,8 @@ struct SelectWs {
   uint32_t* tile_gt;                 // [rows][tiles] keys above the threshold bucket
   uint32_t* tile_off;                // [rows][tiles] output offset of the tile
   uint32_t* tile_eqb;                // [rows][tiles] threshold ties before the tile
+  uint32_t* tile_cnt;                // [rows][tiles] listed positions, or ~0u when they did not fit
+  uint16_t* tlist;                   // [rows][tiles][kTileList] in-tile offsets at or above the bucket
   int64_t cand_cap, tiles;
 };
 size_t select_ws_bytes(int64_t rows, int64_t n_max);

@@ -10,14 +10,17 @@
 // lowest positions with key == T.  The producer (the scoring kernel) writes
 // the keys and a histogram of their top 12 bits.  Then:
 //   collect  -- every workgroup resolves the threshold bucket from the
-//               histogram itself, counts its tile's keys above the bucket and
-//               appends the bucket's keys as (key, position) candidates;
+//               histogram itself, counts its tile's keys above the bucket,
+//               appends the bucket's keys as (key, position) candidates and
+//               lists, in position order, the tile's positions at or above
+//               the bucket (when at most kTileList of them);
 //   finalize -- one workgroup per row finds T and need_eq among the
 //               candidates (two more radix digits, in LDS), every tile's
 //               output offset, the -1 padding and the pool length;
-//   emit     -- every tile writes its selected positions in ascending order.
+//   emit     -- every tile writes its selected positions in ascending order,
+//               from its list (or from all its keys when the list overflowed).
 // No workgroup waits for or elects another; kernel boundaries order the
-// passes.  The key array is read twice after it is written.
+// passes.  The key array is read once in full after it is written.
 #include "common.h"
 #include "internal.h"
 #include "select_dev.h"
@@ -38,7 +41,8 @@ size_t select_ws_bytes(int64_t rows, int64_t n_max) {
   b += align256(sizeof(SelectRowCtl) * rows);
   b += align256(sizeof(uint32_t) * 4096 * rows);
   b += align256(sizeof(uint32_t) * 2 * cap * rows);
-  b += 3 * align256(sizeof(uint32_t) * tiles * rows);
+  b += 4 * align256(sizeof(uint32_t) * tiles * rows);
+  b += align256(sizeof(uint16_t) * kTileList * tiles * rows);
   return b;
 }
 
@@ -51,17 +55,27 @@ SelectWs select_ws_carve(void* base, int64_t rows, int64_t n_max) {
   w.cand = (uint32_t*)p; p += align256(sizeof(uint32_t) * 2 * cap * rows);
   w.tile_gt = (uint32_t*)p; p += align256(sizeof(uint32_t) * tiles * rows);
   w.tile_off = (uint32_t*)p; p += align256(sizeof(uint32_t) * tiles * rows);
-  w.tile_eqb = (uint32_t*)p;
+  w.tile_eqb = (uint32_t*)p; p += align256(sizeof(uint32_t) * tiles * rows);
+  w.tile_cnt = (uint32_t*)p; p += align256(sizeof(uint32_t) * tiles * rows);
+  w.tlist = (uint16_t*)p;
   w.cand_cap = cap;
   w.tiles = tiles;
   return w;
 }
 
-// The 16 keys a thread handles in the unordered passes: positions
-// base + 4*(tid + 256*i) + (0..3), i = 0..3, loaded as four 16-byte vectors
-// (coalesced across the workgroup) before any of them is used.  Positions at
-// or past nv read as 0 (absent).  Rows are padded to a multiple of 64 keys, so
-// a vector that starts below nv stays inside the row.
+// ------------------------------------------------------------- kernels ---
+
+__global__ void select_clear_kernel(uint32_t* p, int64_t n_words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The 16 keys a thread handles: positions base + 1024*i + 4*tid + j
+// (i, j = 0..3), loaded as four 16-byte vectors (coalesced across the
+// workgroup) before any of them is used.  Positions at or past nv read as 0
+// (absent); rows are padded to a multiple of 64 keys, so a vector that starts
+// below nv stays inside the row.  Ordering by (i, tid, j) is position order.
 __device__ __forceinline__ void load_tile_keys(const uint32_t* kr, int64_t base, int64_t nv, uint32_t (&k)[16]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -73,20 +87,13 @@ __device__ __forceinline__ void load_tile_keys(const uint32_t* kr, int64_t base,
   }
 }
 
-// ------------------------------------------------------------- kernels ---
-
-__global__ void select_clear_kernel(uint32_t* p, int64_t n_words) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
-// collect: counts above the threshold bucket per tile; appends the bucket.
+// collect: counts above the threshold bucket per tile; appends the bucket;
+// lists the tile's positions at or above the bucket in position order.
 __global__ void __launch_bounds__(256)
 select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
                       const int32_t* __restrict__ n_valid, int k) {
   __shared__ uint32_t red[4], res[4];
-  __shared__ uint32_t slot0;
+  __shared__ uint32_t slot0, ltot[2];
   const int64_t row = blockIdx.y;
   const int64_t nv = n_valid[row];
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
@@ -94,6 +101,7 @@ select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t ke
   load_tile_keys(keys + row * key_stride, base, nv, kk);   // in flight during the resolution
   const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
   uint32_t gt = 0, nc = 0;
+  uint32_t nl[4] = {0u, 0u, 0u, 0u};   // listed keys per round i
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const bool valid = kk[i] != 0u;
@@ -104,9 +112,37 @@ select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t ke
       gt += valid && bkt > L.d;
       nc += valid && bkt == L.d;
     }
+    nl[i >> 2] += valid && (L.mode == 1u || bkt >= L.d);
   }
+  const int64_t tix = row * ws.tiles + blockIdx.x;
   const uint32_t g_incl = block_prefix_sum_256(gt, red);
-  if (threadIdx.x == 255) ws.tile_gt[row * ws.tiles + blockIdx.x] = g_incl;
+  if (threadIdx.x == 255) ws.tile_gt[tix] = g_incl;
+  // Per-round prefix sums, two rounds per word (16-bit fields; a round holds
+  // at most 1024 keys).
+  const uint32_t w01 = nl[0] | (nl[1] << 16), w23 = nl[2] | (nl[3] << 16);
+  const uint32_t i01 = block_prefix_sum_256(w01, red);
+  const uint32_t i23 = block_prefix_sum_256(w23, red);
+  if (threadIdx.x == 255) { ltot[0] = i01; ltot[1] = i23; }
+  __syncthreads();
+  const uint32_t t0 = ltot[0] & 0xFFFFu, t1 = ltot[0] >> 16, t2 = ltot[1] & 0xFFFFu, t3 = ltot[1] >> 16;
+  const uint32_t count = t0 + t1 + t2 + t3;
+  if (threadIdx.x == 0) ws.tile_cnt[tix] = count <= (uint32_t)kTileList ? count : ~0u;
+  if (count <= (uint32_t)kTileList) {
+    const uint32_t ex01 = i01 - w01, ex23 = i23 - w23;
+    const uint32_t start[4] = {ex01 & 0xFFFFu, t0 + (ex01 >> 16), t0 + t1 + (ex23 & 0xFFFFu),
+                               t0 + t1 + t2 + (ex23 >> 16)};
+    uint16_t* lst = ws.tlist + tix * kTileList;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t at = start[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t key = kk[4 * i + j];
+        if (key != 0u && (L.mode == 1u || (key >> 20) >= L.d))
+          lst[at++] = (uint16_t)(1024 * i + 4 * threadIdx.x + j);
+      }
+    }
+  }
   if (L.mode != 0u) return;
   const uint32_t c_incl = block_prefix_sum_256(nc, red);
   if (threadIdx.x == 255) slot0 = c_incl ? atomicAdd(&ws.ctl[row].cand_count, c_incl) : 0u;
@@ -117,9 +153,8 @@ select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t ke
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (kk[i] != 0u && (kk[i] >> 20) == L.d) {
-      const int64_t pos = base + 4 * ((int64_t)threadIdx.x + 256 * (i >> 2)) + (i & 3);
       cr[2 * slot] = kk[i];
-      cr[2 * slot + 1] = (uint32_t)pos;
+      cr[2 * slot + 1] = (uint32_t)(base + 4 * ((int64_t)threadIdx.x + 256 * (i >> 2)) + (i & 3));
       ++slot;
     }
   }
@@ -276,8 +311,68 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   const int64_t nv = n_valid[row];
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
   if (base >= nv) return;
-  const int64_t p0 = base + (int64_t)threadIdx.x * PER;
   const uint32_t* kr = keys + row * key_stride;
+  const int64_t tix = row * tiles + blockIdx.x;
+  const uint32_t cnt = ws.tile_cnt[tix];
+  if (cnt != ~0u) {
+    // The tile's positions at or above the threshold bucket, in position
+    // order: thread t takes list entries 2t and 2t+1.
+    const uint16_t* lst = ws.tlist + tix * kTileList;
+    const uint32_t thr = ws.ctl[row].thr, need_eq = ws.ctl[row].need_eq;
+    const uint32_t off0 = ws.tile_off[tix];
+    const uint32_t eqb0 = ws.tile_eqb[tix];
+    uint32_t lk[2];
+    int64_t lp[2];
+    bool lh[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t c = 2 * threadIdx.x + q;
+      lh[q] = c < cnt;
+      lp[q] = base + (lh[q] ? lst[c] : 0);
+      lk[q] = lh[q] ? kr[lp[q]] : 0u;
+    }
+    uint32_t n_eq = 0, n_gt = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      n_gt += lh[q] && lk[q] > thr;
+      n_eq += lh[q] && lk[q] == thr;
+    }
+    const uint32_t eq_incl = block_prefix_sum_256(n_eq, red);
+    const uint32_t eq_rank = eqb0 + eq_incl - n_eq;
+    uint32_t my_take = 0;
+    if (need_eq > eq_rank) my_take = (need_eq - eq_rank) < n_eq ? (need_eq - eq_rank) : n_eq;
+    const uint32_t sel = n_gt + my_take;
+    const uint32_t sel_incl = block_prefix_sum_256(sel, red);
+    uint32_t slot = off0 + sel_incl - sel;
+    uint32_t taken_eq = 0;
+    const int32_t* map = out.map ? out.map + row * out.map_stride : nullptr;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!lh[q]) break;
+      bool take = lk[q] > thr;
+      if (!take && lk[q] == thr) {
+        take = taken_eq < my_take;
+        ++taken_eq;
+      }
+      if (!take) continue;
+      if (slot >= (uint32_t)k) break;
+      if (out.expand == 0) {
+        const int32_t id = map ? map[lp[q]] : (int32_t)lp[q];
+        out.idx[row * (int64_t)k + slot] = id;
+        if (out.score) out.score[row * (int64_t)k + slot] = key_score(lk[q]);
+      } else {
+        const int64_t cap = (int64_t)k * out.expand;
+        const int32_t lim = out.expand_limit[row];
+        for (int u = 0; u < out.expand; ++u) {
+          const int64_t id = lp[q] * out.expand + u;
+          out.idx[row * cap + (int64_t)slot * out.expand + u] = id < lim ? (int32_t)id : -1;
+        }
+      }
+      ++slot;
+    }
+    return;
+  }
+  const int64_t p0 = base + (int64_t)threadIdx.x * PER;
   uint32_t kk[PER];
 #pragma unroll
   for (int i = 0; i < PER / 4; ++i) {
@@ -287,8 +382,8 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
     for (int j = 0; j < 4; ++j) kk[4 * i + j] = (p0 + 4 * i + j < nv) ? v[j] : 0u;
   }
   const uint32_t thr = ws.ctl[row].thr, need_eq = ws.ctl[row].need_eq;
-  const uint32_t off0 = ws.tile_off[row * tiles + blockIdx.x];
-  const uint32_t eqb0 = ws.tile_eqb[row * tiles + blockIdx.x];
+  const uint32_t off0 = ws.tile_off[tix];
+  const uint32_t eqb0 = ws.tile_eqb[tix];
   uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
