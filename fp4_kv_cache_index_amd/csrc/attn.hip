@@ -10,26 +10,32 @@
 // d_v channels of the same row.
 //
 // gfx950 mapping.  A workgroup holds one query row and a contiguous split of
-// its entry list (Top-K rows, then the window rows).  Its 8 waves (two per
-// SIMD) form 4 head groups of 16 heads; the two waves of a head group own
-// one half each of the 64 entries of a chunk for S and one half each of the
-// 512 output dims for O (64 fp32 accumulator registers per lane).  Chunks of
-// 64 entries are double-buffered in LDS as fp16 rows: while a chunk is
-// consumed, the next one is dequantised into the other buffer and the rows
-// of the one after it are in flight.  The rows are gathered by index and
-// dequantised with the gfx950 scaled converts (v_cvt_scalef32_pk_f16_fp4 /
-// _fp8, which apply the power-of-two part of their scale; the E4M3 scale of
-// a main row is applied as an fp16 multiply) -- exact, since E2M1 x E4M3 has
-// at most 6 significant bits within [2^-10, 2688] -- and then
-//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16 (q rounded to fp16 once), each
-//                 wave for its 32 entries,
-//   online softmax in fp32 (exp2 domain); the wave pair exchanges row maxima
-//                 and its P fragments through LDS,
-//   O  += P V     on the same instruction, P taken straight from the S^T
-//                 accumulators (their lane layout is the A-operand layout of
-//                 P once the k index is permuted identically for V), and V
-//                 read from the same fp16 rows with the LDS transpose read
-//                 (ds_read_b64_tr_b16), so no transposed copy is stored.
+// its entry list (Top-K rows, then the window rows); workgroups are numbered
+// so that the splits of one row land on the same XCD and share its q in L2.
+// Chunks of 64 entries are double-buffered in LDS as fp16 rows: while a
+// chunk is consumed, the next one is dequantised into the other buffer and
+// the rows of the one after it are in flight.  A gather task is one entry's
+// 32-channel block, consecutive lanes taking consecutive 16-byte pieces of a
+// row; the rows are dequantised with the gfx950 scaled converts
+// (v_cvt_scalef32_pk_f16_fp4 / _fp8, which apply the power-of-two part of
+// their scale; the E4M3 scale of a main row is applied as an fp16 multiply)
+// -- exact, since E2M1 x E4M3 has at most 6 significant bits within
+// [2^-10, 2688].  q is read once per workgroup with coalesced loads, rounded
+// to fp16 once and passed through LDS into registers.  Then, per chunk,
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16: the 8 waves (two per SIMD) are
+//                 4 head groups of 16 heads x 2 halves of the chunk's entries,
+//                 q held in registers;
+//   online softmax in fp32 (exp2 domain); the two waves of a head group
+//                 exchange row maxima; P fragments and per-head rescale
+//                 factors go to LDS;
+//   O  += P V     on the same instruction, the waves now 2 halves of the
+//                 heads (32 each) x 4 quarters of the output dims, so every V
+//                 fragment serves two head tiles (64 fp32 accumulator
+//                 registers per lane).  P keeps the lane layout of the S^T
+//                 accumulators (the A-operand layout once the k index is
+//                 permuted identically for V), and V is read from the same
+//                 fp16 rows with the LDS transpose read (ds_read_b64_tr_b16),
+//                 so no transposed copy is stored.
 // Splits write unnormalised partial (O, m, l); a combine kernel merges them
 // with the log-sum-exp rule and adds the sink.
 #include "common.h"
@@ -58,13 +64,13 @@ __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
 }
 
 constexpr int kMaxSpan = 640;       // entries per split (ids staged in LDS)
-constexpr int kAttnThreads = 512;   // 8 waves; wave w: heads 16*(w&3).., output dims 256*(w>>2)..
+constexpr int kAttnThreads = 512;   // 8 waves (see the mapping above)
 
-// Raw bytes of one gather task: two entries (2*ep, 2*ep+1) of one 16-channel group.
+// Raw bytes of one gather task: one entry, one 32-channel block.
 struct RawTask {
-  uint32_t w[2][4];   // main: 8 code bytes in w[k][0..1]; window: 16 value bytes
-  uint32_t sc[2];     // scale byte (E4M3 for main rows, E8M0 for window rows)
-  uint32_t kind;      // 2 bits per entry: 0 skip, 1 main, 2 window
+  uint32_t w[8];      // main: 16 code bytes in w[0..3]; window: 32 value bytes
+  uint32_t sc;        // main: the block's two E4M3 scale bytes; window: its E8M0 byte
+  uint32_t kind;      // 0 skip, 1 main, 2 window
 };
 
 template <int DQK, int DV>
@@ -72,19 +78,28 @@ __global__ void __launch_bounds__(kAttnThreads)
 sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
                          float* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = AttnShape<DQK>;
-  constexpr int NT = DV / 32;                         // output tiles per wave (half the dims)
-  constexpr int NTASK = (kChunk / 2) * S::G16;        // (entry pair, group) tasks per chunk
-  constexpr int NEP = kChunk / 2;                     // entry pairs per chunk
+  constexpr int NT = DV / 64;                         // output dim tiles per wave (a quarter of the dims)
+  constexpr int NB = DQK / 32;                        // 32-channel blocks per row
+  constexpr int NTASK = kChunk * NB;                  // (entry, block) tasks per chunk
+  constexpr int QP = DQK + 8;                         // fp16 pitch of the staged q rows
+  static_assert(64 * QP <= kChunk * S::PITCH, "q staging must fit one K buffer");
   constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
   __shared__ __attribute__((aligned(16))) _Float16 kbuf[2][kChunk * S::PITCH];   // K rows, row-major, 2 chunks
-  __shared__ int32_t eid[kMaxSpan];   // main: token id; window: window row; -1 = skip
+  __shared__ __attribute__((aligned(16))) int32_t eid[kMaxSpan];   // main: token id; window: window row; -1 = skip
   __shared__ float pmx[2][64];        // per-head partial maxima / sums of the two dim halves
-  __shared__ __attribute__((aligned(16))) v8h pex[8][64];   // P fragments exchanged between wave pairs
+  __shared__ __attribute__((aligned(16))) v8h pex[8][64];   // P fragments of every S wave
+  __shared__ __attribute__((aligned(16))) float alf[64];     // per-head rescale factor of the chunk
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  const int64_t row = blockIdx.y;
-  const int split = blockIdx.x;
+  // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs in
+  // launch order; renumber them so that the splits of one query row (which
+  // all read its q) sit on the same XCD and share its L2.
+  const int nwg = gridDim.x * gridDim.y;
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int flat = (nwg & 7) == 0 ? (lin & 7) * (nwg >> 3) + (lin >> 3) : lin;
+  const int64_t row = flat / gridDim.x;
+  const int split = flat - (int)row * gridDim.x;
   const int64_t b = row / a.Tq;
   const int H = a.H;
   const int K = a.k_top;
@@ -119,17 +134,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     eid[e - e_begin] = v;
   }
 
-  // q fragments of this wave's 16 heads: lane holds head 16*wave + c16,
+  // q fragments of this wave's 16 heads: lane holds head 16*hg + c16,
   // dims 32*i + 8*g .. +8 of k-step i (the B operand of S^T = K Q^T).
   const int hg = wave & 3, dh = wave >> 2;
   const bool active = 16 * hg < H;
   const int head_b = 16 * hg + c16;
   v8h qf[S::KQ];
-  if (active) {
-    const float* qrow = a.q + (row * H + head_b) * (int64_t)DQK;
-#pragma unroll
-    for (int i = 0; i < S::KQ; ++i) qf[i] = load_f32x8_as_f16(qrow + 32 * i + 8 * g);
-  }
   const float sl2 = a.softmax_scale * kLog2e;
   const uint8_t* codes_b = a.kv_codes + b * a.c_bstride;
   const uint8_t* scales_b = a.kv_scales + b * a.s_bstride;
@@ -137,8 +147,10 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   const uint8_t* ss_b = a.swa_scales ? a.swa_scales + b * a.ss_bstride : nullptr;
   __syncthreads();
 
-  // ---- gather: task = (entry pair ep, 16-channel group gq), ep fastest so
-  // that a wave's V^T stores hit consecutive words.
+  // ---- gather: task = (entry e, 32-channel block j), j fastest, so that
+  // consecutive lanes read consecutive 16-byte pieces of one row.
+  const bool sc_pair = ((reinterpret_cast<uintptr_t>(a.kv_scales) | (uint64_t)a.s_bstride | (uint64_t)a.s_rstride) &
+                        1u) == 0;
   RawTask raw[TPT];
   auto gather = [&](int c0) {
 #pragma unroll
@@ -146,46 +158,44 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       const int task = threadIdx.x + u * kAttnThreads;
       raw[u].kind = 0;
       if (task < NTASK) {
-        const int ep = task % NEP, gq = task / NEP;
+        const int e = task / NB, j = task - (task / NB) * NB;
+        const int ce = c0 + e;
+        const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
+        if (id >= 0 && ce < K) {
+          const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 16 * j);
+          raw[u].w[0] = cp[0]; raw[u].w[1] = cp[1]; raw[u].w[2] = cp[2]; raw[u].w[3] = cp[3];
+          const uint8_t* sp = scales_b + (int64_t)id * a.s_rstride + 2 * j;
+          raw[u].sc = sc_pair ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+          raw[u].kind = 1u;
+        } else if (id >= 0) {
+          const uint32_t* vp = reinterpret_cast<const uint32_t*>(sv_b + (int64_t)id * a.sv_rstride + 32 * j);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int ce = c0 + 2 * ep + k;
-          const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
-          if (id >= 0 && ce < K) {
-            const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 8 * gq);
-            raw[u].w[k][0] = cp[0];
-            raw[u].w[k][1] = cp[1];
-            raw[u].sc[k] = scales_b[(int64_t)id * a.s_rstride + gq];
-            raw[u].kind |= 1u << (2 * k);
-          } else if (id >= 0) {
-            const uint32_t* vp = reinterpret_cast<const uint32_t*>(sv_b + (int64_t)id * a.sv_rstride + 16 * gq);
-            raw[u].w[k][0] = vp[0]; raw[u].w[k][1] = vp[1]; raw[u].w[k][2] = vp[2]; raw[u].w[k][3] = vp[3];
-            raw[u].sc[k] = ss_b[(int64_t)id * a.ss_rstride + (gq >> 1)];
-            raw[u].kind |= 2u << (2 * k);
-          }
+          for (int i = 0; i < 8; ++i) raw[u].w[i] = vp[i];
+          raw[u].sc = ss_b[(int64_t)id * a.ss_rstride + j];
+          raw[u].kind = 2u;
         }
       }
     }
   };
-  // ---- dequantise the staged bytes into K rows and V^T columns.
+  // ---- dequantise the staged bytes into fp16 K rows.
   auto store = [&](_Float16* kt) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
       if (task >= NTASK) break;
-      const int ep = task % NEP, gq = task / NEP;
-      uint32_t hv[2][8];
+      const int e = task / NB, j = task - (task / NB) * NB;
+      uint32_t hv[16];
+      if (raw[u].kind == 1u) {
+        // E2M1 -> fp16 in hardware (scale 1), then the E4M3 scale of each
+        // 16-channel group as an fp16 multiply; both steps are exact (at most
+        // 6 significant bits).
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t kind = (raw[u].kind >> (2 * k)) & 3u;
-        if (kind == 1u) {
-          // E2M1 -> fp16 in hardware (scale 1), then the E4M3 scale as an fp16
-          // multiply; both steps are exact (at most 6 significant bits).
-          _Float16 sh = (_Float16)e4m3_to_f32(raw[u].sc[k]);
-          v2h s2 = {sh, sh};
+        for (int hgp = 0; hgp < 2; ++hgp) {
+          const _Float16 sh = (_Float16)e4m3_to_f32((raw[u].sc >> (8 * hgp)) & 0xFFu);
+          const v2h s2 = {sh, sh};
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const uint32_t word = raw[u].w[k][i >> 2];
+            const uint32_t word = raw[u].w[2 * hgp + (i >> 2)];
             v2h v;
             switch (i & 3) {
               case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0); break;
@@ -194,39 +204,62 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
               default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3); break;
             }
             v = v * s2;
-            hv[k][i] = __builtin_bit_cast(uint32_t, v);
+            hv[8 * hgp + i] = __builtin_bit_cast(uint32_t, v);
           }
-        } else if (kind == 2u) {
-          // E4M3 -> fp16 scaled by the E8M0 power of two, in one instruction.
-          const float sc = e8m0_to_f32(raw[u].sc[k]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t word = raw[u].w[k][i >> 1];
-            v2h v = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, true)
-                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, false);
-            hv[k][i] = __builtin_bit_cast(uint32_t, v);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) hv[k][i] = 0u;
         }
-        uint4* dst = reinterpret_cast<uint4*>(kt + (2 * ep + k) * S::PITCH + 16 * gq);
-        dst[0] = uint4{hv[k][0], hv[k][1], hv[k][2], hv[k][3]};
-        dst[1] = uint4{hv[k][4], hv[k][5], hv[k][6], hv[k][7]};
+      } else if (raw[u].kind == 2u) {
+        // E4M3 -> fp16 scaled by the E8M0 power of two, in one instruction.
+        const float sc = e8m0_to_f32(raw[u].sc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t word = raw[u].w[i >> 1];
+          v2h v = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, true)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, false);
+          hv[i] = __builtin_bit_cast(uint32_t, v);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hv[i] = 0u;
       }
+      uint4* dst = reinterpret_cast<uint4*>(kt + e * S::PITCH + 32 * j);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) dst[p] = uint4{hv[4 * p], hv[4 * p + 1], hv[4 * p + 2], hv[4 * p + 3]};
     }
   };
 
-  v4f o[NT];
+  // O tiles: wave (ph, dq) owns heads 32*ph .. +31 (two 16-head tiles) and
+  // output dims 128*dq .. +127.
+  const int ph = wave & 1, dq = wave >> 1;
+  const bool pv_active = 32 * ph < H;
+  v4f o[2][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[t][n] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  if (e_begin < e_end) {
-    gather(e_begin);
-    store(kbuf[0]);
+  if (e_begin < e_end) gather(e_begin);
+  // q of all heads through LDS (the second K buffer is free until the first
+  // iteration refills it): coalesced fp32 loads, one fp16 rounding, then each
+  // wave reads its B fragments.
+  {
+    _Float16* qs = kbuf[1];
+    const float4* qrow = reinterpret_cast<const float4*>(a.q + row * H * (int64_t)DQK);
+    const int n4 = H * DQK / 4;
+    for (int i = threadIdx.x; i < n4; i += kAttnThreads) {
+      const float4 v = qrow[i];
+      const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
+      v2h lo = {(_Float16)v.x, (_Float16)v.y}, hi = {(_Float16)v.z, (_Float16)v.w};
+      *reinterpret_cast<uint2*>(qs + h * QP + d) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < S::KQ; ++i) qf[i] = *reinterpret_cast<const v8h*>(qs + head_b * QP + 32 * i + 8 * g);
+    }
   }
+  if (e_begin < e_end) store(kbuf[0]);
   __syncthreads();
   if (e_begin + kChunk < e_end) gather(e_begin + kChunk);
   int cur = 0;
@@ -296,27 +329,41 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       l_run = l_run * alpha + psum;
       m_run = m_new;
       pex[wave][lane] = pa;
+    } else {
+      v8h pz;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pz[i] = (_Float16)0.0f;
+      pex[wave][lane] = pz;
     }
+    if (dh == 0 && g == 0) alf[16 * hg + c16] = alpha;
     __syncthreads();
-    if (active) {
-      // P for entries 0..31 (k-step 0) comes from dim half 0, 32..63 from half 1.
-      const v8h p_own = pex[wave][lane], p_oth = pex[wave ^ 4][lane];
-      const v8h p0 = dh == 0 ? p_own : p_oth, p1 = dh == 0 ? p_oth : p_own;
-      if (!__all(alpha == 1.0f)) {
-        float al[4];
+    if (pv_active) {
+      // P of head tile t for entries 32j .. (k-step j) was written by the S
+      // wave of head group 2*ph + t and entry half j.
+      v8h pf[2][2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r, 64);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          o[n][0] *= al[0]; o[n][1] *= al[1]; o[n][2] *= al[2]; o[n][3] *= al[3];
-        }
+        for (int j = 0; j < 2; ++j) pf[t][j] = pex[2 * ph + t + 4 * j][lane];
+      float4 al[2];
+      al[0] = *reinterpret_cast<const float4*>(&alf[32 * ph + 4 * g]);
+      al[1] = *reinterpret_cast<const float4*>(&alf[32 * ph + 16 + 4 * g]);
+      if (!__all(al[0].x == 1.0f && al[0].y == 1.0f && al[0].z == 1.0f && al[0].w == 1.0f && al[1].x == 1.0f &&
+                 al[1].y == 1.0f && al[1].z == 1.0f && al[1].w == 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            o[t][n][0] *= al[t].x; o[t][n][1] *= al[t].y; o[t][n][2] *= al[t].z; o[t][n][3] *= al[t].w;
+          }
       }
-      // ---- O += P V over dims 256*dh ..; k-step j: entries 32j + {4g..4g+3, 16+4g..16+4g+3}.
+      // ---- O += P V over dims 128*dq ..; k-step j: entries 32j + {4g..4g+3, 16+4g..16+4g+3}.
       // V is read from the row-major K rows with the LDS transpose read: in each
       // 16-lane group, source lane s names entry (.. + s/4), dims 4(s%4)..+3, and
-      // lane i receives dim i of those four entries.
+      // lane i receives dim i of those four entries.  Each V fragment serves both
+      // head tiles.
       const int s16 = lane & 15;
-      const _Float16* vbase = kt + (4 * g + (s16 >> 2)) * S::PITCH + 256 * dh + 4 * (s16 & 3);
+      const _Float16* vbase = kt + (4 * g + (s16 >> 2)) * S::PITCH + 128 * dq + 4 * (s16 & 3);
       typedef short v4s __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) v4s* lds_v4s;
       constexpr int VB = 4;
@@ -334,10 +381,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           }
         }
 #pragma unroll
-        for (int jn = 0; jn < VB; ++jn) {
-          o[n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p0, vf[jn][0], o[n0 + jn], 0, 0, 0);
-          o[n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p1, vf[jn][1], o[n0 + jn], 0, 0, 0);
-        }
+        for (int jn = 0; jn < VB; ++jn)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            o[t][n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[t][0], vf[jn][0], o[t][n0 + jn], 0, 0, 0);
+            o[t][n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[t][1], vf[jn][1], o[t][n0 + jn], 0, 0, 0);
+          }
       }
     }
     // Next chunk into the other buffer (last read one iteration ago), then
@@ -355,20 +404,24 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (active && g == 0) pmx[dh][16 * hg + c16] = l_tot;
   __syncthreads();
-  if (!active) return;
-  l_tot += pmx[dh ^ 1][16 * hg + c16];
   const int64_t pbase = (row * splits + split) * (int64_t)H;
-  if (g == 0 && dh == 0) {
+  if (active && g == 0 && dh == 0) {
+    l_tot += pmx[1][16 * hg + c16];
     part_ml[(pbase + head_b) * 2 + 0] = m_run;
     part_ml[(pbase + head_b) * 2 + 1] = l_tot;
   }
+  if (!pv_active) return;
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int t = 0; t < 2; ++t) {
+    if (32 * ph + 16 * t >= H) break;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int h = 16 * hg + 4 * g + r;
-      part_o[(pbase + h) * DV + 256 * dh + 16 * n + c16] = o[n][r];
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 32 * ph + 16 * t + 4 * g + r;
+        part_o[(pbase + h) * DV + 128 * dq + 16 * n + c16] = o[t][n][r];
+      }
+  }
 }
 
 // Merge split partials: out = sum_s O_s 2^(m_s - M) / L, L = sum_s l_s 2^(m_s - M)

@@ -78,7 +78,7 @@ def test_tiny_config_decode_attention():
 @gpu
 @pytest.mark.parametrize("d_qk,H,K,W,n_invalid", [(576, 64, 2048, 128, 0), (576, 64, 300, 50, 40),
                                                   (512, 64, 512, 128, 7), (576, 32, 64, 0, 3),
-                                                  (512, 16, 33, 1, 0)])
+                                                  (576, 48, 200, 17, 5), (512, 16, 33, 1, 0)])
 def test_decode_shapes_invalid_entries_and_ragged_windows(d_qk, H, K, W, n_invalid):
     require_gpu()
     announce(f"attn decode d_qk={d_qk} H={H} K={K} W={W} invalid={n_invalid}")
