@@ -23,10 +23,10 @@
 
 namespace csa2 {
 
-#ifndef CSA2_SCAN_TILE
-#define CSA2_SCAN_TILE 4096
-#endif
-constexpr int kScanTile = CSA2_SCAN_TILE;   // max tokens per workgroup of the flat scan
+// Tokens per workgroup of the flat scan.  Small enough for several rounds of
+// workgroups per compute unit, so that one workgroup's histogram flush and
+// key burst overlap the others' streaming.
+constexpr int kScanTile = 1024;
 constexpr int kPoolTile = 512;        // pool positions per workgroup (later layers)
 constexpr int kScanWaves = 4;
 // 16-token MFMA groups per wave iteration (bytes in flight per wave =
@@ -327,16 +327,20 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     for (int64_t i = 4 * threadIdx.x; i < tn; i += 4 * 256)
       *reinterpret_cast<v4u*>(keys + row * key_stride + tile0 + i) = *reinterpret_cast<const v4u*>(&kst[i]);
   }
-  uint32_t* gh = tok.hist1 + row * 4096;
+  // Two adjacent bins per 64-bit atomic: the row histogram's 32-bit counters
+  // 2i and 2i+1 are the low and high halves of one little-endian 64-bit word.
+  uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + row * 4096);
   for (int i = threadIdx.x; i < 2048; i += 256) {
     const uint32_t v = hist[i];
-    if (v & 0xFFFFu) atomic_add_agent(gh + 2 * i, v & 0xFFFFu);
-    if (v >> 16) atomic_add_agent(gh + 2 * i + 1, v >> 16);
+    if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
   }
-  uint32_t* gbh = pool ? blk.hist1 + row * 4096 : nullptr;
-  if (pool)
-    for (int i = threadIdx.x; i < 4096; i += 256)
-      if (bhist[i]) atomic_add_agent(gbh + i, bhist[i]);
+  if (pool) {
+    uint64_t* gbh = reinterpret_cast<uint64_t*>(blk.hist1 + row * 4096);
+    for (int i = threadIdx.x; i < 2048; i += 256) {
+      const uint32_t lo = bhist[2 * i], hi = bhist[2 * i + 1];
+      if (lo | hi) atomic_add_agent64(gbh + i, (uint64_t)lo | ((uint64_t)hi << 32));
+    }
+  }
 }
 
 template <int DI, int HB, bool H8>
@@ -344,11 +348,7 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
   int64_t rows = (int64_t)a.B * a.Tq;
-  // Largest tile (fewest histogram flushes) that still gives >= 4 workgroups
-  // per compute unit; at least 1024 tokens.
-  int tile = kScanTile;
-  const int64_t want = 4LL * device_cu_count();
-  while (tile > 1024 && rows * ((a.n_max + tile - 1) / tile) < want) tile >>= 1;
+  const int tile = kScanTile;
   int64_t tiles = (a.n_max + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
   SelectWs bw = blk ? *blk : tok;
