@@ -61,7 +61,7 @@ struct ScoreLayout {
 static ScoreLayout score_layout(int64_t B, int64_t Tq, int64_t n_max, int32_t pool_block) {
   ScoreLayout L{};
   L.rows = B * Tq;
-  L.n_stride = round_up(n_max > 0 ? n_max : 1, 128);   // the flat scan writes keys in 128-position pieces
+  L.n_stride = round_up(n_max > 0 ? n_max : 1, 64);
   size_t o = 0;
   L.off_keys = o; o += al256(sizeof(uint32_t) * L.rows * L.n_stride);
   L.off_nvalid = o; o += al256(sizeof(int32_t) * L.rows);
