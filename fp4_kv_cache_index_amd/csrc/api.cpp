@@ -176,6 +176,7 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
   if (n_max > (int64_t)kSelTile * kMaxSelTiles || (int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
   if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;  // 16-byte slices per lane
   if ((k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
+  if (k_row_stride >= (int64_t)1 << 22) return CSA2_EUNSUPPORTED;   // 32-bit row offsets in the scan
   ScoreLayout L = score_layout(B, Tq, n_max, pool ? pool_block : 0);
   if (ws_bytes < L.total) return CSA2_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;

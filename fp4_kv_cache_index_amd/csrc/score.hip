@@ -108,95 +108,37 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HP + 256];
   __shared__ float wsh[HMAX];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = blockIdx.y;
   const int64_t b = row / Tq;
   constexpr bool pool = POOL;
-
-  int64_t nv;
-  if (GATHER) {
-    int64_t pl = pool_len[row];
-    nv = pl < 0 ? 0 : (pl > pool_cap ? pool_cap : pl);
-  } else {
-    int64_t c = ctx_len[b];
-    if (q_pos) {
-      int64_t qp = (int64_t)q_pos[row] + 1;
-      if (qp < c) c = qp;
+  if (n_max <= 0) {   // nothing addressable: no position is visible
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      n_valid_out[row] = 0;
+      if (pool) nb_valid_out[row] = 0;
     }
-    nv = c < 0 ? 0 : (c > n_max ? n_max : c);
+    return;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    n_valid_out[row] = (int32_t)nv;
-    if (pool) nb_valid_out[row] = (int32_t)((nv + pool_block - 1) / pool_block);
-  }
-
-  for (int i = threadIdx.x; i < 4096; i += 256) {
-    if (i <= 2048) hist[i] = 0u;
-    if (pool) bhist[i] = 0u;
-  }
-  if (threadIdx.x < HMAX) wsh[threadIdx.x] = threadIdx.x < H_I ? w[row * H_I + threadIdx.x] : 0.0f;
-  __syncthreads();
-  float wv[HP];   // head weights (0 past H_I), wave-uniform: scalar registers
-#pragma unroll
-  for (int h = 0; h < HP; ++h)
-    wv[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsh[h])));
-
-  // Whole-line loads (D_I = 128, one head block): every token of a group of
-  // 8 takes two B columns -- 2m holds bytes 32g..32g+15 of its row, 2m+1
-  // bytes 32g+16..32g+31 (lane group g) -- so the 8 lanes of a token read its
-  // whole 128-byte row in one instruction.  Two MFMA pairs with the matching
-  // halves of the query rows give the two partial dots, which one adjacent-
-  // lane exchange joins (exact: integers below 2^24).
-  constexpr bool FULL = (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
-  // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
   const int c16 = lane & 15, g = lane >> 4;
-  long qh[2][2];   // FULL: [parity e][step s] = bytes 32g + 16e + 8s .. +8
-  if (FULL) {
-    const bool hv = c16 < H_I;
-    const uint8_t* qp = q_idx + (row * H_I + (hv ? c16 : 0)) * DI + 32 * g;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const v2u v = hv ? *reinterpret_cast<const v2u*>(qp + 16 * e + 8 * st) : v2u{0u, 0u};
-        qh[e][st] = as_long(v[0], v[1]);
-      }
-  }
-  long qa[HB][KS];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    int h = c16 + 16 * hb;
-    Frag<CH> f;
-    load_frag<CH, DI>(f, frag_base<DI>(q_idx + (row * H_I + h) * DI, g), h < H_I);
-#pragma unroll
-    for (int i = 0; i < KS; ++i) qa[hb][i] = as_long(f.w[2 * i], f.w[2 * i + 1]);
-  }
-  __syncthreads();
-
+  constexpr bool FULL = (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
   const int64_t tile0 = (int64_t)blockIdx.x * tile;
   constexpr int pitch = HP;
   float* my = dots[wave];
   const uint8_t* kb = k_idx + b * k_bstride;
-  if (GATHER) {   // pool token ids of the tile, read from LDS by the loads below
-    const int32_t* prow = pool_idx + row * (int64_t)pool_cap;
-    for (int i = threadIdx.x; i < tile; i += 256) {
-      const int64_t p = tile0 + i;
-      ptok[i] = p < nv ? prow[p] : 0;
-    }
-    __syncthreads();
-  }
-
   // Each wave owns tile/4 consecutive positions, SG*16 per iteration; the
   // next iteration's key rows are in flight while this one is scored.  Loads
   // are issued unconditionally (positions past the wave's range read the
-  // last row of the range again and are never scored) so that waiting for
-  // one batch never waits for the batch behind it.
+  // last row of the range again, or 0 through the buffer range check, and
+  // are never scored) so that waiting for one batch never waits for the
+  // batch behind it.
   constexpr int SG = kScanGroups<HB>;
   constexpr int IT = 16 * SG;
   const int64_t wbase = tile0 + (int64_t)wave * (tile / kScanWaves);
+  // Until the visible count is known, loads are clamped to the addressable
+  // rows only (n_max > 0 here); rows past the visible count are never scored.
   int64_t wend = wbase + tile / kScanWaves;
-  if (wend > nv) wend = nv;
-  const int64_t wlast = wend - 1;
+  if (wend > n_max) wend = n_max;
+  int64_t wlast = wend - 1;
 
   auto frag_ptr = [&](int64_t pos) -> const uint8_t* {
     const int64_t p = pos < wend ? pos : wlast;
@@ -209,11 +151,34 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     return kb + tokid * k_rstride + 16 * (2 * g + (c16 & 1));
   };
 
+  // Flat whole-line scan: buffer loads over exactly the wave's rows (the
+  // hardware returns 0 for offsets past the end, without a memory access),
+  // so no row clamps; offsets are 32-bit (row strides below 4 MiB).
+  constexpr bool BUF = FULL && !GATHER;
+  const uint32_t rs32 = (uint32_t)k_rstride;
+  const uint32_t lane_off = (uint32_t)(c16 >> 1) * rs32 + 16u * (uint32_t)(2 * g + (c16 & 1));
+  auto wave_rsrc = [&](int64_t lim) {
+    const int64_t n = lim > wbase ? (lim - wbase) * k_rstride : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb + wbase * k_rstride), (short)0,
+                                             (int)(n < 0xFFFFFFFFLL ? n : 0xFFFFFFFFLL), 0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t krs = wave_rsrc(wend);
   // Two fragment buffers used in ping-pong: while one batch of IT tokens is
   // scored, the other batch's loads are in flight.
   Frag<CH> fa[SG], fb[SG];
   auto load_batch = [&](Frag<CH>(&f)[SG], int64_t base) {
-    if constexpr (FULL) {
+    if constexpr (BUF) {
+      const uint32_t boff = (uint32_t)(base - wbase) * rs32;
+#pragma unroll
+      for (int u = 0; u < 2 * SG; ++u) {
+        // (the uniform part stays in a scalar register: offsets recomputed per
+        // batch instead of eight loop-invariant vector registers)
+        const uint32_t uoff = __builtin_amdgcn_readfirstlane(boff + (uint32_t)(8 * u) * rs32);
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off + uoff, 0, 2 /* non-temporal */);
+        f[u >> 1].w[4 * (u & 1) + 0] = v[0]; f[u >> 1].w[4 * (u & 1) + 1] = v[1];
+        f[u >> 1].w[4 * (u & 1) + 2] = v[2]; f[u >> 1].w[4 * (u & 1) + 3] = v[3];
+      }
+    } else if constexpr (FULL) {
       // 8 groups of 8 tokens; group u = 2s + half lands in f[s].w[4*half ..]
 #pragma unroll
       for (int u = 0; u < 2 * SG; ++u) {
@@ -226,6 +191,102 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
       for (int s = 0; s < SG; ++s) load_frag<CH, DI>(f[s], frag_ptr(base + 16 * s + c16), true);
     }
   };
+
+  // Prologue loads first (visible count, weights, query fragments); the
+  // flat scan then issues its first two key batches at once, so that the
+  // stream starts while these are in flight (the vector-memory counter
+  // retires in order: waiting for them below does not wait for the keys).
+  int64_t craw;
+  if (GATHER) craw = pool_len[row];
+  else {
+    craw = ctx_len[b];
+    if (q_pos) {
+      const int64_t qp = (int64_t)q_pos[row] + 1;
+      if (qp < craw) craw = qp;
+    }
+  }
+  // Unconditional loads from in-range addresses; the zeroing of heads past
+  // H_I happens after the key loads are issued (a select on a loaded value
+  // waits for it, and the counter retires in order).
+  const float wraw = w[row * H_I + (threadIdx.x < H_I ? threadIdx.x : H_I - 1)];
+  // Whole-line loads (D_I = 128, one head block): every token of a group of
+  // 8 takes two B columns -- 2m holds bytes 32g..32g+15 of its row, 2m+1
+  // bytes 32g+16..32g+31 (lane group g) -- so the 8 lanes of a token read its
+  // whole 128-byte row in one instruction.  Two MFMA pairs with the matching
+  // halves of the query rows give the two partial dots, which one adjacent-
+  // lane exchange joins (exact: integers below 2^24).
+  // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
+  long qh[2][2];   // FULL: [parity e][step s] = bytes 32g + 16e + 8s .. +8
+  long qa[HB][KS];
+  const bool hv = c16 < H_I;
+  if constexpr (FULL) {
+    const uint8_t* qp = q_idx + (row * H_I + (hv ? c16 : 0)) * DI + 32 * g;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const v2u v = *reinterpret_cast<const v2u*>(qp + 16 * e + 8 * st);
+        qh[e][st] = as_long(v[0], v[1]);
+      }
+  } else {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      int h = c16 + 16 * hb;
+      Frag<CH> f;
+      load_frag<CH, DI>(f, frag_base<DI>(q_idx + (row * H_I + h) * DI, g), h < H_I);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) qa[hb][i] = as_long(f.w[2 * i], f.w[2 * i + 1]);
+    }
+  }
+  if constexpr (!GATHER) {
+    load_batch(fa, wbase);
+    load_batch(fb, wbase + IT);
+    __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the prologue's waits
+  }
+  if constexpr (FULL) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) qh[e][st] = hv ? qh[e][st] : 0L;
+    // The query fragments must have arrived before the stream loop (so that
+    // the loop's waits cover only its own batches).
+    asm volatile("" ::"v"(qh[0][0]), "v"(qh[0][1]), "v"(qh[1][0]), "v"(qh[1][1]));
+  }
+  const float wload = threadIdx.x < HMAX && threadIdx.x < H_I ? wraw : 0.0f;
+
+  int64_t nv;
+  if (GATHER) nv = craw < 0 ? 0 : (craw > pool_cap ? pool_cap : craw);
+  else nv = craw < 0 ? 0 : (craw > n_max ? n_max : craw);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    n_valid_out[row] = (int32_t)nv;
+    if (pool) nb_valid_out[row] = (int32_t)((nv + pool_block - 1) / pool_block);
+  }
+
+  for (int i = threadIdx.x; i < 4096; i += 256) {
+    if (i <= 2048) hist[i] = 0u;
+    if (pool) bhist[i] = 0u;
+  }
+  if (threadIdx.x < HMAX) wsh[threadIdx.x] = wload;
+  __syncthreads();
+  float wv[HP];   // head weights (0 past H_I), wave-uniform: scalar registers
+#pragma unroll
+  for (int h = 0; h < HP; ++h)
+    wv[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsh[h])));
+  if (GATHER) {   // pool token ids of the tile, read from LDS by the loads below
+    const int32_t* prow = pool_idx + row * (int64_t)pool_cap;
+    for (int i = threadIdx.x; i < tile; i += 256) {
+      const int64_t p = tile0 + i;
+      ptok[i] = p < nv ? prow[p] : 0;
+    }
+    __syncthreads();
+  }
+
+  // From here on the wave's range ends at the visible count.
+  wend = wbase + tile / kScanWaves;
+  if (wend > nv) wend = nv;
+  wlast = wend - 1;
+  if constexpr (BUF) krs = wave_rsrc(wend);
+
   auto score_batch = [&](const Frag<CH>(&f)[SG], int64_t it) {
     if constexpr (FULL) {
 #pragma unroll
@@ -308,9 +369,11 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   };
 
   const int nb = wend > wbase ? (int)((wend - wbase + IT - 1) / IT) : 0;
-  if (nb > 0) {
-    load_batch(fa, wbase);
-    load_batch(fb, wbase + IT);
+  if constexpr (GATHER) {
+    if (nb > 0) {
+      load_batch(fa, wbase);
+      load_batch(fb, wbase + IT);
+    }
   }
   for (int ib = 0; ib < nb; ib += 2) {
     score_batch(fa, wbase + (int64_t)ib * IT);

@@ -115,6 +115,8 @@ int swa_fp8_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_st
  * q_idx    [B][Tq][H_I][D_I] E4M3 bytes.     w [B][Tq][H_I] float32.
  * k_idx    row j of sequence b at k_idx + b*k_batch_stride + j*k_row_stride
  *          (bytes), D_I E4M3 bytes per row; n_max rows are addressable.
+ *          k_row_stride: a multiple of 8 (of 16 when D_I >= 128), below 4 MiB
+ *          (CSA2_EUNSUPPORTED otherwise).
  * ctx_len  [B] int32 (values clamped to [0, n_max]).
  * q_pos    [B][Tq] int32 or NULL (NULL: every row sees the whole context).
  * topk_idx [B][Tq][k_top] int32 out; topk_score [B][Tq][k_top] float out or NULL.

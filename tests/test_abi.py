@@ -69,8 +69,12 @@ def test_invalid_arguments_are_rejected_on_the_host():
     args[19] = fake
     args[20] = 16  # too small
     assert lib.csa2_index_score_topk(*args) == 3
-    # pool requested with a bad block size
+    # key rows 4 MiB apart or more are beyond the scan's 32-bit row offsets
     args[20] = 1 << 30
+    args[4] = 1 << 22
+    assert lib.csa2_index_score_topk(*args) == 2
+    args[4] = 128
+    # pool requested with a bad block size
     args[15], args[16], args[17], args[18] = 3, 16, fake, fake
     assert lib.csa2_index_score_topk(*args) == 1
     # trace attach validation
