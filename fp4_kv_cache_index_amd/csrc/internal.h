@@ -53,7 +53,8 @@ struct SelectRowCtl {                // per-row control block (64 bytes)
   uint32_t thr;                      // final threshold key T
   uint32_t need_eq;                  // ties at T to take (lowest positions)
   uint32_t total;                    // number of positions emitted
-  uint32_t pad[12];
+  uint32_t l1_total, l1_mode, l1_d, l1_above, l1_cnt;   // first-digit state (collect pass)
+  uint32_t pad[7];
 };
 
 constexpr int kTileList = 512;       // positions listed per tile by the collect pass

@@ -13,7 +13,8 @@
 //               histogram itself, counts its tile's keys above the bucket,
 //               appends the bucket's keys as (key, position) candidates and
 //               lists, in position order, the tile's positions at or above
-//               the bucket (when at most kTileList of them);
+//               the bucket (when at most kTileList of them); the row's
+//               first workgroup also records the resolved first digit;
 //   finalize -- one workgroup per row finds T and need_eq among the
 //               candidates (two more radix digits, in LDS), every tile's
 //               output offset, the -1 padding and the pool length;
@@ -100,6 +101,10 @@ select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t ke
   uint32_t kk[16];
   load_tile_keys(keys + row * key_stride, base, nv, kk);   // in flight during the resolution
   const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {   // published for the finalize pass
+    SelectRowCtl& c = ws.ctl[row];
+    c.l1_total = L.total; c.l1_mode = L.mode; c.l1_d = L.d; c.l1_above = L.above; c.l1_cnt = L.cnt;
+  }
   uint32_t gt = 0, nc = 0;
   uint32_t nl[4] = {0u, 0u, 0u, 0u};   // listed keys per round i
 #pragma unroll
@@ -186,9 +191,14 @@ select_finalize_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t k
   __shared__ uint32_t carry[2];
   const int64_t row = blockIdx.x;
   const int64_t tiles = ws.tiles;
+  // The first 256 tiles' counts are loaded up front (their latency overlaps
+  // the candidate staging and the digit passes).
+  const uint32_t gt_pre = threadIdx.x < tiles ? ws.tile_gt[row * tiles + threadIdx.x] : 0u;
   const int64_t nv = n_valid[row];
-  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
-  const uint32_t nc = L.mode == 0u ? ws.ctl[row].cand_count : 0u;
+  // First-digit state as the collect pass resolved it from the histogram.
+  const SelectRowCtl& c0 = ws.ctl[row];
+  const Level1 L{c0.l1_total, c0.l1_mode, c0.l1_d, c0.l1_above, c0.l1_cnt};
+  const uint32_t nc = L.mode == 0u ? c0.cand_count : 0u;
   const uint32_t* cr = ws.cand + row * 2 * ws.cand_cap;
   const bool in_lds = nc <= (uint32_t)kCandLds;
   if (in_lds) {
@@ -251,7 +261,7 @@ select_finalize_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t k
     const int64_t t = t0 + threadIdx.x;
     uint32_t g = 0, e = 0;
     if (t < tiles) {
-      g = ws.tile_gt[row * tiles + t] + tsel[t];
+      g = (t0 == 0 ? gt_pre : ws.tile_gt[row * tiles + t]) + tsel[t];
       e = teq[t];
     }
     const uint32_t c_out = carry[0], c_eq = carry[1];
