@@ -425,40 +425,55 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 }
 
 // Merge split partials: out = sum_s O_s 2^(m_s - M) / L, L = sum_s l_s 2^(m_s - M)
-// (+ 2^(sink*log2e - M)), lse = (M + log2 L) ln 2.
+// (+ 2^(sink*log2e - M)), lse = (M + log2 L) ln 2.  One workgroup per
+// (row, head): the split maxima are reduced in parallel, then each thread
+// accumulates its four output dims over the splits in ascending order with
+// sixteen splits' loads in flight.
 template <int DV>
 __global__ void __launch_bounds__(128)
 sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H,
                            const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse) {
+  static_assert(DV == 4 * 128, "one float4 of output dims per thread");
+  __shared__ float red[2];
   const int64_t rh = blockIdx.x;            // row * H + h
   const int h = (int)(rh % H);
   const int64_t row = rh / H;
-  float M = -__builtin_inff();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float sk = sink ? sink[h] * kLog2e : -__builtin_inff();
-  for (int s = 0; s < splits; ++s) {
-    float m = part_ml[((row * splits + s) * H + h) * 2];
-    M = fmaxf(M, m);
-  }
-  M = fmaxf(M, sk);
+  const float* mlb = part_ml + (row * splits * (int64_t)H + h) * 2;   // split s at mlb[2 * s * H]
+  float mx = -__builtin_inff();
+  for (int sp = threadIdx.x; sp < splits; sp += 128) mx = fmaxf(mx, mlb[2 * (int64_t)sp * H]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), sk);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.0f;
-  float acc[DV / 128];
-#pragma unroll
-  for (int i = 0; i < DV / 128; ++i) acc[i] = 0.0f;
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < splits; ++s) {
-      const int64_t pi = (row * splits + s) * H + h;
-      float m = part_ml[pi * 2];
-      if (m == -__builtin_inff()) continue;
-      float wgt = __builtin_amdgcn_exp2f(m - M);
-      L += part_ml[pi * 2 + 1] * wgt;
+    const float4* ob = reinterpret_cast<const float4*>(part_o + (row * splits * (int64_t)H + h) * DV) + threadIdx.x;
+    constexpr int U = 16;
+    for (int s0 = 0; s0 < splits; s0 += U) {
+      float2 ml[U];
+      float4 ov[U];
 #pragma unroll
-      for (int i = 0; i < DV / 128; ++i) acc[i] += part_o[pi * DV + threadIdx.x + 128 * i] * wgt;
+      for (int u = 0; u < U; ++u) {
+        const int sp = s0 + u < splits ? s0 + u : splits - 1;
+        ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
+        ov[u] = ob[(int64_t)sp * H * (DV / 4)];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u >= splits || ml[u].x == -__builtin_inff()) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ml[u].x - M);
+        L += ml[u].y * wgt;
+        acc.x += ov[u].x * wgt; acc.y += ov[u].y * wgt; acc.z += ov[u].z * wgt; acc.w += ov[u].w * wgt;
+      }
     }
     if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-  for (int i = 0; i < DV / 128; ++i) out[rh * DV + threadIdx.x + 128 * i] = acc[i] * inv;
+  reinterpret_cast<float4*>(out + rh * DV)[threadIdx.x] = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
   if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
