@@ -23,12 +23,15 @@
 
 namespace csa2 {
 
-// Tokens per workgroup of the flat scan.  Small enough for several rounds of
-// workgroups per compute unit, so that one workgroup's histogram flush and
-// key burst overlap the others' streaming.
-constexpr int kScanTile = 1024;
+// Waves per workgroup: 16 for the flat scan with one head block (one large
+// tile per compute unit, so that each workgroup's prologue, histogram flush
+// and key burst are paid once per 16K tokens), 4 for the pool gather and the
+// wide-head variants (their LDS tiles are larger).
+template <bool GATHER, int HB>
+constexpr int kScanWavesT = (!GATHER && HB == 1) ? 16 : 4;
+constexpr int kScanTileMax = 16384;   // flat-scan tokens per 16-wave workgroup (largest)
+constexpr int kScanTileSmall = 1024;  // flat-scan tokens per 4-wave workgroup
 constexpr int kPoolTile = 512;        // pool positions per workgroup (later layers)
-constexpr int kScanWaves = 4;
 // 16-token MFMA groups per wave iteration (bytes in flight per wave =
 // 2 * 16 * groups * D_I); fewer for 32 indexer heads to bound the LDS tile.
 #ifndef CSA2_SCAN_GROUPS
@@ -78,7 +81,7 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 // GATHER = false: tokens j = tile positions of the row (flat scan).
 // GATHER = true : position p maps to token pool_idx[row][p] (pool layers).
 template <int DI, int HB, bool GATHER, bool POOL, bool H8>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB>))
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
                    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
@@ -88,6 +91,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
                    SelectWs tok,
                    int pool_block, int nblocks, uint32_t* __restrict__ bkeys, int64_t bkey_stride,
                    int32_t* __restrict__ nb_valid_out, SelectWs blk) {
+  constexpr int NW = kScanWavesT<GATHER, HB>;
+  constexpr int NT = 64 * NW;
   constexpr int CH = DI / 4;           // bytes of a key row per lane
   constexpr int KS = DI / 32;          // MFMA k-steps
   constexpr int HMAX = 16 * HB;
@@ -95,17 +100,17 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // 16*HB MFMA rows (padding heads have zero queries and weight 0).
   constexpr int HP = H8 ? 8 : HMAX;
   // Top-12-bit histogram, two 16-bit bins per word (a tile holds at most
-  // 4096 positions); the last word takes positions past the visible count.
+  // 16384 positions); the last word takes positions past the visible count.
   __shared__ uint32_t hist[2049];
   // Flat scan: the tile's keys are staged here and leave in one coalesced
   // burst at the end (interleaving small key stores with the key-row stream
   // costs more than the LDS round trip).
   constexpr bool kStage = !GATHER && !POOL;
-  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? kScanTile : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? (NW == 16 ? kScanTileMax : kScanTileSmall) : 1];
   __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
   __shared__ uint32_t bhist[POOL ? 4096 : 1];
   // per wave: the batch's dots, then one 4-float trash slot per lane (whole-line path)
-  __shared__ __attribute__((aligned(16))) float dots[kScanWaves][16 * kScanGroups<HB> * HP + 256];
+  __shared__ __attribute__((aligned(16))) float dots[NW][16 * kScanGroups<HB> * HP + 256];
   __shared__ float wsh[HMAX];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -133,10 +138,10 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // batch behind it.
   constexpr int SG = kScanGroups<HB>;
   constexpr int IT = 16 * SG;
-  const int64_t wbase = tile0 + (int64_t)wave * (tile / kScanWaves);
+  const int64_t wbase = tile0 + (int64_t)wave * (tile / NW);
   // Until the visible count is known, loads are clamped to the addressable
   // rows only (n_max > 0 here); rows past the visible count are never scored.
-  int64_t wend = wbase + tile / kScanWaves;
+  int64_t wend = wbase + tile / NW;
   if (wend > n_max) wend = n_max;
   int64_t wlast = wend - 1;
 
@@ -262,7 +267,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     if (pool) nb_valid_out[row] = (int32_t)((nv + pool_block - 1) / pool_block);
   }
 
-  for (int i = threadIdx.x; i < 4096; i += 256) {
+  for (int i = threadIdx.x; i < 4096; i += NT) {
     if (i <= 2048) hist[i] = 0u;
     if (pool) bhist[i] = 0u;
   }
@@ -274,7 +279,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     wv[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wsh[h])));
   if (GATHER) {   // pool token ids of the tile, read from LDS by the loads below
     const int32_t* prow = pool_idx + row * (int64_t)pool_cap;
-    for (int i = threadIdx.x; i < tile; i += 256) {
+    for (int i = threadIdx.x; i < tile; i += NT) {
       const int64_t p = tile0 + i;
       ptok[i] = p < nv ? prow[p] : 0;
     }
@@ -282,7 +287,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
 
   // From here on the wave's range ends at the visible count.
-  wend = wbase + tile / kScanWaves;
+  wend = wbase + tile / NW;
   if (wend > nv) wend = nv;
   wlast = wend - 1;
   if constexpr (BUF) krs = wave_rsrc(wend);
@@ -387,19 +392,19 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     if (tend > nv) tend = nv;
     // Whole 64-position groups: they stay inside the row's key stride.
     const int64_t tn = tend > tile0 ? ((tend - tile0 + 63) & ~63LL) : 0;
-    for (int64_t i = 4 * threadIdx.x; i < tn; i += 4 * 256)
+    for (int64_t i = 4 * threadIdx.x; i < tn; i += 4 * NT)
       *reinterpret_cast<v4u*>(keys + row * key_stride + tile0 + i) = *reinterpret_cast<const v4u*>(&kst[i]);
   }
   // Two adjacent bins per 64-bit atomic: the row histogram's 32-bit counters
   // 2i and 2i+1 are the low and high halves of one little-endian 64-bit word.
   uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + row * 4096);
-  for (int i = threadIdx.x; i < 2048; i += 256) {
+  for (int i = threadIdx.x; i < 2048; i += NT) {
     const uint32_t v = hist[i];
     if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
   }
   if (pool) {
     uint64_t* gbh = reinterpret_cast<uint64_t*>(blk.hist1 + row * 4096);
-    for (int i = threadIdx.x; i < 2048; i += 256) {
+    for (int i = threadIdx.x; i < 2048; i += NT) {
       const uint32_t lo = bhist[2 * i], hi = bhist[2 * i + 1];
       if (lo | hi) atomic_add_agent64(gbh + i, (uint64_t)lo | ((uint64_t)hi << 32));
     }
@@ -411,18 +416,21 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
   int64_t rows = (int64_t)a.B * a.Tq;
-  const int tile = kScanTile;
+  constexpr int NW = kScanWavesT<false, HB>;
+  // The largest tile that still gives every compute unit a workgroup.
+  int tile = NW == 16 ? kScanTileMax : kScanTileSmall;
+  while (tile > kScanTileSmall && rows * ((a.n_max + tile - 1) / tile) < device_cu_count()) tile >>= 1;
   int64_t tiles = (a.n_max + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
   SelectWs bw = blk ? *blk : tok;
   dim3 grid((unsigned)tiles, (unsigned)rows);
   if (a.pool_block > 0) {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8>), grid, dim3(256), 0, s, a.q_idx, a.w,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
                 a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok,
                 a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
   } else {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8>), grid, dim3(256), 0, s, a.q_idx, a.w,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
                 a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok, 0,
                 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, bw);
@@ -438,7 +446,8 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
   int64_t rows = (int64_t)B * Tq;
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8>), dim3((unsigned)tiles, (unsigned)rows), dim3(256),
+  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8>), dim3((unsigned)tiles, (unsigned)rows),
+              dim3(64 * kScanWavesT<true, HB>),
               0, s, q_idx, w, k_idx, k_bstride, k_rstride, (const int32_t*)nullptr, (const int32_t*)nullptr,
               pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, key_stride, n_valid, ws,
               0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
