@@ -194,14 +194,20 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
   }
   ScoreArgs a{q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max, k_top,
               pool ? pool_block : 0, pool ? pool_nblocks : 0};
+  const SelectOut tout{topk_idx, topk_score, nullptr, 0, 0, nullptr, nullptr};
+  if (!pool && n_max <= kSmallSel) {
+    // Short rows: one workgroup per row selects from the keys alone.
+    SelectWs none = tok;
+    none.hist1 = nullptr;
+    hipError_t e = launch_index_score(a, keys, L.n_stride, n_valid, none, nullptr, 0, nullptr, nullptr, s);
+    if (e == hipSuccess) e = select_small(keys, L.n_stride, n_valid, L.rows, k_top, tout, s);
+    return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+  }
   hipError_t e = select_clear(tok, L.rows, s);
   if (e == hipSuccess && pool) e = select_clear(blk, L.rows, s);
   if (e == hipSuccess)
     e = launch_index_score(a, keys, L.n_stride, n_valid, tok, bkeys, L.nb_stride, nb_valid, pool ? &blk : nullptr, s);
-  if (e == hipSuccess) {
-    SelectOut out{topk_idx, topk_score, nullptr, 0, 0, nullptr, nullptr};
-    e = select_finish(tok, keys, L.n_stride, n_valid, L.rows, k_top, out, s);
-  }
+  if (e == hipSuccess) e = select_finish(tok, keys, L.n_stride, n_valid, L.rows, k_top, tout, s);
   if (e == hipSuccess && pool) {
     SelectOut out{pool_idx, nullptr, nullptr, 0, pool_block, n_valid, pool_len};
     e = select_finish(blk, bkeys, L.nb_stride, nb_valid, L.rows, pool_nblocks, out, s);
@@ -241,14 +247,21 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
   int32_t* n_valid = (int32_t*)base;
   base += al256(sizeof(int32_t) * rows);
   SelectWs sw = select_ws_carve(base, rows, pool_cap);
+  const SelectOut out{topk_idx, topk_score, pool_idx, pool_cap, 0, nullptr, nullptr};
+  if (pool_cap <= kSmallSel) {
+    // Pools that fit one workgroup: select from the keys alone.
+    SelectWs none = sw;
+    none.hist1 = nullptr;
+    hipError_t e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B,
+                                     Tq, H_I, D_I, k_top, keys, cap, n_valid, none, s);
+    if (e == hipSuccess) e = select_small(keys, cap, n_valid, rows, k_top, out, s);
+    return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+  }
   hipError_t e = select_clear(sw, rows, s);
   if (e == hipSuccess)
     e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B, Tq, H_I,
                           D_I, k_top, keys, cap, n_valid, sw, s);
-  if (e == hipSuccess) {
-    SelectOut out{topk_idx, topk_score, pool_idx, pool_cap, 0, nullptr, nullptr};
-    e = select_finish(sw, keys, cap, n_valid, rows, k_top, out, s);
-  }
+  if (e == hipSuccess) e = select_finish(sw, keys, cap, n_valid, rows, k_top, out, s);
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }
 

@@ -89,6 +89,12 @@ struct SelectOut {
 
 // Clears the control blocks and first-digit histograms of `rows` rows.
 hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s);
+// Rows of at most kSmallSel positions: one workgroup per row does the whole
+// selection from the keys (no histogram: producers given a null hist1 skip
+// their flush, and no clear pass is needed).  Not for pool expansion.
+constexpr int kSmallSel = 16384;
+hipError_t select_small(const uint32_t* keys, int64_t key_stride, const int32_t* n_valid, int64_t rows, int k,
+                        const SelectOut& out, hipStream_t s);
 // collect + finalize + emit, after the producer has written keys and hist1.
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
                          int64_t rows, int k, const SelectOut& out, hipStream_t s);

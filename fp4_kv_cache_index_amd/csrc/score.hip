@@ -397,10 +397,13 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
   // Two adjacent bins per 64-bit atomic: the row histogram's 32-bit counters
   // 2i and 2i+1 are the low and high halves of one little-endian 64-bit word.
-  uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + row * 4096);
-  for (int i = threadIdx.x; i < 2048; i += NT) {
-    const uint32_t v = hist[i];
-    if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
+  // A null histogram means the caller selects from the keys alone.
+  if (tok.hist1) {
+    uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + row * 4096);
+    for (int i = threadIdx.x; i < 2048; i += NT) {
+      const uint32_t v = hist[i];
+      if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
+    }
   }
   if (pool) {
     uint64_t* gbh = reinterpret_cast<uint64_t*>(blk.hist1 + row * 4096);
@@ -616,6 +619,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
     if (cb < nchunks) score_chunk(fb, cb);
   }
   __syncthreads();
+  if (!tok.hist1) return;
   for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
     const uint32_t v = hist[i];
     if (!v) continue;
@@ -753,6 +757,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     }
   }
   __syncthreads();
+  if (!tok.hist1) return;
   for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
     const uint32_t v = hist[i];
     if (!v) continue;

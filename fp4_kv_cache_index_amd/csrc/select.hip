@@ -437,7 +437,157 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   }
 }
 
+// small: the whole selection of a row in one 1024-thread workgroup when the
+// row has at most kSmallSel positions (pool layers, short contexts).  Thread
+// t holds positions 16t .. 16t+15 in registers, so thread order is position
+// order; three radix digits (12, 12, 8 bits) over the row's keys give T and
+// the ties to take, with histograms in LDS; then every thread emits its
+// selected positions at its offset.  No global histogram, no clear pass.
+constexpr int kSmallThreads = 1024;
+static_assert(kSmallSel == 16 * kSmallThreads, "16 positions per thread");
+
+// Digit of the histogram at which the count from the top reaches `need`;
+// `total` gets the histogram's sum (the digit is meaningless when need > total).
+__device__ Digit small_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res, uint32_t& total) {
+  constexpr int BPT = 4096 / kSmallThreads;
+  uint32_t h[BPT];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    h[i] = hist[threadIdx.x * BPT + i];
+    sum += h[i];
+  }
+  const uint32_t incl = block_scan<kSmallThreads, true>(sum, red);
+  const uint32_t excl = incl - sum;
+  if (threadIdx.x == 0) res[4] = incl;
+  if (excl < need && need <= incl) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (run + h[i] >= need && run < need) {
+        res[0] = threadIdx.x * BPT + i;
+        res[1] = run;
+        res[2] = h[i];
+      }
+      run += h[i];
+    }
+  }
+  __syncthreads();
+  Digit r{res[0], res[1], res[2]};
+  total = res[4];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kSmallThreads)
+select_small_kernel(const uint32_t* __restrict__ keys, int64_t key_stride, const int32_t* __restrict__ n_valid, int k,
+                    SelectOut out) {
+  constexpr int NT = kSmallThreads, PT = kSmallSel / NT;
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t red[NT / 64], res[5];
+  const int64_t row = blockIdx.x;
+  int64_t nv = n_valid[row];
+  if (nv > kSmallSel) nv = kSmallSel;   // (the host guarantees it)
+  const uint32_t* kr = keys + row * key_stride;
+  const int p0 = PT * threadIdx.x;
+  uint32_t kk[PT];
+#pragma unroll
+  for (int i = 0; i < PT; i += 4) {
+    // rows are padded to a multiple of 64 keys: a vector starting below nv
+    // stays inside the row
+    v4u v = {0u, 0u, 0u, 0u};
+    if (p0 + i < nv) v = *reinterpret_cast<const v4u*>(kr + p0 + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kk[i + j] = p0 + i + j < nv ? v[j] : 0u;
+  }
+  // Threshold T and ties to take; every visible position (key != 0) when
+  // there are at most k of them.
+  bool take_all = nv <= k;
+  uint32_t thr = 0u, need_eq = 0u;
+  if (!take_all) {
+    uint32_t need = (uint32_t)k, prefix = 0u;
+    int shift = 20;
+    for (int level = 0; level < 3; ++level) {
+      const int width = level < 2 ? 12 : 8;
+      for (int i = threadIdx.x; i < 4096; i += NT) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < PT; ++e)
+        if (kk[e] != 0u && (level == 0 || (kk[e] >> (shift + width)) == prefix))
+          atomicAdd(&hist[(kk[e] >> shift) & ((1u << width) - 1u)], 1u);
+      __syncthreads();
+      uint32_t total;
+      const Digit D = small_digit(hist, need, red, res, total);
+      if (level == 0 && total <= (uint32_t)k) {
+        take_all = true;
+        break;
+      }
+      prefix = (prefix << width) | D.d;
+      need -= D.above;
+      if (need == D.cnt) {   // the whole bucket is taken
+        const uint32_t lowb = prefix << shift;
+        thr = lowb ? lowb - 1u : 0u;
+        need_eq = 0u;
+        break;
+      }
+      if (level == 2) {
+        thr = prefix;
+        need_eq = need;
+        break;
+      }
+      shift -= level == 0 ? 12 : 8;
+    }
+  }
+  // Emission: ties at T go to the lowest positions.
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    gt += kk[e] != 0u && (take_all || kk[e] > thr);
+    eq += !take_all && kk[e] != 0u && kk[e] == thr;
+  }
+  const uint32_t eq_incl = block_scan<NT, false>(eq, red);
+  const uint32_t eq_before = eq_incl - eq;
+  uint32_t take = 0;
+  if (need_eq > eq_before) take = need_eq - eq_before < eq ? need_eq - eq_before : eq;
+  const uint32_t sel = gt + take;
+  const uint32_t s_incl = block_scan<NT, false>(sel, red);
+  uint32_t slot = s_incl - sel;
+  uint32_t taken = 0;
+  int32_t* oi = out.idx + row * (int64_t)k;
+  float* os = out.score ? out.score + row * (int64_t)k : nullptr;
+  const int32_t* map = out.map ? out.map + row * out.map_stride : nullptr;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    if (kk[e] == 0u) continue;
+    bool pick = take_all || kk[e] > thr;
+    if (!pick && kk[e] == thr && taken < take) {
+      pick = true;
+      ++taken;
+    }
+    if (pick && slot < (uint32_t)k) {
+      const int pos = p0 + e;
+      oi[slot] = map ? map[pos] : pos;
+      if (os) os[slot] = key_score(kk[e]);
+      ++slot;
+    }
+  }
+  if (threadIdx.x == NT - 1) res[3] = s_incl;
+  __syncthreads();
+  for (int64_t i = res[3] + threadIdx.x; i < k; i += NT) {
+    oi[i] = -1;
+    if (os) os[i] = -__builtin_inff();
+  }
+}
+
 // ---------------------------------------------------------------- host ---
+
+hipError_t select_small(const uint32_t* keys, int64_t key_stride, const int32_t* n_valid, int64_t rows, int k,
+                        const SelectOut& out, hipStream_t s) {
+  if (out.expand != 0) return hipErrorInvalidValue;
+  CSA2_LAUNCH("select_small", select_small_kernel, dim3((unsigned)rows), dim3(kSmallThreads), 0, s, keys, key_stride,
+              n_valid, k, out);
+  return hipGetLastError();
+}
 
 hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s) {
   // ctl and hist1 are carved contiguously.

@@ -40,6 +40,35 @@ __device__ __forceinline__ uint32_t block_prefix_sum_256(uint32_t v, uint32_t* r
   return v + add;
 }
 
+// Inclusive prefix (SUFFIX = false: thread t gets v_0 + ... + v_t) or
+// suffix (SUFFIX = true: v_t + ... + v_{NT-1}) sum over the NT threads of a
+// workgroup.  `red` is LDS scratch of NT/64 words.
+template <int NT, bool SUFFIX>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red) {
+  constexpr int NWV = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    if (SUFFIX) {
+      const uint32_t y = __shfl_down(v, off, 64);
+      if (lane + off < 64) v += y;
+    } else {
+      const uint32_t y = __shfl_up(v, off, 64);
+      if (lane >= off) v += y;
+    }
+  }
+  if (lane == (SUFFIX ? 0 : 63)) red[wv] = v;
+  __syncthreads();
+  uint32_t add = 0;
+  if (SUFFIX) {
+    for (int w2 = wv + 1; w2 < NWV; ++w2) add += red[w2];
+  } else {
+    for (int w2 = 0; w2 < wv; ++w2) add += red[w2];
+  }
+  __syncthreads();
+  return v + add;
+}
+
 // Digit of a BINS-bin histogram (global or shared memory) at which the
 // running count from the top reaches `need` (1 <= need <= total):
 //   sum_{e>d} h[e] < need <= sum_{e>=d} h[e].

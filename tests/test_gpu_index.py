@@ -48,12 +48,15 @@ def test_tiny_config_full_layer_topk():
     _run_and_check(lay["q_idx"], lay["w"], k_idx, ctx, wl.K)
 
 
+# Rows of at most 16384 positions are selected by one workgroup per row,
+# longer rows by the tiled multi-kernel select: sizes on both sides.
 @gpu
+@pytest.mark.parametrize("N", [3 * 4096 + 577, 5 * 4096 + 577])
 @pytest.mark.parametrize("H_I,D_I,K", [(8, 128, 2048), (32, 128, 512), (4, 64, 256), (3, 32, 100), (16, 256, 64)])
-def test_ragged_contexts_and_shapes(H_I, D_I, K):
+def test_ragged_contexts_and_shapes(H_I, D_I, K, N):
     require_gpu()
-    announce(f"index_score_topk ragged H_I={H_I} D_I={D_I} K={K}")
-    B, N = 4, 3 * 4096 + 577
+    announce(f"index_score_topk ragged H_I={H_I} D_I={D_I} K={K} N={N}")
+    B = 4
     k_idx = inputs.int_e4m3((B, N, D_I), 11, 0, "k_idx", device="cuda")
     q_idx = inputs.int_e4m3((B, 1, H_I, D_I), 11, 1, "q_idx", device="cuda")
     w = inputs.normal_f32((B, 1, H_I), 11, 1, "w", device="cuda")
@@ -62,10 +65,11 @@ def test_ragged_contexts_and_shapes(H_I, D_I, K):
 
 
 @gpu
-def test_all_ties_and_padding():
+@pytest.mark.parametrize("N", [9000, 30000])
+def test_all_ties_and_padding(N):
     require_gpu()
-    announce("index_score_topk all ties (q = 0) and K > context")
-    B, N, H_I, D_I = 2, 9000, 8, 128
+    announce(f"index_score_topk all ties (q = 0) and K > context N={N}")
+    B, H_I, D_I = 2, 8, 128
     k_idx = inputs.int_e4m3((B, N, D_I), 12, 0, "k_idx", device="cuda")
     q_idx = torch.zeros((B, 1, H_I, D_I), dtype=torch.uint8, device="cuda")
     w = inputs.normal_f32((B, 1, H_I), 12, 1, "w", device="cuda")
@@ -77,14 +81,30 @@ def test_all_ties_and_padding():
 
 
 @gpu
-def test_heavy_ties_small_integer_weights():
+@pytest.mark.parametrize("N", [12000, 20000])
+def test_heavy_ties_small_integer_weights(N):
     require_gpu()
-    announce("index_score_topk heavy ties")
-    B, N, H_I, D_I = 2, 20000, 8, 128
+    announce(f"index_score_topk heavy ties N={N}")
+    B, H_I, D_I = 2, 8, 128
     k_idx = inputs.int_e4m3((B, N, D_I), 13, 0, "k_idx", lo=-1, hi=1, device="cuda")
     q_idx = inputs.int_e4m3((B, 1, H_I, D_I), 13, 1, "q_idx", lo=0, hi=1, device="cuda")
     w = torch.ones((B, 1, H_I), dtype=torch.float32, device="cuda")
     ctx = torch.tensor([N, N - 3], dtype=torch.int32, device="cuda")
+    _run_and_check(q_idx, w, k_idx, ctx, 2048)
+
+
+@gpu
+@pytest.mark.parametrize("N", [16384, 16385])
+def test_select_size_boundary(N):
+    """Longest row for the one-workgroup select and one position past it;
+    the second sequence has fewer visible positions than K."""
+    require_gpu()
+    announce(f"index_score_topk select boundary N={N}")
+    B, H_I, D_I = 2, 8, 128
+    k_idx = inputs.int_e4m3((B, N, D_I), 16, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, 1, H_I, D_I), 16, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, 1, H_I), 16, 1, "w", device="cuda")
+    ctx = torch.tensor([N, 2000], dtype=torch.int32, device="cuda")
     _run_and_check(q_idx, w, k_idx, ctx, 2048)
 
 
@@ -125,7 +145,8 @@ def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K):
 
 
 @gpu
-@pytest.mark.parametrize("block,nblocks,K", [(8, 64, 256), (8, 2048, 2048), (4, 100, 64), (1, 300, 300), (16, 40, 128)])
+@pytest.mark.parametrize("block,nblocks,K", [(8, 64, 256), (8, 2048, 2048), (4, 100, 64), (1, 300, 300), (16, 40, 128),
+                                             (16, 1100, 512)])
 def test_hierarchical_pool_and_pool_topk(block, nblocks, K):
     require_gpu()
     announce(f"pool block={block} nblocks={nblocks} K={K}")
