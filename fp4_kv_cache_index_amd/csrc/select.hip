@@ -438,144 +438,225 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
 }
 
 // small: the whole selection of a row in one 1024-thread workgroup when the
-// row has at most kSmallSel positions (pool layers, short contexts).  Thread
-// t holds positions 16t .. 16t+15 in registers, so thread order is position
-// order; three radix digits (12, 12, 8 bits) over the row's keys give T and
-// the ties to take, with histograms in LDS; then every thread emits its
-// selected positions at its offset.  No global histogram, no clear pass.
+// row has at most kSmallSel positions (pool layers, short contexts).  The
+// row is cut into 4 groups of 4096 positions; thread t holds positions
+// 4t .. 4t+3 of every group (and their map entries) in registers, so each
+// load instruction of a wave reads 1 KB of consecutive keys.  Three radix
+// digits (12, 12, 8 bits) over the row's keys give T and the ties to take,
+// with one LDS histogram per level cleared together at the start.  The
+// output offsets follow position order, (group, thread, element): one
+// prefix sum over threads of four packed (above T, equal to T) counts, one
+// per group, plus the totals of the earlier groups.  No global histogram,
+// no clear pass.
 constexpr int kSmallThreads = 1024;
-static_assert(kSmallSel == 16 * kSmallThreads, "16 positions per thread");
+constexpr int kSmallGroups = 4;
+static_assert(kSmallSel == 4 * kSmallGroups * kSmallThreads, "4 positions per thread and group");
 
-// Digit of the histogram at which the count from the top reaches `need`;
-// `total` gets the histogram's sum (the digit is meaningless when need > total).
+// Digit of a BINS-bin LDS histogram (4096 or 256) at which the count from
+// the top reaches `need`, as (d, count above d, count at d); `total` gets the
+// histogram's sum (the digit is meaningless when need > total).  Thread t
+// reads bins 4g .. 4g+3 of group g = BINS/4 - 1 - t, so a prefix sum over
+// threads counts from the top.
+template <int BINS>
 __device__ Digit small_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res, uint32_t& total) {
-  constexpr int BPT = 4096 / kSmallThreads;
-  uint32_t h[BPT];
-  uint32_t sum = 0;
+  constexpr int G = BINS / 4;
+  static_assert(G == kSmallThreads || G == 64, "one group per thread or per lane of the first wave");
+  if (G == kSmallThreads || threadIdx.x < 64) {
+    const int g = G - 1 - threadIdx.x;
+    const v4u h = reinterpret_cast<const v4u*>(hist)[g];
+    const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+    const uint32_t incl = G == kSmallThreads ? block_scan<kSmallThreads>(sum, red) : wave_prefix_sum(sum);
+    if (threadIdx.x == G - 1) res[4] = incl;
+    uint32_t run = incl - sum;
+    if (run < need && need <= incl) {
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = hist[threadIdx.x * BPT + i];
-    sum += h[i];
-  }
-  const uint32_t incl = block_scan<kSmallThreads, true>(sum, red);
-  const uint32_t excl = incl - sum;
-  if (threadIdx.x == 0) res[4] = incl;
-  if (excl < need && need <= incl) {
-    uint32_t run = excl;
-#pragma unroll
-    for (int i = BPT - 1; i >= 0; --i) {
-      if (run + h[i] >= need && run < need) {
-        res[0] = threadIdx.x * BPT + i;
-        res[1] = run;
-        res[2] = h[i];
+      for (int j = 3; j >= 0; --j) {
+        if (run < need && need <= run + h[j]) {
+          res[0] = 4 * g + j;
+          res[1] = run;
+          res[2] = h[j];
+        }
+        run += h[j];
       }
-      run += h[i];
     }
   }
   __syncthreads();
-  Digit r{res[0], res[1], res[2]};
   total = res[4];
-  __syncthreads();
-  return r;
+  return Digit{res[0], res[1], res[2]};
 }
 
 __global__ void __launch_bounds__(kSmallThreads)
 select_small_kernel(const uint32_t* __restrict__ keys, int64_t key_stride, const int32_t* __restrict__ n_valid, int k,
                     SelectOut out) {
-  constexpr int NT = kSmallThreads, PT = kSmallSel / NT;
-  __shared__ uint32_t hist[4096];
-  __shared__ uint32_t red[NT / 64], res[5];
+  constexpr int NT = kSmallThreads, NG = kSmallGroups, GS = 4 * NT, PT = 4 * NG;
+  constexpr int NWV = NT / 64;
+  __shared__ __align__(16) uint32_t hist0[4096];
+  __shared__ __align__(16) uint32_t hist1[4096];
+  __shared__ __align__(16) uint32_t hist2[256];
+  __shared__ __align__(16) uint32_t red[NG * NWV];
+  __shared__ uint32_t res[5];
   const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 1024; i += NT) {
+    reinterpret_cast<v4u*>(hist0)[i] = v4u{0u, 0u, 0u, 0u};
+    reinterpret_cast<v4u*>(hist1)[i] = v4u{0u, 0u, 0u, 0u};
+  }
+  if (threadIdx.x < 64) reinterpret_cast<v4u*>(hist2)[threadIdx.x] = v4u{0u, 0u, 0u, 0u};
   int64_t nv = n_valid[row];
   if (nv > kSmallSel) nv = kSmallSel;   // (the host guarantees it)
   const uint32_t* kr = keys + row * key_stride;
-  const int p0 = PT * threadIdx.x;
+  const int32_t* map = out.map ? out.map + row * out.map_stride : nullptr;
+  // kk[4g + j] is position g*GS + 4t + j.
   uint32_t kk[PT];
+  int32_t mp[PT];
 #pragma unroll
-  for (int i = 0; i < PT; i += 4) {
+  for (int g = 0; g < NG; ++g) {
+    const int p = g * GS + 4 * threadIdx.x;
     // rows are padded to a multiple of 64 keys: a vector starting below nv
     // stays inside the row
     v4u v = {0u, 0u, 0u, 0u};
-    if (p0 + i < nv) v = *reinterpret_cast<const v4u*>(kr + p0 + i);
+    if (p < nv) v = *reinterpret_cast<const v4u*>(kr + p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kk[i + j] = p0 + i + j < nv ? v[j] : 0u;
+    for (int j = 0; j < 4; ++j) {
+      kk[4 * g + j] = p + j < nv ? v[j] : 0u;
+      mp[4 * g + j] = p + j;
+    }
   }
+  if (map) {
+    if (((uintptr_t)map & 15u) == 0) {
+      // the map row holds at least nv entries, but not a whole last vector
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int p = g * GS + 4 * threadIdx.x;
+        if (p + 3 < nv) {
+          const v4u m = *reinterpret_cast<const v4u*>(map + p);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mp[4 * g + j] = (int32_t)m[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (p + j < nv) mp[4 * g + j] = map[p + j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PT; ++e) {
+        const int p = (e >> 2) * GS + 4 * threadIdx.x + (e & 3);
+        if (p < nv) mp[e] = map[p];
+      }
+    }
+  }
+  __syncthreads();   // histograms cleared
   // Threshold T and ties to take; every visible position (key != 0) when
   // there are at most k of them.
   bool take_all = nv <= k;
   uint32_t thr = 0u, need_eq = 0u;
   if (!take_all) {
-    uint32_t need = (uint32_t)k, prefix = 0u;
-    int shift = 20;
-    for (int level = 0; level < 3; ++level) {
-      const int width = level < 2 ? 12 : 8;
-      for (int i = threadIdx.x; i < 4096; i += NT) hist[i] = 0u;
-      __syncthreads();
 #pragma unroll
-      for (int e = 0; e < PT; ++e)
-        if (kk[e] != 0u && (level == 0 || (kk[e] >> (shift + width)) == prefix))
-          atomicAdd(&hist[(kk[e] >> shift) & ((1u << width) - 1u)], 1u);
-      __syncthreads();
-      uint32_t total;
-      const Digit D = small_digit(hist, need, red, res, total);
-      if (level == 0 && total <= (uint32_t)k) {
-        take_all = true;
-        break;
+    for (int e = 0; e < PT; ++e)
+      if (kk[e]) atomicAdd(&hist0[kk[e] >> 20], 1u);
+    __syncthreads();
+    uint32_t total;
+    const Digit D0 = small_digit<4096>(hist0, (uint32_t)k, red, res, total);
+    if (total <= (uint32_t)k) {
+      take_all = true;
+    } else {
+      uint32_t need = (uint32_t)k - D0.above, prefix = D0.d;
+      if (need == D0.cnt) {   // the whole bucket is taken
+        thr = prefix ? (prefix << 20) - 1u : 0u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < PT; ++e)
+          if (kk[e] != 0u && (kk[e] >> 20) == prefix) atomicAdd(&hist1[(kk[e] >> 8) & 0xFFFu], 1u);
+        __syncthreads();
+        const Digit D1 = small_digit<4096>(hist1, need, red, res, total);
+        need -= D1.above;
+        prefix = (prefix << 12) | D1.d;
+        if (need == D1.cnt) {
+          thr = prefix ? (prefix << 8) - 1u : 0u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < PT; ++e)
+            if (kk[e] != 0u && (kk[e] >> 8) == prefix) atomicAdd(&hist2[kk[e] & 0xFFu], 1u);
+          __syncthreads();
+          const Digit D2 = small_digit<256>(hist2, need, red, res, total);
+          thr = (prefix << 8) | D2.d;
+          need_eq = need - D2.above;
+        }
       }
-      prefix = (prefix << width) | D.d;
-      need -= D.above;
-      if (need == D.cnt) {   // the whole bucket is taken
-        const uint32_t lowb = prefix << shift;
-        thr = lowb ? lowb - 1u : 0u;
-        need_eq = 0u;
-        break;
-      }
-      if (level == 2) {
-        thr = prefix;
-        need_eq = need;
-        break;
-      }
-      shift -= level == 0 ? 12 : 8;
     }
   }
-  // Emission: ties at T go to the lowest positions.
-  uint32_t gt = 0, eq = 0;
+  // Emission: ties at T go to the lowest positions.  Per group, the counts
+  // above T and at T are packed in one word (each total is at most 4096).
+  uint32_t cnt[NG];
 #pragma unroll
-  for (int e = 0; e < PT; ++e) {
-    gt += kk[e] != 0u && (take_all || kk[e] > thr);
-    eq += !take_all && kk[e] != 0u && kk[e] == thr;
+  for (int g = 0; g < NG; ++g) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = kk[4 * g + j];
+      gt += x != 0u && (take_all || x > thr);
+      eq += !take_all && x != 0u && x == thr;
+    }
+    cnt[g] = (gt << 16) | eq;
   }
-  const uint32_t eq_incl = block_scan<NT, false>(eq, red);
-  const uint32_t eq_before = eq_incl - eq;
-  uint32_t take = 0;
-  if (need_eq > eq_before) take = need_eq - eq_before < eq ? need_eq - eq_before : eq;
-  const uint32_t sel = gt + take;
-  const uint32_t s_incl = block_scan<NT, false>(sel, red);
-  uint32_t slot = s_incl - sel;
-  uint32_t taken = 0;
+  uint32_t incl[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) incl[g] = wave_prefix_sum(cnt[g]);
+  if (lane == 63) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) red[g * NWV + wv] = incl[g];
+  }
+  __syncthreads();
+  uint32_t base = 0;   // packed totals of the earlier groups
+  uint32_t before[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    uint32_t waves_before = 0, group_total = 0;
+#pragma unroll
+    for (int q = 0; q < NWV / 4; ++q) {
+      const v4u r = reinterpret_cast<const v4u*>(red + g * NWV)[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        waves_before += 4 * q + j < wv ? r[j] : 0u;
+        group_total += r[j];
+      }
+    }
+    before[g] = base + waves_before + incl[g] - cnt[g];
+    base += group_total;
+  }
   int32_t* oi = out.idx + row * (int64_t)k;
   float* os = out.score ? out.score + row * (int64_t)k : nullptr;
-  const int32_t* map = out.map ? out.map + row * out.map_stride : nullptr;
 #pragma unroll
-  for (int e = 0; e < PT; ++e) {
-    if (kk[e] == 0u) continue;
-    bool pick = take_all || kk[e] > thr;
-    if (!pick && kk[e] == thr && taken < take) {
-      pick = true;
-      ++taken;
-    }
-    if (pick && slot < (uint32_t)k) {
-      const int pos = p0 + e;
-      oi[slot] = map ? map[pos] : pos;
-      if (os) os[slot] = key_score(kk[e]);
-      ++slot;
+  for (int g = 0; g < NG; ++g) {
+    const uint32_t eq_before = before[g] & 0xFFFFu;
+    uint32_t slot = (before[g] >> 16) + (eq_before < need_eq ? eq_before : need_eq);
+    const uint32_t eq = cnt[g] & 0xFFFFu;
+    uint32_t take = 0;
+    if (need_eq > eq_before) take = need_eq - eq_before < eq ? need_eq - eq_before : eq;
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = kk[4 * g + j];
+      if (x == 0u) continue;
+      bool pick = take_all || x > thr;
+      if (!pick && x == thr && taken < take) {
+        pick = true;
+        ++taken;
+      }
+      if (pick && slot < (uint32_t)k) {
+        oi[slot] = mp[4 * g + j];
+        if (os) os[slot] = key_score(x);
+        ++slot;
+      }
     }
   }
-  if (threadIdx.x == NT - 1) res[3] = s_incl;
-  __syncthreads();
-  for (int64_t i = res[3] + threadIdx.x; i < k; i += NT) {
-    oi[i] = -1;
-    if (os) os[i] = -__builtin_inff();
+  // Exactly k are selected unless every visible position is.
+  if (take_all) {
+    for (int64_t i = (base >> 16) + threadIdx.x; i < k; i += NT) {
+      oi[i] = -1;
+      if (os) os[i] = -__builtin_inff();
+    }
   }
 }
 

@@ -40,32 +40,40 @@ __device__ __forceinline__ uint32_t block_prefix_sum_256(uint32_t v, uint32_t* r
   return v + add;
 }
 
-// Inclusive prefix (SUFFIX = false: thread t gets v_0 + ... + v_t) or
-// suffix (SUFFIX = true: v_t + ... + v_{NT-1}) sum over the NT threads of a
-// workgroup.  `red` is LDS scratch of NT/64 words.
-template <int NT, bool SUFFIX>
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// shifts by 1, 2, 4 and 8 inside each 16-lane row, then lane 15 of a row
+// into the next row and lane 31 into the upper half.  Lanes whose source is
+// outside the row receive 0.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return (uint32_t)x;
+}
+
+// Inclusive prefix sum over the NT (<= 1024) threads of a workgroup: thread
+// t gets v_0 + ... + v_t.  `red` is 16-byte aligned LDS scratch of NT/64
+// words; it is read after the function returns, so a later call must use
+// other scratch or come after another barrier.
+template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red) {
   constexpr int NWV = NT / 64;
+  static_assert(NWV % 4 == 0 && NWV <= 16, "whole 16-byte groups of wave totals");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    if (SUFFIX) {
-      const uint32_t y = __shfl_down(v, off, 64);
-      if (lane + off < 64) v += y;
-    } else {
-      const uint32_t y = __shfl_up(v, off, 64);
-      if (lane >= off) v += y;
-    }
-  }
-  if (lane == (SUFFIX ? 0 : 63)) red[wv] = v;
+  v = wave_prefix_sum(v);
+  if (lane == 63) red[wv] = v;
   __syncthreads();
   uint32_t add = 0;
-  if (SUFFIX) {
-    for (int w2 = wv + 1; w2 < NWV; ++w2) add += red[w2];
-  } else {
-    for (int w2 = 0; w2 < wv; ++w2) add += red[w2];
+#pragma unroll
+  for (int g = 0; g < NWV / 4; ++g) {
+    const v4u r = reinterpret_cast<const v4u*>(red)[g];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add += 4 * g + j < wv ? r[j] : 0u;
   }
-  __syncthreads();
   return v + add;
 }
 

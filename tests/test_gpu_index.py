@@ -146,7 +146,7 @@ def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K):
 
 @gpu
 @pytest.mark.parametrize("block,nblocks,K", [(8, 64, 256), (8, 2048, 2048), (4, 100, 64), (1, 300, 300), (16, 40, 128),
-                                             (16, 1100, 512)])
+                                             (16, 1100, 512), (1, 150, 64)])
 def test_hierarchical_pool_and_pool_topk(block, nblocks, K):
     require_gpu()
     announce(f"pool block={block} nblocks={nblocks} K={K}")
