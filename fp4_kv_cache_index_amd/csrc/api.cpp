@@ -55,7 +55,8 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 
 struct ScoreLayout {
   int64_t rows, n_stride, nb_max, nb_stride;
-  size_t off_keys, off_nvalid, off_tok, off_bkeys, off_nbvalid, off_blk, total;
+  int64_t th_stride;   // per-tile histograms per row (one-workgroup select), or 0
+  size_t off_keys, off_nvalid, off_tok, off_bkeys, off_nbvalid, off_blk, off_th, total;
 };
 
 static ScoreLayout score_layout(int64_t B, int64_t Tq, int64_t n_max, int32_t pool_block) {
@@ -72,6 +73,9 @@ static ScoreLayout score_layout(int64_t B, int64_t Tq, int64_t n_max, int32_t po
     L.off_bkeys = o; o += al256(sizeof(uint32_t) * L.rows * L.nb_stride);
     L.off_nbvalid = o; o += al256(sizeof(int32_t) * L.rows);
     L.off_blk = o; o += al256(select_ws_bytes(L.rows, L.nb_max));
+  } else if (n_max <= kLocalSel) {
+    L.th_stride = index_score_tiles_bound(n_max);
+    L.off_th = o; o += al256(sizeof(uint32_t) * 2048 * L.rows * L.th_stride);
   }
   L.total = o;
   return L;
@@ -195,12 +199,18 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
   ScoreArgs a{q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max, k_top,
               pool ? pool_block : 0, pool ? pool_nblocks : 0};
   const SelectOut tout{topk_idx, topk_score, nullptr, 0, 0, nullptr, nullptr};
-  if (!pool && n_max <= kSmallSel) {
-    // Short rows: one workgroup per row selects from the keys alone.
-    SelectWs none = tok;
-    none.hist1 = nullptr;
-    hipError_t e = launch_index_score(a, keys, L.n_stride, n_valid, none, nullptr, 0, nullptr, nullptr, s);
-    if (e == hipSuccess) e = select_small(keys, L.n_stride, n_valid, L.rows, k_top, tout, s);
+  if (!pool && n_max <= kLocalSel) {
+    // Rows of at most 64K positions: one workgroup per row selects, with the
+    // first digit from the scan's per-tile histograms (the dense prefill
+    // path writes none: there the select builds it).
+    const int64_t tiles = index_score_tiles(a);
+    SelectWs th = tok;
+    th.hist1 = nullptr;
+    th.tile_hist = tiles > 0 ? (uint32_t*)(base + L.off_th) : nullptr;
+    th.th_stride = L.th_stride;
+    hipError_t e = launch_index_score(a, keys, L.n_stride, n_valid, th, nullptr, 0, nullptr, nullptr, s);
+    if (e == hipSuccess)
+      e = select_local(keys, L.n_stride, n_valid, L.rows, k_top, n_max, th.tile_hist, L.th_stride, tiles, tout, s);
     return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
   }
   hipError_t e = select_clear(tok, L.rows, s);
@@ -248,13 +258,15 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
   base += al256(sizeof(int32_t) * rows);
   SelectWs sw = select_ws_carve(base, rows, pool_cap);
   const SelectOut out{topk_idx, topk_score, pool_idx, pool_cap, 0, nullptr, nullptr};
-  if (pool_cap <= kSmallSel) {
-    // Pools that fit one workgroup: select from the keys alone.
+  if (pool_cap <= kLocalSelMap) {
+    // Pools that fit one workgroup: the select builds the first digit itself
+    // (the pool scan's small tiles would leave many per-tile histograms to
+    // add up).
     SelectWs none = sw;
     none.hist1 = nullptr;
     hipError_t e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B,
                                      Tq, H_I, D_I, k_top, keys, cap, n_valid, none, s);
-    if (e == hipSuccess) e = select_small(keys, cap, n_valid, rows, k_top, out, s);
+    if (e == hipSuccess) e = select_local(keys, cap, n_valid, rows, k_top, pool_cap, nullptr, 0, 0, out, s);
     return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
   }
   hipError_t e = select_clear(sw, rows, s);

@@ -69,6 +69,12 @@ struct SelectWs {
   uint32_t* tile_cnt;                // [rows][tiles] listed positions, or ~0u when they did not fit
   uint16_t* tlist;                   // [rows][tiles][kTileList] in-tile offsets at or above the bucket
   int64_t cand_cap, tiles;
+  // Used by the scoring kernels only when hist1 is null: when set, each
+  // scoring workgroup stores its own top-12-bit histogram (2048 words, two
+  // 16-bit bins per word, bin 2i in the low half of word i) at
+  // tile_hist[(row * th_stride + tile) * 2048].
+  uint32_t* tile_hist = nullptr;
+  int64_t th_stride = 0;
 };
 size_t select_ws_bytes(int64_t rows, int64_t n_max);
 SelectWs select_ws_carve(void* base, int64_t rows, int64_t n_max);
@@ -89,11 +95,16 @@ struct SelectOut {
 
 // Clears the control blocks and first-digit histograms of `rows` rows.
 hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s);
-// Rows of at most kSmallSel positions: one workgroup per row does the whole
-// selection from the keys (no histogram: producers given a null hist1 skip
-// their flush, and no clear pass is needed).  Not for pool expansion.
-constexpr int kSmallSel = 16384;
-hipError_t select_small(const uint32_t* keys, int64_t key_stride, const int32_t* n_valid, int64_t rows, int k,
+// Rows of at most kLocalSel positions (kLocalSelMap with a map): one
+// workgroup per row does the whole selection from the keys, taking the
+// first radix digit from the producer's per-tile histograms when tile_hist
+// is given (`tiles` of them per row, th_stride apart) and building it itself
+// otherwise.  No clear pass is needed.  n_max bounds n_valid.  Not for pool
+// expansion.
+constexpr int kLocalSel = 65536;
+constexpr int kLocalSelMap = 32768;
+hipError_t select_local(const uint32_t* keys, int64_t key_stride, const int32_t* n_valid, int64_t rows, int k,
+                        int64_t n_max, const uint32_t* tile_hist, int64_t th_stride, int64_t tiles,
                         const SelectOut& out, hipStream_t s);
 // collect + finalize + emit, after the producer has written keys and hist1.
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
@@ -110,6 +121,11 @@ struct ScoreArgs {
 hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                               const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                               const SelectWs* blk, hipStream_t s);
+// Workgroups per row of the flat scan (0 when the dense prefill path
+// scores instead, which writes no per-tile histograms), and an upper bound
+// of it for any device.
+int64_t index_score_tiles(const ScoreArgs& a);
+int64_t index_score_tiles_bound(int64_t n_max);
 hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
                              int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
                              int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,

@@ -101,7 +101,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   constexpr int HP = H8 ? 8 : HMAX;
   // Top-12-bit histogram, two 16-bit bins per word (a tile holds at most
   // 16384 positions); the last word takes positions past the visible count.
-  __shared__ uint32_t hist[2049];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2052];
   // Flat scan: the tile's keys are staged here and leave in one coalesced
   // burst at the end (interleaving small key stores with the key-row stream
   // costs more than the LDS round trip).
@@ -397,13 +397,17 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
   // Two adjacent bins per 64-bit atomic: the row histogram's 32-bit counters
   // 2i and 2i+1 are the low and high halves of one little-endian 64-bit word.
-  // A null histogram means the caller selects from the keys alone.
   if (tok.hist1) {
     uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + row * 4096);
     for (int i = threadIdx.x; i < 2048; i += NT) {
       const uint32_t v = hist[i];
       if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
     }
+  } else if (tok.tile_hist) {
+    // The tile's histogram as it stands (two 16-bit bins per word), one slot
+    // per tile: plain stores, nothing to clear beforehand.
+    v4u* th = reinterpret_cast<v4u*>(tok.tile_hist + (row * tok.th_stride + blockIdx.x) * 2048);
+    for (int i = threadIdx.x; i < 512; i += NT) th[i] = reinterpret_cast<const v4u*>(hist)[i];
   }
   if (pool) {
     uint64_t* gbh = reinterpret_cast<uint64_t*>(blk.hist1 + row * 4096);
@@ -414,15 +418,21 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
 }
 
+// Flat-scan tile: the largest that still gives every compute unit a
+// workgroup (16-wave workgroups), else kScanTileSmall.
+static int scan_tile(int64_t rows, int64_t n_max, int nw) {
+  int tile = nw == 16 ? kScanTileMax : kScanTileSmall;
+  while (tile > kScanTileSmall && rows * ((n_max + tile - 1) / tile) < device_cu_count()) tile >>= 1;
+  return tile;
+}
+
 template <int DI, int HB, bool H8>
 static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
   int64_t rows = (int64_t)a.B * a.Tq;
   constexpr int NW = kScanWavesT<false, HB>;
-  // The largest tile that still gives every compute unit a workgroup.
-  int tile = NW == 16 ? kScanTileMax : kScanTileSmall;
-  while (tile > kScanTileSmall && rows * ((a.n_max + tile - 1) / tile) < device_cu_count()) tile >>= 1;
+  const int tile = scan_tile(rows, a.n_max, NW);
   int64_t tiles = (a.n_max + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
   SelectWs bw = blk ? *blk : tok;
@@ -839,6 +849,19 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
 #define CALL_SCAN(D, H, E) launch_scan_t<D, H, E>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
   CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_SCAN);
 #undef CALL_SCAN
+}
+
+int64_t index_score_tiles(const ScoreArgs& a) {
+  if (prefill_gemm_applies(a)) return 0;
+  const int64_t rows = (int64_t)a.B * a.Tq;
+  const int tile = scan_tile(rows, a.n_max, a.H_I <= 16 ? kScanWavesT<false, 1> : kScanWavesT<false, 2>);
+  const int64_t tiles = (a.n_max + tile - 1) / tile;
+  return tiles < 1 ? 1 : tiles;
+}
+
+int64_t index_score_tiles_bound(int64_t n_max) {
+  const int64_t tiles = (n_max + kScanTileSmall - 1) / kScanTileSmall;
+  return tiles < 1 ? 1 : tiles;
 }
 
 hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,

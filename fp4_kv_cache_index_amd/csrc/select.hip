@@ -437,236 +437,422 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   }
 }
 
-// small: the whole selection of a row in one 1024-thread workgroup when the
-// row has at most kSmallSel positions (pool layers, short contexts).  The
-// row is cut into 4 groups of 4096 positions; thread t holds positions
-// 4t .. 4t+3 of every group (and their map entries) in registers, so each
-// load instruction of a wave reads 1 KB of consecutive keys.  Three radix
-// digits (12, 12, 8 bits) over the row's keys give T and the ties to take,
-// with one LDS histogram per level cleared together at the start.  The
-// output offsets follow position order, (group, thread, element): one
-// prefix sum over threads of four packed (above T, equal to T) counts, one
-// per group, plus the totals of the earlier groups.  No global histogram,
-// no clear pass.
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallGroups = 4;
-static_assert(kSmallSel == 4 * kSmallGroups * kSmallThreads, "4 positions per thread and group");
+// local: the whole selection of a row in one 1024-thread workgroup when the
+// row has at most kLocalSel positions.  Wave w owns the NS*64 consecutive
+// positions from w*NS*64, element s of its lane l being position
+// w*NS*64 + 64s + l: each load instruction of a wave reads 256 consecutive
+// bytes, and the order (wave, s, lane) is position order.
+//   level 0    -- the top-12-bit histogram, summed from the producer's
+//                 per-tile histograms or built here in LDS, gives the
+//                 threshold bucket;
+//   candidates -- when the bucket and everything above it fit in LDS
+//                 (kLocalCand entries), those keys are packed there in
+//                 position order, and levels 1-2 and the emission run over
+//                 them; otherwise over the registers.
+// Packing in position order: a wave counts its selected elements (a ballot
+// and a population count per element, in scalar registers), the wave
+// totals give every wave its base, and a second pass writes each selected
+// element at its wave's running count plus its mbcnt rank.
+constexpr int kLocalThreads = 1024;
+constexpr int kLocalCand = 8192;
+static_assert(kLocalSel == 64 * kLocalThreads && kLocalSelMap == 32 * kLocalThreads, "64 or 32 elements per thread");
 
-// Digit of a BINS-bin LDS histogram (4096 or 256) at which the count from
-// the top reaches `need`, as (d, count above d, count at d); `total` gets the
-// histogram's sum (the digit is meaningless when need > total).  Thread t
-// reads bins 4g .. 4g+3 of group g = BINS/4 - 1 - t, so a prefix sum over
-// threads counts from the top.
-template <int BINS>
-__device__ Digit small_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res, uint32_t& total) {
-  constexpr int G = BINS / 4;
-  static_assert(G == kSmallThreads || G == 64, "one group per thread or per lane of the first wave");
-  if (G == kSmallThreads || threadIdx.x < 64) {
-    const int g = G - 1 - threadIdx.x;
-    const v4u h = reinterpret_cast<const v4u*>(hist)[g];
-    const uint32_t sum = h[0] + h[1] + h[2] + h[3];
-    const uint32_t incl = G == kSmallThreads ? block_scan<kSmallThreads>(sum, red) : wave_prefix_sum(sum);
-    if (threadIdx.x == G - 1) res[4] = incl;
-    uint32_t run = incl - sum;
-    if (run < need && need <= incl) {
+// Inclusive prefix sum over the workgroup, plus the workgroup total.
+__device__ __forceinline__ uint32_t local_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+  constexpr int NWV = kLocalThreads / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  v = wave_prefix_sum(v);
+  if (lane == 63) red[wv] = v;
+  __syncthreads();
+  uint32_t add = 0, tot = 0;
 #pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (run < need && need <= run + h[j]) {
-          res[0] = 4 * g + j;
-          res[1] = run;
-          res[2] = h[j];
-        }
-        run += h[j];
+  for (int g = 0; g < NWV / 4; ++g) {
+    const v4u r = reinterpret_cast<const v4u*>(red)[g];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      add += 4 * g + j < wv ? r[j] : 0u;
+      tot += r[j];
+    }
+  }
+  total = tot;
+  return v + add;
+}
+
+// Digit of a 4096-bin histogram at which the count from the top reaches
+// `need`, from the bins 4g .. 4g+3 (g = 1023 - thread) that each thread
+// holds: (d, count above d, count at d); `total` gets the histogram's sum
+// (the digit is meaningless when need > total).  `red` and `res` are LDS.
+__device__ Digit local_digit_regs(const uint32_t (&h)[4], uint32_t need, uint32_t* red, uint32_t* res,
+                                  uint32_t& total) {
+  const int g = kLocalThreads - 1 - threadIdx.x;
+  const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+  uint32_t tot;
+  const uint32_t incl = local_scan(sum, red, tot);
+  uint32_t run = incl - sum;
+  if (run < need && need <= incl) {
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (run < need && need <= run + h[j]) {
+        res[0] = 4 * g + j;
+        res[1] = run;
+        res[2] = h[j];
       }
+      run += h[j];
     }
   }
   __syncthreads();
-  total = res[4];
+  total = tot;
   return Digit{res[0], res[1], res[2]};
 }
 
-__global__ void __launch_bounds__(kSmallThreads)
-select_small_kernel(const uint32_t* __restrict__ keys, int64_t key_stride, const int32_t* __restrict__ n_valid, int k,
-                    SelectOut out) {
-  constexpr int NT = kSmallThreads, NG = kSmallGroups, GS = 4 * NT, PT = 4 * NG;
-  constexpr int NWV = NT / 64;
-  __shared__ __align__(16) uint32_t hist0[4096];
+// The same for an LDS histogram of 4096 or 256 bins (the latter on the
+// first wave only).
+template <int BINS>
+__device__ Digit local_digit(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t* res) {
+  if constexpr (BINS == 4096) {
+    const v4u v = reinterpret_cast<const v4u*>(hist)[kLocalThreads - 1 - threadIdx.x];
+    const uint32_t h[4] = {v[0], v[1], v[2], v[3]};
+    uint32_t total;
+    return local_digit_regs(h, need, red, res, total);
+  } else {
+    static_assert(BINS == 256, "4096 or 256 bins");
+    if (threadIdx.x < 64) {
+      const int g = 63 - threadIdx.x;
+      const v4u h = reinterpret_cast<const v4u*>(hist)[g];
+      const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+      const uint32_t incl = wave_prefix_sum(sum);
+      uint32_t run = incl - sum;
+      if (run < need && need <= incl) {
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (run < need && need <= run + h[j]) {
+            res[0] = 4 * g + j;
+            res[1] = run;
+            res[2] = h[j];
+          }
+          run += h[j];
+        }
+      }
+    }
+    __syncthreads();
+    return Digit{res[0], res[1], res[2]};
+  }
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Base of this wave and total over the workgroup of the per-wave counts
+// `cnt` (wave-uniform).  `wtot` is LDS of 16 words, read after the call.
+__device__ __forceinline__ uint32_t wave_base(uint32_t cnt, uint32_t* wtot, uint32_t& total) {
+  constexpr int NWV = kLocalThreads / 64;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lane == 0) wtot[wv] = cnt;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int g = 0; g < NWV / 4; ++g) {
+    const v4u r = reinterpret_cast<const v4u*>(wtot)[g];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      base += 4 * g + j < wv ? r[j] : 0u;
+      tot += r[j];
+    }
+  }
+  total = tot;
+  return base;
+}
+
+template <int NS, bool MAP, bool TH>
+__global__ void __launch_bounds__(kLocalThreads)
+select_local_kernel(const uint32_t* __restrict__ keys, int64_t key_stride, const int32_t* __restrict__ n_valid, int k,
+                    const uint32_t* __restrict__ tile_hist, int64_t th_stride, int tiles, SelectOut out) {
+  constexpr int NT = kLocalThreads, NWV = NT / 64, WS = 64 * NS;   // WS: positions per wave
+  __shared__ __align__(16) uint32_t hist0[TH ? 4 : 4096];
   __shared__ __align__(16) uint32_t hist1[4096];
   __shared__ __align__(16) uint32_t hist2[256];
-  __shared__ __align__(16) uint32_t red[NG * NWV];
-  __shared__ uint32_t res[5];
+  __shared__ __align__(16) uint32_t red[NWV];
+  __shared__ __align__(16) uint32_t wtot[2][NWV];
+  // (keys and ids apart: a 64-bit pair store would tie every key register
+  // to a free neighbour)
+  __shared__ __align__(16) uint32_t cand_key[kLocalCand];
+  __shared__ __align__(16) int32_t cand_id[kLocalCand];
+  __shared__ uint32_t res[4];
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 1024; i += NT) {
-    reinterpret_cast<v4u*>(hist0)[i] = v4u{0u, 0u, 0u, 0u};
+  const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  for (int i = t; i < 1024; i += NT) {
+    if (!TH) reinterpret_cast<v4u*>(hist0)[i] = v4u{0u, 0u, 0u, 0u};
     reinterpret_cast<v4u*>(hist1)[i] = v4u{0u, 0u, 0u, 0u};
   }
-  if (threadIdx.x < 64) reinterpret_cast<v4u*>(hist2)[threadIdx.x] = v4u{0u, 0u, 0u, 0u};
-  int64_t nv = n_valid[row];
-  if (nv > kSmallSel) nv = kSmallSel;   // (the host guarantees it)
-  const uint32_t* kr = keys + row * key_stride;
-  const int32_t* map = out.map ? out.map + row * out.map_stride : nullptr;
-  // kk[4g + j] is position g*GS + 4t + j.
-  uint32_t kk[PT];
-  int32_t mp[PT];
+  if (t < 64) reinterpret_cast<v4u*>(hist2)[t] = v4u{0u, 0u, 0u, 0u};
+  int64_t nv64 = n_valid[row];
+  if (nv64 > NS * NT) nv64 = NS * NT;   // (the host guarantees it)
+  const int nv = (int)(nv64 < 0 ? 0 : nv64);
+  const int wbase = wv * WS;            // first position of this wave
+  // Positions at or past nv read as 0.
+  const uint32_t* kr = keys + row * key_stride + wbase + lane;
+  uint32_t kk[NS];
+  if (wbase + WS <= nv) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int p = g * GS + 4 * threadIdx.x;
-    // rows are padded to a multiple of 64 keys: a vector starting below nv
-    // stays inside the row
-    v4u v = {0u, 0u, 0u, 0u};
-    if (p < nv) v = *reinterpret_cast<const v4u*>(kr + p);
+    for (int s = 0; s < NS; ++s) kk[s] = kr[64 * s];
+  } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kk[4 * g + j] = p + j < nv ? v[j] : 0u;
-      mp[4 * g + j] = p + j;
-    }
+    for (int s = 0; s < NS; ++s) kk[s] = wbase + 64 * s + lane < nv ? kr[64 * s] : 0u;
   }
-  if (map) {
-    if (((uintptr_t)map & 15u) == 0) {
-      // the map row holds at least nv entries, but not a whole last vector
+  int32_t mp[MAP ? NS : 1];
+  if constexpr (MAP) {
+    const int32_t* mr = out.map + row * out.map_stride + wbase + lane;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int p = g * GS + 4 * threadIdx.x;
-        if (p + 3 < nv) {
-          const v4u m = *reinterpret_cast<const v4u*>(map + p);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) mp[4 * g + j] = (int32_t)m[j];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (p + j < nv) mp[4 * g + j] = map[p + j];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < PT; ++e) {
-        const int p = (e >> 2) * GS + 4 * threadIdx.x + (e & 3);
-        if (p < nv) mp[e] = map[p];
-      }
-    }
+    for (int s = 0; s < NS; ++s) mp[s] = wbase + 64 * s + lane < nv ? mr[64 * s] : 0;
   }
-  __syncthreads();   // histograms cleared
-  // Threshold T and ties to take; every visible position (key != 0) when
-  // there are at most k of them.
-  bool take_all = nv <= k;
-  uint32_t thr = 0u, need_eq = 0u;
-  if (!take_all) {
-#pragma unroll
-    for (int e = 0; e < PT; ++e)
-      if (kk[e]) atomicAdd(&hist0[kk[e] >> 20], 1u);
-    __syncthreads();
-    uint32_t total;
-    const Digit D0 = small_digit<4096>(hist0, (uint32_t)k, red, res, total);
-    if (total <= (uint32_t)k) {
-      take_all = true;
-    } else {
-      uint32_t need = (uint32_t)k - D0.above, prefix = D0.d;
-      if (need == D0.cnt) {   // the whole bucket is taken
-        thr = prefix ? (prefix << 20) - 1u : 0u;
-      } else {
-#pragma unroll
-        for (int e = 0; e < PT; ++e)
-          if (kk[e] != 0u && (kk[e] >> 20) == prefix) atomicAdd(&hist1[(kk[e] >> 8) & 0xFFFu], 1u);
-        __syncthreads();
-        const Digit D1 = small_digit<4096>(hist1, need, red, res, total);
-        need -= D1.above;
-        prefix = (prefix << 12) | D1.d;
-        if (need == D1.cnt) {
-          thr = prefix ? (prefix << 8) - 1u : 0u;
-        } else {
-#pragma unroll
-          for (int e = 0; e < PT; ++e)
-            if (kk[e] != 0u && (kk[e] >> 8) == prefix) atomicAdd(&hist2[kk[e] & 0xFFu], 1u);
-          __syncthreads();
-          const Digit D2 = small_digit<256>(hist2, need, red, res, total);
-          thr = (prefix << 8) | D2.d;
-          need_eq = need - D2.above;
-        }
-      }
-    }
-  }
-  // Emission: ties at T go to the lowest positions.  Per group, the counts
-  // above T and at T are packed in one word (each total is at most 4096).
-  uint32_t cnt[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x = kk[4 * g + j];
-      gt += x != 0u && (take_all || x > thr);
-      eq += !take_all && x != 0u && x == thr;
-    }
-    cnt[g] = (gt << 16) | eq;
-  }
-  uint32_t incl[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) incl[g] = wave_prefix_sum(cnt[g]);
-  if (lane == 63) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) red[g * NWV + wv] = incl[g];
-  }
-  __syncthreads();
-  uint32_t base = 0;   // packed totals of the earlier groups
-  uint32_t before[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    uint32_t waves_before = 0, group_total = 0;
-#pragma unroll
-    for (int q = 0; q < NWV / 4; ++q) {
-      const v4u r = reinterpret_cast<const v4u*>(red + g * NWV)[q];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        waves_before += 4 * q + j < wv ? r[j] : 0u;
-        group_total += r[j];
-      }
-    }
-    before[g] = base + waves_before + incl[g] - cnt[g];
-    base += group_total;
-  }
+  // Output ids are recomputed from an opaque copy of the lane position, so
+  // that the load addresses are not kept alive for them.
+  int p_id = wbase + lane;
+  asm volatile("" : "+v"(p_id));
+  auto id_of = [&](int s) -> int32_t { if constexpr (MAP) return mp[s]; else return p_id + 64 * s; };
   int32_t* oi = out.idx + row * (int64_t)k;
   float* os = out.score ? out.score + row * (int64_t)k : nullptr;
+
+  // Level 0.  When every visible position is taken (at most k of them),
+  // keys above T = 0 are selected.
+  bool take_all = nv <= k;
+  Digit D0{0u, 0u, 0u};
+  if (!take_all) {
+    uint32_t h[4] = {0u, 0u, 0u, 0u};
+    if constexpr (TH) {
+      const uint2* th = reinterpret_cast<const uint2*>(tile_hist + row * th_stride * 2048) + (NT - 1 - t);
+      auto add = [&](uint2 v) {
+        h[0] += v.x & 0xFFFFu;
+        h[1] += v.x >> 16;
+        h[2] += v.y & 0xFFFFu;
+        h[3] += v.y >> 16;
+      };
+      int i = 0;
+      for (; i + 8 <= tiles; i += 8) {   // eight loads in flight
+        uint2 v[8];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const uint32_t eq_before = before[g] & 0xFFFFu;
-    uint32_t slot = (before[g] >> 16) + (eq_before < need_eq ? eq_before : need_eq);
-    const uint32_t eq = cnt[g] & 0xFFFFu;
-    uint32_t take = 0;
-    if (need_eq > eq_before) take = need_eq - eq_before < eq ? need_eq - eq_before : eq;
-    uint32_t taken = 0;
+        for (int u = 0; u < 8; ++u) v[u] = th[(i + u) * 1024];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x = kk[4 * g + j];
-      if (x == 0u) continue;
-      bool pick = take_all || x > thr;
-      if (!pick && x == thr && taken < take) {
+        for (int u = 0; u < 8; ++u) add(v[u]);
+      }
+      for (; i < tiles; ++i) add(th[i * 1024]);
+      __syncthreads();   // (LDS clears)
+    } else {
+      __syncthreads();   // histograms cleared
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if (kk[s]) atomicAdd(&hist0[kk[s] >> 20], 1u);
+      __syncthreads();
+      const v4u v = reinterpret_cast<const v4u*>(hist0)[NT - 1 - t];
+      h[0] = v[0]; h[1] = v[1]; h[2] = v[2]; h[3] = v[3];
+    }
+    uint32_t total;
+    D0 = local_digit_regs(h, (uint32_t)k, red, res, total);
+    take_all = total <= (uint32_t)k;
+  }
+  if (take_all) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      cnt += (uint32_t)__popcll(__ballot(kk[s] != 0u));
+      if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);   // a few masks live at a time
+    }
+    uint32_t n;
+    uint32_t run = wave_base(cnt, wtot[0], n);
+    // The writes test the elements again: an opaque bound keeps the compiler
+    // from holding one condition per element across the barrier.
+    uint32_t z = 0u;
+    asm volatile("" : "+v"(z));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint64_t m = __ballot(kk[s] > z);
+      if (kk[s] > z) {
+        const uint32_t slot = run + lane_rank(m);
+        if (slot < (uint32_t)k) {
+          oi[slot] = id_of(s);
+          if (os) os[slot] = key_score(kk[s]);
+        }
+      }
+      run += (uint32_t)__popcll(m);
+      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int64_t i = n + t; i < k; i += NT) {
+      oi[i] = -1;
+      if (os) os[i] = -__builtin_inff();
+    }
+    return;
+  }
+  // T = the k-th largest key: in bucket D0.d; need1 of the bucket's keys are
+  // taken.  Key 0 (absent) can lie in bucket 0 only: lo excludes it.
+  const uint32_t need1 = (uint32_t)k - D0.above;
+  const uint32_t lo = D0.d ? D0.d << 20 : 1u;
+  uint32_t thr, need_eq = 0u;
+  // Candidates: keys >= lo (D0.above + D0.cnt of them).  Counted per wave
+  // first; when they fit in LDS they are packed there in position order as
+  // (key, id).
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    cnt += (uint32_t)__popcll(__ballot(kk[s] >= lo));
+    if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);   // a few masks live at a time
+  }
+  uint32_t ncand;
+  const uint32_t base = wave_base(cnt, wtot[0], ncand);
+  if (ncand <= (uint32_t)kLocalCand) {
+    uint32_t lo2 = lo;   // (opaque, as above)
+    asm volatile("" : "+v"(lo2));
+    uint32_t run = base;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint64_t m = __ballot(kk[s] >= lo2);
+      if (kk[s] >= lo2) {
+        const uint32_t slot = run + lane_rank(m);   // < ncand
+        cand_key[slot] = kk[s];
+        cand_id[slot] = id_of(s);
+      }
+      run += (uint32_t)__popcll(m);
+      if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    if (need1 == D0.cnt) {   // the whole bucket is taken: every candidate
+      thr = lo - 1u;
+    } else {
+      for (uint32_t i = t; i < ncand; i += NT) {
+        const uint32_t x = cand_key[i];
+        if ((x >> 20) == D0.d) atomicAdd(&hist1[(x >> 8) & 0xFFFu], 1u);
+      }
+      __syncthreads();
+      const Digit D1 = local_digit<4096>(hist1, need1, red, res);
+      const uint32_t need2 = need1 - D1.above;
+      const uint32_t p24 = (D0.d << 12) | D1.d;
+      if (need2 == D1.cnt) {
+        thr = p24 ? (p24 << 8) - 1u : 0u;
+      } else {
+        for (uint32_t i = t; i < ncand; i += NT) {
+          const uint32_t x = cand_key[i];
+          if ((x >> 8) == p24) atomicAdd(&hist2[x & 0xFFu], 1u);
+        }
+        __syncthreads();
+        const Digit D2 = local_digit<256>(hist2, need2, red, res);
+        thr = (p24 << 8) | D2.d;   // a visible key: not 0
+        need_eq = need2 - D2.above;
+      }
+    }
+    // Emission from the candidates: thread t takes a run of P consecutive
+    // ones; counts above T and at T are packed (each at most kLocalCand).
+    const uint32_t P = (ncand + NT - 1) / NT;
+    const uint32_t c0 = t * P, c1 = c0 + P < ncand ? c0 + P : ncand;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i = c0; i < c1; ++i) {
+      const uint32_t x = cand_key[i];
+      gt += x > thr;
+      eq += x == thr;
+    }
+    const uint32_t c = (gt << 16) | eq;
+    uint32_t tot;
+    const uint32_t excl = local_scan(c, red, tot) - c;
+    const uint32_t eq_before = excl & 0xFFFFu;
+    uint32_t slot = (excl >> 16) + (eq_before < need_eq ? eq_before : need_eq);
+    uint32_t take = need_eq > eq_before ? (need_eq - eq_before < eq ? need_eq - eq_before : eq) : 0u;
+    for (uint32_t i = c0; i < c1; ++i) {
+      const uint32_t x = cand_key[i];
+      bool pick = x > thr;
+      if (!pick && x == thr && take > 0) {
         pick = true;
-        ++taken;
+        --take;
       }
       if (pick && slot < (uint32_t)k) {
-        oi[slot] = mp[4 * g + j];
+        oi[slot] = cand_id[i];
         if (os) os[slot] = key_score(x);
         ++slot;
       }
     }
+    return;
   }
-  // Exactly k are selected unless every visible position is.
-  if (take_all) {
-    for (int64_t i = (base >> 16) + threadIdx.x; i < k; i += NT) {
-      oi[i] = -1;
-      if (os) os[i] = -__builtin_inff();
+  // Too many candidates for LDS (a crowded bucket): levels 1-2 and the
+  // emission over the registers.
+  {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if ((kk[s] >> 20) == D0.d && kk[s] >= lo) atomicAdd(&hist1[(kk[s] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    const Digit D1 = local_digit<4096>(hist1, need1, red, res);
+    const uint32_t need2 = need1 - D1.above;
+    const uint32_t p24 = (D0.d << 12) | D1.d;
+    if (need2 == D1.cnt) {
+      thr = p24 ? (p24 << 8) - 1u : 0u;
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if ((kk[s] >> 8) == p24 && kk[s] >= lo) atomicAdd(&hist2[kk[s] & 0xFFu], 1u);
+      __syncthreads();
+      const Digit D2 = local_digit<256>(hist2, need2, red, res);
+      thr = (p24 << 8) | D2.d;
+      need_eq = need2 - D2.above;
     }
+  }
+  // The selection: keys above T, then the need_eq lowest positions at T.
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    cg += (uint32_t)__popcll(__ballot(kk[s] > thr));
+    ce += (uint32_t)__popcll(__ballot(kk[s] == thr));
+    if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+  uint32_t ng, ne;
+  uint32_t run_g = wave_base(cg, wtot[0], ng);
+  uint32_t run_e = wave_base(ce, wtot[1], ne);
+  uint32_t thr2 = thr;   // (opaque, as above)
+  asm volatile("" : "+v"(thr2));
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint64_t mg = __ballot(kk[s] > thr2);
+    const uint64_t me = __ballot(kk[s] == thr2);
+    const uint32_t eb = run_e + lane_rank(me);   // ties before this element
+    const bool pick = kk[s] > thr2 || (kk[s] == thr2 && eb < need_eq);
+    if (pick) {
+      const uint32_t slot = run_g + lane_rank(mg) + (eb < need_eq ? eb : need_eq);
+      if (slot < (uint32_t)k) {
+        oi[slot] = id_of(s);
+        if (os) os[slot] = key_score(kk[s]);
+      }
+    }
+    run_g += (uint32_t)__popcll(mg);
+    run_e += (uint32_t)__popcll(me);
+    if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // ---------------------------------------------------------------- host ---
 
-hipError_t select_small(const uint32_t* keys, int64_t key_stride, const int32_t* n_valid, int64_t rows, int k,
+hipError_t select_local(const uint32_t* keys, int64_t key_stride, const int32_t* n_valid, int64_t rows, int k,
+                        int64_t n_max, const uint32_t* tile_hist, int64_t th_stride, int64_t tiles,
                         const SelectOut& out, hipStream_t s) {
-  if (out.expand != 0) return hipErrorInvalidValue;
-  CSA2_LAUNCH("select_small", select_small_kernel, dim3((unsigned)rows), dim3(kSmallThreads), 0, s, keys, key_stride,
-              n_valid, k, out);
+  if (out.expand != 0 || n_max > kLocalSel || (out.map && n_max > kLocalSelMap)) return hipErrorInvalidValue;
+  if (tile_hist && (tiles < 1 || tiles > th_stride)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)rows), block(kLocalThreads);
+  const int nt = (int)tiles;
+#define CSA2_LOCAL(NS, MAP, TH)                                                                                    \
+  CSA2_LAUNCH("select_local", (select_local_kernel<NS, MAP, TH>), grid, block, 0, s, keys, key_stride, n_valid, k, \
+              tile_hist, th_stride, nt, out)
+  const bool th = tile_hist != nullptr;
+  if (n_max <= 16 * kLocalThreads) {
+    if (out.map) {
+      if (th) CSA2_LOCAL(16, true, true); else CSA2_LOCAL(16, true, false);
+    } else {
+      if (th) CSA2_LOCAL(16, false, true); else CSA2_LOCAL(16, false, false);
+    }
+  } else if (n_max <= 32 * kLocalThreads) {
+    if (out.map) {
+      if (th) CSA2_LOCAL(32, true, true); else CSA2_LOCAL(32, true, false);
+    } else {
+      if (th) CSA2_LOCAL(32, false, true); else CSA2_LOCAL(32, false, false);
+    }
+  } else {
+    if (th) CSA2_LOCAL(64, false, true); else CSA2_LOCAL(64, false, false);
+  }
+#undef CSA2_LOCAL
   return hipGetLastError();
 }
 

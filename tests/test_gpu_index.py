@@ -48,10 +48,11 @@ def test_tiny_config_full_layer_topk():
     _run_and_check(lay["q_idx"], lay["w"], k_idx, ctx, wl.K)
 
 
-# Rows of at most 16384 positions are selected by one workgroup per row,
-# longer rows by the tiled multi-kernel select: sizes on both sides.
+# Rows of at most 65536 positions are selected by one workgroup per row
+# (holding 16K, 32K or 64K positions), longer rows by the tiled multi-kernel
+# select: sizes in each class.
 @gpu
-@pytest.mark.parametrize("N", [3 * 4096 + 577, 5 * 4096 + 577])
+@pytest.mark.parametrize("N", [3 * 4096 + 577, 5 * 4096 + 577, 16 * 4096 + 577])
 @pytest.mark.parametrize("H_I,D_I,K", [(8, 128, 2048), (32, 128, 512), (4, 64, 256), (3, 32, 100), (16, 256, 64)])
 def test_ragged_contexts_and_shapes(H_I, D_I, K, N):
     require_gpu()
@@ -65,7 +66,7 @@ def test_ragged_contexts_and_shapes(H_I, D_I, K, N):
 
 
 @gpu
-@pytest.mark.parametrize("N", [9000, 30000])
+@pytest.mark.parametrize("N", [9000, 30000, 70000])
 def test_all_ties_and_padding(N):
     require_gpu()
     announce(f"index_score_topk all ties (q = 0) and K > context N={N}")
@@ -81,7 +82,7 @@ def test_all_ties_and_padding(N):
 
 
 @gpu
-@pytest.mark.parametrize("N", [12000, 20000])
+@pytest.mark.parametrize("N", [12000, 20000, 70000])
 def test_heavy_ties_small_integer_weights(N):
     require_gpu()
     announce(f"index_score_topk heavy ties N={N}")
@@ -94,10 +95,10 @@ def test_heavy_ties_small_integer_weights(N):
 
 
 @gpu
-@pytest.mark.parametrize("N", [16384, 16385])
+@pytest.mark.parametrize("N", [16384, 16385, 32768, 32769, 65536, 65537])
 def test_select_size_boundary(N):
-    """Longest row for the one-workgroup select and one position past it;
-    the second sequence has fewer visible positions than K."""
+    """Longest rows of each one-workgroup select size and one position past
+    them; the second sequence has fewer visible positions than K."""
     require_gpu()
     announce(f"index_score_topk select boundary N={N}")
     B, H_I, D_I = 2, 8, 128
@@ -146,7 +147,7 @@ def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K):
 
 @gpu
 @pytest.mark.parametrize("block,nblocks,K", [(8, 64, 256), (8, 2048, 2048), (4, 100, 64), (1, 300, 300), (16, 40, 128),
-                                             (16, 1100, 512), (1, 150, 64)])
+                                             (16, 1100, 512), (16, 2100, 512), (1, 150, 64)])
 def test_hierarchical_pool_and_pool_topk(block, nblocks, K):
     require_gpu()
     announce(f"pool block={block} nblocks={nblocks} K={K}")
