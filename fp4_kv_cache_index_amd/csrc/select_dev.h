@@ -55,28 +55,6 @@ __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
   return (uint32_t)x;
 }
 
-// Inclusive prefix sum over the NT (<= 1024) threads of a workgroup: thread
-// t gets v_0 + ... + v_t.  `red` is 16-byte aligned LDS scratch of NT/64
-// words; it is read after the function returns, so a later call must use
-// other scratch or come after another barrier.
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red) {
-  constexpr int NWV = NT / 64;
-  static_assert(NWV % 4 == 0 && NWV <= 16, "whole 16-byte groups of wave totals");
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  v = wave_prefix_sum(v);
-  if (lane == 63) red[wv] = v;
-  __syncthreads();
-  uint32_t add = 0;
-#pragma unroll
-  for (int g = 0; g < NWV / 4; ++g) {
-    const v4u r = reinterpret_cast<const v4u*>(red)[g];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) add += 4 * g + j < wv ? r[j] : 0u;
-  }
-  return v + add;
-}
-
 // Digit of a BINS-bin histogram (global or shared memory) at which the
 // running count from the top reaches `need` (1 <= need <= total):
 //   sum_{e>d} h[e] < need <= sum_{e>=d} h[e].
