@@ -17,22 +17,16 @@ Trace& thread_trace() {
   return t;
 }
 
-void trace_before(hipStream_t s, const char* name) {
+bool trace_launch(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   Trace& t = thread_trace();
-  if (!t.active) return;
-  t.skipping = t.only[0] != 0 && std::strcmp(name, t.only) != 0;
-  if (t.skipping) return;
-  if (t.count < t.capacity) {
-    hipEventRecord(t.events[2 * t.count], s);
-    if (t.names) t.names[t.count] = name;
-  }
-}
-
-void trace_after(hipStream_t s) {
-  Trace& t = thread_trace();
-  if (!t.active || t.skipping) return;
-  if (t.count < t.capacity) hipEventRecord(t.events[2 * t.count + 1], s);
-  ++t.count;
+  if (!t.active) return false;
+  if (t.only[0] != 0 && std::strcmp(name, t.only) != 0) return false;
+  const int c = t.count++;
+  if (c >= t.capacity) return false;   // counted, not timed
+  *start = t.events[2 * c];
+  *stop = t.events[2 * c + 1];
+  if (t.names) t.names[c] = name;
+  return true;
 }
 
 int device_cu_count() {

@@ -1,13 +1,16 @@
 // Internal (host-side) interface between the C ABI and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace csa2 {
 
-// Kernel launch with the optional per-thread trace (events around the launch).
+// Kernel launch with the optional per-thread trace: a traced launch carries
+// its start and stop events in the dispatch itself (hipExtLaunchKernelGGL),
+// so tracing puts no marker between kernels on the stream.
 struct Trace {
   hipEvent_t* events = nullptr;
   const char** names = nullptr;
@@ -15,18 +18,21 @@ struct Trace {
   int count = 0;
   bool active = false;
   char only[64] = {0};      // non-empty: trace only launches of this kernel name
-  bool skipping = false;    // the current launch is not traced
 };
 Trace& thread_trace();
 
-void trace_before(hipStream_t s, const char* name);
-void trace_after(hipStream_t s);
+// True when the calling thread traces this launch; then *start and *stop are
+// the events to attach to it.
+bool trace_launch(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
-#define CSA2_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
-  do {                                                                             \
-    ::csa2::trace_before((stream), (name));                                       \
-    hipLaunchKernelGGL(kernel, (grid), (block), (shmem), (stream), __VA_ARGS__);   \
-    ::csa2::trace_after((stream));                                                 \
+#define CSA2_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                                       \
+  do {                                                                                                   \
+    hipEvent_t ev_start__ = nullptr, ev_stop__ = nullptr;                                                \
+    if (::csa2::trace_launch((name), &ev_start__, &ev_stop__))                                           \
+      hipExtLaunchKernelGGL(kernel, (grid), (block), (shmem), (stream), ev_start__, ev_stop__, 0u,       \
+                            __VA_ARGS__);                                                                \
+    else                                                                                                 \
+      hipLaunchKernelGGL(kernel, (grid), (block), (shmem), (stream), __VA_ARGS__);                       \
   } while (0)
 
 // Number of compute units of the current device (cached per device).

@@ -218,11 +218,13 @@ int csa2_sparse_attn_prefill(const float* q,
 
 /*
  * Kernel trace for measurement harnesses.  While a trace is attached to the
- * calling host thread, each kernel the library launches from that thread is
- * bracketed by hipEventRecord on its stream: events[2*i] before and
- * events[2*i+1] after the i-th launch (HOST array of hipEvent_t created by
- * the caller), and names[i] (HOST array, nullable) receives the kernel's
- * static name.  Launches past `capacity` are counted but not recorded.
+ * calling host thread, each kernel the library launches from that thread
+ * carries events[2*i] and events[2*i+1] as the start and stop events of its
+ * dispatch (hipExtLaunchKernelGGL; the elapsed time between them is the
+ * kernel's execution, and no separate event record is put on the stream) for
+ * the i-th launch (HOST array of hipEvent_t created by the caller), and
+ * names[i] (HOST array, nullable) receives the kernel's static name.
+ * Launches past `capacity` are counted but not recorded.
  * csa2_trace_detach returns the number of launches since attach through
  * *n_launches (nullable) and stops recording.
  */
