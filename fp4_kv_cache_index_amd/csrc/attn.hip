@@ -38,6 +38,8 @@
 //                 so no transposed copy is stored.
 // Splits write unnormalised partial (O, m, l); a combine kernel merges them
 // with the log-sum-exp rule and adds the sink.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -452,24 +454,32 @@ sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __rest
   float L = 0.0f;
   if (M != -__builtin_inff()) {
     const float4* ob = reinterpret_cast<const float4*>(part_o + (row * splits * (int64_t)H + h) * DV) + threadIdx.x;
-    constexpr int U = 16;
-    for (int s0 = 0; s0 < splits; s0 += U) {
-      float2 ml[U];
-      float4 ov[U];
+    // Batches of U splits with all their loads in flight (U no larger than
+    // needed: padding loads are issue slots too), in ascending split order.
+    auto run = [&](auto u_tag) {
+      constexpr int U = decltype(u_tag)::value;
+      for (int s0 = 0; s0 < splits; s0 += U) {
+        float2 ml[U];
+        float4 ov[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sp = s0 + u < splits ? s0 + u : splits - 1;
-        ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
-        ov[u] = ob[(int64_t)sp * H * (DV / 4)];
-      }
+        for (int u = 0; u < U; ++u) {
+          const int sp = s0 + u < splits ? s0 + u : splits - 1;
+          ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
+          ov[u] = ob[(int64_t)sp * H * (DV / 4)];
+        }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (s0 + u >= splits || ml[u].x == -__builtin_inff()) continue;
-        const float wgt = __builtin_amdgcn_exp2f(ml[u].x - M);
-        L += ml[u].y * wgt;
-        acc.x += ov[u].x * wgt; acc.y += ov[u].y * wgt; acc.z += ov[u].z * wgt; acc.w += ov[u].w * wgt;
+        for (int u = 0; u < U; ++u) {
+          if (s0 + u >= splits || ml[u].x == -__builtin_inff()) continue;
+          const float wgt = __builtin_amdgcn_exp2f(ml[u].x - M);
+          L += ml[u].y * wgt;
+          acc.x += ov[u].x * wgt; acc.y += ov[u].y * wgt; acc.z += ov[u].z * wgt; acc.w += ov[u].w * wgt;
+        }
       }
-    }
+    };
+    if (splits <= 2) run(std::integral_constant<int, 2>{});
+    else if (splits <= 4) run(std::integral_constant<int, 4>{});
+    else if (splits <= 8) run(std::integral_constant<int, 8>{});
+    else run(std::integral_constant<int, 16>{});
     if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
