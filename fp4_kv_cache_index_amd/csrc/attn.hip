@@ -249,11 +249,26 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     _Float16* qs = kbuf[1];
     const float4* qrow = reinterpret_cast<const float4*>(a.q + row * H * (int64_t)DQK);
     const int n4 = H * DQK / 4;
-    for (int i = threadIdx.x; i < n4; i += kAttnThreads) {
-      const float4 v = qrow[i];
-      const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
-      v2h lo = {(_Float16)v.x, (_Float16)v.y}, hi = {(_Float16)v.z, (_Float16)v.w};
-      *reinterpret_cast<uint2*>(qs + h * QP + d) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    // QB loads per thread in flight before the first conversion (one at a
+    // time, each round trip also waited for the chunk's gather loads).
+    constexpr int QB = 9;
+    for (int i0 = threadIdx.x; i0 < n4; i0 += QB * kAttnThreads) {
+      float4 v[QB];
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int i = i0 + u * kAttnThreads;
+        if (i < n4) v[u] = qrow[i];
+      }
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int i = i0 + u * kAttnThreads;
+        if (i < n4) {
+          const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
+          v2h lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
+          *reinterpret_cast<uint2*>(qs + h * QP + d) =
+              uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      }
     }
     __syncthreads();
     if (active) {
