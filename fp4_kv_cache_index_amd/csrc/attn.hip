@@ -124,13 +124,23 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     n_swa = sl < 0 ? 0 : (sl > a.W ? a.W : sl);
   }
   const int32_t* idx_row = a.topk_idx + row * (int64_t)K;
-  for (int e = e_begin + threadIdx.x; e < e_end; e += kAttnThreads) {
+  // Entry ids of the split, both loads of a thread in flight at once.
+  static_assert(kMaxSpan <= 2 * kAttnThreads, "two entries per thread");
+  int32_t ld[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = e_begin + (int)threadIdx.x + u * kAttnThreads;
+    ld[u] = e < e_end && e < K ? idx_row[e] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = e_begin + (int)threadIdx.x + u * kAttnThreads;
+    if (e >= e_end) break;
     int32_t v = -1;
     if (e < K) {
-      int64_t id = idx_row[e];
-      if (id >= 0 && id < ctx) v = (int32_t)id;
+      if (ld[u] >= 0 && ld[u] < ctx) v = ld[u];
     } else {
-      int64_t wv = e - K;
+      const int64_t wv = e - K;
       if (wv < n_swa) v = (int32_t)(swa_r0 + wv);
     }
     eid[e - e_begin] = v;
