@@ -170,7 +170,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       const int task = threadIdx.x + u * kAttnThreads;
       raw[u].kind = 0;
       if (task < NTASK) {
-        const int e = task / NB, j = task - (task / NB) * NB;
+        const int e = task / NB;
+        // The block's byte offsets are recomputed every chunk (an opaque j):
+        // hoisted out of the loop, their 64-bit addresses held registers
+        // across it and forced spills.
+        int j = task - (task / NB) * NB;
+        asm volatile("" : "+v"(j));
         const int ce = c0 + e;
         const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
         if (id >= 0 && ce < K) {
@@ -191,6 +196,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   };
   // ---- dequantise the staged bytes into fp16 K rows.
   auto store = [&](_Float16* kt) {
+    // Every staged word counts as read here, whatever the task's kind, so
+    // that no load into these registers is still pending when the next
+    // gather overwrites them (the compiler would otherwise wait there,
+    // between the gather's own loads).
+#pragma unroll
+    for (int u = 0; u < TPT; ++u)
+      asm volatile("" ::"v"(raw[u].w[0]), "v"(raw[u].w[1]), "v"(raw[u].w[2]), "v"(raw[u].w[3]), "v"(raw[u].w[4]),
+                   "v"(raw[u].w[5]), "v"(raw[u].w[6]), "v"(raw[u].w[7]), "v"(raw[u].sc));
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
@@ -455,7 +468,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 // (+ 2^(sink*log2e - M)), lse = (M + log2 L) ln 2.  One workgroup per
 // (row, head): the split maxima are reduced in parallel, then each thread
 // accumulates its four output dims over the splits in ascending order with
-// sixteen splits' loads in flight.
+// the loads of up to sixteen splits in flight.
 template <int DV>
 __global__ void __launch_bounds__(128)
 sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H,
