@@ -132,6 +132,18 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const int e = e_begin + (int)threadIdx.x + u * kAttnThreads;
     ld[u] = e < e_end && e < K ? idx_row[e] : -1;
   }
+  // q of all heads (at most 64): its loads follow the ids' and are in flight
+  // while the ids are staged; every thread issues the same number (clamped
+  // addresses), so waiting for the ids does not wait for them.
+  constexpr int QL = (64 * DQK / 4 + kAttnThreads - 1) / kAttnThreads;   // float4 loads per thread
+  const float4* qrow = reinterpret_cast<const float4*>(a.q + row * H * (int64_t)DQK);
+  const int n4 = H * DQK / 4;
+  float4 qv[QL];
+#pragma unroll
+  for (int u = 0; u < QL; ++u) {
+    const int i = (int)threadIdx.x + u * kAttnThreads;
+    qv[u] = qrow[i < n4 ? i : n4 - 1];
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int e = e_begin + (int)threadIdx.x + u * kAttnThreads;
@@ -264,35 +276,22 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  if (e_begin < e_end) gather(e_begin);
   // q of all heads through LDS (the second K buffer is free until the first
-  // iteration refills it): coalesced fp32 loads, one fp16 rounding, then each
-  // wave reads its B fragments.
+  // iteration refills it): one fp16 rounding, then each wave reads its B
+  // fragments; the first chunk's loads are issued in between.
   {
     _Float16* qs = kbuf[1];
-    const float4* qrow = reinterpret_cast<const float4*>(a.q + row * H * (int64_t)DQK);
-    const int n4 = H * DQK / 4;
-    // QB loads per thread in flight before the first conversion (one at a
-    // time, each round trip also waited for the chunk's gather loads).
-    constexpr int QB = 9;
-    for (int i0 = threadIdx.x; i0 < n4; i0 += QB * kAttnThreads) {
-      float4 v[QB];
 #pragma unroll
-      for (int u = 0; u < QB; ++u) {
-        const int i = i0 + u * kAttnThreads;
-        if (i < n4) v[u] = qrow[i];
-      }
-#pragma unroll
-      for (int u = 0; u < QB; ++u) {
-        const int i = i0 + u * kAttnThreads;
-        if (i < n4) {
-          const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
-          v2h lo = {(_Float16)v[u].x, (_Float16)v[u].y}, hi = {(_Float16)v[u].z, (_Float16)v[u].w};
-          *reinterpret_cast<uint2*>(qs + h * QP + d) =
-              uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        }
+    for (int u = 0; u < QL; ++u) {
+      const int i = (int)threadIdx.x + u * kAttnThreads;
+      if (i < n4) {
+        const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
+        v2h lo = {(_Float16)qv[u].x, (_Float16)qv[u].y}, hi = {(_Float16)qv[u].z, (_Float16)qv[u].w};
+        *reinterpret_cast<uint2*>(qs + h * QP + d) =
+            uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       }
     }
+    if (e_begin < e_end) gather(e_begin);
     __syncthreads();
     if (active) {
 #pragma unroll
