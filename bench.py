@@ -328,7 +328,7 @@ def main():
         achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": counter_traffic(dom) if wl.name == "decode64k" else None, "kernel": dom,
+                "traffic": counter_traffic(dom) if args.workload == "decode64k" else None, "kernel": dom,
                 "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     cpu = None
     if not args.no_cpu_baseline:
