@@ -9,12 +9,13 @@
 // belong to the selection, the selection is {key > T} plus the need_eq
 // lowest positions with key == T.  The producer (the scoring kernel) writes
 // the keys and a histogram of their top 12 bits.  Then:
-//   collect  -- every workgroup resolves the threshold bucket from the
-//               histogram itself, counts its tile's keys above the bucket,
+//   level1   -- (many tiles) one workgroup per row resolves the threshold
+//               bucket (the first digit) from the histogram and records it;
+//               with few tiles every collect workgroup resolves it itself;
+//   collect  -- every workgroup counts its tile's keys above the bucket,
 //               appends the bucket's keys as (key, position) candidates and
 //               lists, in position order, the tile's positions at or above
-//               the bucket (when at most kTileList of them); the row's
-//               first workgroup also records the resolved first digit;
+//               the bucket (when at most kTileList of them);
 //   finalize -- one workgroup per row finds T and need_eq among the
 //               candidates (two more radix digits, in LDS), every tile's
 //               output offset, the -1 padding and the pool length;
@@ -88,22 +89,47 @@ __device__ __forceinline__ void load_tile_keys(const uint32_t* kr, int64_t base,
   }
 }
 
+// level 1: one workgroup per row resolves the first digit from the row's
+// histogram and records it for the collect and finalize passes (rows with
+// many tiles: each collect workgroup would read the 16 KB histogram, as many
+// bytes as its keys).
+constexpr int64_t kLevel1Pass = 16384;   // collect workgroups from which the pass pays
+__global__ void __launch_bounds__(256) select_level1_kernel(SelectWs ws, int k) {
+  __shared__ uint32_t red[4], res[4];
+  const int64_t row = blockIdx.x;
+  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
+  if (threadIdx.x == 0) {
+    SelectRowCtl& c = ws.ctl[row];
+    c.l1_total = L.total; c.l1_mode = L.mode; c.l1_d = L.d; c.l1_above = L.above; c.l1_cnt = L.cnt;
+  }
+}
+
 // collect: counts above the threshold bucket per tile; appends the bucket;
 // lists the tile's positions at or above the bucket in position order.
+// With PRE the level-1 pass has recorded the first digit; otherwise every
+// workgroup resolves it from the histogram (cheaper when the row has few
+// tiles than one more launch) and the row's first one records it.
+template <bool PRE>
 __global__ void __launch_bounds__(256)
 select_collect_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_stride,
                       const int32_t* __restrict__ n_valid, int k) {
-  __shared__ uint32_t red[4], res[4];
+  __shared__ uint32_t red[4], res[PRE ? 1 : 4];
   __shared__ uint32_t slot0, ltot[2];
   const int64_t row = blockIdx.y;
   const int64_t nv = n_valid[row];
   const int64_t base = (int64_t)blockIdx.x * kSelTile;
   uint32_t kk[16];
   load_tile_keys(keys + row * key_stride, base, nv, kk);   // in flight during the resolution
-  const Level1 L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {   // published for the finalize pass
-    SelectRowCtl& c = ws.ctl[row];
-    c.l1_total = L.total; c.l1_mode = L.mode; c.l1_d = L.d; c.l1_above = L.above; c.l1_cnt = L.cnt;
+  Level1 L;
+  if constexpr (PRE) {
+    const SelectRowCtl& c = ws.ctl[row];
+    L = Level1{c.l1_total, c.l1_mode, c.l1_d, c.l1_above, c.l1_cnt};
+  } else {
+    L = resolve_level1(ws.hist1 + row * 4096, (uint32_t)k, red, res);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      SelectRowCtl& c = ws.ctl[row];
+      c.l1_total = L.total; c.l1_mode = L.mode; c.l1_d = L.d; c.l1_above = L.above; c.l1_cnt = L.cnt;
+    }
   }
   uint32_t gt = 0, nc = 0;
   uint32_t nl[4] = {0u, 0u, 0u, 0u};   // listed keys per round i
@@ -869,7 +895,14 @@ hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s) {
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
                          int64_t rows, int k, const SelectOut& out, hipStream_t s) {
   dim3 grid((unsigned)ws.tiles, (unsigned)rows);
-  CSA2_LAUNCH("select_collect", select_collect_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k);
+  if (ws.tiles * rows >= kLevel1Pass) {
+    CSA2_LAUNCH("select_level1", select_level1_kernel, dim3((unsigned)rows), dim3(256), 0, s, ws, k);
+    CSA2_LAUNCH("select_collect", select_collect_kernel<true>, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid,
+                k);
+  } else {
+    CSA2_LAUNCH("select_collect", select_collect_kernel<false>, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid,
+                k);
+  }
   CSA2_LAUNCH("select_finalize", select_finalize_kernel, dim3((unsigned)rows), dim3(256), 0, s, ws, keys, key_stride,
               n_valid, k, out);
   CSA2_LAUNCH("select_emit", select_emit_kernel, grid, dim3(256), 0, s, ws, keys, key_stride, n_valid, k, out);
