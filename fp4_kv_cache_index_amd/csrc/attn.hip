@@ -37,7 +37,8 @@
 //                 fp16 rows with the LDS transpose read (ds_read_b64_tr_b16),
 //                 so no transposed copy is stored.
 // Splits write unnormalised partial (O, m, l); a combine kernel merges them
-// with the log-sum-exp rule and adds the sink.
+// with the log-sum-exp rule and adds the sink.  A row with a single split
+// (4096-query prefill chunks) is normalised by the split kernel itself.
 #include <type_traits>
 
 #include "common.h"
@@ -443,6 +444,41 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (active && g == 0) pmx[dh][16 * hg + c16] = l_tot;
   __syncthreads();
+  if (splits == 1) {
+    // The row's only split: normalise here, with the combine's operations in
+    // its order (O * 2^(m - M), then * 1/L; L = l * 2^(m - M) + 2^(sink - M)),
+    // and write out and lse; no partials and no combine launch.
+    if (active && g == 0 && dh == 0) {
+      l_tot += pmx[1][head_b];
+      const float sk = a.sink ? a.sink[head_b] * kLog2e : -__builtin_inff();
+      const float M = fmaxf(m_run, sk);
+      float w = 0.0f, L = 0.0f;
+      if (M != -__builtin_inff()) {
+        if (m_run != -__builtin_inff()) {
+          w = __builtin_amdgcn_exp2f(m_run - M);
+          L += l_tot * w;
+        }
+        if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
+      }
+      pmx[0][head_b] = w;
+      pmx[1][head_b] = L > 0.0f ? 1.0f / L : 0.0f;
+      if (a.lse) a.lse[row * H + head_b] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+    }
+    __syncthreads();
+    if (!pv_active) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (32 * ph + 16 * t >= H) break;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 32 * ph + 16 * t + 4 * g + r;
+        const float w = pmx[0][h], inv = pmx[1][h];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) a.out[(row * H + h) * DV + 128 * dq + 16 * n + c16] = (o[t][n][r] * w) * inv;
+      }
+    }
+    return;
+  }
   const int64_t pbase = (row * splits + split) * (int64_t)H;
   if (active && g == 0 && dh == 0) {
     l_tot += pmx[1][16 * hg + c16];
@@ -554,8 +590,9 @@ static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipSt
   float* part_ml = (float*)((char*)ws + ((po + 255) & ~(size_t)255));
   CSA2_LAUNCH("sparse_attn_split", (sparse_attn_split_kernel<DQK, DV>), dim3(real_splits, (unsigned)rows),
               dim3(kAttnThreads), 0, s, a, prefill ? 1 : 0, real_splits, span, part_o, part_ml);
-  CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV>), dim3((unsigned)(rows * a.H)), dim3(128), 0,
-              s, part_o, part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+  if (real_splits > 1)   // (a single split normalises and writes the output itself)
+    CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV>), dim3((unsigned)(rows * a.H)), dim3(128), 0,
+                s, part_o, part_ml, real_splits, a.H, a.sink, a.out, a.lse);
   return hipGetLastError();
 }
 

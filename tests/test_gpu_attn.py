@@ -119,6 +119,31 @@ def test_topk_covering_context_is_dense_attention_and_sink():
 
 
 @gpu
+def test_single_split_rows_normalise_in_place():
+    """256 rows fill the chip with one workgroup each: a row's entries form a
+    single split (several chunks), which writes the normalised output and lse
+    itself; sink (one head without), invalid entries, ragged windows."""
+    require_gpu()
+    announce("attn decode 256 rows, single split per row, sink")
+    B, N, d_qk, H, K, W = 256, 400, 576, 16, 200, 32
+    kv_x, codes, scales, swa_x, sv, ss = _make_caches(B, N, d_qk, W, 24)
+    q = inputs.normal_f32((B, H, d_qk), 24, 2, "q", device="cuda")
+    idx = inputs.random_index_lists(B, K, N, 24, device="cuda", n_invalid=9)
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ctx[1::3] = N - 150
+    swa_len = torch.arange(B, dtype=torch.int32, device="cuda") % (W + 1)
+    sink = inputs.normal_f32((H,), 24, 3, "sink", device="cuda")
+    sink[5] = float("-inf")
+    scale = 1.0 / np.sqrt(576.0)
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, sv, ss, swa_len, scale, sink=sink,
+                                            want_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = _oracle_decode(np_(q), np_(kv_x), np_(idx), np_(ctx), np_(swa_x), np_(swa_len), d_qk, 512,
+                                    scale, sink=np_(sink))
+    _check(out, lse, want_o, want_l)
+
+
+@gpu
 def test_empty_entry_sets():
     require_gpu()
     announce("attn decode empty entry sets")
