@@ -66,7 +66,6 @@ __device__ __forceinline__ v8h load_f32x8_as_f16(const float* p) {
   return r;
 }
 
-constexpr int kMaxSpan = 640;       // entries per split (ids staged in LDS)
 constexpr int kAttnThreads = 512;   // 8 waves (see the mapping above)
 
 // Raw bytes of one gather task: one entry, one 32-channel block.
@@ -88,7 +87,9 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   static_assert(64 * QP <= kChunk * S::PITCH, "q staging must fit one K buffer");
   constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
   __shared__ __attribute__((aligned(16))) _Float16 kbuf[2][kChunk * S::PITCH];   // K rows, row-major, 2 chunks
-  __shared__ __attribute__((aligned(16))) int32_t eid[kMaxSpan];   // main: token id; window: window row; -1 = skip
+  // Entry ids of three chunks (the one consumed, the one being dequantised,
+  // the one being gathered): main: token id; window: window row; -1 = skip.
+  __shared__ __attribute__((aligned(16))) int32_t eidc[3][kChunk];
   __shared__ float pmx[2][64];        // per-head partial maxima / sums of the two dim halves
   __shared__ __attribute__((aligned(16))) v8h pex[8][64];   // P fragments of every S wave
   __shared__ __attribute__((aligned(16))) float alf[64];     // per-head rescale factor of the chunk
@@ -125,14 +126,17 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     n_swa = sl < 0 ? 0 : (sl > a.W ? a.W : sl);
   }
   const int32_t* idx_row = a.topk_idx + row * (int64_t)K;
-  // Entry ids of the split, both loads of a thread in flight at once.
-  static_assert(kMaxSpan <= 2 * kAttnThreads, "two entries per thread");
-  int32_t ld[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = e_begin + (int)threadIdx.x + u * kAttnThreads;
-    ld[u] = e < e_end && e < K ? idx_row[e] : -1;
-  }
+  // Validated id of entry ce (raw: its Top-K slot when ce < K).
+  auto entry_id = [&](int ce, int32_t raw) -> int32_t {
+    if (ce >= e_end) return -1;
+    if (ce < K) return raw >= 0 && raw < ctx ? raw : -1;
+    const int64_t wv = ce - K;
+    return wv < n_swa ? (int32_t)(swa_r0 + wv) : -1;
+  };
+  // Ids of the first two chunks (threads 0..127, one entry each).
+  static_assert(2 * kChunk <= kAttnThreads, "one entry per thread");
+  const int ce0 = e_begin + (int)threadIdx.x;
+  const int32_t ld0 = threadIdx.x < 2 * kChunk && ce0 < e_end && ce0 < K ? idx_row[ce0] : -1;
   // q of all heads (at most 64): its loads follow the ids' and are in flight
   // while the ids are staged; every thread issues the same number (clamped
   // addresses), so waiting for the ids does not wait for them.
@@ -145,19 +149,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const int i = (int)threadIdx.x + u * kAttnThreads;
     qv[u] = qrow[i < n4 ? i : n4 - 1];
   }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = e_begin + (int)threadIdx.x + u * kAttnThreads;
-    if (e >= e_end) break;
-    int32_t v = -1;
-    if (e < K) {
-      if (ld[u] >= 0 && ld[u] < ctx) v = ld[u];
-    } else {
-      const int64_t wv = e - K;
-      if (wv < n_swa) v = (int32_t)(swa_r0 + wv);
-    }
-    eid[e - e_begin] = v;
-  }
+  if (threadIdx.x < 2 * kChunk) eidc[threadIdx.x / kChunk][threadIdx.x % kChunk] = entry_id(ce0, ld0);
 
   // q fragments of this wave's 16 heads: lane holds head 16*hg + c16,
   // dims 32*i + 8*g .. +8 of k-step i (the B operand of S^T = K Q^T).
@@ -177,7 +169,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   const bool sc_pair = ((reinterpret_cast<uintptr_t>(a.kv_scales) | (uint64_t)a.s_bstride | (uint64_t)a.s_rstride) &
                         1u) == 0;
   RawTask raw[TPT];
-  auto gather = [&](int c0) {
+  auto gather = [&](int c0, int slot) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
@@ -190,7 +182,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         int j = task - (task / NB) * NB;
         asm volatile("" : "+v"(j));
         const int ce = c0 + e;
-        const int32_t id = ce < e_end ? eid[ce - e_begin] : -1;
+        const int32_t id = ce < e_end ? eidc[slot][e] : -1;
         if (id >= 0 && ce < K) {
           const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 16 * j);
           raw[u].w[0] = cp[0]; raw[u].w[1] = cp[1]; raw[u].w[2] = cp[2]; raw[u].w[3] = cp[3];
@@ -292,7 +284,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
             uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       }
     }
-    if (e_begin < e_end) gather(e_begin);
+    if (e_begin < e_end) gather(e_begin, 0);
     __syncthreads();
     if (active) {
 #pragma unroll
@@ -301,11 +293,16 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   }
   if (e_begin < e_end) store(kbuf[0]);
   __syncthreads();
-  if (e_begin + kChunk < e_end) gather(e_begin + kChunk);
-  int cur = 0;
-  for (int c0 = e_begin; c0 < e_end; c0 += kChunk, cur ^= 1) {
+  if (e_begin + kChunk < e_end) gather(e_begin + kChunk, 1);
+  int cur = 0, slot = 0;   // kbuf and id slot of the chunk being consumed
+  for (int c0 = e_begin; c0 < e_end; c0 += kChunk, cur ^= 1, slot = slot == 2 ? 0 : slot + 1) {
     const bool has_next = c0 + kChunk < e_end;
     const _Float16* kt = kbuf[cur];
+    const int slot2 = slot == 0 ? 2 : slot - 1;   // (slot + 2) % 3: the chunk after next
+    // Ids of the chunk after next (wave 0), stored before the first barrier.
+    const int ce2 = c0 + 2 * kChunk + lane;
+    int32_t ld2 = -1;
+    if (wave == 0 && ce2 < e_end && ce2 < K) ld2 = idx_row[ce2];
     // ---- S^T = K Q^T for this wave's 2 tiles of 16 entries: entries 32*dh ..
     float z[8];
     float cmax = -__builtin_inff();
@@ -338,7 +335,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int ce = c0 + 32 * dh + 16 * t + 4 * g + r;
-          bool ok = ce < e_end && eid[ce - e_begin] >= 0;
+          bool ok = ce < e_end && eidc[slot][ce - c0] >= 0;
           float v = ok ? st[t][r] * sl2 : -__builtin_inff();
           z[4 * t + r] = v;
           cmax = fmaxf(cmax, v);
@@ -347,6 +344,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
       if (g == 0) pmx[dh][16 * hg + c16] = cmax;
     }
+    if (wave == 0 && c0 + 2 * kChunk < e_end) eidc[slot2][lane] = entry_id(ce2, ld2);
     __syncthreads();
     float alpha = 1.0f;
     if (active) {
@@ -433,7 +431,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     // the loads of the chunk after it.
     if (has_next) {
       store(kbuf[cur ^ 1]);
-      if (c0 + 2 * kChunk < e_end) gather(c0 + 2 * kChunk);
+      if (c0 + 2 * kChunk < e_end) gather(c0 + 2 * kChunk, slot2);
     }
     __syncthreads();
   }
@@ -564,10 +562,8 @@ int attn_num_splits(int64_t rows, int k_top, int W) {
   // One resident workgroup per compute unit (LDS and registers allow one).
   int E = k_top + W;
   int max_splits = (E + 63) / 64;
-  int min_splits = (E + kMaxSpan - 1) / kMaxSpan;
   int64_t want = ((int64_t)device_cu_count() + rows - 1) / rows;
   int s = (int)(want < 1 ? 1 : (want > max_splits ? max_splits : want));
-  if (s < min_splits) s = min_splits;
   return s < 1 ? 1 : s;
 }
 
