@@ -616,21 +616,42 @@ select_local_kernel(const uint32_t* __restrict__ keys, int64_t key_stride, const
   if (nv64 > NS * NT) nv64 = NS * NT;   // (the host guarantees it)
   const int nv = (int)(nv64 < 0 ? 0 : nv64);
   const int wbase = wv * WS;            // first position of this wave
-  // Positions at or past nv read as 0.
-  const uint32_t* kr = keys + row * key_stride + wbase + lane;
+  // The first tiles' histogram words are requested before the keys, so that
+  // the first digit can be resolved while the keys stream in.
+  constexpr int TP = 8;
+  uint2 thv[TH ? TP : 1];
+  const uint2* th = TH ? reinterpret_cast<const uint2*>(tile_hist + row * th_stride * 2048) + (NT - 1 - t) : nullptr;
+  if constexpr (TH) {
+#pragma unroll
+    for (int i = 0; i < TP; ++i) thv[i] = i < tiles && nv > k ? th[i * 1024] : uint2{0u, 0u};
+  }
+  // Loads through buffer descriptors, one per 1024 positions of the wave,
+  // whose range ends at nv: positions at or past nv read as 0 without a
+  // memory access, every lane issues the same loads (no branch, so no wait
+  // between them), and the 256-byte step of s fits the instruction offset.
+  auto rsrc = [&](const void* base, int q) {
+    const int64_t rem = (int64_t)nv - (wbase + 1024 * q);
+    const int bytes = rem <= 0 ? 0 : (rem >= 1024 ? 4096 : (int)rem * 4);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  };
+  const uint32_t* kr = keys + row * key_stride + wbase;
   uint32_t kk[NS];
-  if (wbase + WS <= nv) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kk[s] = kr[64 * s];
-  } else {
+  for (int q = 0; q < NS / 16; ++q) {
+    const auto rk = rsrc(kr + 1024 * q, q);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kk[s] = wbase + 64 * s + lane < nv ? kr[64 * s] : 0u;
+    for (int s = 0; s < 16; ++s) kk[16 * q + s] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * lane + 256 * s, 0, 0);
   }
   int32_t mp[MAP ? NS : 1];
   if constexpr (MAP) {
-    const int32_t* mr = out.map + row * out.map_stride + wbase + lane;
+    const int32_t* mr = out.map + row * out.map_stride + wbase;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) mp[s] = wbase + 64 * s + lane < nv ? mr[64 * s] : 0;
+    for (int q = 0; q < NS / 16; ++q) {
+      const auto rm = rsrc(mr + 1024 * q, q);
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        mp[16 * q + s] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, 4 * lane + 256 * s, 0, 0);
+    }
   }
   // Output ids are recomputed from an opaque copy of the lane position, so
   // that the load addresses are not kept alive for them.
@@ -647,14 +668,15 @@ select_local_kernel(const uint32_t* __restrict__ keys, int64_t key_stride, const
   if (!take_all) {
     uint32_t h[4] = {0u, 0u, 0u, 0u};
     if constexpr (TH) {
-      const uint2* th = reinterpret_cast<const uint2*>(tile_hist + row * th_stride * 2048) + (NT - 1 - t);
       auto add = [&](uint2 v) {
         h[0] += v.x & 0xFFFFu;
         h[1] += v.x >> 16;
         h[2] += v.y & 0xFFFFu;
         h[3] += v.y >> 16;
       };
-      int i = 0;
+#pragma unroll
+      for (int i = 0; i < TP; ++i) add(thv[i]);
+      int i = TP;
       for (; i + 8 <= tiles; i += 8) {   // eight loads in flight
         uint2 v[8];
 #pragma unroll
