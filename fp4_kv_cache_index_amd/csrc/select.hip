@@ -75,17 +75,22 @@ __global__ void select_clear_kernel(uint32_t* p, int64_t n_words) {
 
 // The 16 keys a thread handles: positions base + 1024*i + 4*tid + j
 // (i, j = 0..3), loaded as four 16-byte vectors (coalesced across the
-// workgroup) before any of them is used.  Positions at or past nv read as 0
-// (absent); rows are padded to a multiple of 64 keys, so a vector that starts
-// below nv stays inside the row.  Ordering by (i, tid, j) is position order.
+// workgroup) before any of them is used.  The loads go through a buffer
+// descriptor whose range ends at nv rounded up to a whole vector (rows are
+// padded to a multiple of 64 keys, so that stays inside the row): every lane
+// issues the same four loads with no branch, hence no wait between them, and
+// vectors past the range read 0.  Positions at or past nv are then cleared.
+// Ordering by (i, tid, j) is position order.
 __device__ __forceinline__ void load_tile_keys(const uint32_t* kr, int64_t base, int64_t nv, uint32_t (&k)[16]) {
+  const int64_t rem = nv - base;
+  const int bytes = rem <= 0 ? 0 : (rem >= kSelTile ? 4 * kSelTile : 4 * (int)((rem + 3) & ~3LL));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kr + base), (short)0, bytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t p = base + 4 * ((int64_t)threadIdx.x + 256 * i);
-    v4u v = {0u, 0u, 0u, 0u};
-    if (p < nv) v = *reinterpret_cast<const v4u*>(kr + p);
+    const int q = 4 * ((int)threadIdx.x + 256 * i);
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * q, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k[4 * i + j] = (p + j < nv) ? v[j] : 0u;
+    for (int j = 0; j < 4; ++j) k[4 * i + j] = (base + q + j < nv) ? v[j] : 0u;
   }
 }
 
@@ -349,24 +354,33 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   if (base >= nv) return;
   const uint32_t* kr = keys + row * key_stride;
   const int64_t tix = row * tiles + blockIdx.x;
+  // The pass's control words, all requested at once.
   const uint32_t cnt = ws.tile_cnt[tix];
+  const uint32_t thr = ws.ctl[row].thr, need_eq = ws.ctl[row].need_eq;
+  const uint32_t off0 = ws.tile_off[tix];
+  const uint32_t eqb0 = ws.tile_eqb[tix];
   if (cnt != ~0u) {
     // The tile's positions at or above the threshold bucket, in position
     // order: thread t takes list entries 2t and 2t+1.
     const uint16_t* lst = ws.tlist + tix * kTileList;
-    const uint32_t thr = ws.ctl[row].thr, need_eq = ws.ctl[row].need_eq;
-    const uint32_t off0 = ws.tile_off[tix];
-    const uint32_t eqb0 = ws.tile_eqb[tix];
     uint32_t lk[2];
     int64_t lp[2];
     bool lh[2];
+    // Both list entries first (their slots always exist), then both keys
+    // from selected addresses: two round trips, with no branch between loads.
+    static_assert(2 * 256 == kTileList, "two list slots per thread");
+    uint32_t le[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) le[q] = lst[2 * threadIdx.x + q];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t c = 2 * threadIdx.x + q;
-      lh[q] = c < cnt;
-      lp[q] = base + (lh[q] ? lst[c] : 0);
-      lk[q] = lh[q] ? kr[lp[q]] : 0u;
+      lh[q] = 2 * threadIdx.x + q < cnt;
+      lp[q] = base + (lh[q] ? le[q] : 0u);
     }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lk[q] = kr[lp[q]];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lk[q] = lh[q] ? lk[q] : 0u;
     uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -410,16 +424,19 @@ select_emit_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t key_s
   }
   const int64_t p0 = base + (int64_t)threadIdx.x * PER;
   uint32_t kk[PER];
+  {
+    // (as in load_tile_keys: a descriptor ending at nv rounded up to a
+    // vector, unconditional loads, positions past nv cleared)
+    const int64_t rem = nv - base;
+    const int bytes = rem >= kSelTile ? 4 * kSelTile : 4 * (int)((rem + 3) & ~3LL);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kr + base), (short)0, bytes, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
-    v4u v = {0u, 0u, 0u, 0u};
-    if (p0 + 4 * i < nv) v = *reinterpret_cast<const v4u*>(kr + p0 + 4 * i);
+    for (int i = 0; i < PER / 4; ++i) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (PER * (int)threadIdx.x + 4 * i), 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kk[4 * i + j] = (p0 + 4 * i + j < nv) ? v[j] : 0u;
+      for (int j = 0; j < 4; ++j) kk[4 * i + j] = (p0 + 4 * i + j < nv) ? v[j] : 0u;
+    }
   }
-  const uint32_t thr = ws.ctl[row].thr, need_eq = ws.ctl[row].need_eq;
-  const uint32_t off0 = ws.tile_off[tix];
-  const uint32_t eqb0 = ws.tile_eqb[tix];
   uint32_t n_eq = 0, n_gt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
