@@ -12,26 +12,33 @@
 // gfx950 mapping.  A workgroup holds one query row and a contiguous split of
 // its entry list (Top-K rows, then the window rows); workgroups are numbered
 // so that the splits of one row land on the same XCD and share its q in L2.
-// Chunks of 64 entries are double-buffered in LDS as fp16 rows: while a
-// chunk is consumed, the next one is dequantised into the other buffer and
-// the rows of the one after it are in flight.  A gather task is one entry's
-// 32-channel block, consecutive lanes taking consecutive 16-byte pieces of a
-// row; the rows are dequantised with the gfx950 scaled converts
+// Its 8 waves take two roles.  Chunks of 32 entries pass through three fp16
+// K-row buffers in LDS: in iteration i the four S waves score chunk i, the
+// four PV waves accumulate chunk i-1, and every wave dequantises its share of
+// chunk i+1 (gathered into registers one iteration earlier) and issues the
+// loads of chunk i+2; one barrier per iteration.  The PV waves dequantise
+// before their products and the S waves after theirs, so that one role's
+// VALU work overlaps the other's matrix products.  A gather task is one
+// entry's 32-channel block, consecutive lanes taking consecutive 16-byte
+// pieces of a row; the rows are dequantised with the gfx950 scaled converts
 // (v_cvt_scalef32_pk_f16_fp4 / _fp8, which apply the power-of-two part of
-// their scale; the E4M3 scale of a main row is applied as an fp16 multiply)
-// -- exact, since E2M1 x E4M3 has at most 6 significant bits within
-// [2^-10, 2688].  q is read once per workgroup with coalesced loads, rounded
-// to fp16 once and passed through LDS into registers.  Then, per chunk,
-//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16: the 8 waves (two per SIMD) are
-//                 4 head groups of 16 heads x 2 halves of the chunk's entries,
-//                 q held in registers;
-//   online softmax in fp32 (exp2 domain); the two waves of a head group
-//                 exchange row maxima; P fragments and per-head rescale
-//                 factors go to LDS;
-//   O  += P V     on the same instruction, the waves now 2 halves of the
-//                 heads (32 each) x 4 quarters of the output dims, so every V
-//                 fragment serves two head tiles (64 fp32 accumulator
-//                 registers per lane).  P keeps the lane layout of the S^T
+// their scale; the E4M3 scales of a main row are converted to fp16 by the
+// fp8 convert and applied as an fp16 multiply) -- exact, since E2M1 x E4M3
+// has at most 6 significant bits within [2^-10, 2688].  q is read once per
+// workgroup with coalesced loads, rounded to fp16 once and passed through
+// LDS into the S waves' registers.  Per chunk,
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_f16: S wave w holds heads 16w .. +15
+//                 (q in registers) and scores all 32 entries (two tiles of
+//                 16), its K fragment reads running ahead of the products;
+//   online softmax in fp32 (exp2 domain) with a lazily moved reference
+//                 maximum: it moves only when a chunk exceeds it by more
+//                 than 2^8 (log2 units), so P stays below 256, exact to
+//                 fp16's relative precision, and O is rarely rescaled; P
+//                 fragments and per-head rescale factors go to LDS;
+//   O  += P V     on the same instruction: PV wave d holds all heads (four
+//                 16-head tiles, 128 fp32 accumulator registers per lane) and
+//                 output dims 128d .. +127, so every V fragment serves four
+//                 head tiles.  P keeps the lane layout of the S^T
 //                 accumulators (the A-operand layout once the k index is
 //                 permuted identically for V), and V is read from the same
 //                 fp16 rows with the LDS transpose read (ds_read_b64_tr_b16),
@@ -46,7 +53,8 @@
 
 namespace csa2 {
 
-constexpr int kChunk = 64;           // entries per LDS chunk
+constexpr int kChunk = 32;           // entries per LDS chunk
+constexpr float kLazy = 8.0f;        // move threshold of the reference maximum (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -80,19 +88,20 @@ __global__ void __launch_bounds__(kAttnThreads)
 sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
                          float* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = AttnShape<DQK>;
-  constexpr int NT = DV / 64;                         // output dim tiles per wave (a quarter of the dims)
+  constexpr int NT = DV / 64;                         // 16-dim output tiles per PV wave (a quarter of the dims)
   constexpr int NB = DQK / 32;                        // 32-channel blocks per row
   constexpr int NTASK = kChunk * NB;                  // (entry, block) tasks per chunk
   constexpr int QP = DQK + 8;                         // fp16 pitch of the staged q rows
-  static_assert(64 * QP <= kChunk * S::PITCH, "q staging must fit one K buffer");
+  static_assert(64 * QP <= 2 * kChunk * S::PITCH, "q staging must fit two K buffers");
   constexpr int TPT = (NTASK + kAttnThreads - 1) / kAttnThreads;
-  __shared__ __attribute__((aligned(16))) _Float16 kbuf[2][kChunk * S::PITCH];   // K rows, row-major, 2 chunks
-  // Entry ids of three chunks (the one consumed, the one being dequantised,
-  // the one being gathered): main: token id; window: window row; -1 = skip.
-  __shared__ __attribute__((aligned(16))) int32_t eidc[3][kChunk];
-  __shared__ float pmx[2][64];        // per-head partial maxima / sums of the two dim halves
-  __shared__ __attribute__((aligned(16))) v8h pex[8][64];   // P fragments of every S wave
-  __shared__ __attribute__((aligned(16))) float alf[64];     // per-head rescale factor of the chunk
+  // K rows of three chunks: the one the S waves read, the one the PV waves
+  // read as V, the one being dequantised.
+  __shared__ __attribute__((aligned(16))) _Float16 kbuf[3][kChunk * S::PITCH];
+  // Entry ids of four chunks (main: token id; window: window row; -1 = skip).
+  __shared__ __attribute__((aligned(16))) int32_t eidc[4][kChunk];
+  __shared__ __attribute__((aligned(16))) v8h pex[2][4][64];   // P fragments of the 4 S waves, 2 chunks
+  __shared__ __attribute__((aligned(16))) float alf[2][64];     // per-head rescale factor, 2 chunks
+  __shared__ float pml[2][64];                                  // epilogue: per-head (w, 1/L)
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
@@ -133,10 +142,10 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const int64_t wv = ce - K;
     return wv < n_swa ? (int32_t)(swa_r0 + wv) : -1;
   };
-  // Ids of the first two chunks (threads 0..127, one entry each).
-  static_assert(2 * kChunk <= kAttnThreads, "one entry per thread");
+  // Ids of the first three chunks (one entry per thread).
+  static_assert(3 * kChunk <= kAttnThreads, "one entry per thread");
   const int ce0 = e_begin + (int)threadIdx.x;
-  const int32_t ld0 = threadIdx.x < 2 * kChunk && ce0 < e_end && ce0 < K ? idx_row[ce0] : -1;
+  const int32_t ld0 = threadIdx.x < 3 * kChunk && ce0 < e_end && ce0 < K ? idx_row[ce0] : -1;
   // q of all heads (at most 64): its loads follow the ids' and are in flight
   // while the ids are staged; every thread issues the same number (clamped
   // addresses), so waiting for the ids does not wait for them.
@@ -149,14 +158,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const int i = (int)threadIdx.x + u * kAttnThreads;
     qv[u] = qrow[i < n4 ? i : n4 - 1];
   }
-  if (threadIdx.x < 2 * kChunk) eidc[threadIdx.x / kChunk][threadIdx.x % kChunk] = entry_id(ce0, ld0);
+  if (threadIdx.x < 3 * kChunk) eidc[threadIdx.x / kChunk][threadIdx.x % kChunk] = entry_id(ce0, ld0);
 
-  // q fragments of this wave's 16 heads: lane holds head 16*hg + c16,
-  // dims 32*i + 8*g .. +8 of k-step i (the B operand of S^T = K Q^T).
-  const int hg = wave & 3, dh = wave >> 2;
-  const bool active = 16 * hg < H;
+  // Roles: waves 0..3 are S waves (16 heads each, every entry of a chunk),
+  // waves 4..7 PV waves (every head, a quarter of the output dims each).
+  const bool s_wave = wave < 4;
+  const int hg = wave & 3;
+  const bool active = s_wave && 16 * hg < H;
   const int head_b = 16 * hg + c16;
-  v8h qf[S::KQ];
   const float sl2 = a.softmax_scale * kLog2e;
   const uint8_t* codes_b = a.kv_codes + b * a.c_bstride;
   const uint8_t* scales_b = a.kv_scales + b * a.s_bstride;
@@ -164,10 +173,10 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   const uint8_t* ss_b = a.swa_scales ? a.swa_scales + b * a.ss_bstride : nullptr;
   __syncthreads();
 
-  // ---- gather: task = (entry e, 32-channel block j), j fastest, so that
-  // consecutive lanes read consecutive 16-byte pieces of one row.
   const bool sc_pair = ((reinterpret_cast<uintptr_t>(a.kv_scales) | (uint64_t)a.s_bstride | (uint64_t)a.s_rstride) &
                         1u) == 0;
+  // ---- gather: task = (entry e, 32-channel block j), j fastest, so that
+  // consecutive lanes read consecutive 16-byte pieces of one row.
   RawTask raw[TPT];
   auto gather = [&](int c0, int slot) {
 #pragma unroll
@@ -217,12 +226,12 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       uint32_t hv[16];
       if (raw[u].kind == 1u) {
         // E2M1 -> fp16 in hardware (scale 1), then the E4M3 scale of each
-        // 16-channel group as an fp16 multiply; both steps are exact (at most
-        // 6 significant bits).
+        // 16-channel group (converted to fp16 by the fp8 convert) as an fp16
+        // multiply; every step is exact (at most 6 significant bits).
+        const v2h sc2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[u].sc, 1.0f, false);
 #pragma unroll
         for (int hgp = 0; hgp < 2; ++hgp) {
-          const _Float16 sh = (_Float16)e4m3_to_f32((raw[u].sc >> (8 * hgp)) & 0xFFu);
-          const v2h s2 = {sh, sh};
+          const v2h s2 = hgp ? __builtin_shufflevector(sc2, sc2, 1, 1) : __builtin_shufflevector(sc2, sc2, 0, 0);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const uint32_t word = raw[u].w[2 * hgp + (i >> 2)];
@@ -257,220 +266,259 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     }
   };
 
-  // O tiles: wave (ph, dq) owns heads 32*ph .. +31 (two 16-head tiles) and
-  // output dims 128*dq .. +127.
-  const int ph = wave & 1, dq = wave >> 1;
-  const bool pv_active = 32 * ph < H;
-  v4f o[2][NT];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) o[t][n] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
-
-  // q of all heads through LDS (the second K buffer is free until the first
-  // iteration refills it): one fp16 rounding, then each wave reads its B
-  // fragments; the first chunk's loads are issued in between.
-  {
-    _Float16* qs = kbuf[1];
-#pragma unroll
-    for (int u = 0; u < QL; ++u) {
-      const int i = (int)threadIdx.x + u * kAttnThreads;
-      if (i < n4) {
-        const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
-        v2h lo = {(_Float16)qv[u].x, (_Float16)qv[u].y}, hi = {(_Float16)qv[u].z, (_Float16)qv[u].w};
-        *reinterpret_cast<uint2*>(qs + h * QP + d) =
-            uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-      }
+  const int nch = e_end > e_begin ? (e_end - e_begin + kChunk - 1) / kChunk : 0;
+  // Dequantise chunk it+1 into the buffer last read as V one iteration ago,
+  // then issue the loads of chunk it+2 (every wave takes a share).
+  auto advance = [&](int it, int c0, int kb_next) {
+    if (it + 1 < nch) {
+      store(kbuf[kb_next]);
+      if (it + 2 < nch) gather(c0 + 2 * kChunk, (it + 2) & 3);
     }
-    if (e_begin < e_end) gather(e_begin, 0);
-    __syncthreads();
+  };
+
+  // q of all heads through LDS (buffers 1 and 2 are free until the first
+  // iterations refill them), rounded to fp16 once; the first chunk's loads
+  // are issued before the wait for q.
+  _Float16* qs = kbuf[1];
+  if (nch > 0) gather(e_begin, 0);
+#pragma unroll
+  for (int u = 0; u < QL; ++u) {
+    const int i = (int)threadIdx.x + u * kAttnThreads;
+    if (i < n4) {
+      const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
+      v2h lo = {(_Float16)qv[u].x, (_Float16)qv[u].y}, hi = {(_Float16)qv[u].z, (_Float16)qv[u].w};
+      *reinterpret_cast<uint2*>(qs + h * QP + d) =
+          uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
+  }
+  __syncthreads();
+
+  // Iteration it: S waves score chunk it, PV waves accumulate chunk it-1,
+  // every wave dequantises part of chunk it+1 and issues the loads of chunk
+  // it+2; one barrier per iteration.  The two roles run separate copies of
+  // the loop, so that each holds only its own state in registers.
+  if (s_wave) {
+    // ================================================================ S waves
+    v8h qf[S::KQ];
     if (active) {
 #pragma unroll
       for (int i = 0; i < S::KQ; ++i) qf[i] = *reinterpret_cast<const v8h*>(qs + head_b * QP + 32 * i + 8 * g);
     }
-  }
-  if (e_begin < e_end) store(kbuf[0]);
-  __syncthreads();
-  if (e_begin + kChunk < e_end) gather(e_begin + kChunk, 1);
-  int cur = 0, slot = 0;   // kbuf and id slot of the chunk being consumed
-  for (int c0 = e_begin; c0 < e_end; c0 += kChunk, cur ^= 1, slot = slot == 2 ? 0 : slot + 1) {
-    const bool has_next = c0 + kChunk < e_end;
-    const _Float16* kt = kbuf[cur];
-    const int slot2 = slot == 0 ? 2 : slot - 1;   // (slot + 2) % 3: the chunk after next
-    // Ids of the chunk after next (wave 0), stored before the first barrier.
-    const int ce2 = c0 + 2 * kChunk + lane;
-    int32_t ld2 = -1;
-    if (wave == 0 && ce2 < e_end && ce2 < K) ld2 = idx_row[ce2];
-    // ---- S^T = K Q^T for this wave's 2 tiles of 16 entries: entries 32*dh ..
-    float z[8];
-    float cmax = -__builtin_inff();
-    if (active) {
-      v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-      const _Float16* krow0 = kt + (32 * dh + c16) * S::PITCH + 8 * g;
-      const _Float16* krow1 = krow0 + 16 * S::PITCH;
-      constexpr int BATCH = 6;
-#pragma unroll
-      for (int i0 = 0; i0 < S::KQ; i0 += BATCH) {
-        v8h ka[BATCH], kb[BATCH];
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-          if (i0 + j < S::KQ) {
-            ka[j] = *reinterpret_cast<const v8h*>(krow0 + 32 * (i0 + j));
-            kb[j] = *reinterpret_cast<const v8h*>(krow1 + 32 * (i0 + j));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-          if (i0 + j < S::KQ) {
-            st[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[j], qf[i0 + j], st[0], 0, 0, 0);
-            st[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[j], qf[i0 + j], st[1], 0, 0, 0);
-          }
-        }
-      }
-      // st[t][r] = S^T[entry 32dh + 16t + 4g + r][head c16]
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int ce = c0 + 32 * dh + 16 * t + 4 * g + r;
-          bool ok = ce < e_end && eidc[slot][ce - c0] >= 0;
-          float v = ok ? st[t][r] * sl2 : -__builtin_inff();
-          z[4 * t + r] = v;
-          cmax = fmaxf(cmax, v);
-        }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      if (g == 0) pmx[dh][16 * hg + c16] = cmax;
-    }
-    if (wave == 0 && c0 + 2 * kChunk < e_end) eidc[slot2][lane] = entry_id(ce2, ld2);
+    float m_run = -__builtin_inff();
+    float l_run = 0.0f;
+    if (nch > 0) store(kbuf[0]);
+    if (nch > 1) gather(e_begin + kChunk, 1);
     __syncthreads();
-    float alpha = 1.0f;
-    if (active) {
-      cmax = fmaxf(cmax, pmx[dh ^ 1][16 * hg + c16]);   // max over the whole 64-entry chunk
-      const float m_new = fmaxf(m_run, cmax);
-      float psum = 0.0f;
-      v8h pa;
-      if (m_new == -__builtin_inff()) {
+    int kb = 0;
+    for (int it = 0; it <= nch; ++it) {
+      const int c0 = e_begin + it * kChunk;
+      const int pb = it & 1;
+      const int kb_next = kb == 2 ? 0 : kb + 1;
+      if (it < nch) {
+        const _Float16* kt = kbuf[kb];
+        float z[8];
+        float cmax = -__builtin_inff();
+        if (active) {
+          // Two accumulator chains per entry tile (even / odd k-steps), and
+          // the K fragment reads kept KA ahead of the products consuming them.
+          v4f sa[2][2] = {{v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}},
+                          {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}}};
+          const _Float16* krow0 = kt + c16 * S::PITCH + 8 * g;
+          const _Float16* krow1 = krow0 + 16 * S::PITCH;
+          v8h ka[S::KQ], kc[S::KQ];
+#pragma unroll
+          for (int i = 0; i < S::KQ; ++i) {
+            ka[i] = *reinterpret_cast<const v8h*>(krow0 + 32 * i);
+            kc[i] = *reinterpret_cast<const v8h*>(krow1 + 32 * i);
+          }
+#pragma unroll
+          for (int i = 0; i < S::KQ; ++i) {
+            sa[0][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i], qf[i], sa[0][i & 1], 0, 0, 0);
+            sa[1][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[i], qf[i], sa[1][i & 1], 0, 0, 0);
+          }
+          constexpr int KA = 12;
+          __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * S::KQ - KA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, KA, 0);
+          v4f st[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[t][r] = sa[t][0][r] + sa[t][1][r];
+          // st[t][r] = S^T[entry 16t + 4g + r][head c16]
+          const int4 id0 = *reinterpret_cast<const int4*>(&eidc[it & 3][4 * g]);
+          const int4 id1 = *reinterpret_cast<const int4*>(&eidc[it & 3][16 + 4 * g]);
+          const int idv[8] = {id0.x, id0.y, id0.z, id0.w, id1.x, id1.y, id1.z, id1.w};
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = idv[4 * t + r] >= 0 ? st[t][r] * sl2 : -__builtin_inff();
+              z[4 * t + r] = v;
+              cmax = fmaxf(cmax, v);
+            }
+          cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+          cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        }
+        float alpha = 1.0f;
+        v8h pa;
 #pragma unroll
         for (int i = 0; i < 8; ++i) pa[i] = (_Float16)0.0f;
-      } else {
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (active) {
+          // The reference maximum moves only when the chunk's maximum exceeds
+          // it by more than kLazy (log2 units): P stays below 2^kLazy, exact
+          // to fp16's relative precision, and the PV waves rescale O rarely.
+          const float m_new = cmax > m_run + kLazy ? cmax : m_run;
+          float psum = 0.0f;
+          if (m_new != -__builtin_inff()) {
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float p = __builtin_amdgcn_exp2f(z[i] - m_new);
-          psum += p;
-          pa[i] = (_Float16)p;
+            for (int i = 0; i < 8; ++i) {
+              float p = __builtin_amdgcn_exp2f(z[i] - m_new);
+              psum += p;
+              pa[i] = (_Float16)p;
+            }
+          }
+          l_run = l_run * alpha + psum;
+          m_run = m_new;
         }
+        pex[pb][hg][lane] = pa;
+        if (g == 0) alf[pb][16 * hg + c16] = alpha;
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      pex[wave][lane] = pa;
-    } else {
-      v8h pz;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pz[i] = (_Float16)0.0f;
-      pex[wave][lane] = pz;
+      advance(it, c0, kb_next);
+      __syncthreads();
+      kb = kb_next;
     }
-    if (dh == 0 && g == 0) alf[16 * hg + c16] = alpha;
-    __syncthreads();
-    if (pv_active) {
-      // P of head tile t for entries 32j .. (k-step j) was written by the S
-      // wave of head group 2*ph + t and entry half j.
-      v8h pf[2][2];
+    // per-head (m, l): l summed over the 4 lane groups
+    float l_tot = l_run;
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (splits == 1) {
+      // The row's only split: normalise here, with the combine's operations
+      // in its order (O * 2^(m - M), then * 1/L; L = l * 2^(m - M) +
+      // 2^(sink - M)), and write out and lse; no partials, no combine launch.
+      if (active && g == 0) {
+        const float sk = a.sink ? a.sink[head_b] * kLog2e : -__builtin_inff();
+        const float M = fmaxf(m_run, sk);
+        float w = 0.0f, L = 0.0f;
+        if (M != -__builtin_inff()) {
+          if (m_run != -__builtin_inff()) {
+            w = __builtin_amdgcn_exp2f(m_run - M);
+            L += l_tot * w;
+          }
+          if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
+        }
+        pml[0][head_b] = w;
+        pml[1][head_b] = L > 0.0f ? 1.0f / L : 0.0f;
+        if (a.lse) a.lse[row * H + head_b] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+      }
+      __syncthreads();
+      return;
+    }
+    if (active && g == 0) {
+      const int64_t pbase = (row * splits + split) * (int64_t)H;
+      part_ml[(pbase + head_b) * 2 + 0] = m_run;
+      part_ml[(pbase + head_b) * 2 + 1] = l_tot;
+    }
+    return;
+  }
+
+  // ================================================================ PV waves
+  // Wave dq owns all heads (4 tiles of 16) and output dims 128*dq .. +127.
+  const int dq = wave & 3;
+  v4f o[4][NT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) pf[t][j] = pex[2 * ph + t + 4 * j][lane];
-      float4 al[2];
-      al[0] = *reinterpret_cast<const float4*>(&alf[32 * ph + 4 * g]);
-      al[1] = *reinterpret_cast<const float4*>(&alf[32 * ph + 16 + 4 * g]);
-      if (!__all(al[0].x == 1.0f && al[0].y == 1.0f && al[0].z == 1.0f && al[0].w == 1.0f && al[1].x == 1.0f &&
-                 al[1].y == 1.0f && al[1].z == 1.0f && al[1].w == 1.0f)) {
+    for (int n = 0; n < NT; ++n) o[t][n] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Wave 4 keeps the raw ids of chunk it+3 in flight: issued before the
+  // loads of chunk it+1, so the dequantisation's wait for those covers them,
+  // and no wait for the gather is needed anywhere else in the loop.
+  const bool id_lane = wave == 4 && lane < kChunk && K > 0;
+  int32_t ldn = 0;
+  if (id_lane) {
+    const int ce = e_begin + 3 * kChunk + lane;
+    ldn = idx_row[ce < K ? ce : K - 1];
+  }
+  if (nch > 0) store(kbuf[0]);
+  if (nch > 1) gather(e_begin + kChunk, 1);
+  __syncthreads();
+  int kb = 0;
+  for (int it = 0; it <= nch; ++it) {
+    const int c0 = e_begin + it * kChunk;
+    const int pb = it & 1;
+    const int kb_prev = kb == 0 ? 2 : kb - 1, kb_next = kb == 2 ? 0 : kb + 1;
+    // The dequantisation comes first here (the S waves end with it), so
+    // that one role's VALU work overlaps the other's products.
+    if (it + 1 < nch) {
+      store(kbuf[kb_next]);
+      if (id_lane) {
+        const int ce = c0 + 3 * kChunk + lane;
+        if (it + 3 < nch) eidc[(it + 3) & 3][lane] = entry_id(ce, ldn);
+        const int cn = ce + kChunk;
+        ldn = idx_row[cn < K ? cn : K - 1];
+      }
+      if (it + 2 < nch) gather(c0 + 2 * kChunk, (it + 2) & 3);
+    }
+    if (it >= 1) {
+      // O += P V for chunk it-1; k index: entries {4g..4g+3, 16+4g..16+4g+3},
+      // the lane layout of the S^T accumulators.
+      const _Float16* kt = kbuf[kb_prev];
+      // V from the row-major K rows with the LDS transpose read: in each
+      // 16-lane group, source lane s names entry (.. + s/4), dims
+      // 4(s%4)..+3, and lane i receives dim i of those four entries.  Read
+      // first: V does not depend on this chunk's P.
+      const int s16 = lane & 15;
+      const _Float16* vbase = kt + (4 * g + (s16 >> 2)) * S::PITCH + 128 * dq + 4 * (s16 & 3);
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      v8h vf[NT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int n = 0; n < NT; ++n) {
+        const _Float16* vp = vbase + 16 * n;
+        v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vp));
+        v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vp + 16 * S::PITCH));
+        vf[n] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      v8h pf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pf[t] = pex[pb ^ 1][t][lane];
+      float4 al[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const float4*>(&alf[pb ^ 1][16 * t + 4 * g]);
+      bool ones = true;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        ones = ones && al[t].x == 1.0f && al[t].y == 1.0f && al[t].z == 1.0f && al[t].w == 1.0f;
+      if (!__all(ones)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             o[t][n][0] *= al[t].x; o[t][n][1] *= al[t].y; o[t][n][2] *= al[t].z; o[t][n][3] *= al[t].w;
           }
       }
-      // ---- O += P V over dims 128*dq ..; k-step j: entries 32j + {4g..4g+3, 16+4g..16+4g+3}.
-      // V is read from the row-major K rows with the LDS transpose read: in each
-      // 16-lane group, source lane s names entry (.. + s/4), dims 4(s%4)..+3, and
-      // lane i receives dim i of those four entries.  Each V fragment serves both
-      // head tiles.
-      const int s16 = lane & 15;
-      const _Float16* vbase = kt + (4 * g + (s16 >> 2)) * S::PITCH + 128 * dq + 4 * (s16 & 3);
-      typedef short v4s __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) v4s* lds_v4s;
-      constexpr int VB = 4;
 #pragma unroll
-      for (int n0 = 0; n0 < NT; n0 += VB) {
-        v8h vf[VB][2];
+      for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int jn = 0; jn < VB; ++jn) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const _Float16* vp = vbase + 32 * j * S::PITCH + 16 * (n0 + jn);
-            v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vp));
-            v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(vp + 16 * S::PITCH));
-            vf[jn][j] = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-        }
-#pragma unroll
-        for (int jn = 0; jn < VB; ++jn)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            o[t][n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[t][0], vf[jn][0], o[t][n0 + jn], 0, 0, 0);
-            o[t][n0 + jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[t][1], vf[jn][1], o[t][n0 + jn], 0, 0, 0);
-          }
-      }
-    }
-    // Next chunk into the other buffer (last read one iteration ago), then
-    // the loads of the chunk after it.
-    if (has_next) {
-      store(kbuf[cur ^ 1]);
-      if (c0 + 2 * kChunk < e_end) gather(c0 + 2 * kChunk, slot2);
+        for (int t = 0; t < 4; ++t) o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[t], vf[n], o[t][n], 0, 0, 0);
     }
     __syncthreads();
+    kb = kb_next;
   }
-
-  // ---- partial results: l summed over the 4 lane groups and both dim halves
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (active && g == 0) pmx[dh][16 * hg + c16] = l_tot;
-  __syncthreads();
   if (splits == 1) {
-    // The row's only split: normalise here, with the combine's operations in
-    // its order (O * 2^(m - M), then * 1/L; L = l * 2^(m - M) + 2^(sink - M)),
-    // and write out and lse; no partials and no combine launch.
-    if (active && g == 0 && dh == 0) {
-      l_tot += pmx[1][head_b];
-      const float sk = a.sink ? a.sink[head_b] * kLog2e : -__builtin_inff();
-      const float M = fmaxf(m_run, sk);
-      float w = 0.0f, L = 0.0f;
-      if (M != -__builtin_inff()) {
-        if (m_run != -__builtin_inff()) {
-          w = __builtin_amdgcn_exp2f(m_run - M);
-          L += l_tot * w;
-        }
-        if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
-      }
-      pmx[0][head_b] = w;
-      pmx[1][head_b] = L > 0.0f ? 1.0f / L : 0.0f;
-      if (a.lse) a.lse[row * H + head_b] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
-    }
-    __syncthreads();
-    if (!pv_active) return;
+    __syncthreads();   // the S waves' (w, 1/L)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (32 * ph + 16 * t >= H) break;
+    for (int t = 0; t < 4; ++t) {
+      if (16 * t >= H) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int h = 32 * ph + 16 * t + 4 * g + r;
-        const float w = pmx[0][h], inv = pmx[1][h];
+        const int h = 16 * t + 4 * g + r;
+        const float w = pml[0][h], inv = pml[1][h];
 #pragma unroll
         for (int n = 0; n < NT; ++n) a.out[(row * H + h) * DV + 128 * dq + 16 * n + c16] = (o[t][n][r] * w) * inv;
       }
@@ -478,20 +526,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     return;
   }
   const int64_t pbase = (row * splits + split) * (int64_t)H;
-  if (active && g == 0 && dh == 0) {
-    l_tot += pmx[1][16 * hg + c16];
-    part_ml[(pbase + head_b) * 2 + 0] = m_run;
-    part_ml[(pbase + head_b) * 2 + 1] = l_tot;
-  }
-  if (!pv_active) return;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    if (32 * ph + 16 * t >= H) break;
+  for (int t = 0; t < 4; ++t) {
+    if (16 * t >= H) break;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int h = 32 * ph + 16 * t + 4 * g + r;
+        const int h = 16 * t + 4 * g + r;
         part_o[(pbase + h) * DV + 128 * dq + 16 * n + c16] = o[t][n][r];
       }
   }
