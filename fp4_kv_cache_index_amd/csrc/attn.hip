@@ -46,7 +46,6 @@
 // Splits write unnormalised partial (O, m, l); a combine kernel merges them
 // with the log-sum-exp rule and adds the sink.  A row with a single split
 // (4096-query prefill chunks) is normalised by the split kernel itself.
-#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -541,62 +540,85 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 
 // Merge split partials: out = sum_s O_s 2^(m_s - M) / L, L = sum_s l_s 2^(m_s - M)
 // (+ 2^(sink*log2e - M)), lse = (M + log2 L) ln 2.  One workgroup per
-// (row, head): the split maxima are reduced in parallel, then each thread
-// accumulates its four output dims over the splits in ascending order with
-// the loads of up to sixteen splits in flight.
-template <int DV>
-__global__ void __launch_bounds__(128)
+// (row, head) of G groups of DV/DPL threads (DPL output dims per thread):
+// every wave reduces the split maxima itself, then group k accumulates
+// splits k, k + G, ... with the loads of U of them in flight, and the
+// groups' sums are added in group order through LDS.  G, U and DPL follow
+// the split count, so that a row's splits are usually read in one round
+// trip without padding loads.
+template <int DV, int U, int DPL, int MAXG>
+__global__ void __launch_bounds__(512)
 sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H,
                            const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse) {
-  static_assert(DV == 4 * 128, "one float4 of output dims per thread");
-  __shared__ float red[2];
+  constexpr int GT = DV / DPL;              // threads per group
+  constexpr int NV = DPL / 4;               // float4 per thread and split
+  static_assert(DPL % 4 == 0 && GT % 64 == 0, "whole waves of float4 columns");
+  __shared__ float4 accs[(MAXG - 1) * GT * NV + 1];   // sums of groups 1..G-1 (G <= MAXG)
+  __shared__ float lsum[MAXG];
   const int64_t rh = blockIdx.x;            // row * H + h
   const int h = (int)(rh % H);
   const int64_t row = rh / H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int grp = threadIdx.x / GT, gl = threadIdx.x % GT;
+  const int G = blockDim.x / GT;
   const float sk = sink ? sink[h] * kLog2e : -__builtin_inff();
   const float* mlb = part_ml + (row * splits * (int64_t)H + h) * 2;   // split s at mlb[2 * s * H]
   float mx = -__builtin_inff();
-  for (int sp = threadIdx.x; sp < splits; sp += 128) mx = fmaxf(mx, mlb[2 * (int64_t)sp * H]);
+  for (int sp = lane; sp < splits; sp += 64) mx = fmaxf(mx, mlb[2 * (int64_t)sp * H]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), sk);
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float M = fmaxf(mx, sk);
+  float4 acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = float4{0.f, 0.f, 0.f, 0.f};
   float L = 0.0f;
   if (M != -__builtin_inff()) {
-    const float4* ob = reinterpret_cast<const float4*>(part_o + (row * splits * (int64_t)H + h) * DV) + threadIdx.x;
-    // Batches of U splits with all their loads in flight (U no larger than
-    // needed: padding loads are issue slots too), in ascending split order.
-    auto run = [&](auto u_tag) {
-      constexpr int U = decltype(u_tag)::value;
-      for (int s0 = 0; s0 < splits; s0 += U) {
-        float2 ml[U];
-        float4 ov[U];
+    const float4* ob = reinterpret_cast<const float4*>(part_o + (row * splits * (int64_t)H + h) * DV) + NV * gl;
+    for (int s0 = grp; s0 < splits; s0 += G * U) {
+      float2 ml[U];
+      float4 ov[U][NV];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int sp = s0 + u < splits ? s0 + u : splits - 1;
-          ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
-          ov[u] = ob[(int64_t)sp * H * (DV / 4)];
-        }
+      for (int u = 0; u < U; ++u) {
+        const int sp = s0 + u * G < splits ? s0 + u * G : s0;
+        ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (s0 + u >= splits || ml[u].x == -__builtin_inff()) continue;
-          const float wgt = __builtin_amdgcn_exp2f(ml[u].x - M);
-          L += ml[u].y * wgt;
-          acc.x += ov[u].x * wgt; acc.y += ov[u].y * wgt; acc.z += ov[u].z * wgt; acc.w += ov[u].w * wgt;
+        for (int v = 0; v < NV; ++v) ov[u][v] = ob[(int64_t)sp * H * (DV / 4) + v];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u * G >= splits || ml[u].x == -__builtin_inff()) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ml[u].x - M);
+        L += ml[u].y * wgt;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          acc[v].x += ov[u][v].x * wgt; acc[v].y += ov[u][v].y * wgt;
+          acc[v].z += ov[u][v].z * wgt; acc[v].w += ov[u][v].w * wgt;
         }
       }
-    };
-    if (splits <= 2) run(std::integral_constant<int, 2>{});
-    else if (splits <= 4) run(std::integral_constant<int, 4>{});
-    else if (splits <= 8) run(std::integral_constant<int, 8>{});
-    else run(std::integral_constant<int, 16>{});
-    if (sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
+    }
   }
+  if (MAXG > 1 && G > 1) {
+    if (grp > 0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) accs[((grp - 1) * NV + v) * GT + gl] = acc[v];
+      if (gl == 0) lsum[grp] = L;
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    for (int k = 1; k < G; ++k) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float4 x = accs[((k - 1) * NV + v) * GT + gl];
+        acc[v].x += x.x; acc[v].y += x.y; acc[v].z += x.z; acc[v].w += x.w;
+      }
+      L += lsum[k];
+    }
+  }
+  if (M != -__builtin_inff() && sk != -__builtin_inff()) L += __builtin_amdgcn_exp2f(sk - M);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  reinterpret_cast<float4*>(out + rh * DV)[threadIdx.x] = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  float4* op = reinterpret_cast<float4*>(out + rh * DV) + NV * gl;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) op[v] = float4{acc[v].x * inv, acc[v].y * inv, acc[v].z * inv, acc[v].w * inv};
   if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
@@ -628,9 +650,26 @@ static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipSt
   float* part_ml = (float*)((char*)ws + ((po + 255) & ~(size_t)255));
   CSA2_LAUNCH("sparse_attn_split", (sparse_attn_split_kernel<DQK, DV>), dim3(real_splits, (unsigned)rows),
               dim3(kAttnThreads), 0, s, a, prefill ? 1 : 0, real_splits, span, part_o, part_ml);
-  if (real_splits > 1)   // (a single split normalises and writes the output itself)
-    CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV>), dim3((unsigned)(rows * a.H)), dim3(128), 0,
-                s, part_o, part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+  if (real_splits > 1) {   // (a single split normalises and writes the output itself)
+    // Up to 4 splits: one group of 128 threads (4 dims each) with every
+    // split in flight; more: groups of 64 threads (8 dims each) over up to
+    // 4 or 8 splits each.
+    const dim3 grid((unsigned)(rows * a.H));
+    if (real_splits <= 4) {
+      CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV, 4, 4, 1>), grid, dim3(DV / 4), 0, s, part_o,
+                  part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+    } else {
+      const int U = real_splits <= 16 ? 4 : 8;
+      int G = (real_splits + U - 1) / U;
+      if (G > 8) G = 8;
+      if (U == 4)
+        CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV, 4, 8, 8>), grid, dim3(64 * G), 0, s, part_o,
+                    part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+      else
+        CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV, 8, 8, 8>), grid, dim3(64 * G), 0, s, part_o,
+                    part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+    }
+  }
   return hipGetLastError();
 }
 
