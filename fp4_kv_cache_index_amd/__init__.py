@@ -345,18 +345,25 @@ class KernelTrace:
     launch instead of two per library launch).
     """
 
-    def __init__(self, capacity=4096, only=None):
+    # hipEventDisableSystemFence: the events only carry timestamps, so they
+    # need no system-scope acquire / release around the timed dispatch (with
+    # it, each traced launch paid an L2 write-back inside its own timing and
+    # a gap of several microseconds before the next kernel).
+    EVENT_FLAGS = 0x20000000
+
+    def __init__(self, capacity=4096, only=None, flags=None):
         self.capacity = capacity
         self.only = only
         self._hip = ctypes.CDLL("libamdhip64.so")
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(c_void_p)]
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(c_void_p), ctypes.c_uint]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), c_void_p, c_void_p]
         self._hip.hipEventDestroy.argtypes = [c_void_p]
+        fl = self.EVENT_FLAGS if flags is None else flags
         self.events = (c_void_p * (2 * capacity))()
         for i in range(2 * capacity):
             e = c_void_p()
-            if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(e), fl) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.events[i] = e
         self.names = (ctypes.c_char_p * capacity)()
         self.count = 0
