@@ -35,8 +35,8 @@ METRIC = "CSA2 decode queries/s + achieved HBM GB/s (% peak), 64K–1M ctx"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="decode64k")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=0, help="sequences timed for the CPU baseline (0 = auto)")
