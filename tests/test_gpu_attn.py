@@ -97,6 +97,28 @@ def test_decode_shapes_invalid_entries_and_ragged_windows(d_qk, H, K, W, n_inval
 
 
 @gpu
+def test_rising_scores_move_the_softmax_reference():
+    """Entries ordered by rising head-0 score and a large softmax scale: the
+    running maximum of that head moves by more than 2^8 (log2 units) in many
+    chunks of a split, so the accumulated O is rescaled between chunks, and
+    the other heads see random orders.  q takes quarter steps, exact in fp16,
+    so at this scale the logits still meet the tolerance."""
+    require_gpu()
+    announce("attn decode rising scores B64 K1024 scale 0.5")
+    B, N, d_qk, H, K = 64, 1100, 576, 64, 1024
+    kv_x, codes, scales, _, _, _ = _make_caches(B, N, d_qk, 0, 31)
+    q = (torch.round(inputs.normal_f32((B, H, d_qk), 31, 2, "q", device="cuda") * 4) / 4).contiguous()
+    s0 = torch.bmm(kv_x, q[:, 0, :, None].contiguous()).squeeze(-1)
+    idx = torch.argsort(s0, dim=1)[:, N - K:].to(torch.int32).contiguous()   # top K, ascending
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    scale = 0.5
+    out, lse = csa2.csa2_sparse_attn_decode(q, codes, scales, idx, ctx, None, None, None, scale, want_lse=True)
+    torch.cuda.synchronize()
+    want_o, want_l = _oracle_decode(np_(q), np_(kv_x), np_(idx), np_(ctx), None, None, d_qk, 512, scale)
+    _check(out, lse, want_o, want_l)
+
+
+@gpu
 def test_topk_covering_context_is_dense_attention_and_sink():
     require_gpu()
     announce("attn decode K >= N (dense) with sink")
