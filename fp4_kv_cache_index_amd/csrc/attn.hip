@@ -623,9 +623,12 @@ sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __rest
 }
 
 int attn_num_splits(int64_t rows, int k_top, int W) {
-  // One resident workgroup per compute unit (LDS and registers allow one).
+  // One resident workgroup per compute unit (LDS and registers allow one),
+  // but at least 128 entries (four chunks) per split: with fewer rows than
+  // compute units, shorter splits took no less time each and only added
+  // partials for the combine.
   int E = k_top + W;
-  int max_splits = (E + 63) / 64;
+  int max_splits = (E + 127) / 128;
   int64_t want = ((int64_t)device_cu_count() + rows - 1) / rows;
   int s = (int)(want < 1 ? 1 : (want > max_splits ? max_splits : want));
   return s < 1 ? 1 : s;
