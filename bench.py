@@ -165,7 +165,7 @@ class Case:
                 idx = self.topk[li]
             elif kind == "pool":
                 csa2.csa2_hier_pool_topk(L["q_idx"], L["w"], self.k_idx, self.pool_idx, self.pool_len, wl.K,
-                                         workspace=self.ws_pool, out={"topk_idx": self.topk[li]})
+                                         ctx_len=self.ctx, workspace=self.ws_pool, out={"topk_idx": self.topk[li]})
                 idx = self.topk[li]
             elif kind == "reuse":
                 idx = prev

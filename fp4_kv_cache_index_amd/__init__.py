@@ -34,7 +34,7 @@ _SIGS = {
                                              c_void_p]),
     "csa2_hier_pool_topk_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "csa2_hier_pool_topk": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
-                                           c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                           c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                            c_void_p, c_size_t, c_void_p]),
     "csa2_sparse_attn_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "csa2_sparse_attn_decode": (ctypes.c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64,
@@ -212,10 +212,13 @@ def csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top):
     return lib().csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top)
 
 
-def csa2_hier_pool_topk(q_idx, w, k_idx, pool_idx, pool_len, k_top, want_scores=False, workspace=None, out=None):
+def csa2_hier_pool_topk(q_idx, w, k_idx, pool_idx, pool_len, k_top, ctx_len=None, want_scores=False,
+                        workspace=None, out=None):
     """Later hierarchical layer: Top-K over the pool tokens only.
 
-    pool_idx [B][Tq][pool_cap] i32 ascending token ids, pool_len [B][Tq] i32.
+    pool_idx [B][Tq][pool_cap] i32 ascending token ids, pool_len [B][Tq] i32,
+    ctx_len [B] i32 (default: every sequence holds k_idx.shape[1] rows); pool
+    ids outside [0, ctx_len[b]) are skipped.
     Returns dict(topk_idx [B][Tq][k_top], topk_score or None).
     """
     _gpu(q_idx, "q_idx", torch.uint8)
@@ -229,6 +232,9 @@ def csa2_hier_pool_topk(q_idx, w, k_idx, pool_idx, pool_len, k_top, want_scores=
     pool_cap = pool_idx.shape[-1]
     kb, kr = _row_strides(k_idx, "k_idx")
     dev = q_idx.device
+    if ctx_len is None:
+        ctx_len = torch.full((B,), k_idx.shape[1], dtype=torch.int32, device=dev)
+    _gpu(ctx_len, "ctx_len", torch.int32)
     out = out or {}
     topk_idx = out.get("topk_idx")
     if topk_idx is None:
@@ -238,7 +244,7 @@ def csa2_hier_pool_topk(q_idx, w, k_idx, pool_idx, pool_len, k_top, want_scores=
         topk_score = torch.empty(B, Tq, k_top, dtype=torch.float32, device=dev)
     need = csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top)
     ws, ws_bytes = _workspace(need, dev, workspace)
-    _check(lib().csa2_hier_pool_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), kb, kr, _ptr(pool_idx), _ptr(pool_len),
+    _check(lib().csa2_hier_pool_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), kb, kr, _ptr(ctx_len), _ptr(pool_idx), _ptr(pool_len),
                                      pool_cap, B, Tq, H_I, D_I, k_top, _ptr(topk_idx), _ptr(topk_score), _ptr(ws),
                                      ws_bytes, _stream(dev)), "csa2_hier_pool_topk")
     return {"topk_idx": topk_idx, "topk_score": topk_score}

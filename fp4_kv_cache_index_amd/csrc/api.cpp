@@ -228,12 +228,12 @@ size_t csa2_hier_pool_topk_workspace_size(int32_t B, int32_t Tq, int32_t pool_ca
 }
 
 int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_batch_stride,
-                        int64_t k_row_stride, const int32_t* pool_idx, const int32_t* pool_len, int32_t pool_cap,
+                        int64_t k_row_stride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int32_t pool_cap,
                         int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int32_t k_top, int32_t* topk_idx,
                         float* topk_score, void* ws, size_t ws_bytes, void* stream) {
   if (B < 0 || Tq < 0 || pool_cap < 0 || k_top <= 0 || H_I <= 0 || D_I <= 0) return CSA2_EINVAL;
   if (B == 0 || Tq == 0) return CSA2_OK;
-  if (!q_idx || !w || !k_idx || !pool_idx || !pool_len || !topk_idx || !ws) return CSA2_EINVAL;
+  if (!q_idx || !w || !k_idx || !ctx_len || !pool_idx || !pool_len || !topk_idx || !ws) return CSA2_EINVAL;
   if (D_I % 32 != 0 || k_row_stride < D_I || k_batch_stride < 0) return CSA2_EINVAL;
   if (!aligned4(k_idx) || !aligned4(q_idx) || (k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
   if (((uintptr_t)ws & 255u) != 0) return CSA2_EINVAL;
@@ -258,14 +258,14 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
     // add up).
     SelectWs none = sw;
     none.hist1 = nullptr;
-    hipError_t e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B,
+    hipError_t e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, pool_idx, pool_len, pool_cap, B,
                                      Tq, H_I, D_I, k_top, keys, cap, n_valid, none, s);
     if (e == hipSuccess) e = select_local(keys, cap, n_valid, rows, k_top, pool_cap, nullptr, 0, 0, out, s);
     return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
   }
   hipError_t e = select_clear(sw, rows, s);
   if (e == hipSuccess)
-    e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, pool_idx, pool_len, pool_cap, B, Tq, H_I,
+    e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, pool_idx, pool_len, pool_cap, B, Tq, H_I,
                           D_I, k_top, keys, cap, n_valid, sw, s);
   if (e == hipSuccess) e = select_finish(sw, keys, cap, n_valid, rows, k_top, out, s);
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;

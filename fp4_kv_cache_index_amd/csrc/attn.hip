@@ -1,8 +1,8 @@
 // Sparse MLA attention over the Top-K FP4 main-KV rows plus the FP8 window.
 //
 // What it computes (DeepSeek-V4.1-Flash techniques map, "Checked in its
-// code": multi-head latent attention with a single latent KV head and a
-// learnable per-head sink logit in the sparse-MLA softmax denominator; fact
+// code": multi-head latent attention with one latent KV head, and one
+// trainable logit per head that enters only the softmax normaliser; fact
 // sheet: one shared K=V entry per token, a 128-token window per layer; blog,
 // CSA2 paragraph: attention runs over the indexer's Top-K entries of the FP4
 // main cache): for each query row and head h, softmax over the selected

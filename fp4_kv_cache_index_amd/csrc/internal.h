@@ -133,7 +133,7 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
 int64_t index_score_tiles(const ScoreArgs& a);
 int64_t index_score_tiles_bound(int64_t n_max);
 hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                             int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                             int64_t k_rstride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
                              int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
                              int32_t* n_valid, const SelectWs& ws, hipStream_t s);
 

@@ -79,7 +79,9 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 }
 
 // GATHER = false: tokens j = tile positions of the row (flat scan).
-// GATHER = true : position p maps to token pool_idx[row][p] (pool layers).
+// GATHER = true : position p maps to token pool_idx[row][p] (pool layers);
+//                 a pool id outside [0, ctx_len[b]) names no token: the
+//                 position is not visible (key 0) and its loads read row 0.
 template <int DI, int HB, bool GATHER, bool POOL, bool H8>
 __global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB>))
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -145,14 +147,15 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   if (wend > n_max) wend = n_max;
   int64_t wlast = wend - 1;
 
+  // (pool ids are staged as -1 when invalid: their loads read row 0)
   auto frag_ptr = [&](int64_t pos) -> const uint8_t* {
     const int64_t p = pos < wend ? pos : wlast;
-    const int64_t tokid = GATHER ? (int64_t)ptok[p - tile0] : p;
+    const int64_t tokid = GATHER ? (int64_t)max(ptok[p - tile0], 0) : p;
     return frag_base<DI>(kb + tokid * k_rstride, g);
   };
   auto full_ptr = [&](int64_t pos) -> const uint8_t* {
     const int64_t p = pos < wend ? pos : wlast;
-    const int64_t tokid = GATHER ? (int64_t)ptok[p - tile0] : p;
+    const int64_t tokid = GATHER ? (int64_t)max(ptok[p - tile0], 0) : p;
     return kb + tokid * k_rstride + 16 * (2 * g + (c16 & 1));
   };
 
@@ -202,8 +205,11 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // stream starts while these are in flight (the vector-memory counter
   // retires in order: waiting for them below does not wait for the keys).
   int64_t craw;
-  if (GATHER) craw = pool_len[row];
-  else {
+  int64_t ctx_b = 0;   // pool layers: ids at or past it name no token
+  if (GATHER) {
+    craw = pool_len[row];
+    ctx_b = ctx_len[b];
+  } else {
     craw = ctx_len[b];
     if (q_pos) {
       const int64_t qp = (int64_t)q_pos[row] + 1;
@@ -260,7 +266,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   const float wload = threadIdx.x < HMAX && threadIdx.x < H_I ? wraw : 0.0f;
 
   int64_t nv;
-  if (GATHER) nv = craw < 0 ? 0 : (craw > pool_cap ? pool_cap : craw);
+  if (GATHER) nv = (craw < 0 || ctx_b <= 0) ? 0 : (craw > pool_cap ? pool_cap : craw);
   else nv = craw < 0 ? 0 : (craw > n_max ? n_max : craw);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     n_valid_out[row] = (int32_t)nv;
@@ -281,7 +287,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     const int32_t* prow = pool_idx + row * (int64_t)pool_cap;
     for (int i = threadIdx.x; i < tile; i += NT) {
       const int64_t p = tile0 + i;
-      ptok[i] = p < nv ? prow[p] : 0;
+      const int32_t id = p < nv ? prow[p] : -1;
+      ptok[i] = (id >= 0 && id < ctx_b) ? id : -1;
     }
     __syncthreads();
   }
@@ -337,7 +344,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     for (int u = 0; u < SG / 4; ++u) {
       // Lane owns token it + 64u + lane.
       const int64_t j = it + 64 * u + lane;
-      const bool vis = j < wend;
+      bool vis = j < wend;
+      if constexpr (GATHER) vis = vis && ptok[j < wend ? j - tile0 : 0] >= 0;
       float sc = 0.0f;
       const float* src = my + (64 * u + lane) * pitch;
 #pragma unroll
@@ -453,7 +461,7 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
 
 template <int DI, int HB, bool H8>
 static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                                int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                                int64_t k_rstride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
                                 int B, int Tq, int H_I, int k_top, uint32_t* keys, int64_t key_stride,
                                 int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
   int64_t rows = (int64_t)B * Tq;
@@ -461,7 +469,7 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
   if (tiles < 1) tiles = 1;
   CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8>), dim3((unsigned)tiles, (unsigned)rows),
               dim3(64 * kScanWavesT<true, HB>),
-              0, s, q_idx, w, k_idx, k_bstride, k_rstride, (const int32_t*)nullptr, (const int32_t*)nullptr,
+              0, s, q_idx, w, k_idx, k_bstride, k_rstride, ctx_len, (const int32_t*)nullptr,
               pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, key_stride, n_valid, ws,
               0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
   return hipGetLastError();
@@ -865,11 +873,11 @@ int64_t index_score_tiles_bound(int64_t n_max) {
 }
 
 hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                             int64_t k_rstride, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                             int64_t k_rstride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
                              int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
                              int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
 #define CALL_POOL(D, H, E) \
-  launch_pool_t<D, H, E>(q_idx, w, k_idx, k_bstride, k_rstride, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
+  launch_pool_t<D, H, E>(q_idx, w, k_idx, k_bstride, k_rstride, ctx_len, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
                       key_stride, n_valid, ws, s)
   CSA2_DISPATCH_DI_HB(D_I, H_I, CALL_POOL);
 #undef CALL_POOL

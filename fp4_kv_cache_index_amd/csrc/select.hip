@@ -329,11 +329,15 @@ select_finalize_kernel(SelectWs ws, const uint32_t* __restrict__ keys, int64_t k
     for (int64_t i = (int64_t)total * out.expand + threadIdx.x; i < cap; i += 256) oi[i] = -1;
     if (threadIdx.x == 0) {
       // Only the last block of the row can be partial; it is selected when
-      // it is above T, or at T with every tie taken (it is the last tie).
+      // it is above T, or at T when ties are taken at all and every one of
+      // them is (it is the last tie).  With need_eq == 0, T is the key just
+      // below the selection (a whole bucket or sub-bucket taken), and a
+      // block whose key equals it is not selected.
       int32_t len = (int32_t)(total * out.expand);
       if (nv > 0) {
         const uint32_t klast = keys[row * key_stride + nv - 1];
-        const bool sel_last = L.mode == 1u || klast > thr || (klast == thr && eq_all <= need_eq);
+        const bool sel_last =
+            L.mode == 1u || klast > thr || (klast == thr && need_eq > 0u && eq_all <= need_eq);
         if (sel_last) len -= (int32_t)(nv * out.expand - out.expand_limit[row]);
       }
       out.pool_len[row] = len;

@@ -17,9 +17,10 @@
  *     reuse Top-K indices; a hierarchical indexer restricts later layers to a
  *     candidate pool chosen by the first Full layer (blog, CSA2 paragraph;
  *     fact sheet, token selection: 2048-block x 8-position pool).
- *   - Sparse MLA attention with one shared latent K=V row per token and an
- *     optional per-head sink logit in the softmax denominator (techniques
- *     map: multi-head latent attention, learnable attention sink).
+ *   - Sparse MLA attention with one shared latent K=V row per token; an
+ *     optional extra logit per head joins only the softmax normaliser
+ *     (techniques map: multi-head latent attention, learnable attention
+ *     sink).
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a caller-owned DEVICE buffer, except where noted.  The
@@ -146,13 +147,17 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w,
  * pool_len-1] (ascending token ids, as csa2_index_score_topk writes them)
  * with this layer's q_idx / w, and keeps the Top-K by (s desc, token id asc).
  * Output as csa2_index_score_topk: ascending token ids, -1 padded.
- * pool_idx [B][Tq][pool_cap]; pool_len [B][Tq] (clamped to [0, pool_cap]).
- * Entries of pool_idx must be valid rows of k_idx (0 <= id < n rows).
+ * ctx_len  [B] int32: pool ids id with 0 <= id < ctx_len[b] name tokens; any
+ *          other entry (-1 padding, a stale or out-of-range id) is skipped,
+ *          never read.  ctx_len[b] must not exceed the rows k_idx holds for
+ *          sequence b.
+ * pool_idx [B][Tq][pool_cap] ascending among its valid entries;
+ * pool_len [B][Tq] (clamped to [0, pool_cap]).
  */
 size_t csa2_hier_pool_topk_workspace_size(int32_t B, int32_t Tq, int32_t pool_cap, int32_t k_top);
 int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w,
                         const uint8_t* k_idx, int64_t k_batch_stride, int64_t k_row_stride,
-                        const int32_t* pool_idx, const int32_t* pool_len, int32_t pool_cap,
+                        const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int32_t pool_cap,
                         int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int32_t k_top,
                         int32_t* topk_idx, float* topk_score,
                         void* ws, size_t ws_bytes, void* stream);
@@ -178,7 +183,8 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w,
  * swa_scales row w of b at swa_scales + b*ss_batch_stride + w*ss_row_stride (d_qk/32 bytes E8M0);
  * swa_len  [B] int32 (clamped to [0, W]); swa pointers may be NULL when W == 0.
  * sink     [H] float32 or NULL.  out [B][H][d_v] float32; lse [B][H] or NULL.
- * Supported: (d_qk, d_v) in {(576, 512), (512, 512)}; H % 16 == 0, H <= 128.
+ * Supported: (d_qk, d_v) in {(576, 512), (512, 512)}; H % 16 == 0, H <= 64
+ * (CSA2_EUNSUPPORTED otherwise).
  * Arithmetic: dequantised K/V rows and q enter fp16 matrix cores with fp32
  * accumulation; softmax and the output reduction are fp32.
  */

@@ -2,11 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY.
 
-[map] "Checked in its code": multi-head latent attention with a single latent
-KV head (num_key_value_heads = 1 is the MLA latent), partial RoPE on the last
-64 of the 512 head dims, a learnable per-head sink logit added to the
-sparse-MLA softmax denominator (initialised to -inf), and a 128-token sliding
-window kept by every layer; [facts] one shared K=V entry per token, head dim
+[map] "Checked in its code": multi-head latent attention whose single KV
+head is the MLA latent, rotary position on the last 64 of the 512 head
+channels only, one trainable logit per head that enters only the normaliser
+of the softmax (its initial value is -inf), and a window of the last 128
+tokens in every layer; [facts] one shared K=V entry per token, head dim
 512 = nope + rope, the window cache of every layer; [blog] CSA2 paragraph:
 attention runs over the Top-K entries chosen by the indexer.
 

@@ -1,11 +1,11 @@
 """Lightning-style indexer scores (oracle; test infrastructure).
 
-[map] "Checked in its code", row "Indexer-selected sparse attention": a
-dedicated indexer with its own heads and head dim scores past tokens and each
-query attends only to the indexer's top-k tokens, following the DeepSeek
-Sparse Attention lightning-indexer pattern; [facts] token selection: 32 heads
-x 128, top-512, and the indexer K cache holds one key row of index_head_dim
-per token, shared by all indexer heads.
+[map] "Checked in its code", row "Indexer-selected sparse attention": the
+model carries a separate indexer (its own head count and head width) in the
+lightning-indexer style of DeepSeek Sparse Attention; its scores over the
+cached tokens decide which k entries reach attention.  [facts] token
+selection gives 32 heads x 128 and top-512; the indexer K cache keeps one
+key row per token that every indexer head reads.
 
 The pages print no formula.  Reading: the published lightning-indexer form
     I(t, j) = sum_h  w[t, h] * ReLU( q[t, h, :] . k[j, :] )

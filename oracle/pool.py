@@ -1,8 +1,9 @@
 """Hierarchical Sparse Indexer candidate pool (oracle; test infrastructure).
 
-[blog] CSA2 paragraph: in the decoder a Hierarchical Sparse Indexer limits
-later indexing layers to a candidate pool built by the first Full-mode layer,
-so deeper indexer cost no longer grows with context length; [facts] token
+[blog] CSA2 paragraph: the decoder's hierarchical indexer lets only the
+first Full-mode layer score the whole context; it picks a candidate set, and
+the indexers of deeper layers score that set alone, so their cost stays fixed
+as the context grows; [facts] token
 selection: the decoder's hierarchical indexer is limited to a candidate pool
 of 2048 blocks x 8 positions; [map] technique tree, unfiled: blockwise
 candidate-pool selection for sparse indexing; [atlas] OPD stage card: later
@@ -18,8 +19,9 @@ Later layers score only pool tokens and keep their Top-K with ties broken by
 original token index (pool_topk).
 
 Parity: pinned by brute force on tiny inputs, by "pool = all tokens gives the
-flat Top-K", by block size 1 = token Top-K, and by containment of the flat
-Top-K in the pool when nblocks >= K (tests/test_oracle_pool.py).
+flat Top-K", by block size 1 = token Top-K, by containment of the flat Top-K
+in the pool when nblocks >= K, and, for pool_topk, by a pure-Python loop over
+a sparse, unordered-in-score pool with invalid ids (tests/test_oracle_pool.py).
 """
 
 import numpy as np
@@ -57,18 +59,23 @@ def hier_pool(scores, n_visible, block, nblocks):
     return out, len(pool)
 
 
-def pool_topk(q_bytes, w, k_bytes, pool_idx, pool_len, k):
+def pool_topk(q_bytes, w, k_bytes, pool_idx, pool_len, k, ctx_len=None):
     """Top-k over the pool tokens of one query row (later hierarchical layers).
 
-    k_bytes: the full indexer key cache [N][D] of the sequence.
+    k_bytes: the full indexer key cache [N][D] of the sequence.  The first
+    pool_len entries of pool_idx are the candidates (ascending token ids);
+    an entry < 0 or >= ctx_len (default: the cache's row count) names no
+    visible token and is skipped.
     Returns (idx int32 [k] ascending token ids, -1 padded; scores float32 [k]).
     """
-    pl = int(pool_len)
+    pl = max(0, min(int(pool_len), len(pool_idx)))
+    n = np.asarray(k_bytes).shape[0] if ctx_len is None else int(ctx_len)
     ids = np.asarray(pool_idx[:pl], dtype=np.int64)
-    if pl == 0:
+    ids = ids[(ids >= 0) & (ids < n)]
+    if len(ids) == 0:
         return np.full(k, -1, np.int32), np.full(k, -np.inf, np.float32)
     s = combine_heads(head_dots(q_bytes, np.asarray(k_bytes)[ids]), w)
-    return topk_select(s, pl, k, ids=ids)
+    return topk_select(s, len(ids), k, ids=ids)
 
 
 __all__ = ["block_scores", "hier_pool", "pool_topk", "index_scores"]

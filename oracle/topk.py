@@ -1,8 +1,9 @@
 """Exact Top-K token selection (oracle; test infrastructure).
 
-[map] "Checked in its code", row "Indexer-selected sparse attention": each
-query attends only to the top-k tokens chosen by the indexer; [facts] token
-selection: top-512 (the measured workloads use 2048 and 256).
+[map] "Checked in its code", row "Indexer-selected sparse attention": the
+attention of a query is restricted to the k highest-scoring cached entries of
+the indexer; [facts] token selection: k = 512 (the measured workloads use
+2048 and 256).
 
 Readings (the pages give no tie rule, output order or short-context rule):
   * total order: score descending, then token index ascending, comparing

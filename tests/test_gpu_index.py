@@ -159,7 +159,8 @@ def test_hierarchical_pool_and_pool_topk(block, nblocks, K):
     w1 = inputs.normal_f32((B, 1, H_I), 15, 2, "w", device="cuda")
     ctx = torch.tensor([N, N - 3, 1001], dtype=torch.int32, device="cuda")
     res = csa2.csa2_index_score_topk(q0, w0, k_idx, ctx, K, pool_block=block, pool_nblocks=nblocks)
-    later = csa2.csa2_hier_pool_topk(q1, w1, k_idx, res["pool_idx"], res["pool_len"], K, want_scores=True)
+    later = csa2.csa2_hier_pool_topk(q1, w1, k_idx, res["pool_idx"], res["pool_len"], K, ctx_len=ctx,
+                                     want_scores=True)
     torch.cuda.synchronize()
     kh, q0h, w0h, q1h, w1h, ch = map(np_, (k_idx, q0, w0, q1, w1, ctx))
     for b in range(B):
@@ -169,7 +170,7 @@ def test_hierarchical_pool_and_pool_topk(block, nblocks, K):
         assert np.array_equal(np_(res["pool_idx"])[b, 0], pool)
         flat, _ = topk_select(s0, ch[b], K)
         assert np.array_equal(np_(res["topk_idx"])[b, 0], flat)
-        want_i, want_s = P.pool_topk(q1h[b, 0], w1h[b, 0], kh[b], pool, plen, K)
+        want_i, want_s = P.pool_topk(q1h[b, 0], w1h[b, 0], kh[b], pool, plen, K, ctx_len=ch[b])
         assert np.array_equal(np_(later["topk_idx"])[b, 0], want_i)
         assert np.array_equal(np_(later["topk_score"])[b, 0], want_s)
         if nblocks >= K:   # containment: the flat Top-K lies inside the pool
@@ -196,3 +197,110 @@ def test_decode64k_full_size_sampled_rows():
     # every row: ascending, distinct, in range
     got = np_(res["topk_idx"])[:, 0]
     assert np.all(np.diff(got, axis=1) > 0) and got.min() >= 0 and got.max() < wl.N
+
+
+def _dot_rows(dots, D_I=128):
+    """E4M3 key rows whose dot with an all-ones query row is the given integer
+    (the first `dot` bytes are 1.0, the rest 0)."""
+    dots = np.asarray(dots, dtype=np.int64)
+    rows = (np.arange(D_I)[None, :] < dots[:, None]).astype(np.float32)
+    return torch.from_numpy(rows).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+# Block-pool thresholds.  Head 0 has weight -1/8 and an all-ones query, the
+# other heads weight 0, so a token's score is -dot/8 exactly: dot 22 -> -2.75,
+# 24 -> -3.0 (the order-preserving key 0x3FBFFFFF: the bucket 0x3FB with all 20
+# low bits set), 25 -> -3.125, 26 or more -> -3.25 or less.  The context ends
+# in a 3-token partial block whose maximum is -3.0 in every case.
+#   whole_bucket: 64 blocks at -2.75 = the whole top bucket; the threshold is
+#                 the key just below it, which is the last block's key;
+#   ties_partial: 60 blocks at -2.75, 10 at -3.0 (the last among them), 5 at
+#                 -3.125: 4 of the 10 ties are taken, the last block is not;
+#   ties_all:     60 at -2.75, 4 at -3.0 (the last among them), 5 at -3.125:
+#                 every tie is taken, the last (partial) block too.
+@gpu
+@pytest.mark.parametrize("case", ["whole_bucket", "ties_partial", "ties_all"])
+def test_pool_length_at_threshold_keys(case):
+    require_gpu()
+    announce(f"pool length threshold case {case}")
+    rng = np.random.default_rng({"whole_bucket": 1, "ties_partial": 2, "ties_all": 3}[case])
+    nblk, nsel, H_I, D_I, K = 200, 64, 8, 128, 256
+    N = 8 * (nblk - 1) + 3
+    dots = rng.integers(26, 60, N)                      # every block at <= -3.25 by default
+    blocks = rng.permutation(nblk - 1)                  # full blocks in random order
+    n_top = 64 if case == "whole_bucket" else 60
+    n_tie = {"whole_bucket": 20, "ties_partial": 9, "ties_all": 3}[case]   # full tie blocks besides the last
+    top, tie = blocks[:n_top], blocks[n_top:n_top + n_tie]
+    low = blocks[n_top + n_tie:n_top + n_tie + (0 if case == "whole_bucket" else 5)]
+    for c in top:
+        dots[8 * c + rng.integers(0, 8)] = 22
+    for c in tie:
+        dots[8 * c + rng.integers(0, 8)] = 24
+    for c in low:
+        dots[8 * c + rng.integers(0, 8)] = 25
+    dots[N - 3:] = [30, 24, 27]                         # the partial last block: max -3.0
+    k_idx = _dot_rows(dots, D_I).reshape(1, N, D_I).cuda()
+    q = np.zeros((1, 1, H_I, D_I), np.float32)
+    q[0, 0, 0] = 1.0
+    q[0, 0, 1:] = rng.integers(-4, 5, (H_I - 1, D_I))
+    q_idx = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+    w = torch.zeros(1, 1, H_I, dtype=torch.float32)
+    w[0, 0, 0] = -0.125
+    w = w.cuda()
+    q1 = inputs.int_e4m3((1, 1, H_I, D_I), 21, 1, "q_idx", device="cuda")
+    w1 = inputs.normal_f32((1, 1, H_I), 21, 1, "w", device="cuda")
+    ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
+    res = csa2.csa2_index_score_topk(q_idx, w, k_idx, ctx, K, pool_block=8, pool_nblocks=nsel)
+    later = csa2.csa2_hier_pool_topk(q1, w1, k_idx, res["pool_idx"], res["pool_len"], K, ctx_len=ctx,
+                                     want_scores=True)
+    torch.cuda.synchronize()
+    kh = np_(k_idx[0])
+    s0 = I.index_scores(np_(q_idx[0, 0]), np_(w[0, 0]), kh, N)
+    assert np.array_equal(s0, (-dots / 8.0).astype(np.float32))   # the construction holds
+    pool, plen = P.hier_pool(s0, N, 8, nsel)
+    want_len = 8 * nsel - (5 if case == "ties_all" else 0)
+    assert plen == want_len
+    assert int(np_(res["pool_len"])[0, 0]) == plen
+    assert np.array_equal(np_(res["pool_idx"])[0, 0], pool)
+    flat, _ = topk_select(s0, N, K)
+    assert np.array_equal(np_(res["topk_idx"])[0, 0], flat)
+    want_i, want_s = P.pool_topk(np_(q1[0, 0]), np_(w1[0, 0]), kh, pool, plen, K, ctx_len=N)
+    assert np.array_equal(np_(later["topk_idx"])[0, 0], want_i)
+    assert np.array_equal(np_(later["topk_score"])[0, 0], want_s)
+
+
+@gpu
+@pytest.mark.parametrize("pool_cap", [3000, 40000])
+def test_pool_ids_outside_the_context_are_skipped(pool_cap):
+    """-1, negative, stale (>= ctx_len but inside the cache) and far out-of-range
+    ids inside pool_len name no token: never read, never selected.  Both select
+    designs (pools up to 32K positions and longer)."""
+    require_gpu()
+    announce(f"pool with invalid ids, pool_cap={pool_cap}")
+    B, N, H_I, D_I, K = 2, 60000, 8, 128, 700
+    rng = np.random.default_rng(pool_cap)
+    k_idx = inputs.int_e4m3((B, N, D_I), 23, 0, "k_idx", device="cuda")
+    q1 = inputs.int_e4m3((B, 1, H_I, D_I), 23, 1, "q_idx", device="cuda")
+    w1 = inputs.normal_f32((B, 1, H_I), 23, 1, "w", device="cuda")
+    ctx = torch.tensor([N - 5000, N], dtype=torch.int32, device="cuda")
+    pool = np.full((B, 1, pool_cap), -1, np.int32)
+    plen = np.zeros((B, 1), np.int32)
+    for b in range(B):
+        n = pool_cap - 37
+        ids = np.sort(rng.choice(N, n, replace=False)).astype(np.int32)
+        bad = rng.choice(n, n // 10, replace=False)
+        ids[bad[0::3]] = -1
+        ids[bad[1::3]] = -123456
+        ids[bad[2::3]] = 1 << 30
+        pool[b, 0, :n] = ids
+        plen[b, 0] = n
+    pool_t, plen_t = torch.from_numpy(pool).cuda(), torch.from_numpy(plen).cuda()
+    later = csa2.csa2_hier_pool_topk(q1, w1, k_idx, pool_t, plen_t, K, ctx_len=ctx, want_scores=True)
+    torch.cuda.synchronize()
+    kh, ch = np_(k_idx), np_(ctx)
+    for b in range(B):
+        want_i, want_s = P.pool_topk(np_(q1[b, 0]), np_(w1[b, 0]), kh[b], pool[b, 0], plen[b, 0], K, ctx_len=ch[b])
+        assert np.array_equal(np_(later["topk_idx"])[b, 0], want_i)
+        assert np.array_equal(np_(later["topk_score"])[b, 0], want_s)
+        got = np_(later["topk_idx"])[b, 0]
+        assert got[got >= 0].max() < ch[b]

@@ -128,7 +128,7 @@ def test_hier1m_pool_and_nine_pool_layers():
     for li in range(1, len(wl.layers)):
         L = lays[li]
         topk.append(csa2.csa2_hier_pool_topk(L["q_idx"], L["w"], k_idx, r0["pool_idx"], r0["pool_len"],
-                                             wl.K)["topk_idx"])
+                                             wl.K, ctx_len=ctx)["topk_idx"])
     checked_layers = (0, 1, 9)
     outs = {}
     for li in checked_layers:

@@ -84,3 +84,30 @@ def test_prefill_window_rows():
     assert A.prefill_window_rows(92, 90, 30, 8).tolist() == [0, 1, 2]
     assert A.prefill_window_rows(89, 90, 30, 8).tolist() == []
     assert A.prefill_window_rows(150, 90, 30, 8).tolist() == []  # array ends at 119
+
+
+def test_prefill_row_equals_dense_softmax_over_hand_built_entries():
+    """sparse_attn_prefill_row against an independent dense softmax whose entry
+    list is written out here: the Top-K rows with 0 <= id < ctx_len, then the
+    window rows of positions max(p - W + 1, swa_pos0) .. p that the window
+    array holds (row i = position swa_pos0 + i), clipped at both ends."""
+    rng = np.random.default_rng(11)
+    n, d, dv, H, W = 400, 576, 512, 8, 16
+    codes, scales, kv = _cache(rng, n, d)
+    swa_pos0, n_rows = 300, 40            # window array covers positions 300 .. 339
+    sv, ss, sw = _swa(rng, n_rows, d)
+    scale = 0.07
+    cases = [(320, 350), (305, 330), (302, 310), (339, 400), (350, 400), (299, 299), (315, 316)]
+    for p, ctx in cases:
+        q = rng.standard_normal((H, d)).astype(np.float32)
+        idx = np.concatenate([rng.choice(n, 30, replace=False), [-1, n + 2, ctx, ctx - 1]])
+        out, lse = A.sparse_attn_prefill_row(q, codes, scales, idx, ctx, p, sv, ss, swa_pos0, W, d, dv, scale)
+        entries = [kv[i] for i in idx if 0 <= i < ctx]
+        for pos in range(p - W + 1, p + 1):
+            if pos >= swa_pos0 and pos - swa_pos0 < n_rows:
+                entries.append(sw[pos - swa_pos0])
+        keys = np.array(entries)
+        z = scale * (q.astype(np.float64) @ keys.T)
+        want = softmax(z, axis=1) @ keys[:, :dv]
+        assert np.allclose(out, want, rtol=1e-12, atol=1e-14), (p, ctx)
+        assert np.allclose(lse, logsumexp(z, axis=1), rtol=1e-13), (p, ctx)

@@ -68,3 +68,55 @@ def test_flat_topk_is_contained_in_pool():
         pool, plen = P.hier_pool(s, n, 8, nb)
         flat, _ = topk_select(s, n, kk)
         assert set(flat[flat >= 0].tolist()) <= set(pool[:plen].tolist())
+
+
+def _brute_pool_topk(q, w, k_bytes, pool, plen, k, ctx):
+    """Pure-Python restatement: score k_bytes[id] for every valid pool id with
+    integer dots and the fixed-order float32 head sum, sort by (score desc,
+    id asc), keep k, emit ascending ids."""
+    dec = lambda b: torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).double().numpy()
+    qd = dec(q)
+    cand = []
+    for i in range(plen):
+        t = int(pool[i])
+        if t < 0 or t >= ctx:
+            continue
+        kd = dec(k_bytes[t])
+        s = np.float32(0.0)
+        for h in range(q.shape[0]):
+            dot = sum(float(a) * float(b) for a, b in zip(qd[h], kd))
+            s = np.float32(s + np.float32(np.float32(w[h]) * np.float32(max(dot, 0.0))))
+        cand.append((float(s), t))
+    cand.sort(key=lambda c: (-c[0], c[1]))
+    take = sorted(cand[:k], key=lambda c: c[1])
+    ids = [t for _, t in take] + [-1] * (k - len(take))
+    scores = [s for s, _ in take] + [-np.inf] * (k - len(take))
+    return np.array(ids, np.int32), np.array(scores, np.float32)
+
+
+def test_pool_topk_sparse_pool_brute_force():
+    """A sparse, non-contiguous pool (ids far from their positions), with -1
+    and out-of-range ids inside pool_len: pool_topk must score k[pool_idx[i]]
+    (not k[i]) and skip the invalid ids."""
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        n, H, D = 300, 3, 16
+        k_bytes = _e4m3(rng.integers(-4, 5, (n, D)))
+        q = _e4m3(rng.integers(-4, 5, (H, D)))
+        w = rng.standard_normal(H).astype(np.float32)
+        if trial % 3 == 0:
+            w = (rng.integers(-3, 4, H) / 4).astype(np.float32)   # many ties
+        ctx = int(rng.integers(150, n + 1))
+        ids = np.sort(rng.choice(n, int(rng.integers(5, 60)), replace=False))
+        pool = np.full(80, -1, np.int32)
+        pool[: len(ids)] = ids
+        plen = len(ids)
+        if trial % 2 == 1:   # invalid entries inside pool_len
+            pool[1] = -1
+            pool[plen] = n + 3
+            plen += 1
+        k = int(rng.integers(1, 40))
+        got_i, got_s = P.pool_topk(q, w, k_bytes, pool, plen, k, ctx_len=ctx)
+        want_i, want_s = _brute_pool_topk(q, w, k_bytes, pool, plen, k, ctx)
+        assert np.array_equal(got_i, want_i), trial
+        assert np.array_equal(got_s, want_s), trial
