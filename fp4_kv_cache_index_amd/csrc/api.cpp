@@ -60,7 +60,11 @@ static ScoreLayout score_layout(int64_t B, int64_t Tq, int64_t n_max, int32_t po
   size_t o = 0;
   L.off_keys = o; o += al256(sizeof(uint32_t) * L.rows * L.n_stride);
   L.off_nvalid = o; o += al256(sizeof(int32_t) * L.rows);
-  L.off_tok = o; o += al256(select_ws_bytes(L.rows, n_max));
+  // The multi-pass select's state; rows of up to kLocalSel positions (no
+  // pool) are selected by one workgroup each and need none of it.
+  const bool local = pool_block <= 0 && n_max <= kLocalSel;
+  L.off_tok = o;
+  if (!local) o += al256(select_ws_bytes(L.rows, n_max));
   if (pool_block > 0) {
     L.nb_max = (n_max + pool_block - 1) / pool_block;
     L.nb_stride = round_up(L.nb_max > 0 ? L.nb_max : 1, 64);
@@ -181,6 +185,7 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
   char* base = (char*)ws;
   uint32_t* keys = (uint32_t*)(base + L.off_keys);
   int32_t* n_valid = (int32_t*)(base + L.off_nvalid);
+  // (in the one-workgroup select path only tile_hist of it is used)
   SelectWs tok = select_ws_carve(base + L.off_tok, L.rows, n_max);
   SelectWs blk{};
   uint32_t* bkeys = nullptr;
