@@ -32,6 +32,10 @@ _SIGS = {
                                              c_int32, c_int32, c_int32, c_int32, c_int64, c_int32, c_void_p,
                                              c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
                                              c_void_p]),
+    "csa2_index_score_topk_noalloc": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
+                                                     c_void_p, c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
+                                                     c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                                     c_void_p]),
     "csa2_hier_pool_topk_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "csa2_hier_pool_topk": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                            c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,

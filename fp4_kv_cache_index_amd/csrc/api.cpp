@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/csa2.h"
 #include "internal.h"
@@ -108,6 +109,38 @@ static int attn_common_check(const float* q, const uint8_t* kv_codes, int64_t c_
   return CSA2_OK;
 }
 
+// ------------------------------------------------ no-allocation scratch ---
+// Workspace of csa2_index_score_topk_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  On the
+// host its name only stands for the symbol; the device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept here.  Only that address is ever handed to kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's scratch address (CSA2_EHIP if it cannot be found).
+static int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_EHIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return CSA2_EHIP;
+      g_scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return CSA2_OK;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -121,6 +154,8 @@ const char* csa2_status_string(int status) {
     case CSA2_EUNSUPPORTED: return "valid arguments outside the supported shape set";
     case CSA2_EWORKSPACE: return "workspace smaller than the required size";
     case CSA2_EHIP: return "HIP launch error";
+    case CSA2_ESCRATCH:
+      return "the inputs need more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -222,6 +257,25 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
     e = select_finish(blk, bkeys, L.nb_stride, nb_valid, L.rows, pool_nblocks, out, s);
   }
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
+int csa2_index_score_topk_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
+                                  int64_t k_batch_stride, int64_t k_row_stride, const int32_t* ctx_len,
+                                  const int32_t* q_pos, int32_t B, int32_t Tq, int32_t H_I, int32_t D_I,
+                                  int64_t n_max, int32_t k_top, int32_t* topk_idx, float* topk_score,
+                                  int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx, int32_t* pool_len,
+                                  void* stream) {
+  if (B < 0 || Tq < 0 || n_max < 0) return CSA2_EINVAL;
+  if (B == 0 || Tq == 0) return CSA2_OK;
+  const size_t need = csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_idx ? pool_block : 0,
+                                                           pool_nblocks);
+  if (need > kNoallocScratchBytes) return CSA2_ESCRATCH;
+  void* ws = nullptr;
+  const int st = noalloc_scratch(&ws);
+  if (st != CSA2_OK) return st;
+  return csa2_index_score_topk(q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max,
+                               k_top, topk_idx, topk_score, pool_block, pool_nblocks, pool_idx, pool_len, ws,
+                               kNoallocScratchBytes, stream);
 }
 
 size_t csa2_hier_pool_topk_workspace_size(int32_t B, int32_t Tq, int32_t pool_cap, int32_t k_top) {

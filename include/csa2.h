@@ -39,7 +39,8 @@
  *     workspace must be ordered on one stream.
  *   - Return value: a csa2_status (0 = success).  Nothing is enqueued when a
  *     validation error is returned.
- *   - No global mutable state, except the optional per-thread kernel trace.
+ *   - No global mutable state, except the optional per-thread kernel trace
+ *     and the static scratch of csa2_index_score_topk_noalloc.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -56,7 +57,8 @@ enum csa2_status {
   CSA2_EINVAL = 1,       /* null required pointer, bad shape/stride/alignment */
   CSA2_EUNSUPPORTED = 2, /* valid arguments outside the compiled shape set */
   CSA2_EWORKSPACE = 3,   /* ws_bytes smaller than the *_workspace_size() */
-  CSA2_EHIP = 4          /* a HIP launch reported an error */
+  CSA2_EHIP = 4,         /* a HIP launch reported an error */
+  CSA2_ESCRATCH = 5      /* inputs too large for csa2_index_score_topk_noalloc's static scratch */
 };
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -139,6 +141,28 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w,
                           int32_t* topk_idx, float* topk_score,
                           int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx, int32_t* pool_len,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_score_topk_noalloc -- csa2_index_score_topk for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments, results and
+ * kernels, minus ws / ws_bytes.  Its workspace is a static device array of
+ * 64 MiB (64 << 20 bytes) inside the library, one per GPU, kept until the
+ * process ends; the call allocates nothing, and what must start at zero is
+ * cleared by a kernel on `stream`.  Inputs whose
+ * csa2_index_score_topk_workspace_size() exceeds 64 MiB return CSA2_ESCRATCH
+ * with nothing enqueued (e.g. 64 x 64K-token decode rows need 48 MiB, 4 x 1M
+ * with the 2048 x 8 pool 55 MiB).  Every call on one GPU uses that GPU's one
+ * array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.
+ */
+int csa2_index_score_topk_noalloc(const uint8_t* q_idx, const float* w,
+                                  const uint8_t* k_idx, int64_t k_batch_stride, int64_t k_row_stride,
+                                  const int32_t* ctx_len, const int32_t* q_pos,
+                                  int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int64_t n_max, int32_t k_top,
+                                  int32_t* topk_idx, float* topk_score,
+                                  int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx, int32_t* pool_len,
+                                  void* stream);
 
 /*
  * csa2_hier_pool_topk -- later hierarchical-indexer layers (blog, CSA2

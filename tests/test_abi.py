@@ -38,7 +38,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings_and_version():
     lib = _lib_or_skip()
-    for s in range(5):
+    for s in range(6):
         assert lib.csa2_status_string(s)
     assert lib.csa2_status_string(99) == b"unknown status"
     assert re.match(rb"^\d+\.\d+\.\d+$", lib.csa2_version())
