@@ -11,10 +11,14 @@ every cache resident in HBM:
   group128k   Full -> Reindex -> Reuse layers over 16 x 128K;
   hier1m      Full layer with the 2048 x 8 candidate pool + 9 pool layers, 4 x 1M;
   prefill256k one causal chunk of 4096 queries on a 256K cache.
-Prints one JSON line: decode queries/s, algorithmic HBM GB/s, the roofline
-of the dominant kernel (HIP events around each of its launches inside the
-timed region; no other launch is bracketed there), a per-kernel breakdown
-from a separate traced pass, and the CPU oracle timed on a bounded sample.
+Every step is timed by its own pair of HIP events; ms_per_step is their
+median, and between steps (outside the events) a 512 MB buffer is read so
+that no step starts with its inputs in the 256 MB MALL (--no-flush keeps
+the caches warm).  Prints one JSON line: decode queries/s, algorithmic HBM
+GB/s, the roofline of the dominant kernel (HIP events carried by its
+launches inside the timed region; no other launch is bracketed there), a
+per-kernel breakdown from a separate traced pass, and the CPU oracle timed
+on a bounded sample.
 """
 
 import argparse
@@ -42,7 +46,55 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=0, help="sequences timed for the CPU baseline (0 = auto)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (for counter calibration) and exit")
+    p.add_argument("--no-flush", action="store_true",
+                   help="do not write the 512 MB flush buffer between timed steps (MALL left warm)")
     return p.parse_args()
+
+
+# ------------------------------------------------------------ step timer ---
+
+class StepTimer:
+    """Per-step HIP events on one stream, created without the system-scope
+    fence (they only carry timestamps: with the fence every record wrote back
+    the L2 and left gaps of several microseconds around it)."""
+
+    FLAGS = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self, n, stream):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def start(self, i):
+        self.hip.hipEventRecord(self.ev[2 * i], self.stream)
+
+    def stop(self, i):
+        self.hip.hipEventRecord(self.ev[2 * i + 1], self.stream)
+
+    def ms(self):
+        out = []
+        for i in range(len(self.ev) // 2):
+            t = self.ct.c_float()
+            if self.hip.hipEventElapsedTime(self.ct.byref(t), self.ev[2 * i], self.ev[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(t.value)
+        return out
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 # ------------------------------------------------------- counter traffic ---
@@ -282,6 +334,15 @@ def main():
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Between timed steps (outside their events) a 512 MB buffer is read, so
+    # that no step finds its inputs in the 256 MB MALL (or the L2) left by
+    # the previous one.  A read leaves no dirty lines behind (a written flush
+    # buffer made the next step pay for its write-back).
+    flush = None
+    if not args.no_flush:
+        flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+        flush_out = torch.empty((), dtype=torch.int64, device=dev)
+    timer = StepTimer(args.steps, stream)
     # Dominant kernel: the indexer scan over the key cache (decode) or the
     # dense FP8 scoring product (prefill chunk).  Inside the timed region only
     # its launches are bracketed by HIP events, so the step time carries two
@@ -292,11 +353,20 @@ def main():
     with csa2.KernelTrace(capacity=4 * args.steps * max(1, len(wl.layers)), only=dom) as tr:
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            if flush is not None:
+                torch.amax(flush, dim=0, out=flush_out)
+            timer.start(i)
             case.step()
+            timer.stop(i)
         e1.record(stream)
         torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    step_ms = sorted(timer.ms())
+    timer.close()
+    region_ms = e0.elapsed_time(e1)
+    ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] +
+                                                                   step_ms[len(step_ms) // 2])
+    mean_ms = sum(step_ms) / len(step_ms)
     dom_launches = [t for name, t in tr.durations_ms() if name == dom]
     tr.close()
     dom_ms = sum(dom_launches) / len(dom_launches) if dom_launches else float("nan")
@@ -343,6 +413,9 @@ def main():
                    "heads": wl.H, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "window": wl.W,
                    "layers": wl.layers, "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "step_bytes": step_bytes,
+        "step_stats": {"median_ms": round(ms, 5), "mean_ms": round(mean_ms, 5), "min_ms": round(step_ms[0], 5),
+                       "max_ms": round(step_ms[-1], 5), "timed_region_ms": round(region_ms, 3),
+                       "mall_flush_between_steps": flush is not None},
         "kernels_ms_per_step": {k: round(v[0] / n_bd, 5) for k, v in per_kernel.items()},
         "roofline": roof, "cpu_baseline": cpu,
     }

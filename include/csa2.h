@@ -211,6 +211,16 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w,
  * (CSA2_EUNSUPPORTED otherwise).
  * Arithmetic: dequantised K/V rows and q enter fp16 matrix cores with fp32
  * accumulation; softmax and the output reduction are fp32.
+ * Accuracy: main rows (E2M1 x E4M3: at most 6 significant bits within
+ * [2^-10, 2688]) are exact in fp16; window values are exact while every
+ * block's E8M0 code lies in [112, 134] (scales 2^-15 .. 2^7) and are rounded
+ * to fp16 (subnormals below 2^-14, zero below 2^-24, overflow above 65504)
+ * outside it.  q and the softmax weights are rounded to fp16 once (relative
+ * 2^-11), so each logit moves by about softmax_scale * |q_h| |k_e| * 2^-12.
+ * With unit-variance q and rows this keeps every (row, head) output within
+ * 2e-3 relative (max error / max |out|) up to softmax_scale = 4 / sqrt(576);
+ * at larger logit spreads the error grows with that product (about 5e-3 on
+ * outputs and 7e-3 on lse at 12 / sqrt(576)).
  */
 size_t csa2_sparse_attn_decode_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t k_top, int32_t W);
 int csa2_sparse_attn_decode(const float* q,
