@@ -10,7 +10,9 @@ every cache resident in HBM:
   tiny        the same at 1 x 4096 (a parity-sized case);
   group128k   Full -> Reindex -> Reuse layers over 16 x 128K;
   hier1m      Full layer with the 2048 x 8 candidate pool + 9 pool layers, 4 x 1M;
-  prefill256k one causal chunk of 4096 queries on a 256K cache.
+  prefill256k one causal chunk of 4096 queries on a 256K cache;
+  mq2_64k     multi-query decode: 2 query tokens per sequence over 64 x 64K
+              (one pass over the keys for both, then attention per token).
 Every step is timed by its own pair of HIP events; ms_per_step is their
 median, and between steps (outside the events) a 512 MB buffer is read so
 that no step starts with its inputs in the 256 MB MALL (--no-flush keeps
@@ -347,7 +349,7 @@ def main():
     # dense FP8 scoring product (prefill chunk).  Inside the timed region only
     # its launches are bracketed by HIP events, so the step time carries two
     # event records per scoring launch and nothing else.
-    prefill = wl.Tq > 1
+    prefill = wl.Tq >= 16         # (2..15 query rows per sequence: the multi-query scan)
     dom = "index_prefill" if prefill else "index_score"
     n_scan_layers = sum(1 for L in case.layers if L["kind"] in ("full", "reindex"))
     with csa2.KernelTrace(capacity=4 * args.steps * max(1, len(wl.layers)), only=dom) as tr:
@@ -394,7 +396,8 @@ def main():
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
                 "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     else:
-        scan_bytes = (wl.D_I * wl.N + wl.H_I * wl.D_I + 4 * wl.H_I) * wl.B
+        # one pass over the keys serves every query row of a sequence
+        scan_bytes = (wl.D_I * wl.N + wl.Tq * (wl.H_I * wl.D_I + 4 * wl.H_I)) * wl.B
         achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -27,8 +27,10 @@ namespace csa2 {
 // tile per compute unit, so that each workgroup's prologue, histogram flush
 // and key burst are paid once per 16K tokens), 4 for the pool gather and the
 // wide-head variants (their LDS tiles are larger).
-template <bool GATHER, int HB>
-constexpr int kScanWavesT = (!GATHER && HB == 1) ? 16 : 4;
+// With QT > 1 query rows of one sequence per workgroup (multi-query decode),
+// 16 / QT waves: the per-wave dot buffers and the staged keys grow with QT.
+template <bool GATHER, int HB, int QT = 1>
+constexpr int kScanWavesT = QT > 1 ? 16 / QT : ((!GATHER && HB == 1) ? 16 : 4);
 constexpr int kScanTileMax = 16384;   // flat-scan tokens per 16-wave workgroup (largest)
 constexpr int kScanTileSmall = 1024;  // flat-scan tokens per 4-wave workgroup
 constexpr int kPoolTile = 512;        // pool positions per workgroup (later layers)
@@ -82,8 +84,13 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 // GATHER = true : position p maps to token pool_idx[row][p] (pool layers);
 //                 a pool id outside [0, ctx_len[b]) names no token: the
 //                 position is not visible (key 0) and its loads read row 0.
-template <int DI, int HB, bool GATHER, bool POOL, bool H8>
-__global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB>))
+// QT > 1 (D_I = 128, at most 8 indexer heads, flat scan only): the
+// workgroup scores QT query rows of one sequence against the same key rows;
+// query t takes MFMA rows 8t .. 8t+7 (its heads, zero-padded), so two
+// queries fill one 16-row block and four take two, and the key stream is
+// read once for all of them.
+template <int DI, int HB, bool GATHER, bool POOL, bool H8, int QT>
+__global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB, QT>))
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
                    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
@@ -93,22 +100,26 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
                    SelectWs tok,
                    int pool_block, int nblocks, uint32_t* __restrict__ bkeys, int64_t bkey_stride,
                    int32_t* __restrict__ nb_valid_out, SelectWs blk) {
-  constexpr int NW = kScanWavesT<GATHER, HB>;
+  static_assert(QT == 1 || (DI == 128 && HB == 1 && H8 && !GATHER && !POOL), "multi-query scan: flat, 8 heads");
+  constexpr int NW = kScanWavesT<GATHER, HB, QT>;
   constexpr int NT = 64 * NW;
   constexpr int CH = DI / 4;           // bytes of a key row per lane
   constexpr int KS = DI / 32;          // MFMA k-steps
-  constexpr int HMAX = 16 * HB;
-  // Heads kept per token: 8 when the indexer has at most 8 heads, else all
-  // 16*HB MFMA rows (padding heads have zero queries and weight 0).
-  constexpr int HP = H8 ? 8 : HMAX;
-  // Top-12-bit histogram, two 16-bit bins per word (a tile holds at most
-  // 16384 positions); the last word takes positions past the visible count.
-  __shared__ __attribute__((aligned(16))) uint32_t hist[2052];
+  constexpr int HMAX = QT > 1 ? 8 * QT : 16 * HB;   // MFMA rows (query heads, padded)
+  constexpr int RB = QT > 1 ? QT / 2 : 1;           // 16-row blocks of the whole-line path
+  // Heads kept per token: 8 per query when the indexer has at most 8 heads,
+  // else all 16*HB MFMA rows (padding heads have zero queries and weight 0).
+  constexpr int HP = H8 ? 8 * QT : HMAX;
+  // Top-12-bit histogram of each query row, two 16-bit bins per word (a tile
+  // holds at most 16384 positions); the last word takes positions past the
+  // visible count.
+  __shared__ __attribute__((aligned(16))) uint32_t hist[QT][2052];
   // Flat scan: the tile's keys are staged here and leave in one coalesced
   // burst at the end (interleaving small key stores with the key-row stream
   // costs more than the LDS round trip).
   constexpr bool kStage = !GATHER && !POOL;
-  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? (NW == 16 ? kScanTileMax : kScanTileSmall) : 1];
+  constexpr int kTileCap = QT > 1 ? 1024 * NW : (NW == 16 ? kScanTileMax : kScanTileSmall);
+  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? QT * kTileCap : 1];
   __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
   __shared__ uint32_t bhist[POOL ? 4096 : 1];
   // per wave: the batch's dots, then one 4-float trash slot per lane (whole-line path)
@@ -116,12 +127,16 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   __shared__ float wsh[HMAX];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row = blockIdx.y;
-  const int64_t b = row / Tq;
+  // Query rows row .. row + nq - 1 of sequence b (QT == 1: row = blockIdx.y).
+  const int ngrp = (Tq + QT - 1) / QT;
+  const int64_t b = (int64_t)blockIdx.y / ngrp;
+  const int t0 = (int)((int64_t)blockIdx.y - b * ngrp) * QT;
+  const int64_t row = b * Tq + t0;
+  const int nq = Tq - t0 < QT ? Tq - t0 : QT;
   constexpr bool pool = POOL;
   if (n_max <= 0) {   // nothing addressable: no position is visible
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      n_valid_out[row] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < nq) {
+      n_valid_out[row + threadIdx.x] = 0;
       if (pool) nb_valid_out[row] = 0;
     }
     return;
@@ -204,11 +219,25 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // flat scan then issues its first two key batches at once, so that the
   // stream starts while these are in flight (the vector-memory counter
   // retires in order: waiting for them below does not wait for the keys).
-  int64_t craw;
+  int64_t craw;              // visible positions (the largest of the group's queries)
+  int64_t cq[QT];            // QT > 1: per query
   int64_t ctx_b = 0;   // pool layers: ids at or past it name no token
   if (GATHER) {
     craw = pool_len[row];
     ctx_b = ctx_len[b];
+  } else if constexpr (QT > 1) {
+    const int64_t c = ctx_len[b];
+    craw = 0;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      int64_t v = c;
+      if (q_pos) {
+        const int64_t qp = (int64_t)q_pos[row + (t < nq ? t : nq - 1)] + 1;
+        if (qp < v) v = qp;
+      }
+      cq[t] = t < nq ? v : 0;
+      craw = cq[t] > craw ? cq[t] : craw;
+    }
   } else {
     craw = ctx_len[b];
     if (q_pos) {
@@ -218,8 +247,10 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
   // Unconditional loads from in-range addresses; the zeroing of heads past
   // H_I happens after the key loads are issued (a select on a loaded value
-  // waits for it, and the counter retires in order).
-  const float wraw = w[row * H_I + (threadIdx.x < H_I ? threadIdx.x : H_I - 1)];
+  // waits for it, and the counter retires in order).  QT > 1: thread i
+  // holds head i % 8 of query i / 8.
+  const int wq = QT > 1 ? (int)threadIdx.x >> 3 : 0, wh = QT > 1 ? (int)threadIdx.x & 7 : (int)threadIdx.x;
+  const float wraw = w[(row + (wq < nq ? wq : nq - 1)) * H_I + (wh < H_I ? wh : H_I - 1)];
   // Whole-line loads (D_I = 128, one head block): every token of a group of
   // 8 takes two B columns -- 2m holds bytes 32g..32g+15 of its row, 2m+1
   // bytes 32g+16..32g+31 (lane group g) -- so the 8 lanes of a token read its
@@ -227,18 +258,25 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // halves of the query rows give the two partial dots, which one adjacent-
   // lane exchange joins (exact: integers below 2^24).
   // A operand: query head (lane & 15) + 16*hb, slice (lane >> 4) of the row.
-  long qh[2][2];   // FULL: [parity e][step s] = bytes 32g + 16e + 8s .. +8
+  // QT > 1: A row 16*rb + (lane & 15) is head (row & 7) of query (row >> 3).
+  long qh[RB][2][2];   // FULL: [row block][parity e][step s] = bytes 32g + 16e + 8s .. +8
   long qa[HB][KS];
-  const bool hv = c16 < H_I;
+  bool hv[RB];
   if constexpr (FULL) {
-    const uint8_t* qp = q_idx + (row * H_I + (hv ? c16 : 0)) * DI + 32 * g;
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int rb = 0; rb < RB; ++rb) {
+      const int R = 16 * rb + c16;
+      const int qt = QT > 1 ? R >> 3 : 0, qhd = QT > 1 ? R & 7 : R;
+      hv[rb] = qt < nq && qhd < H_I;
+      const uint8_t* qp = q_idx + ((row + (hv[rb] ? qt : 0)) * H_I + (hv[rb] ? qhd : 0)) * DI + 32 * g;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const v2u v = *reinterpret_cast<const v2u*>(qp + 16 * e + 8 * st);
-        qh[e][st] = as_long(v[0], v[1]);
-      }
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const v2u v = *reinterpret_cast<const v2u*>(qp + 16 * e + 8 * st);
+          qh[rb][e][st] = as_long(v[0], v[1]);
+        }
+    }
   } else {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -256,25 +294,41 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
   if constexpr (FULL) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) qh[e][st] = hv ? qh[e][st] : 0L;
-    // The query fragments must have arrived before the stream loop (so that
-    // the loop's waits cover only its own batches).
-    asm volatile("" ::"v"(qh[0][0]), "v"(qh[0][1]), "v"(qh[1][0]), "v"(qh[1][1]));
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) qh[rb][e][st] = hv[rb] ? qh[rb][e][st] : 0L;
+      // The query fragments must have arrived before the stream loop (so
+      // that the loop's waits cover only its own batches).
+      asm volatile("" ::"v"(qh[rb][0][0]), "v"(qh[rb][0][1]), "v"(qh[rb][1][0]), "v"(qh[rb][1][1]));
+    }
   }
-  const float wload = threadIdx.x < HMAX && threadIdx.x < H_I ? wraw : 0.0f;
+  const float wload = threadIdx.x < HMAX && wq < nq && wh < H_I ? wraw : 0.0f;
 
   int64_t nv;
   if (GATHER) nv = (craw < 0 || ctx_b <= 0) ? 0 : (craw > pool_cap ? pool_cap : craw);
   else nv = craw < 0 ? 0 : (craw > n_max ? n_max : craw);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    n_valid_out[row] = (int32_t)nv;
+  int64_t nvq[QT];   // visible positions of each query of the group
+  if constexpr (QT > 1) {
+#pragma unroll
+    for (int t = 0; t < QT; ++t) nvq[t] = cq[t] < 0 ? 0 : (cq[t] > n_max ? n_max : cq[t]);
+  } else {
+    nvq[0] = nv;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < nq) {
+    int64_t v = nvq[0];
+#pragma unroll
+    for (int t = 1; t < QT; ++t) v = (int)threadIdx.x == t ? nvq[t] : v;
+    n_valid_out[row + threadIdx.x] = (int32_t)v;
     if (pool) nb_valid_out[row] = (int32_t)((nv + pool_block - 1) / pool_block);
   }
 
   for (int i = threadIdx.x; i < 4096; i += NT) {
-    if (i <= 2048) hist[i] = 0u;
+    if (i <= 2048) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) hist[t][i] = 0u;
+    }
     if (pool) bhist[i] = 0u;
   }
   if (threadIdx.x < HMAX) wsh[threadIdx.x] = wload;
@@ -305,22 +359,26 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
       for (int u = 0; u < 2 * SG; ++u) {
         const uint32_t* w4 = &f[u >> 1].w[4 * (u & 1)];
         const long lo = as_long(w4[0], w4[1]), hi = as_long(w4[2], w4[3]);
-        v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[0][0], lo, a0, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[0][1], hi, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[1][0], lo, a1, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[1][1], hi, a1, 0, 0, 0);
-        // even column 2m: a0 here plus a1 of the odd column 2m+1 (lane + 1).
-        // (__shfl_xor: the DPP builtins applied to elements of an MFMA result
-        // were folded into a single element by this compiler.)
-        v4f d;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = a0[r] + __shfl_xor(a1[r], 1, 64);
-        // d[r] = dot(head 4g + r, token 8u + m) on the even lanes; the other
-        // lanes write their own trash slot (no branch around the loads' waits)
-        const bool keep = (c16 & 1) == 0 && 4 * g < HP;
-        const int at = keep ? (8 * u + (c16 >> 1)) * pitch + 4 * g : 16 * SG * HP + 4 * lane;
-        *reinterpret_cast<v4f*>(my + at) = d;
+        for (int rb = 0; rb < RB; ++rb) {
+          v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[rb][0][0], lo, a0, 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[rb][0][1], hi, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[rb][1][0], lo, a1, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qh[rb][1][1], hi, a1, 0, 0, 0);
+          // even column 2m: a0 here plus a1 of the odd column 2m+1 (lane + 1).
+          // (__shfl_xor: the DPP builtins applied to elements of an MFMA
+          // result were folded into a single element by this compiler.)
+          v4f d;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d[r] = a0[r] + __shfl_xor(a1[r], 1, 64);
+          // d[r] = dot(A row 16 rb + 4g + r, token 8u + m) on the even lanes;
+          // the other lanes write their own trash slot (no branch around the
+          // loads' waits)
+          const bool keep = (c16 & 1) == 0 && 16 * rb + 4 * g < HP;
+          const int at = keep ? (8 * u + (c16 >> 1)) * pitch + 16 * rb + 4 * g : 16 * SG * HP + 4 * lane;
+          *reinterpret_cast<v4f*>(my + at) = d;
+        }
       }
     } else {
 #pragma unroll
@@ -344,27 +402,35 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     for (int u = 0; u < SG / 4; ++u) {
       // Lane owns token it + 64u + lane.
       const int64_t j = it + 64 * u + lane;
-      bool vis = j < wend;
-      if constexpr (GATHER) vis = vis && ptok[j < wend ? j - tile0 : 0] >= 0;
-      float sc = 0.0f;
+      bool vis_w = j < wend;
+      if constexpr (GATHER) vis_w = vis_w && ptok[j < wend ? j - tile0 : 0] >= 0;
       const float* src = my + (64 * u + lane) * pitch;
+      uint32_t key = 0u;
+      bool vis = vis_w;
+      constexpr int HPQ = QT > 1 ? 8 : HP;   // dots per query in a token's row
 #pragma unroll
-      for (int h4 = 0; h4 < HP; h4 += 4) {
-        const v4f d4 = *reinterpret_cast<const v4f*>(src + h4);
+      for (int t = 0; t < QT; ++t) {
+        if (t >= nq) break;   // (uniform)
+        float sc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // heads past H_I have weight 0: adding +0 leaves the sum unchanged
-          float r = d4[e] > 0.0f ? d4[e] : 0.0f;
-          sc = __fadd_rn(sc, __fmul_rn(wv[h4 + e], r));
+        for (int h4 = 0; h4 < HPQ; h4 += 4) {
+          const v4f d4 = *reinterpret_cast<const v4f*>(src + HPQ * t + h4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // heads past H_I have weight 0: adding +0 leaves the sum unchanged
+            float r = d4[e] > 0.0f ? d4[e] : 0.0f;
+            sc = __fadd_rn(sc, __fmul_rn(wv[HPQ * t + h4 + e], r));
+          }
         }
+        vis = vis_w && (QT == 1 || j < nvq[t]);
+        // Positions up to the next multiple of 64 lie inside the row's key
+        // stride and belong to no other wave; past the visible count they
+        // are never read.
+        key = vis ? score_key(sc) : 0u;
+        if (kStage) kst[t * kTileCap + (j - tile0)] = key;
+        else keys[row * key_stride + j] = key;
+        atomicAdd(&hist[t][vis ? key >> 21 : 2048u], 1u << (16 * ((key >> 20) & 1u)));
       }
-      // Positions up to the next multiple of 64 lie inside the row's key
-      // stride and belong to no other wave; past the visible count they are
-      // never read.
-      uint32_t key = vis ? score_key(sc) : 0u;
-      if (kStage) kst[j - tile0] = key;
-      else keys[row * key_stride + j] = key;
-      atomicAdd(&hist[vis ? key >> 21 : 2048u], 1u << (16 * ((key >> 20) & 1u)));
       if (pool) {
         uint32_t m = key;
         for (int off = 1; off < pool_block; off <<= 1) {
@@ -398,24 +464,35 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   if (kStage) {
     int64_t tend = tile0 + tile;
     if (tend > nv) tend = nv;
-    // Whole 64-position groups: they stay inside the row's key stride.
+    // Whole 64-position groups: they stay inside the row's key stride (every
+    // one of them was written by a wave; past a query's visible count they
+    // hold key 0).
     const int64_t tn = tend > tile0 ? ((tend - tile0 + 63) & ~63LL) : 0;
-    for (int64_t i = 4 * threadIdx.x; i < tn; i += 4 * NT)
-      *reinterpret_cast<v4u*>(keys + row * key_stride + tile0 + i) = *reinterpret_cast<const v4u*>(&kst[i]);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      if (t >= nq) break;
+      for (int64_t i = 4 * threadIdx.x; i < tn; i += 4 * NT)
+        *reinterpret_cast<v4u*>(keys + (row + t) * key_stride + tile0 + i) =
+            *reinterpret_cast<const v4u*>(&kst[t * kTileCap + i]);
+    }
   }
   // Two adjacent bins per 64-bit atomic: the row histogram's 32-bit counters
   // 2i and 2i+1 are the low and high halves of one little-endian 64-bit word.
-  if (tok.hist1) {
-    uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + row * 4096);
-    for (int i = threadIdx.x; i < 2048; i += NT) {
-      const uint32_t v = hist[i];
-      if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    if (t >= nq) break;
+    if (tok.hist1) {
+      uint64_t* gh = reinterpret_cast<uint64_t*>(tok.hist1 + (row + t) * 4096);
+      for (int i = threadIdx.x; i < 2048; i += NT) {
+        const uint32_t v = hist[t][i];
+        if (v) atomic_add_agent64(gh + i, (uint64_t)(v & 0xFFFFu) | ((uint64_t)(v >> 16) << 32));
+      }
+    } else if (tok.tile_hist) {
+      // The tile's histogram as it stands (two 16-bit bins per word), one
+      // slot per tile: plain stores, nothing to clear beforehand.
+      v4u* th = reinterpret_cast<v4u*>(tok.tile_hist + ((row + t) * tok.th_stride + blockIdx.x) * 2048);
+      for (int i = threadIdx.x; i < 512; i += NT) th[i] = reinterpret_cast<const v4u*>(hist[t])[i];
     }
-  } else if (tok.tile_hist) {
-    // The tile's histogram as it stands (two 16-bit bins per word), one slot
-    // per tile: plain stores, nothing to clear beforehand.
-    v4u* th = reinterpret_cast<v4u*>(tok.tile_hist + (row * tok.th_stride + blockIdx.x) * 2048);
-    for (int i = threadIdx.x; i < 512; i += NT) th[i] = reinterpret_cast<const v4u*>(hist)[i];
   }
   if (pool) {
     uint64_t* gbh = reinterpret_cast<uint64_t*>(blk.hist1 + row * 4096);
@@ -428,10 +505,35 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
 
 // Flat-scan tile: the largest that still gives every compute unit a
 // workgroup (16-wave workgroups), else kScanTileSmall.
-static int scan_tile(int64_t rows, int64_t n_max, int nw) {
-  int tile = nw == 16 ? kScanTileMax : kScanTileSmall;
+// (`rows` counts workgroup rows: query rows, or groups of them)
+static int scan_tile(int64_t rows, int64_t n_max, int nw, int qt = 1) {
+  int tile = qt > 1 ? 1024 * nw : (nw == 16 ? kScanTileMax : kScanTileSmall);
   while (tile > kScanTileSmall && rows * ((n_max + tile - 1) / tile) < device_cu_count()) tile >>= 1;
   return tile;
+}
+
+// Query rows per scan workgroup: 2..15 query rows of one sequence (multi-
+// query decode; 16 or more take the dense prefill product) share one pass
+// over the key rows when D_I = 128 and there are at most 8 indexer heads
+// (two queries fill one 16-row MFMA block).
+static int scan_qt(const ScoreArgs& a) {
+  if (a.pool_block > 0 || a.D_I != 128 || a.H_I > 8 || a.Tq < 2) return 1;
+  return a.Tq == 2 ? 2 : 4;
+}
+
+template <int QT>
+static hipError_t launch_scan_mq(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                                 const SelectWs& tok, hipStream_t s) {
+  constexpr int NW = kScanWavesT<false, 1, QT>;
+  const int64_t groups = (int64_t)a.B * ((a.Tq + QT - 1) / QT);
+  const int tile = scan_tile(groups, a.n_max, NW, QT);
+  int64_t tiles = (a.n_max + tile - 1) / tile;
+  if (tiles < 1) tiles = 1;
+  CSA2_LAUNCH("index_score", (index_score_kernel<128, 1, false, false, true, QT>), dim3((unsigned)tiles, (unsigned)groups),
+              dim3(64 * NW), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
+              (const int32_t*)nullptr, (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys,
+              key_stride, n_valid, tok, 0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, tok);
+  return hipGetLastError();
 }
 
 template <int DI, int HB, bool H8>
@@ -446,12 +548,12 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
   SelectWs bw = blk ? *blk : tok;
   dim3 grid((unsigned)tiles, (unsigned)rows);
   if (a.pool_block > 0) {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8, 1>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
                 a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok,
                 a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
   } else {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8, 1>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
                 a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok, 0,
                 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, bw);
@@ -467,7 +569,7 @@ static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint
   int64_t rows = (int64_t)B * Tq;
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8>), dim3((unsigned)tiles, (unsigned)rows),
+  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8, 1>), dim3((unsigned)tiles, (unsigned)rows),
               dim3(64 * kScanWavesT<true, HB>),
               0, s, q_idx, w, k_idx, k_bstride, k_rstride, ctx_len, (const int32_t*)nullptr,
               pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, key_stride, n_valid, ws,
@@ -854,6 +956,11 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
                               const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                               const SelectWs* blk, hipStream_t s) {
   if (prefill_gemm_applies(a)) return launch_prefill(a, keys, key_stride, n_valid, tok, s);
+  switch (scan_qt(a)) {
+    case 2: return launch_scan_mq<2>(a, keys, key_stride, n_valid, tok, s);
+    case 4: return launch_scan_mq<4>(a, keys, key_stride, n_valid, tok, s);
+    default: break;
+  }
 #define CALL_SCAN(D, H, E) launch_scan_t<D, H, E>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
   CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_SCAN);
 #undef CALL_SCAN
@@ -861,8 +968,15 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
 
 int64_t index_score_tiles(const ScoreArgs& a) {
   if (prefill_gemm_applies(a)) return 0;
-  const int64_t rows = (int64_t)a.B * a.Tq;
-  const int tile = scan_tile(rows, a.n_max, a.H_I <= 16 ? kScanWavesT<false, 1> : kScanWavesT<false, 2>);
+  const int qt = scan_qt(a);
+  int tile;
+  if (qt == 2) {
+    tile = scan_tile((int64_t)a.B * ((a.Tq + 1) / 2), a.n_max, kScanWavesT<false, 1, 2>, 2);
+  } else if (qt == 4) {
+    tile = scan_tile((int64_t)a.B * ((a.Tq + 3) / 4), a.n_max, kScanWavesT<false, 1, 4>, 4);
+  } else {
+    tile = scan_tile((int64_t)a.B * a.Tq, a.n_max, a.H_I <= 16 ? kScanWavesT<false, 1> : kScanWavesT<false, 2>);
+  }
   const int64_t tiles = (a.n_max + tile - 1) / tile;
   return tiles < 1 ? 1 : tiles;
 }

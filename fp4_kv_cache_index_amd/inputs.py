@@ -83,6 +83,11 @@ WORKLOADS = {
     "prefill256k": Workload("prefill: B1, 4096 new tokens on 256K ctx, causal, top-2048", 4,
                             B=1, N=262144 + 4096, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048,
                             Tq=4096),
+    # Multi-query decode (speculative verification): two query tokens per
+    # sequence, scored in one pass over the key cache.
+    "mq2_64k": Workload("multi-query decode: B64 x 64K ctx, 2 query tokens per sequence, Full, 64 heads, "
+                        "indexer 8x128, top-2048", 6,
+                        B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048, Tq=2),
     # The pages' own shapes: 512-wide K=V row, indexer 32 x 128, top-512.
     "pages512": Workload("pages' shape: B2 x 8192 ctx, d 512 (K=V), indexer 32x128, top-512", 5,
                          B=2, N=8192, H=64, d_qk=512, d_v=512, H_I=32, D_I=128, K=512,

@@ -304,3 +304,46 @@ def test_pool_ids_outside_the_context_are_skipped(pool_cap):
         assert np.array_equal(np_(later["topk_score"])[b, 0], want_s)
         got = np_(later["topk_idx"])[b, 0]
         assert got[got >= 0].max() < ch[b]
+
+
+@gpu
+@pytest.mark.parametrize("Tq", [2, 3, 4, 7])
+@pytest.mark.parametrize("N,H_I", [(20000, 8), (70001, 5)])
+def test_multi_query_decode_shares_one_key_pass(Tq, N, H_I):
+    """2..15 query rows per sequence (speculative verification): one scan
+    workgroup scores 2 or 4 rows against each key tile.  Every row must equal
+    its own single-row oracle: causal positions at the end of the context,
+    a row with a short visible prefix, ragged contexts, both select designs."""
+    require_gpu()
+    announce(f"multi-query decode Tq={Tq} N={N} H_I={H_I}")
+    B, D_I, K = 3, 128, 512
+    k_idx = inputs.int_e4m3((B, N, D_I), 61, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 61, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 61, 1, "w", device="cuda")
+    ctx = torch.tensor([N, N - 17, N // 3], dtype=torch.int32, device="cuda")
+    q_pos = (ctx[:, None].to(torch.int64) - Tq + torch.arange(Tq, device="cuda")[None, :]).to(torch.int32)
+    q_pos[1, 0] = 300        # a short visible prefix inside a group
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos.contiguous())
+    _run_and_check(q_idx, w, k_idx, ctx, K)   # no positions: every row sees its whole context
+
+
+@gpu
+def test_multi_query_decode64k_sampled_rows():
+    """Two query tokens per sequence at 64 x 64K, the launch shape the
+    benchmark times; rows of the first and last sequence are checked."""
+    require_gpu()
+    announce("multi-query decode B64 x 64K Tq=2, sequences 0 and 63 sampled")
+    B, N, Tq, H_I, D_I, K = 64, 65536, 2, 8, 128, 2048
+    k_idx = inputs.int_e4m3((B, N, D_I), 62, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 62, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 62, 1, "w", device="cuda")
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    q_pos = (torch.arange(Tq, dtype=torch.int32, device="cuda") + N - Tq).repeat(B, 1).contiguous()
+    res = csa2.csa2_index_score_topk(q_idx, w, k_idx, ctx, K, q_pos=q_pos, want_scores=True)
+    torch.cuda.synchronize()
+    for b in (0, B - 1):
+        for t in range(Tq):
+            s = I.index_scores(np_(q_idx[b, t]), np_(w[b, t]), np_(k_idx[b]), N - Tq + t + 1)
+            want_i, want_s = topk_select(s, N - Tq + t + 1, K)
+            assert np.array_equal(np_(res["topk_idx"][b, t]), want_i), (b, t)
+            assert np.array_equal(np_(res["topk_score"][b, t]), want_s), (b, t)
