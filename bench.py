@@ -134,6 +134,8 @@ def layer_bytes(wl, kind, pool_cap=0):
     row = d // 2 + d // 16            # FP4 main row: codes + E4M3 scales
     swa = d + d // 32                 # window row: E4M3 values + E8M0 scales
     attn = K * row + W * swa + 4 * H * d + 4 * H * wl.d_v
+    if wl.page_size:
+        attn += 4 * K                 # the block-table entry of every Top-K token
     idx_q = wl.H_I * wl.D_I + 4 * wl.H_I
     if kind in ("full", "reindex"):
         b = wl.D_I * wl.N + idx_q + 8 * K + attn
@@ -165,6 +167,21 @@ class Case:
             x = inputs.kv_rows_seq(wl, b, device=dev)
             csa2.kv_fp4_quantize(x, codes=self.codes[b], scales=self.scales[b])
             del x
+        if wl.page_size:
+            # Serving layout: the same rows in a pool of pages handed out in a
+            # random order, and each window in a ring (row = position % W).
+            P = wl.page_size
+            npg = (N + P - 1) // P
+            self.n_pages = B * npg + 64
+            self.block_table = inputs.page_order(self.n_pages, B * npg, wl.seed, device=dev).view(B, npg).to(
+                torch.int32).contiguous()
+            self.pool = torch.empty(self.n_pages * P, self.cache.shape[-1], dtype=torch.uint8, device=dev)
+            j = torch.arange(N, device=dev)
+            for b in range(B):
+                self.pool.index_copy_(0, self.block_table[b, j // P].to(torch.int64) * P + j % P, self.cache[b])
+            del self.cache, self.codes, self.scales
+            self.pool_codes, self.pool_scales = self.pool[:, : d // 2], self.pool[:, d // 2:]
+            self.swa_end = torch.full((B,), N, dtype=torch.int32, device=dev)
         self.k_idx = inputs.int_e4m3((B, N, wl.D_I), wl.seed, 0, "k_idx", device=dev)
         self.ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
         self.swa_len = torch.full((B,), wl.W, dtype=torch.int32, device=dev)
@@ -172,6 +189,10 @@ class Case:
         for li, kind in enumerate(wl.layers):
             lay = inputs.decode_layer_inputs(wl, li, device=dev)
             sv, ss = csa2.swa_fp8_quantize(lay["swa_x"])
+            if wl.page_size:   # window rows of positions N-W .. N-1 into their ring rows
+                ring = (torch.arange(wl.W, device=dev) + N - wl.W) % wl.W
+                sv = torch.empty_like(sv).index_copy_(1, ring, sv)
+                ss = torch.empty_like(ss).index_copy_(1, ring, ss)
             ent = {"kind": kind, "q_idx": lay["q_idx"], "w": lay["w"], "sv": sv, "ss": ss,
                    "q": lay["q"] if wl.Tq > 1 else lay["q"][:, 0].contiguous()}
             self.layers.append(ent)
@@ -186,7 +207,7 @@ class Case:
         pb, nb = (wl.pool_block, wl.pool_nblocks) if wl.pool_block else (0, 0)
         self.ws_idx = self._ws(csa2.csa2_index_score_topk_workspace_size(B, wl.Tq, N, wl.K, pb, nb))
         self.ws_attn = self._ws(csa2.csa2_sparse_attn_prefill_workspace_size(B, wl.Tq, wl.H, wl.d_v, wl.K, wl.W)
-                                if wl.Tq > 1 else csa2.csa2_sparse_attn_decode_workspace_size(B, wl.H, wl.d_v, wl.K,
+                                if wl.Tq > 1 or wl.page_size else csa2.csa2_sparse_attn_decode_workspace_size(B, wl.H, wl.d_v, wl.K,
                                                                                             wl.W))
         self.pool_cap = nb * pb
         self.ws_pool = self._ws(csa2.csa2_hier_pool_topk_workspace_size(B, 1, self.pool_cap, wl.K)) if pb else None
@@ -225,7 +246,13 @@ class Case:
                 idx = prev
             else:
                 raise ValueError(kind)
-            if wl.Tq > 1:
+            if wl.page_size:
+                out = self.out.view(wl.B, wl.Tq, wl.H, wl.d_v)
+                q4 = L["q"] if wl.Tq > 1 else L["q"].view(wl.B, 1, wl.H, wl.d_qk)
+                csa2.csa2_sparse_attn_paged(q4, self.pool_codes, self.pool_scales, self.block_table, wl.page_size, idx,
+                                            self.ctx, self.q_pos, L["sv"], L["ss"], self.swa_end, wl.W,
+                                            wl.softmax_scale, d_v=wl.d_v, workspace=self.ws_attn, out=out)
+            elif wl.Tq > 1:
                 out = self.out.view(wl.B, wl.Tq, wl.H, wl.d_v)
                 csa2.csa2_sparse_attn_prefill(L["q"], self.codes, self.scales, idx, self.ctx, self.q_pos, L["sv"],
                                               L["ss"], self.swa_pos0, wl.W, wl.softmax_scale, d_v=wl.d_v,

@@ -52,6 +52,12 @@ _SIGS = {
                                                 c_void_p, c_int64, c_int64, c_void_p, c_int32, c_int32, c_void_p,
                                                 c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
                                                 c_void_p, c_void_p, c_size_t, c_void_p]),
+    "csa2_sparse_attn_paged_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "csa2_sparse_attn_paged": (ctypes.c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                              c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                              c_int64, c_int64, c_void_p, c_int64, c_int64, c_int32, c_void_p,
+                                              c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                              c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "csa2_trace_attach": (ctypes.c_int, [ctypes.POINTER(c_void_p), ctypes.POINTER(ctypes.c_char_p), c_int32]),
     "csa2_trace_only": (ctypes.c_int, [ctypes.c_char_p]),
     "csa2_trace_detach": (ctypes.c_int, [ctypes.POINTER(c_int32)]),
@@ -341,6 +347,68 @@ def csa2_sparse_attn_prefill(q, kv_codes, kv_scales, topk_idx, ctx_len, q_pos, s
                                           _ptr(swa_scales), xb, xr, _ptr(swa_pos0), swa_rows, W, _ptr(sink), B, Tq,
                                           H, d_qk, d_v, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
                                           ws_bytes, _stream(dev)), "csa2_sparse_attn_prefill")
+    return out, lse
+
+
+def csa2_sparse_attn_paged_workspace_size(B, Tq, H, d_v, k_top, W):
+    return lib().csa2_sparse_attn_paged_workspace_size(B, Tq, H, d_v, k_top, W)
+
+
+def csa2_sparse_attn_paged(q, pool_codes, pool_scales, block_table, page_size, topk_idx, ctx_len, q_pos, ring_vals,
+                           ring_scales, swa_end, W, softmax_scale, d_v=512, sink=None, want_lse=False,
+                           workspace=None, out=None, lse=None):
+    """Attention over a paged main cache and ring windows.
+
+    q [B][Tq][H][d_qk] f32; pool_codes [rows][d_qk/2] u8 and pool_scales
+    [rows][d_qk/16] u8 (the page pool, rows = n_pages * page_size; views of one
+    interleaved pool are fine); block_table [B][max_pages] i32; topk_idx
+    [B][Tq][K] i32 token ids; q_pos [B][Tq] i32 (None when Tq == 1);
+    ring_vals [B][R][d_qk] u8, ring_scales [B][R][d_qk/32] u8, swa_end [B] i32
+    (or all None for no window).  Returns (out [B][Tq][H][d_v], lse or None).
+    """
+    _gpu(q, "q", torch.float32)
+    _gpu(pool_codes, "pool_codes", torch.uint8)
+    _gpu(pool_scales, "pool_scales", torch.uint8)
+    _gpu(block_table, "block_table", torch.int32)
+    _gpu(topk_idx, "topk_idx", torch.int32)
+    _gpu(ctx_len, "ctx_len", torch.int32)
+    if not (q.is_contiguous() and topk_idx.is_contiguous() and block_table.is_contiguous()):
+        raise ValueError("q, topk_idx and block_table must be contiguous")
+    if pool_codes.dim() != 2 or pool_codes.stride(1) != 1 or pool_scales.dim() != 2 or pool_scales.stride(1) != 1:
+        raise ValueError("pool_codes / pool_scales must be [rows][bytes] with unit inner stride")
+    B, Tq, H, d_qk = q.shape
+    k_top = topk_idx.shape[-1]
+    n_rows = pool_codes.shape[0]
+    if n_rows % page_size:
+        raise ValueError("the pool must hold whole pages")
+    if q_pos is not None:
+        _gpu(q_pos, "q_pos", torch.int32)
+    if ring_vals is not None:
+        _gpu(ring_vals, "ring_vals", torch.uint8)
+        _gpu(ring_scales, "ring_scales", torch.uint8)
+        _gpu(swa_end, "swa_end", torch.int32)
+        vb, vr = _row_strides(ring_vals, "ring_vals")
+        xb, xr = _row_strides(ring_scales, "ring_scales")
+        R = ring_vals.shape[1]
+    else:
+        vb = vr = xb = xr = 0
+        R = 0
+        W = 0
+    if sink is not None:
+        _gpu(sink, "sink", torch.float32)
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, Tq, H, d_v, dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty(B, Tq, H, dtype=torch.float32, device=dev)
+    need = csa2_sparse_attn_paged_workspace_size(B, Tq, H, d_v, k_top, W)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    _check(lib().csa2_sparse_attn_paged(_ptr(q), _ptr(pool_codes), pool_codes.stride(0), _ptr(pool_scales),
+                                        pool_scales.stride(0), _ptr(block_table), block_table.stride(0), page_size,
+                                        n_rows // page_size, _ptr(topk_idx), k_top, _ptr(ctx_len), _ptr(q_pos),
+                                        _ptr(ring_vals), vb, vr, _ptr(ring_scales), xb, xr, R, _ptr(swa_end), W,
+                                        _ptr(sink), B, Tq, H, d_qk, d_v, float(softmax_scale), _ptr(out),
+                                        _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)), "csa2_sparse_attn_paged")
     return out, lse
 
 

@@ -396,6 +396,49 @@ int csa2_sparse_attn_prefill(const float* q, const uint8_t* kv_codes, int64_t c_
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }
 
+size_t csa2_sparse_attn_paged_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d_v, int32_t k_top,
+                                             int32_t W) {
+  return csa2_sparse_attn_prefill_workspace_size(B, Tq, H, d_v, k_top, W);
+}
+
+int csa2_sparse_attn_paged(const float* q, const uint8_t* kv_codes, int64_t c_row_stride, const uint8_t* kv_scales,
+                           int64_t s_row_stride, const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                           int32_t n_pages, const int32_t* topk_idx, int32_t k_top, const int32_t* ctx_len,
+                           const int32_t* q_pos, const uint8_t* swa_vals, int64_t sv_batch_stride,
+                           int64_t sv_row_stride, const uint8_t* swa_scales, int64_t ss_batch_stride,
+                           int64_t ss_row_stride, int32_t swa_ring, const int32_t* swa_end, int32_t W,
+                           const float* sink, int32_t B, int32_t Tq, int32_t H, int32_t d_qk, int32_t d_v,
+                           float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || Tq < 0) return CSA2_EINVAL;
+  if (B == 0 || Tq == 0) return CSA2_OK;
+  int st = attn_common_check(q, kv_codes, 0, c_row_stride, kv_scales, 0, s_row_stride, topk_idx, k_top, ctx_len,
+                             swa_vals, sv_batch_stride, sv_row_stride, swa_scales, ss_batch_stride, ss_row_stride, W,
+                             B, H, d_qk, d_v, out);
+  if (st != CSA2_OK) return st;
+  if (!block_table || bt_stride < 1 || n_pages < 1) return CSA2_EINVAL;
+  if (page_size < 1 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0) return CSA2_EINVAL;
+  if ((int64_t)n_pages * page_size > INT32_MAX) return CSA2_EUNSUPPORTED;   // pool rows are 32-bit
+  if (!q_pos && Tq != 1) return CSA2_EINVAL;
+  if (W > 0 && (swa_ring < 1 || !swa_end)) return CSA2_EINVAL;
+  if (k_top + W == 0) return CSA2_EINVAL;
+  if ((int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
+  if (!ws || ((uintptr_t)ws & 255u)) return CSA2_EINVAL;
+  if (ws_bytes < csa2_sparse_attn_paged_workspace_size(B, Tq, H, d_v, k_top, W)) return CSA2_EWORKSPACE;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  AttnArgs a{q, kv_codes, 0, c_row_stride, kv_scales, 0, s_row_stride, topk_idx, k_top, ctx_len, q_pos, swa_vals,
+             sv_batch_stride, sv_row_stride, swa_scales, ss_batch_stride, ss_row_stride, nullptr, nullptr, 0, W, sink,
+             B, Tq, H, d_qk, d_v, softmax_scale, out, lse};
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.page_shift = shift;
+  a.n_pages = n_pages;
+  a.swa_ring = W > 0 ? swa_ring : 0;
+  a.swa_end = swa_end;
+  hipError_t e = launch_sparse_attn(a, Tq > 1, ws, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
 int csa2_trace_attach(void** events, const char** names, int32_t capacity) {
   if (capacity < 0 || (capacity > 0 && !events)) return CSA2_EINVAL;
   Trace& t = thread_trace();

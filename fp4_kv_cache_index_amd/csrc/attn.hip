@@ -82,7 +82,10 @@ struct RawTask {
   uint32_t kind;      // 0 skip, 1 main, 2 window
 };
 
-template <int DQK, int DV>
+// PAGED: main rows live in a page pool; a Top-K token id is translated to its
+// pool row (block-table page, offset in the page) when the entry ids are
+// staged, one iteration before the gather reads them.
+template <int DQK, int DV, bool PAGED>
 __global__ void __launch_bounds__(kAttnThreads)
 sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
                          float* __restrict__ part_o, float* __restrict__ part_ml) {
@@ -122,7 +125,20 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 
   const int64_t ctx = a.ctx_len[b];
   int64_t swa_r0 = 0, n_swa = 0;
-  if (prefill) {
+  const int64_t ring = a.swa_ring;
+  if (ring > 0) {
+    // Ring window: position x at row x % ring; the ring holds positions
+    // swa_end - ring .. swa_end - 1.  The query at p sees the window
+    // positions max(p - W + 1, swa_end - ring, 0) .. min(p, swa_end - 1).
+    const int64_t p = a.q_pos ? (int64_t)a.q_pos[row] : ctx - 1;
+    const int64_t end = a.swa_end[b];
+    int64_t lo = p - a.W + 1;
+    if (end - ring > lo) lo = end - ring;
+    if (lo < 0) lo = 0;
+    const int64_t hi = p < end - 1 ? p : end - 1;
+    swa_r0 = lo;                      // first position
+    n_swa = hi >= lo ? hi - lo + 1 : 0;
+  } else if (prefill) {
     int64_t p = a.q_pos[row];
     int64_t p0 = a.swa_pos0[b];
     int64_t lo = p - a.W + 1 > p0 ? p - a.W + 1 : p0;
@@ -139,7 +155,21 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     if (ce >= e_end) return -1;
     if (ce < K) return raw >= 0 && raw < ctx ? raw : -1;
     const int64_t wv = ce - K;
-    return wv < n_swa ? (int32_t)(swa_r0 + wv) : -1;
+    if (wv >= n_swa) return -1;
+    return ring > 0 ? (int32_t)((swa_r0 + wv) % ring) : (int32_t)(swa_r0 + wv);
+  };
+  // Paged main rows: the block-table entry of a token (a load from a
+  // clamped, in-range address) and the pool row it names; a token past the
+  // block table or on a missing page (entry < 0 or >= n_pages) is skipped.
+  const int32_t* bt_row = PAGED ? a.block_table + b * a.bt_stride : nullptr;
+  auto page_of = [&](int ce, int32_t id) -> int32_t {
+    const bool m = ce < K && id >= 0 && (int64_t)(id >> a.page_shift) < a.bt_stride;
+    return bt_row[m ? (id >> a.page_shift) : 0];
+  };
+  auto pool_row = [&](int ce, int32_t id, int32_t pg) -> int32_t {
+    if (ce >= K || id < 0) return id;   // window rows and skipped entries
+    if ((int64_t)(id >> a.page_shift) >= a.bt_stride || pg < 0 || pg >= a.n_pages) return -1;
+    return (pg << a.page_shift) | (id & ((1 << a.page_shift) - 1));
   };
   // Ids of the first three chunks (one entry per thread).
   static_assert(3 * kChunk <= kAttnThreads, "one entry per thread");
@@ -157,7 +187,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const int i = (int)threadIdx.x + u * kAttnThreads;
     qv[u] = qrow[i < n4 ? i : n4 - 1];
   }
-  if (threadIdx.x < 3 * kChunk) eidc[threadIdx.x / kChunk][threadIdx.x % kChunk] = entry_id(ce0, ld0);
+  if constexpr (PAGED) {
+    if (threadIdx.x < 3 * kChunk) {
+      const int32_t v0 = entry_id(ce0, ld0);
+      eidc[threadIdx.x / kChunk][threadIdx.x % kChunk] = pool_row(ce0, v0, page_of(ce0, v0));
+    }
+  } else {
+    if (threadIdx.x < 3 * kChunk) eidc[threadIdx.x / kChunk][threadIdx.x % kChunk] = entry_id(ce0, ld0);
+  }
 
   // Roles: waves 0..3 are S waves (16 heads each, every entry of a chunk),
   // waves 4..7 PV waves (every head, a quarter of the output dims each).
@@ -437,11 +474,21 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   // Wave 4 keeps the raw ids of chunk it+3 in flight: issued before the
   // loads of chunk it+1, so the dequantisation's wait for those covers them,
   // and no wait for the gather is needed anywhere else in the loop.
+  // Paged: the raw ids are loaded two chunks ahead, validated and their
+  // block-table entries loaded one chunk ahead, and the pool rows staged.
   const bool id_lane = wave == 4 && lane < kChunk && K > 0;
-  int32_t ldn = 0;
+  int32_t ldn = 0, vn = -1, pgn = 0;
   if (id_lane) {
     const int ce = e_begin + 3 * kChunk + lane;
-    ldn = idx_row[ce < K ? ce : K - 1];
+    if constexpr (PAGED) {
+      const int32_t r3 = idx_row[ce < K ? ce : K - 1];
+      const int c4 = ce + kChunk;
+      ldn = idx_row[c4 < K ? c4 : K - 1];
+      vn = entry_id(ce, r3);
+      pgn = page_of(ce, vn);
+    } else {
+      ldn = idx_row[ce < K ? ce : K - 1];
+    }
   }
   if (nch > 0) store(kbuf[0]);
   if (nch > 1) gather(e_begin + kChunk, 1);
@@ -457,9 +504,18 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       store(kbuf[kb_next]);
       if (id_lane) {
         const int ce = c0 + 3 * kChunk + lane;
-        if (it + 3 < nch) eidc[(it + 3) & 3][lane] = entry_id(ce, ldn);
-        const int cn = ce + kChunk;
-        ldn = idx_row[cn < K ? cn : K - 1];
+        if constexpr (PAGED) {
+          if (it + 3 < nch) eidc[(it + 3) & 3][lane] = pool_row(ce, vn, pgn);
+          const int c4 = ce + kChunk;
+          vn = entry_id(c4, ldn);
+          pgn = page_of(c4, vn);
+          const int c5 = c4 + kChunk;
+          ldn = idx_row[c5 < K ? c5 : K - 1];
+        } else {
+          if (it + 3 < nch) eidc[(it + 3) & 3][lane] = entry_id(ce, ldn);
+          const int cn = ce + kChunk;
+          ldn = idx_row[cn < K ? cn : K - 1];
+        }
       }
       if (it + 2 < nch) gather(c0 + 2 * kChunk, (it + 2) & 3);
     }
@@ -640,7 +696,7 @@ size_t attn_ws_bytes(int64_t rows, int H, int d_v, int splits) {
   return ((po + 255) & ~(size_t)255) + ((pm + 255) & ~(size_t)255);
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool PAGED>
 static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.Tq;
   const int splits = attn_num_splits(rows, a.k_top, a.W);
@@ -651,7 +707,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipSt
   size_t po = sizeof(float) * (size_t)rows * real_splits * a.H * DV;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + ((po + 255) & ~(size_t)255));
-  CSA2_LAUNCH("sparse_attn_split", (sparse_attn_split_kernel<DQK, DV>), dim3(real_splits, (unsigned)rows),
+  CSA2_LAUNCH("sparse_attn_split", (sparse_attn_split_kernel<DQK, DV, PAGED>), dim3(real_splits, (unsigned)rows),
               dim3(kAttnThreads), 0, s, a, prefill ? 1 : 0, real_splits, span, part_o, part_ml);
   if (real_splits > 1) {   // (a single split normalises and writes the output itself)
     // Up to 4 splits: one group of 128 threads (4 dims each) with every
@@ -677,8 +733,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipSt
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, bool prefill, void* ws, hipStream_t s) {
-  if (a.d_qk == 576 && a.d_v == 512) return launch_attn_t<576, 512>(a, prefill, ws, s);
-  if (a.d_qk == 512 && a.d_v == 512) return launch_attn_t<512, 512>(a, prefill, ws, s);
+  const bool paged = a.block_table != nullptr;
+  if (a.d_qk == 576 && a.d_v == 512)
+    return paged ? launch_attn_t<576, 512, true>(a, prefill, ws, s) : launch_attn_t<576, 512, false>(a, prefill, ws, s);
+  if (a.d_qk == 512 && a.d_v == 512)
+    return paged ? launch_attn_t<512, 512, true>(a, prefill, ws, s) : launch_attn_t<512, 512, false>(a, prefill, ws, s);
   return hipErrorInvalidValue;
 }
 

@@ -151,6 +151,12 @@ struct AttnArgs {
   int W; const float* sink;
   int B, Tq, H, d_qk, d_v; float softmax_scale;
   float* out; float* lse;
+  // Paged main rows (block_table != null): pool row of token j of sequence b
+  // = block_table[b * bt_stride + (j >> page_shift)] << page_shift | (j & mask).
+  const int32_t* block_table = nullptr; int64_t bt_stride = 0; int page_shift = 0; int n_pages = 0;
+  // Ring window (swa_ring > 0): position x at row x % swa_ring; swa_end[b]
+  // is one past the newest position written.
+  int swa_ring = 0; const int32_t* swa_end = nullptr;
 };
 int attn_num_splits(int64_t rows, int k_top, int W);
 size_t attn_ws_bytes(int64_t rows, int H, int d_v, int splits);

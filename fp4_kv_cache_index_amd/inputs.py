@@ -62,6 +62,7 @@ class Workload:
     pool_block: int = 0
     pool_nblocks: int = 0
     softmax_scale: float = 0.0
+    page_size: int = 0   # > 0: main rows in a page pool (random page order), window in a ring
 
     def __post_init__(self):
         if self.softmax_scale == 0.0:
@@ -88,6 +89,11 @@ WORKLOADS = {
     "mq2_64k": Workload("multi-query decode: B64 x 64K ctx, 2 query tokens per sequence, Full, 64 heads, "
                         "indexer 8x128, top-2048", 6,
                         B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048, Tq=2),
+    # Serving layout: the decode64k step with the main rows in a pool of
+    # 64-token pages (random page order) and each window in a 128-row ring.
+    "paged64k": Workload("paged decode: B64 x 64K ctx, 64-token pages, ring window, Full, 64 heads, "
+                         "indexer 8x128, top-2048", 7,
+                         B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048, page_size=64),
     # The pages' own shapes: 512-wide K=V row, indexer 32 x 128, top-512.
     "pages512": Workload("pages' shape: B2 x 8192 ctx, d 512 (K=V), indexer 32x128, top-512", 5,
                          B=2, N=8192, H=64, d_qk=512, d_v=512, H_I=32, D_I=128, K=512,
@@ -138,6 +144,12 @@ def random_index_lists(B, K, N, seed, layer=0, device="cpu", n_invalid=0):
         bad[:, ::2] = N + 7
         out[:, K - n_invalid:] = bad
     return out
+
+
+def page_order(n_pages, n_used, seed, device="cpu"):
+    """A random order of the pool's pages (the first n_used are handed out)."""
+    g = _gen(seed, 0, "kv", device)
+    return torch.randperm(n_pages, generator=g, device=device)[:n_used]
 
 
 def kv_rows_seq(wl, b, device="cpu"):

@@ -257,6 +257,45 @@ int csa2_sparse_attn_prefill(const float* q,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_sparse_attn_paged -- the same attention over a serving-cache layout
+ * (techniques map, technique tree: KV cache management; fact sheet: every
+ * layer keeps its own 128-token window): the main KV rows of all sequences
+ * live in one page pool, and each sequence's window is a ring.  Decode (Tq =
+ * 1) and multi-query decode / prefill chunks (Tq > 1, one Top-K list per
+ * query row).
+ *   Page pool: rows 0 .. n_pages*page_size-1, row r at kv_codes +
+ *     r*c_row_stride (d_qk/2 bytes) and kv_scales + r*s_row_stride (d_qk/16
+ *     bytes).  Token j of sequence b is pool row
+ *     block_table[b*bt_stride + j/page_size] * page_size + j % page_size.
+ *     page_size: a power of two; n_pages * page_size < 2^31.  A Top-K id < 0
+ *     or >= ctx_len[b], past the block table (j/page_size >= bt_stride) or
+ *     on a block-table entry outside [0, n_pages) is skipped, never read.
+ *   Ring window: swa_vals / swa_scales hold swa_ring rows per sequence (batch
+ *     and row strides in bytes); window position x is ring row x % swa_ring,
+ *     and swa_end[b] is one past the newest position written, so the ring
+ *     holds positions swa_end[b]-swa_ring .. swa_end[b]-1.  The query at
+ *     position p (q_pos[b][t]; NULL only when Tq == 1, then p =
+ *     ctx_len[b]-1) sees window positions max(p-W+1, swa_end[b]-swa_ring, 0)
+ *     .. min(p, swa_end[b]-1).
+ * q [B][Tq][H][d_qk]; topk_idx [B][Tq][k_top] (token ids); out
+ * [B][Tq][H][d_v]; lse [B][Tq][H] or NULL.  Supported shapes and accuracy
+ * as csa2_sparse_attn_decode; the result equals that of the linear layouts
+ * holding the same rows.
+ */
+size_t csa2_sparse_attn_paged_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d_v, int32_t k_top,
+                                             int32_t W);
+int csa2_sparse_attn_paged(const float* q,
+                           const uint8_t* kv_codes, int64_t c_row_stride,
+                           const uint8_t* kv_scales, int64_t s_row_stride,
+                           const int32_t* block_table, int64_t bt_stride, int32_t page_size, int32_t n_pages,
+                           const int32_t* topk_idx, int32_t k_top, const int32_t* ctx_len, const int32_t* q_pos,
+                           const uint8_t* swa_vals, int64_t sv_batch_stride, int64_t sv_row_stride,
+                           const uint8_t* swa_scales, int64_t ss_batch_stride, int64_t ss_row_stride,
+                           int32_t swa_ring, const int32_t* swa_end, int32_t W, const float* sink,
+                           int32_t B, int32_t Tq, int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,
+                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel trace for measurement harnesses.  While a trace is attached to the
  * calling host thread, each kernel the library launches from that thread
  * carries events[2*i] and events[2*i+1] as the start and stop events of its

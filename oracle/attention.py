@@ -25,10 +25,19 @@ Readings: d_qk = 576 / d_v = 512 follow the measured workloads' "512 + 64"
 latent; the pages' own 512-wide K=V row is the d_qk = d_v = 512 variant.
 The inverse RoPE of the output is not part of this step.
 
+Paged cache and ring window (a serving layout of the same caches, [map]
+technique tree, KV cache management; [facts] every layer's own 128-token
+window): a sequence's token j lives in pool row block_table[j // P] * P +
+j % P; window position x lives in ring row x % R, and the ring holds the R
+most recent positions.  Reading: the entries and the arithmetic are those of
+the linear layout; only the addressing differs.
+
 Parity: pinned by closed forms -- one entry returns exactly its V, q = 0
 returns the mean of V, sink = -inf equals no sink, a huge sink drives o to 0,
 K >= context equals dense softmax attention written independently, and the
-result is invariant under permuting the Top-K list (tests/test_oracle_attention.py).
+result is invariant under permuting the Top-K list; the paged/ring row equals
+the linear-layout row on caches scattered by a test-written block table and
+ring placement (tests/test_oracle_attention.py).
 """
 
 import numpy as np
@@ -110,4 +119,52 @@ def sparse_attn_prefill_row(q, kv_codes, kv_scales, idx, ctx_len, q_pos, swa_val
     if len(wr):
         rows.append(mxfp8_dequantize(swa_vals[wr], swa_scales[wr], d_qk))
     keys = np.concatenate(rows, axis=0) if rows else np.zeros((0, d_qk))
+    return attend(q, keys, d_v, scale, sink)
+
+
+def paged_row(block_table, page_size, token):
+    """Pool row of a sequence's token in a paged cache: the page named by the
+    sequence's block-table entry token // page_size, at offset token % page_size.
+    Returns -1 when the block table has no entry there or it is negative."""
+    slot = int(token) // int(page_size)
+    if slot < 0 or slot >= len(block_table) or int(block_table[slot]) < 0:
+        return -1
+    return int(block_table[slot]) * int(page_size) + int(token) % int(page_size)
+
+
+def ring_window_rows(q_pos, window, swa_end, ring):
+    """Ring rows of the window positions a query at q_pos sees: positions
+    max(q_pos - window + 1, swa_end - ring, 0) .. min(q_pos, swa_end - 1), the
+    ring holding position x at row x % ring (and positions swa_end - ring ..
+    swa_end - 1 only)."""
+    lo = max(int(q_pos) - int(window) + 1, int(swa_end) - int(ring), 0)
+    hi = min(int(q_pos), int(swa_end) - 1)
+    return np.array([x % int(ring) for x in range(lo, hi + 1)], dtype=np.int64)
+
+
+def sparse_attn_paged_row(q, pool_codes, pool_scales, block_table, page_size, n_pages, idx, ctx_len, q_pos,
+                          ring_vals, ring_scales, ring, swa_end, window, d_qk, d_v, scale, sink=None):
+    """One query of a paged main cache with a ring window.
+
+    pool_codes / pool_scales: the page pool's rows [n_pages * page_size][...];
+    block_table: the sequence's page numbers; idx: logical token ids (Top-K),
+    skipped when < 0, >= ctx_len, or when their page entry is missing or not
+    a page of the pool; ring_vals / ring_scales: the sequence's ring [ring][...].
+    """
+    rows = []
+    for t in np.asarray(idx, dtype=np.int64):
+        if t < 0 or t >= int(ctx_len):
+            continue
+        r = paged_row(block_table, page_size, t)
+        if r < 0 or r >= int(n_pages) * int(page_size):
+            continue
+        rows.append(r)
+    keys = []
+    if rows:
+        rows = np.array(rows, dtype=np.int64)
+        keys.append(fp4_dequantize(pool_codes[rows], pool_scales[rows], d_qk))
+    wr = ring_window_rows(q_pos, window, swa_end, ring) if ring_vals is not None else np.zeros(0, np.int64)
+    if len(wr):
+        keys.append(mxfp8_dequantize(ring_vals[wr], ring_scales[wr], d_qk))
+    keys = np.concatenate(keys, axis=0) if keys else np.zeros((0, d_qk))
     return attend(q, keys, d_v, scale, sink)

@@ -111,3 +111,57 @@ def test_prefill_row_equals_dense_softmax_over_hand_built_entries():
         want = softmax(z, axis=1) @ keys[:, :dv]
         assert np.allclose(out, want, rtol=1e-12, atol=1e-14), (p, ctx)
         assert np.allclose(lse, logsumexp(z, axis=1), rtol=1e-13), (p, ctx)
+
+
+def test_paged_ring_row_equals_the_linear_layout():
+    """The same rows scattered into a page pool by a random block table (with
+    unused and missing pages) and the window into a ring: the paged row must
+    equal the linear row built from the original arrays (decode: the last
+    W positions; multi-query: each query's causal window)."""
+    rng = np.random.default_rng(21)
+    n, d, dv, H, W, P = 333, 576, 512, 8, 16, 16
+    codes, scales, _ = _cache(rng, n, d)
+    n_pages = 40
+    npg = (n + P - 1) // P
+    pages = rng.permutation(n_pages)[:npg]            # logical page -> pool page
+    pool_c = np.zeros((n_pages * P, codes.shape[1]), np.uint8)
+    pool_s = np.zeros((n_pages * P, scales.shape[1]), np.uint8)
+    for j in range(n):
+        r = pages[j // P] * P + j % P
+        pool_c[r], pool_s[r] = codes[j], scales[j]
+    bt = np.full(npg + 3, -1, np.int64)
+    bt[:npg] = pages
+    R = 24                                            # ring of 24 rows, positions up to 339 written
+    swa_end = 340
+    sv_lin, ss_lin, _ = _swa(rng, swa_end, d)         # linear window array: row i = position i
+    ring_v = np.zeros((R, sv_lin.shape[1]), np.uint8)
+    ring_s = np.zeros((R, ss_lin.shape[1]), np.uint8)
+    for x in range(swa_end - R, swa_end):
+        ring_v[x % R], ring_s[x % R] = sv_lin[x], ss_lin[x]
+    scale = 0.05
+    for p in (339, 336, 330):
+        q = rng.standard_normal((H, d)).astype(np.float32)
+        idx = np.concatenate([rng.choice(n, 40, replace=False), [-1, n + 4]])
+        o1, l1 = A.sparse_attn_paged_row(q, pool_c, pool_s, bt, P, n_pages, idx, n, p, ring_v, ring_s, R,
+                                         swa_end, W, d, dv, scale)
+        # the ring holds positions swa_end - R .. swa_end - 1 (330's window
+        # starts at 315, which the ring has already overwritten)
+        o2, l2 = A.sparse_attn_prefill_row(q, codes, scales, idx, n, p, sv_lin[swa_end - R:], ss_lin[swa_end - R:],
+                                           swa_end - R, W, d, dv, scale)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), p
+    # a missing page entry drops exactly the tokens of that page
+    bt2 = bt.copy()
+    bt2[3] = -1
+    q = rng.standard_normal((H, d)).astype(np.float32)
+    idx = np.arange(40, 80)
+    o1, l1 = A.sparse_attn_paged_row(q, pool_c, pool_s, bt2, P, n_pages, idx, n, 339, None, None, R, swa_end, W,
+                                     d, dv, scale)
+    keep = idx[(idx // P) != 3]
+    o2, l2 = A.sparse_attn_decode_row(q, codes, scales, keep, n, None, None, 0, d, dv, scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # hand example of the addressing
+    assert A.paged_row([5, 2, 7], 4, 9) == 7 * 4 + 1      # token 9: slot 2, offset 1
+    assert A.paged_row([5, 2, 7], 4, 5) == 2 * 4 + 1      # token 5: slot 1, offset 1
+    assert A.paged_row([5, -1], 4, 5) == -1 and A.paged_row([5], 4, 4) == -1
+    assert A.ring_window_rows(10, 4, 11, 6).tolist() == [7 % 6, 8 % 6, 9 % 6, 10 % 6]
+    assert A.ring_window_rows(10, 8, 11, 6).tolist() == [5, 0, 1, 2, 3, 4]   # ring keeps 5..10 only
