@@ -11,6 +11,9 @@ every cache resident in HBM:
   group128k   Full -> Reindex -> Reuse layers over 16 x 128K;
   hier1m      Full layer with the 2048 x 8 candidate pool + 9 pool layers, 4 x 1M;
   prefill256k one causal chunk of 4096 queries on a 256K cache;
+  enc128k     encoder group (one cache entry per two tokens): Full + 5 Reuse
+              layers over 16 x 64K entries;
+  paged64k    decode64k with the main rows in a page pool and ring windows;
   mq2_64k     multi-query decode: 2 query tokens per sequence over 64 x 64K
               (one pass over the keys for both, then attention per token).
 Every step is timed by its own pair of HIP events; ms_per_step is their
@@ -441,7 +444,7 @@ def main():
         "vs_baseline": None, "dtype": "fp8+fp16 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.N, "query_tokens": wl.Tq,
                    "heads": wl.H, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "window": wl.W,
-                   "layers": wl.layers, "parallelism": "single GPU"},
+                   "layers": wl.layers, "tokens_per_entry": wl.m, "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "step_bytes": step_bytes,
         "step_stats": {"median_ms": round(ms, 5), "mean_ms": round(mean_ms, 5), "min_ms": round(step_ms[0], 5),
                        "max_ms": round(step_ms[-1], 5), "timed_region_ms": round(region_ms, 3),

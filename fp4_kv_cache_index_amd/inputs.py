@@ -63,6 +63,7 @@ class Workload:
     pool_nblocks: int = 0
     softmax_scale: float = 0.0
     page_size: int = 0   # > 0: main rows in a page pool (random page order), window in a ring
+    m: int = 1           # tokens per cache entry (2: the encoder layers' compressed entries); N counts entries
 
     def __post_init__(self):
         if self.softmax_scale == 0.0:
@@ -89,6 +90,12 @@ WORKLOADS = {
     "mq2_64k": Workload("multi-query decode: B64 x 64K ctx, 2 query tokens per sequence, Full, 64 heads, "
                         "indexer 8x128, top-2048", 6,
                         B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048, Tq=2),
+    # Encoder-side CSA2: one cache entry per two tokens (128K tokens -> 64K
+    # entries), a group of one Full layer and five Reuse layers.
+    "enc128k": Workload("encoder group: B16 x 128K tokens (m=2: 64K entries), Full + 5 Reuse, 64 heads, "
+                        "indexer 8x128, top-2048", 8,
+                        B=16, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048,
+                        layers=["full"] + ["reuse"] * 5, m=2),
     # Serving layout: the decode64k step with the main rows in a pool of
     # 64-token pages (random page order) and each window in a 128-row ring.
     "paged64k": Workload("paged decode: B64 x 64K ctx, 64-token pages, ring window, Full, 64 heads, "

@@ -72,3 +72,16 @@ def visible_count(ctx_len, q_pos=None):
     if q_pos is not None:
         n = min(n, int(q_pos) + 1)
     return max(n, 0)
+
+
+def visible_entries(q_pos, m):
+    """Cache entries a query at token position q_pos may see when each entry
+    compresses m consecutive tokens (entry j covers tokens m*j .. m*j + m - 1).
+
+    [facts] layer pattern and attn.kv_groups: the encoder's CSA2 layers keep
+    one main-KV / indexer-K entry per m = 2 tokens, the decoder's one per
+    token.  Reading (the pages give no rule for a partly filled entry): an
+    entry is visible once every token it covers is at or before q_pos, so the
+    count is floor((q_pos + 1) / m).
+    """
+    return max(0, (int(q_pos) + 1) // int(m))

@@ -12,7 +12,9 @@ oracle: Top-K indices and pools bit for bit, attention per (row, head) within
     attending with the Reindex layer's own index buffer);
   * hier1m: 4 x 1M, a Full layer building the 2048 x 8 candidate pool and nine
     pool-restricted layers;
-  * prefill256k: 4096 causal queries appended to a 262,144-token context.
+  * prefill256k: 4096 causal queries appended to a 262,144-token context;
+  * enc128k: an encoder group, one Full and five Reuse layers over caches of
+    one entry per two tokens (16 x 128K tokens = 64K entries).
 """
 
 import numpy as np
@@ -192,3 +194,41 @@ def test_prefill256k_sampled_queries():
                                                    v8, s8, int(np_(swa_pos0)[0]), wl.W, wl.d_qk, wl.d_v,
                                                    wl.softmax_scale)
         _check_attn(np_(out[0, t]), np_(lse[0, t]), want_o, want_l)
+
+
+@gpu
+def test_enc128k_full_and_five_reuse_layers():
+    """Encoder-side CSA2 (m = 2): the Full layer scores 64K entries per
+    sequence for a query at token 131,070, whose last entry (tokens 131,070
+    and 131,071) is not complete yet, so 65,535 entries are visible; five Reuse
+    layers attend with the copied indices and their own queries and windows."""
+    require_gpu()
+    wl = inputs.WORKLOADS["enc128k"]
+    announce("enc128k B16 x 64K entries (m=2): Full + 5 Reuse, sequences 0 and 15 sampled")
+    codes, scales, k_idx = _build_cache(wl)
+    p = 2 * wl.N - 2
+    n_vis = I.visible_entries(p, wl.m)
+    assert n_vis == wl.N - 1
+    ctx = torch.full((wl.B,), n_vis, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((wl.B,), wl.W, dtype=torch.int32, device="cuda")
+    lays = [inputs.decode_layer_inputs(wl, li, device="cuda") for li in range(len(wl.layers))]
+    idx0 = csa2.csa2_index_score_topk(lays[0]["q_idx"], lays[0]["w"], k_idx, ctx, wl.K)["topk_idx"][:, 0].contiguous()
+    outs = []
+    for li in range(len(wl.layers)):
+        L = lays[li]
+        idx = idx0 if li == 0 else idx0.clone()     # Reuse: copied indices
+        sv, ss = csa2.swa_fp8_quantize(L["swa_x"])
+        outs.append(csa2.csa2_sparse_attn_decode(L["q"][:, 0].contiguous(), codes, scales, idx, ctx, sv, ss, swa_len,
+                                                 wl.softmax_scale, want_lse=True))
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        s = I.index_scores(np_(lays[0]["q_idx"][b, 0]), np_(lays[0]["w"][b, 0]), np_(k_idx[b]), n_vis)
+        want_i, _ = topk_select(s, n_vis, wl.K)
+        got = np_(idx0[b])
+        assert np.array_equal(got, want_i), b
+        assert got.max() < n_vis                    # the incomplete entry is never chosen
+        for li in (0, 2, 5):
+            L = lays[li]
+            want_o, want_l = _oracle_decode_attn(wl, b, np_(L["q"][b, 0]), got, np_(L["swa_x"][b]))
+            o, l = outs[li]
+            _check_attn(np_(o[b]), np_(l[b]), want_o, want_l)

@@ -75,3 +75,15 @@ def test_visibility_prefix():
     assert I.visible_count(100, None) == 100
     assert I.visible_count(100, 41) == 42
     assert I.visible_count(30, 41) == 30
+
+
+def test_visible_entries_of_compressed_caches():
+    """m = 1 is the token count; for m = 2 a brute-force count of entries whose
+    two tokens are all at or before the query."""
+    for p in range(0, 50):
+        assert I.visible_entries(p, 1) == p + 1
+        for m in (2, 3, 4):
+            brute = sum(1 for j in range(100) if all(t <= p for t in range(m * j, m * j + m)))
+            assert I.visible_entries(p, m) == brute
+    assert I.visible_entries(131071, 2) == 65536 and I.visible_entries(131070, 2) == 65535
+    assert I.visible_entries(-1, 2) == 0
