@@ -66,6 +66,30 @@ def index_scores(q_bytes, w, k_bytes, n_visible):
     return s
 
 
+def head_dots_mxfp4(q_bytes, k_codes, k_scales):
+    """Dots d[h, j] = q_h . k_j with E4M3 queries and MXFP4 keys (E2M1 codes,
+    E8M0 scale per 32 channels) -> float64 [H][N].  Every product is exact in
+    float64 and each sum too while a key's shared exponents span fewer than
+    about 25 binades."""
+    from .quant import mxfp4_dequantize
+    q = e4m3fn_decode(np.asarray(q_bytes, dtype=np.uint8))
+    k = mxfp4_dequantize(k_codes, k_scales, q.shape[1])
+    return q @ k.T
+
+
+def index_scores_mxfp4(q_bytes, w, k_codes, k_scales, n_visible):
+    """index_scores with the pages' MXFP4 indexer keys ([facts] indexer K
+    groups: E2M1 with E8M0 scales per 32 channels, 68 bytes per entry): the
+    same ReLU, weights and fixed-order float32 head sum over exact dots."""
+    k_codes = np.asarray(k_codes)
+    n = k_codes.shape[0]
+    nv = max(0, min(int(n_visible), n))
+    s = np.full(n, -np.inf, dtype=np.float32)
+    if nv > 0:
+        s[:nv] = combine_heads(head_dots_mxfp4(q_bytes, k_codes[:nv], np.asarray(k_scales)[:nv]), w)
+    return s
+
+
 def visible_count(ctx_len, q_pos=None):
     """Length of the visible prefix for a query: min(ctx_len, q_pos + 1)."""
     n = int(ctx_len)

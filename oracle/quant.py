@@ -24,11 +24,21 @@ v1.0 conversion -- shared exponent floor(log2(amax)) - 8 (8 = largest E4M3
 exponent), clamped to the E8M0 range, code 127 for an all-zero group;
 elements are E4M3 RNE-with-saturation of x / 2^shared_exp.
 
+mxfp4_quantize -- indexer K write ([facts] indexer K groups: MXFP4, E2M1
+values with one E8M0 scale per 32 channels, 64 + 4 = 68 bytes per 128-channel
+entry).  No rule on the pages; reading: the OCP MX v1.0 conversion -- shared
+exponent floor(log2(amax)) - 2 (2 = largest E2M1 exponent), clamped to the
+E8M0 range, code 127 for an all-zero group; elements are the E2M1 value
+nearest x / 2^shared_exp, ties to the even code, saturating at 6 (the same
+nearest-value rule as fp4_quantize, with the power-of-two scale).
+
 Parity: fp4_quantize pinned by an exhaustive tie/threshold sweep over all 126
 positive finite scales written with exact rational arithmetic, by round-trip
 of grid points and by the error bound of half a grid gap; mxfp8_quantize by
-the closed-form exponent on powers of two and by round-trip
-(tests/test_oracle_quant.py).
+the closed-form exponent on powers of two and by round-trip; mxfp4_quantize by
+an exact-rational nearest-value sweep on ties and neighbours of every
+threshold at several shared exponents, the exponent closed form and
+round-trip (tests/test_oracle_quant.py).
 """
 
 import numpy as np
@@ -109,3 +119,42 @@ def mxfp8_dequantize(vals, scales, d):
     v = e4m3fn_decode(vals[:, :d]).reshape(rows, d // 32, 32)
     s = e8m0_decode(scales[:, : d // 32])
     return (v * s[..., None]).reshape(rows, d)
+
+
+def mxfp4_shared_exponent_code(amax_f32):
+    """E8M0 scale byte of a 32-channel group for E2M1 elements."""
+    amax = np.asarray(amax_f32, dtype=np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    _, ex = np.frexp(safe)  # floor(log2(amax)) = ex - 1
+    e = (ex - 1) - 2
+    code = np.clip(e + 127, 0, 254)
+    return np.where(amax > 0, code, 127).astype(np.uint8)
+
+
+def mxfp4_quantize(x):
+    """Quantise float32 rows [rows][d] to (codes [rows][d/2] u8 packed E2M1, scales [rows][d/32] u8 E8M0)."""
+    x = np.asarray(x, dtype=np.float32)
+    rows, d = x.shape
+    assert d % 32 == 0
+    g = x.reshape(rows, d // 32, 32)
+    amax = np.abs(g).max(axis=-1)
+    scode = mxfp4_shared_exponent_code(amax)
+    s = e8m0_decode(scode)  # exact power of two
+    absx = np.abs(g).astype(np.float64)
+    mag = e2m1_nearest_code(absx, np.broadcast_to(s[..., None], absx.shape))
+    neg = (g < 0) & (mag != 0)
+    code = (mag | (neg.astype(np.int64) << 3)).reshape(rows, d)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scode
+
+
+def mxfp4_dequantize(codes, scales, d):
+    """Decode packed E2M1 codes with E8M0 per-32 scales to float64 rows [rows][d]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    c = np.empty((rows, d), dtype=np.int64)
+    c[:, 0::2] = codes[:, : d // 2] & 0xF
+    c[:, 1::2] = codes[:, : d // 2] >> 4
+    v = e2m1_decode(c).reshape(rows, d // 32, 32)
+    return (v * e8m0_decode(scales[:, : d // 32])[..., None]).reshape(rows, d)

@@ -87,3 +87,37 @@ def test_visible_entries_of_compressed_caches():
             assert I.visible_entries(p, m) == brute
     assert I.visible_entries(131071, 2) == 65536 and I.visible_entries(131070, 2) == 65535
     assert I.visible_entries(-1, 2) == 0
+
+
+def test_mxfp4_key_dots_and_scores_against_exact_rationals():
+    """Dots with MXFP4 keys against a pure-Python Fraction computation of
+    sum_c q_c * e2m1(code_c) * 2^(scale_{c/32} - 127), and the scores' fixed-
+    order float32 head sum over them."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    H, D, N = 3, 128, 40
+    qv = rng.integers(-4, 5, (H, D))
+    q = _ints_to_e4m3(qv)
+    codes = rng.integers(0, 256, (N, D // 2)).astype(np.uint8)
+    scales = rng.integers(120, 135, (N, D // 32)).astype(np.uint8)
+    mags = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+    w = rng.standard_normal(H).astype(np.float32)
+    d = I.head_dots_mxfp4(q, codes, scales)
+    s = I.index_scores_mxfp4(q, w, codes, scales, N - 3)
+    for j in range(N):
+        exact = []
+        for h in range(H):
+            acc = Fraction(0)
+            for c in range(D):
+                nib = (int(codes[j, c // 2]) >> (4 * (c % 2))) & 0xF
+                val = mags[nib & 7] * (-1 if nib & 8 else 1) * Fraction(2) ** (int(scales[j, c // 32]) - 127)
+                acc += int(qv[h, c]) * val
+            exact.append(acc)
+            assert d[h, j] == float(acc)
+        if j < N - 3:
+            ref = np.float32(0)
+            for h in range(H):
+                ref = np.float32(ref + np.float32(w[h] * np.float32(max(float(exact[h]), 0.0))))
+            assert s[j] == ref
+        else:
+            assert s[j] == -np.inf

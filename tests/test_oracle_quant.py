@@ -144,3 +144,58 @@ def test_fp4_huge_and_tiny_groups():
     x = np.array([[1e-40] * 8 + [-3e-39] * 8, [2.0 ** -12] * 16], dtype=np.float32)
     codes, sc = Q.fp4_quantize(x)
     assert sc.tolist() == [[0], [0]] and np.all(codes == 0)
+
+
+def test_mxfp4_shared_exponent_and_ties_at_several_exponents():
+    """MXFP4 (OCP MX): shared exponent floor(log2 amax) - 2; elements rounded to
+    the nearest E2M1 magnitude of x / 2^X, ties to the even code, saturating at 6
+    -- checked with the exact-rational threshold statement on every tie and its
+    float32 neighbours, at shared exponents -6 .. 6."""
+    ts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 0.1, 5.9, 6.0, 7.5]
+    rows, Xs = [], []
+    for X in range(-6, 7):
+        s = 2.0 ** X
+        amax = np.float32(7.9 * s)          # floor(log2(7.9 * 2^X)) = X + 2
+        for t in ts:
+            x = np.float32(t * s)
+            vals = [amax, x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(0)), -x,
+                    -np.nextafter(x, np.float32(np.inf))]
+            vals += [np.float32(0)] * (32 - len(vals))
+            rows.append(vals)
+            Xs.append(X)
+    Xa = np.array(rows, dtype=np.float32)
+    codes, sc = Q.mxfp4_quantize(Xa)
+    assert np.array_equal(sc[:, 0], np.array(Xs) + 127)
+    for i in range(Xa.shape[0]):
+        s = 2.0 ** Xs[i]
+        got = np.empty(32, np.int64)
+        got[0::2], got[1::2] = codes[i] & 0xF, codes[i] >> 4
+        for j in range(32):
+            v = float(Xa[i, j])
+            want = _threshold_code(abs(v), s)
+            if v < 0 and want:
+                want |= 8
+            assert got[j] == want, (Xs[i], v, got[j], want)
+
+
+def test_mxfp4_zero_group_round_trip_and_entry_bytes():
+    x = np.zeros((1, 128), np.float32)
+    c, s = Q.mxfp4_quantize(x)
+    assert s.tolist() == [[127] * 4] and not c.any()
+    # grid points of four different exponents round-trip exactly
+    rng = np.random.default_rng(0)
+    grid = np.array(MAGS, np.float64)
+    y = np.empty((3, 128))
+    for r in range(3):
+        for blk in range(4):
+            X = int(rng.integers(-4, 5))
+            vals = rng.choice(grid, 32) * rng.choice([-1, 1], 32) * 2.0 ** X
+            vals[0] = 6 * 2.0 ** X                  # sets the block's exponent to X
+            y[r, 32 * blk: 32 * blk + 32] = vals
+    c, s = Q.mxfp4_quantize(y.astype(np.float32))
+    assert c.shape == (3, 64) and s.shape == (3, 4)     # 64 code bytes + 4 scale bytes = 68 per entry
+    assert np.array_equal(Q.mxfp4_dequantize(c, s, 128), y)
+    # the shared exponent's closed form on powers of two, clamped to the E8M0 range
+    amax = np.array([2.0 ** e for e in (-140, -130, -3, 0, 1, 2, 5, 127)], np.float32)
+    want = np.clip(np.array([-140, -130, -3, 0, 1, 2, 5, 127]) - 2 + 127, 0, 254)
+    assert np.array_equal(Q.mxfp4_shared_exponent_code(amax), want)
