@@ -14,6 +14,7 @@ every cache resident in HBM:
   enc128k     encoder group (one cache entry per two tokens): Full + 5 Reuse
               layers over 16 x 64K entries;
   paged64k    decode64k with the main rows in a page pool and ring windows;
+  mxfp4_64k   decode64k with the pages' MXFP4 indexer keys (68 bytes per token);
   mq2_64k     multi-query decode: 2 query tokens per sequence over 64 x 64K
               (one pass over the keys for both, then attention per token).
 Every step is timed by its own pair of HIP events; ms_per_step is their
@@ -140,8 +141,9 @@ def layer_bytes(wl, kind, pool_cap=0):
     if wl.page_size:
         attn += 4 * K                 # the block-table entry of every Top-K token
     idx_q = wl.H_I * wl.D_I + 4 * wl.H_I
+    key = wl.D_I // 2 + wl.D_I // 32 if wl.mxfp4 else wl.D_I     # indexer key bytes per token
     if kind in ("full", "reindex"):
-        b = wl.D_I * wl.N + idx_q + 8 * K + attn
+        b = key * wl.N + idx_q + 8 * K + attn
         if wl.pool_block:
             b += 4 * wl.pool_nblocks * wl.pool_block        # pool write
         return b
@@ -185,7 +187,16 @@ class Case:
             del self.cache, self.codes, self.scales
             self.pool_codes, self.pool_scales = self.pool[:, : d // 2], self.pool[:, d // 2:]
             self.swa_end = torch.full((B,), N, dtype=torch.int32, device=dev)
-        self.k_idx = inputs.int_e4m3((B, N, wl.D_I), wl.seed, 0, "k_idx", device=dev)
+        if wl.mxfp4:   # the pages' indexer K: E2M1 codes + E8M0 scale per 32 channels, two arrays
+            self.k_codes = torch.empty(B, N, wl.D_I // 2, dtype=torch.uint8, device=dev)
+            self.k_scales = torch.empty(B, N, wl.D_I // 32, dtype=torch.uint8, device=dev)
+            for b in range(B):
+                x = inputs.idx_key_rows((N, wl.D_I), wl.seed * 7919 + b, device=dev)
+                csa2.idx_mxfp4_quantize(x, codes=self.k_codes[b], scales=self.k_scales[b])
+                del x
+            self.k_idx = None
+        else:
+            self.k_idx = inputs.int_e4m3((B, N, wl.D_I), wl.seed, 0, "k_idx", device=dev)
         self.ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
         self.swa_len = torch.full((B,), wl.W, dtype=torch.int32, device=dev)
         self.layers = []
@@ -238,8 +249,12 @@ class Case:
                                  out={"topk_idx": self.topk[li], "pool_idx": self.pool_idx, "pool_len": self.pool_len})
                 else:
                     extra = dict(out={"topk_idx": self.topk[li]})
-                csa2.csa2_index_score_topk(L["q_idx"], L["w"], self.k_idx, self.ctx, wl.K, q_pos=self.q_pos,
-                                           workspace=self.ws_idx, **extra)
+                if wl.mxfp4:
+                    csa2.csa2_index_score_topk_mxfp4(L["q_idx"], L["w"], self.k_codes, self.k_scales, self.ctx,
+                                                     wl.K, q_pos=self.q_pos, workspace=self.ws_idx, **extra)
+                else:
+                    csa2.csa2_index_score_topk(L["q_idx"], L["w"], self.k_idx, self.ctx, wl.K, q_pos=self.q_pos,
+                                               workspace=self.ws_idx, **extra)
                 idx = self.topk[li]
             elif kind == "pool":
                 csa2.csa2_hier_pool_topk(L["q_idx"], L["w"], self.k_idx, self.pool_idx, self.pool_len, wl.K,
@@ -274,7 +289,7 @@ class Case:
         if wl.Tq > 1:
             # A prefill chunk streams the key cache once for all its queries.
             n_scan = sum(1 for L in self.layers if L["kind"] in ("full", "reindex"))
-            total -= n_scan * wl.D_I * wl.N * wl.B * (wl.Tq - 1)
+            total -= n_scan * (wl.D_I // 2 + wl.D_I // 32 if wl.mxfp4 else wl.D_I) * wl.N * wl.B * (wl.Tq - 1)
         return total
 
 
@@ -300,13 +315,16 @@ def cpu_baseline(case, n_seq, budget_s=10.0):
     for b in range(wl.B):
         if b >= n_seq and t_tot >= budget_s:
             break
-        k_idx = h(case.k_idx[b])
+        k_idx = None if wl.mxfp4 else h(case.k_idx[b])
+        kcb = h(case.k_codes[b]) if wl.mxfp4 else None
+        ksb = h(case.k_scales[b]) if wl.mxfp4 else None
         kv_x = h(inputs.kv_rows_seq(wl, b, device=case.dev))
         qi, w, q = h(L["q_idx"][b]), h(L["w"][b]), h(L["q"][b])
         swa_x = swa_all[b]
         for t in range(wl.Tq if wl.Tq == 1 else 1):
             t0 = time.perf_counter()
-            s = I.index_scores(qi[t], w[t], k_idx, wl.N)
+            s = (I.index_scores_mxfp4(qi[t], w[t], kcb, ksb, wl.N) if wl.mxfp4
+                 else I.index_scores(qi[t], w[t], k_idx, wl.N))
             idx, _ = topk_select(s, wl.N, wl.K)
             t1 = time.perf_counter()
             # set-up: the oracle's own cache rows for the selected ids and the window
@@ -427,7 +445,8 @@ def main():
                 "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     else:
         # one pass over the keys serves every query row of a sequence
-        scan_bytes = (wl.D_I * wl.N + wl.Tq * (wl.H_I * wl.D_I + 4 * wl.H_I)) * wl.B
+        key = wl.D_I // 2 + wl.D_I // 32 if wl.mxfp4 else wl.D_I
+        scan_bytes = (key * wl.N + wl.Tq * (wl.H_I * wl.D_I + 4 * wl.H_I)) * wl.B
         achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -444,7 +463,9 @@ def main():
         "vs_baseline": None, "dtype": "fp8+fp16 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.N, "query_tokens": wl.Tq,
                    "heads": wl.H, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "window": wl.W,
-                   "layers": wl.layers, "tokens_per_entry": wl.m, "parallelism": "single GPU"},
+                   "layers": wl.layers, "tokens_per_entry": wl.m,
+                   "indexer_keys": "MXFP4 (E2M1 + E8M0/32)" if wl.mxfp4 else "E4M3 integers",
+                   "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "step_bytes": step_bytes,
         "step_stats": {"median_ms": round(ms, 5), "mean_ms": round(mean_ms, 5), "min_ms": round(step_ms[0], 5),
                        "max_ms": round(step_ms[-1], 5), "timed_region_ms": round(region_ms, 3),

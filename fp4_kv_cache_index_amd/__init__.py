@@ -27,11 +27,21 @@ _SIGS = {
                                        c_void_p]),
     "swa_fp8_quantize": (ctypes.c_int, [c_void_p, c_int64, c_int32, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                         c_void_p]),
+    "idx_mxfp4_quantize": (ctypes.c_int, [c_void_p, c_int64, c_int32, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                          c_void_p]),
     "csa2_index_score_topk_workspace_size": (c_size_t, [c_int32, c_int32, c_int64, c_int32, c_int32, c_int32]),
     "csa2_index_score_topk": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                              c_int32, c_int32, c_int32, c_int32, c_int64, c_int32, c_void_p,
                                              c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
                                              c_void_p]),
+    "csa2_index_score_topk_mxfp4": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
+                                                   c_int64, c_int64, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                                   c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "csa2_hier_pool_topk_mxfp4": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64,
+                                                 c_int64, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                                 c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
+                                                 c_void_p]),
     "csa2_index_score_topk_noalloc": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p,
                                                      c_void_p, c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
                                                      c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
@@ -165,6 +175,24 @@ def swa_fp8_quantize(x, vals=None, scales=None):
     return vals, scales
 
 
+def idx_mxfp4_quantize(x, codes=None, scales=None):
+    """MXFP4 indexer-K write of float32 rows x [..., d] -> (codes [..., d/2] u8, scales [..., d/32] u8 E8M0)."""
+    _gpu(x, "x", torch.float32)
+    d = x.shape[-1]
+    x2 = x.reshape(-1, d)
+    if x2.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    lead = x.shape[:-1]
+    if codes is None:
+        codes = torch.empty(*lead, d // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(*lead, d // 32, dtype=torch.uint8, device=x.device)
+    c2, s2 = codes.view(-1, codes.shape[-1]), scales.view(-1, scales.shape[-1])
+    _check(lib().idx_mxfp4_quantize(_ptr(x2), x2.shape[0], d, x2.stride(0), _ptr(c2), c2.stride(0), _ptr(s2),
+                                    s2.stride(0), _stream(x.device)), "idx_mxfp4_quantize")
+    return codes, scales
+
+
 # ----------------------------------------------------------- indexer + topk ---
 
 def csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block=0, pool_nblocks=0):
@@ -216,6 +244,83 @@ def csa2_index_score_topk(q_idx, w, k_idx, ctx_len, k_top, q_pos=None, pool_bloc
                                        pool_nblocks, _ptr(pool_idx), _ptr(pool_len), _ptr(ws), ws_bytes,
                                        _stream(dev)), "csa2_index_score_topk")
     return {"topk_idx": topk_idx, "topk_score": topk_score, "pool_idx": pool_idx, "pool_len": pool_len}
+
+
+def _mx_keys(k_codes, k_scales):
+    _gpu(k_codes, "k_codes", torch.uint8)
+    _gpu(k_scales, "k_scales", torch.uint8)
+    cb, cr = _row_strides(k_codes, "k_codes")
+    sb, sr = _row_strides(k_scales, "k_scales")
+    return cb, cr, sb, sr
+
+
+def csa2_index_score_topk_mxfp4(q_idx, w, k_codes, k_scales, ctx_len, k_top, q_pos=None, pool_block=0,
+                                pool_nblocks=0, want_scores=False, workspace=None, out=None):
+    """csa2_index_score_topk over MXFP4 keys: k_codes [B][N][D_I/2] u8, k_scales [B][N][D_I/32] u8 (E8M0)."""
+    _gpu(q_idx, "q_idx", torch.uint8)
+    _gpu(w, "w", torch.float32)
+    _gpu(ctx_len, "ctx_len", torch.int32)
+    B, Tq, H_I, D_I = q_idx.shape
+    if not q_idx.is_contiguous() or not w.is_contiguous() or tuple(w.shape) != (B, Tq, H_I):
+        raise ValueError("q_idx / w must be contiguous [B][Tq][H_I][D_I] / [B][Tq][H_I]")
+    cb, cr, sb, sr = _mx_keys(k_codes, k_scales)
+    n_max = k_codes.shape[1]
+    if q_pos is not None:
+        _gpu(q_pos, "q_pos", torch.int32)
+    dev = q_idx.device
+    out = out or {}
+    topk_idx = out.get("topk_idx")
+    if topk_idx is None:
+        topk_idx = torch.empty(B, Tq, k_top, dtype=torch.int32, device=dev)
+    topk_score = out.get("topk_score")
+    if want_scores and topk_score is None:
+        topk_score = torch.empty(B, Tq, k_top, dtype=torch.float32, device=dev)
+    pool_idx = pool_len = None
+    if pool_nblocks > 0:
+        pool_idx = out.get("pool_idx")
+        if pool_idx is None:
+            pool_idx = torch.empty(B, Tq, pool_nblocks * pool_block, dtype=torch.int32, device=dev)
+        pool_len = out.get("pool_len")
+        if pool_len is None:
+            pool_len = torch.empty(B, Tq, dtype=torch.int32, device=dev)
+    need = csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block, pool_nblocks)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    _check(lib().csa2_index_score_topk_mxfp4(_ptr(q_idx), _ptr(w), _ptr(k_codes), cb, cr, _ptr(k_scales), sb, sr,
+                                             _ptr(ctx_len), _ptr(q_pos), B, Tq, H_I, D_I, n_max, k_top,
+                                             _ptr(topk_idx), _ptr(topk_score), pool_block, pool_nblocks,
+                                             _ptr(pool_idx), _ptr(pool_len), _ptr(ws), ws_bytes, _stream(dev)),
+           "csa2_index_score_topk_mxfp4")
+    return {"topk_idx": topk_idx, "topk_score": topk_score, "pool_idx": pool_idx, "pool_len": pool_len}
+
+
+def csa2_hier_pool_topk_mxfp4(q_idx, w, k_codes, k_scales, pool_idx, pool_len, k_top, ctx_len=None,
+                              want_scores=False, workspace=None, out=None):
+    """csa2_hier_pool_topk over MXFP4 keys (arrays as in csa2_index_score_topk_mxfp4)."""
+    _gpu(q_idx, "q_idx", torch.uint8)
+    _gpu(w, "w", torch.float32)
+    _gpu(pool_idx, "pool_idx", torch.int32)
+    _gpu(pool_len, "pool_len", torch.int32)
+    B, Tq, H_I, D_I = q_idx.shape
+    cb, cr, sb, sr = _mx_keys(k_codes, k_scales)
+    pool_cap = pool_idx.shape[-1]
+    dev = q_idx.device
+    if ctx_len is None:
+        ctx_len = torch.full((B,), k_codes.shape[1], dtype=torch.int32, device=dev)
+    _gpu(ctx_len, "ctx_len", torch.int32)
+    out = out or {}
+    topk_idx = out.get("topk_idx")
+    if topk_idx is None:
+        topk_idx = torch.empty(B, Tq, k_top, dtype=torch.int32, device=dev)
+    topk_score = out.get("topk_score")
+    if want_scores and topk_score is None:
+        topk_score = torch.empty(B, Tq, k_top, dtype=torch.float32, device=dev)
+    need = csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    _check(lib().csa2_hier_pool_topk_mxfp4(_ptr(q_idx), _ptr(w), _ptr(k_codes), cb, cr, _ptr(k_scales), sb, sr,
+                                           _ptr(ctx_len), _ptr(pool_idx), _ptr(pool_len), pool_cap, B, Tq, H_I,
+                                           D_I, k_top, _ptr(topk_idx), _ptr(topk_score), _ptr(ws), ws_bytes,
+                                           _stream(dev)), "csa2_hier_pool_topk_mxfp4")
+    return {"topk_idx": topk_idx, "topk_score": topk_score}
 
 
 def csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top):

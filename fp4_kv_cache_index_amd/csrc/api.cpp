@@ -186,6 +186,18 @@ int swa_fp8_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_st
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }
 
+int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_stride, uint8_t* codes,
+                       int64_t codes_row_stride, uint8_t* scales, int64_t scales_row_stride, void* stream) {
+  if (n_rows < 0 || d <= 0 || d % 32 != 0) return CSA2_EINVAL;
+  if (n_rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_EINVAL;
+  if (x_row_stride < d || codes_row_stride < d / 2 || scales_row_stride < d / 32) return CSA2_EINVAL;
+  if (!aligned4(x) || !aligned4(codes) || (codes_row_stride & 3)) return CSA2_EINVAL;
+  hipError_t e = launch_idx_mxfp4_quantize(x, n_rows, d, x_row_stride, codes, codes_row_stride, scales,
+                                           scales_row_stride, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
 size_t csa2_index_score_topk_workspace_size(int32_t B, int32_t Tq, int64_t n_max, int32_t k_top,
                                             int32_t pool_block, int32_t pool_nblocks) {
   (void)k_top;
@@ -194,29 +206,49 @@ size_t csa2_index_score_topk_workspace_size(int32_t B, int32_t Tq, int64_t n_max
   return score_layout(B, Tq, n_max, pool_block > 0 ? pool_block : 0).total;
 }
 
-int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_batch_stride,
-                          int64_t k_row_stride, const int32_t* ctx_len, const int32_t* q_pos, int32_t B, int32_t Tq,
-                          int32_t H_I, int32_t D_I, int64_t n_max, int32_t k_top, int32_t* topk_idx,
-                          float* topk_score, int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx,
-                          int32_t* pool_len, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace csa2 {
+
+// Scoring + Top-K (+ pool) for E4M3 keys (a.k_scales == null) or MXFP4 keys.
+static int score_topk_impl(ScoreArgs a, int32_t* topk_idx, float* topk_score, int32_t* pool_idx, int32_t* pool_len,
+                           void* ws, size_t ws_bytes, hipStream_t s) {
+  const int32_t B = a.B, Tq = a.Tq, H_I = a.H_I, D_I = a.D_I, k_top = a.k_top;
+  const int64_t n_max = a.n_max, k_row_stride = a.k_rstride, k_batch_stride = a.k_bstride;
+  const bool f4 = a.k_scales != nullptr;
   if (B < 0 || Tq < 0 || n_max < 0 || k_top <= 0 || H_I <= 0 || D_I <= 0) return CSA2_EINVAL;
   if (B == 0 || Tq == 0) return CSA2_OK;
-  if (!q_idx || !w || !k_idx || !ctx_len || !topk_idx || !ws) return CSA2_EINVAL;
-  if (D_I % 32 != 0 || k_row_stride < D_I || k_batch_stride < 0) return CSA2_EINVAL;
-  if (!aligned4(k_idx) || (k_row_stride & 3) || (k_batch_stride & 3) || !aligned4(q_idx)) return CSA2_EINVAL;
+  if (!a.q_idx || !a.w || !a.k_idx || !a.ctx_len || !topk_idx || !ws) return CSA2_EINVAL;
   if (((uintptr_t)ws & 255u) != 0) return CSA2_EINVAL;
+  if (!aligned4(a.q_idx)) return CSA2_EINVAL;
   const bool pool = pool_idx != nullptr;
   if (pool) {
-    if (!pool_len || pool_nblocks <= 0 || !pool_block_ok(pool_block)) return CSA2_EINVAL;
+    if (!pool_len || a.pool_nblocks <= 0 || !pool_block_ok(a.pool_block)) return CSA2_EINVAL;
+  } else {
+    a.pool_block = 0;
+    a.pool_nblocks = 0;
   }
-  if (!d_idx_ok(D_I) || H_I > 32) return CSA2_EUNSUPPORTED;
+  if (f4) {
+    // MXFP4: code rows of D_I/2 bytes read as 16-byte pieces, scale rows of
+    // D_I/32 bytes read as one 32-bit word.
+    if (D_I % 32 != 0 || k_row_stride < D_I / 2 || k_batch_stride < 0 || a.ks_rstride < D_I / 32 ||
+        a.ks_bstride < 0)
+      return CSA2_EINVAL;
+    if (((uintptr_t)a.k_idx & 15) || (k_row_stride & 15) || (k_batch_stride & 15)) return CSA2_EINVAL;
+    if (((uintptr_t)a.k_scales & 3) || (a.ks_rstride & 3) || (a.ks_bstride & 3)) return CSA2_EINVAL;
+    if (D_I != 128 || H_I > 32) return CSA2_EUNSUPPORTED;
+    if (k_row_stride >= (int64_t)1 << 22 || a.ks_rstride >= (int64_t)1 << 22) return CSA2_EUNSUPPORTED;
+  } else {
+    if (D_I % 32 != 0 || k_row_stride < D_I || k_batch_stride < 0) return CSA2_EINVAL;
+    if (!aligned4(a.k_idx) || (k_row_stride & 3) || (k_batch_stride & 3)) return CSA2_EINVAL;
+    if (!d_idx_ok(D_I) || H_I > 32) return CSA2_EUNSUPPORTED;
+    if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;  // 16-byte slices per lane
+    if ((k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
+    if (k_row_stride >= (int64_t)1 << 22) return CSA2_EUNSUPPORTED;   // 32-bit row offsets in the scan
+  }
   if (n_max > (int64_t)kSelTile * kMaxSelTiles || (int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
-  if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;  // 16-byte slices per lane
-  if ((k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
-  if (k_row_stride >= (int64_t)1 << 22) return CSA2_EUNSUPPORTED;   // 32-bit row offsets in the scan
-  ScoreLayout L = score_layout(B, Tq, n_max, pool ? pool_block : 0);
+  ScoreLayout L = score_layout(B, Tq, n_max, pool ? a.pool_block : 0);
   if (ws_bytes < L.total) return CSA2_EWORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
   uint32_t* keys = (uint32_t*)(base + L.off_keys);
   int32_t* n_valid = (int32_t*)(base + L.off_nvalid);
@@ -230,8 +262,6 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
     nb_valid = (int32_t*)(base + L.off_nbvalid);
     blk = select_ws_carve(base + L.off_blk, L.rows, L.nb_max);
   }
-  ScoreArgs a{q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max, k_top,
-              pool ? pool_block : 0, pool ? pool_nblocks : 0};
   const SelectOut tout{topk_idx, topk_score, nullptr, 0, 0, nullptr, nullptr};
   if (!pool && n_max <= kLocalSel) {
     // Rows of at most 64K positions: one workgroup per row selects, with the
@@ -253,10 +283,39 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k
     e = launch_index_score(a, keys, L.n_stride, n_valid, tok, bkeys, L.nb_stride, nb_valid, pool ? &blk : nullptr, s);
   if (e == hipSuccess) e = select_finish(tok, keys, L.n_stride, n_valid, L.rows, k_top, tout, s);
   if (e == hipSuccess && pool) {
-    SelectOut out{pool_idx, nullptr, nullptr, 0, pool_block, n_valid, pool_len};
-    e = select_finish(blk, bkeys, L.nb_stride, nb_valid, L.rows, pool_nblocks, out, s);
+    SelectOut out{pool_idx, nullptr, nullptr, 0, a.pool_block, n_valid, pool_len};
+    e = select_finish(blk, bkeys, L.nb_stride, nb_valid, L.rows, a.pool_nblocks, out, s);
   }
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
+}  // namespace csa2
+
+extern "C" {
+
+int csa2_index_score_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_batch_stride,
+                          int64_t k_row_stride, const int32_t* ctx_len, const int32_t* q_pos, int32_t B, int32_t Tq,
+                          int32_t H_I, int32_t D_I, int64_t n_max, int32_t k_top, int32_t* topk_idx,
+                          float* topk_score, int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx,
+                          int32_t* pool_len, void* ws, size_t ws_bytes, void* stream) {
+  ScoreArgs a{q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max, k_top,
+              pool_block, pool_nblocks};
+  return score_topk_impl(a, topk_idx, topk_score, pool_idx, pool_len, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int csa2_index_score_topk_mxfp4(const uint8_t* q_idx, const float* w, const uint8_t* k_codes, int64_t kc_batch_stride,
+                                int64_t kc_row_stride, const uint8_t* k_scales, int64_t ks_batch_stride,
+                                int64_t ks_row_stride, const int32_t* ctx_len, const int32_t* q_pos, int32_t B,
+                                int32_t Tq, int32_t H_I, int32_t D_I, int64_t n_max, int32_t k_top, int32_t* topk_idx,
+                                float* topk_score, int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx,
+                                int32_t* pool_len, void* ws, size_t ws_bytes, void* stream) {
+  if (!k_scales && B > 0 && Tq > 0) return CSA2_EINVAL;
+  ScoreArgs a{q_idx, w, k_codes, kc_batch_stride, kc_row_stride, ctx_len, q_pos, B, Tq, H_I, D_I, n_max, k_top,
+              pool_block, pool_nblocks};
+  a.k_scales = k_scales;
+  a.ks_bstride = ks_batch_stride;
+  a.ks_rstride = ks_row_stride;
+  return score_topk_impl(a, topk_idx, topk_score, pool_idx, pool_len, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int csa2_index_score_topk_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_idx,
@@ -286,22 +345,35 @@ size_t csa2_hier_pool_topk_workspace_size(int32_t B, int32_t Tq, int32_t pool_ca
          al256(select_ws_bytes(rows, pool_cap));
 }
 
-int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_batch_stride,
-                        int64_t k_row_stride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int32_t pool_cap,
-                        int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int32_t k_top, int32_t* topk_idx,
-                        float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace csa2 {
+
+static int hier_pool_impl(ScoreArgs a, const int32_t* pool_idx, const int32_t* pool_len, int32_t pool_cap,
+                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int32_t B = a.B, Tq = a.Tq, H_I = a.H_I, D_I = a.D_I, k_top = a.k_top;
+  const int64_t k_row_stride = a.k_rstride, k_batch_stride = a.k_bstride;
+  const bool f4 = a.k_scales != nullptr;
   if (B < 0 || Tq < 0 || pool_cap < 0 || k_top <= 0 || H_I <= 0 || D_I <= 0) return CSA2_EINVAL;
   if (B == 0 || Tq == 0) return CSA2_OK;
-  if (!q_idx || !w || !k_idx || !ctx_len || !pool_idx || !pool_len || !topk_idx || !ws) return CSA2_EINVAL;
-  if (D_I % 32 != 0 || k_row_stride < D_I || k_batch_stride < 0) return CSA2_EINVAL;
-  if (!aligned4(k_idx) || !aligned4(q_idx) || (k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
-  if (((uintptr_t)ws & 255u) != 0) return CSA2_EINVAL;
-  if (!d_idx_ok(D_I) || H_I > 32) return CSA2_EUNSUPPORTED;
-  if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;
+  if (!a.q_idx || !a.w || !a.k_idx || !a.ctx_len || !pool_idx || !pool_len || !topk_idx || !ws) return CSA2_EINVAL;
+  if (!aligned4(a.q_idx) || ((uintptr_t)ws & 255u) != 0) return CSA2_EINVAL;
+  if (f4) {
+    if (D_I % 32 != 0 || k_row_stride < D_I / 2 || k_batch_stride < 0 || a.ks_rstride < D_I / 32 ||
+        a.ks_bstride < 0)
+      return CSA2_EINVAL;
+    if (((uintptr_t)a.k_idx & 15) || (k_row_stride & 15) || (k_batch_stride & 15)) return CSA2_EINVAL;
+    if (((uintptr_t)a.k_scales & 3) || (a.ks_rstride & 3) || (a.ks_bstride & 3)) return CSA2_EINVAL;
+    if (D_I != 128 || H_I > 32) return CSA2_EUNSUPPORTED;
+  } else {
+    if (D_I % 32 != 0 || k_row_stride < D_I || k_batch_stride < 0) return CSA2_EINVAL;
+    if (!aligned4(a.k_idx) || (k_row_stride & 7) || (k_batch_stride & 7)) return CSA2_EINVAL;
+    if (!d_idx_ok(D_I) || H_I > 32) return CSA2_EUNSUPPORTED;
+    if (D_I >= 128 && (k_row_stride & 15)) return CSA2_EINVAL;
+  }
   if ((int64_t)B * Tq > 65535 || pool_cap > kSelTile * kMaxSelTiles) return CSA2_EUNSUPPORTED;
   size_t need = csa2_hier_pool_topk_workspace_size(B, Tq, pool_cap, k_top);
   if (ws_bytes < need) return CSA2_EWORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
   int64_t rows = (int64_t)B * Tq;
   int64_t cap = round_up(pool_cap > 0 ? pool_cap : 1, 64);   // key row stride
   char* base = (char*)ws;
@@ -317,17 +389,42 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_i
     // add up).
     SelectWs none = sw;
     none.hist1 = nullptr;
-    hipError_t e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, pool_idx, pool_len, pool_cap, B,
-                                     Tq, H_I, D_I, k_top, keys, cap, n_valid, none, s);
+    hipError_t e = launch_pool_score(a, pool_idx, pool_len, pool_cap, keys, cap, n_valid, none, s);
     if (e == hipSuccess) e = select_local(keys, cap, n_valid, rows, k_top, pool_cap, nullptr, 0, 0, out, s);
     return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
   }
   hipError_t e = select_clear(sw, rows, s);
-  if (e == hipSuccess)
-    e = launch_pool_score(q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, pool_idx, pool_len, pool_cap, B, Tq, H_I,
-                          D_I, k_top, keys, cap, n_valid, sw, s);
+  if (e == hipSuccess) e = launch_pool_score(a, pool_idx, pool_len, pool_cap, keys, cap, n_valid, sw, s);
   if (e == hipSuccess) e = select_finish(sw, keys, cap, n_valid, rows, k_top, out, s);
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
+}  // namespace csa2
+
+extern "C" {
+
+int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_batch_stride,
+                        int64_t k_row_stride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len,
+                        int32_t pool_cap, int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int32_t k_top,
+                        int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  ScoreArgs a{q_idx, w, k_idx, k_batch_stride, k_row_stride, ctx_len, nullptr, B, Tq, H_I, D_I, (int64_t)pool_cap,
+              k_top, 0, 0};
+  return hier_pool_impl(a, pool_idx, pool_len, pool_cap, topk_idx, topk_score, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int csa2_hier_pool_topk_mxfp4(const uint8_t* q_idx, const float* w, const uint8_t* k_codes, int64_t kc_batch_stride,
+                              int64_t kc_row_stride, const uint8_t* k_scales, int64_t ks_batch_stride,
+                              int64_t ks_row_stride, const int32_t* ctx_len, const int32_t* pool_idx,
+                              const int32_t* pool_len, int32_t pool_cap, int32_t B, int32_t Tq, int32_t H_I,
+                              int32_t D_I, int32_t k_top, int32_t* topk_idx, float* topk_score, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!k_scales && B > 0 && Tq > 0) return CSA2_EINVAL;
+  ScoreArgs a{q_idx, w, k_codes, kc_batch_stride, kc_row_stride, ctx_len, nullptr, B, Tq, H_I, D_I,
+              (int64_t)pool_cap, k_top, 0, 0};
+  a.k_scales = k_scales;
+  a.ks_bstride = ks_batch_stride;
+  a.ks_rstride = ks_row_stride;
+  return hier_pool_impl(a, pool_idx, pool_len, pool_cap, topk_idx, topk_score, ws, ws_bytes, (hipStream_t)stream);
 }
 
 size_t csa2_sparse_attn_decode_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t k_top, int32_t W) {

@@ -42,6 +42,9 @@ int device_cu_count();
 hipError_t launch_kv_fp4_quantize(const float* x, int64_t n_rows, int d, int64_t x_stride,
                                   uint8_t* codes, int64_t c_stride, uint8_t* scales, int64_t s_stride,
                                   hipStream_t s);
+hipError_t launch_idx_mxfp4_quantize(const float* x, int64_t n_rows, int d, int64_t x_stride,
+                                     uint8_t* codes, int64_t c_stride, uint8_t* scales, int64_t s_stride,
+                                     hipStream_t s);
 hipError_t launch_swa_fp8_quantize(const float* x, int64_t n_rows, int d, int64_t x_stride,
                                    uint8_t* vals, int64_t v_stride, uint8_t* scales, int64_t s_stride,
                                    hipStream_t s);
@@ -119,10 +122,13 @@ hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_s
 // ------------------------------------------------------------- scoring ---
 struct ScoreArgs {
   const uint8_t* q_idx; const float* w;
-  const uint8_t* k_idx; int64_t k_bstride, k_rstride;
+  const uint8_t* k_idx; int64_t k_bstride, k_rstride;    // E4M3 key rows, or MXFP4 code rows
   const int32_t* ctx_len; const int32_t* q_pos;
   int B, Tq, H_I, D_I; int64_t n_max; int k_top;
   int pool_block, pool_nblocks;
+  // MXFP4 keys (k_scales != null): E2M1 codes at k_idx, one E8M0 byte per 32
+  // channels at k_scales + b * ks_bstride + j * ks_rstride.
+  const uint8_t* k_scales = nullptr; int64_t ks_bstride = 0, ks_rstride = 0;
 };
 hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                               const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
@@ -132,10 +138,10 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
 // of it for any device.
 int64_t index_score_tiles(const ScoreArgs& a);
 int64_t index_score_tiles_bound(int64_t n_max);
-hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                             int64_t k_rstride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
-                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
-                             int32_t* n_valid, const SelectWs& ws, hipStream_t s);
+// Pool layers: a.q_idx / a.w / keys / ctx_len / B / Tq / H_I / D_I / k_top
+// (and the MXFP4 scales) as in ScoreArgs.
+hipError_t launch_pool_score(const ScoreArgs& a, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                             uint32_t* keys, int64_t key_stride, int32_t* n_valid, const SelectWs& ws, hipStream_t s);
 
 // ----------------------------------------------------------- attention ---
 struct AttnArgs {

@@ -1,5 +1,6 @@
-// Cache writers: FP4 main KV (E2M1 + E4M3 per 16 channels) and the FP8
-// sliding window (E4M3 + E8M0 per 32 channels).
+// Cache writers: FP4 main KV (E2M1 + E4M3 per 16 channels), the FP8
+// sliding window (E4M3 + E8M0 per 32 channels) and the MXFP4 indexer keys
+// (E2M1 + E8M0 per 32 channels).
 //
 // The main-KV format is the one the DeepSeek-V4.1 blog gives for CSA2 (FP4
 // E2M1 values, one E4M3 scale per 16 channels) with the fact sheet's entry
@@ -108,6 +109,62 @@ swa_fp8_quantize_kernel(const float* __restrict__ x, int64_t n_groups, int gpr, 
   }
 }
 
+// Indexer K write (fact sheet, indexer K groups: MXFP4, E2M1 values with one
+// E8M0 scale per 32 channels).  One thread per 32-channel group: 128 B in,
+// 16 code bytes + 1 scale byte out.  Shared exponent floor(log2 amax) - 2
+// (the OCP MX rule; 2 is E2M1's largest exponent), code 127 for an all-zero
+// group; each element takes the E2M1 value nearest x / 2^shared, ties to the
+// even code, saturating at 6 -- the same threshold comparisons as the main
+// KV write with a power-of-two scale (every t * 2^e is exact in float32).
+__global__ void __launch_bounds__(256)
+idx_mxfp4_quantize_kernel(const float* __restrict__ x, int64_t n_groups, int gpr, int64_t x_stride,
+                          uint8_t* __restrict__ codes, int64_t c_stride, uint8_t* __restrict__ scales,
+                          int64_t s_stride) {
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < n_groups;
+       gid += (int64_t)gridDim.x * blockDim.x) {
+    int64_t row = gid / gpr;
+    int g = (int)(gid - row * gpr);
+    const float* src = x + row * x_stride + (int64_t)g * 32;
+    float v[32];
+    if ((((uintptr_t)src) & 15u) == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float4 f = reinterpret_cast<const float4*>(src)[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = src[i];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    uint32_t code = 127u;
+    if (amax > 0.0f) {
+      uint32_t u = __float_as_uint(amax);
+      int e = (u >= 0x00800000u) ? (int)(u >> 23) - 127 : (31 - __clz((int)u)) - 149;  // floor(log2 amax)
+      int c = e - 2 + 127;
+      code = (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
+    }
+    const float sc = e8m0_to_f32(code);   // 2^(code - 127), exact (subnormal for code 0)
+    const float t025 = 0.25f * sc, t075 = 0.75f * sc, t125 = 1.25f * sc, t175 = 1.75f * sc;
+    const float t250 = 2.5f * sc, t350 = 3.5f * sc, t500 = 5.0f * sc;
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float a = fabsf(v[i]);
+      uint32_t c = (uint32_t)(a > t025) + (uint32_t)(a >= t075) + (uint32_t)(a > t125) + (uint32_t)(a >= t175) +
+                   (uint32_t)(a > t250) + (uint32_t)(a >= t350) + (uint32_t)(a > t500);
+      c |= (c != 0u && v[i] < 0.0f) ? 8u : 0u;
+      words[i >> 3] |= c << (4 * (i & 7));
+    }
+    uint32_t* c32 = reinterpret_cast<uint32_t*>(codes + row * c_stride + (int64_t)g * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c32[i] = words[i];
+    scales[row * s_stride + g] = (uint8_t)code;
+  }
+}
+
 static int grid_for(int64_t work, int block) {
   int64_t g = (work + block - 1) / block;
   int64_t cap = (int64_t)device_cu_count() * 32;
@@ -122,6 +179,17 @@ hipError_t launch_kv_fp4_quantize(const float* x, int64_t n_rows, int d, int64_t
   int64_t n_groups = n_rows * gpr;
   if (n_groups == 0) return hipSuccess;
   CSA2_LAUNCH("kv_fp4_quantize", kv_fp4_quantize_kernel, dim3(grid_for(n_groups, 256)), dim3(256), 0, s,
+              x, n_groups, gpr, x_stride, codes, c_stride, scales, s_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_idx_mxfp4_quantize(const float* x, int64_t n_rows, int d, int64_t x_stride,
+                                     uint8_t* codes, int64_t c_stride, uint8_t* scales, int64_t s_stride,
+                                     hipStream_t s) {
+  int gpr = d / 32;
+  int64_t n_groups = n_rows * gpr;
+  if (n_groups == 0) return hipSuccess;
+  CSA2_LAUNCH("idx_mxfp4_quantize", idx_mxfp4_quantize_kernel, dim3(grid_for(n_groups, 256)), dim3(256), 0, s,
               x, n_groups, gpr, x_stride, codes, c_stride, scales, s_stride);
   return hipGetLastError();
 }

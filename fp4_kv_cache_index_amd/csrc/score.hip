@@ -89,10 +89,22 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 // query t takes MFMA rows 8t .. 8t+7 (its heads, zero-padded), so two
 // queries fill one 16-row block and four take two, and the key stream is
 // read once for all of them.
-template <int DI, int HB, bool GATHER, bool POOL, bool H8, int QT>
+// F4: MXFP4 keys (the pages' indexer K: E2M1 codes, one E8M0 scale per 32
+// channels, D_I = 128).  The products run on the scaled matrix instruction
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = the E4M3 query rows and B = 16
+// keys' codes, the E8M0 scale of each B lane's 32 channels passed per lane.
+// Measured lane layout of that instruction (128 K values): an FP4 lane of
+// group g holds K 32g .. 32g+31 in 16 bytes, low nibble first, so a lane
+// takes bytes 16g .. 16g+15 of its key's code row and the byte g of its scale
+// row; an FP8 lane of group g holds K 16g .. 16g+15 then 64+16g .. 64+16g+15,
+// so the query fragments take those bytes.  With integer-valued queries the
+// products and partial sums stay exact in fp32 while a key's four exponents
+// span at most 11 binades.
+template <int DI, int HB, bool GATHER, bool POOL, bool H8, int QT, bool F4>
 __global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB, QT>))
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
+                   const uint8_t* __restrict__ k_scales, int64_t ks_bstride, int64_t ks_rstride,
                    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
                    const int32_t* __restrict__ pool_idx, const int32_t* __restrict__ pool_len, int pool_cap,
                    int Tq, int H_I, int64_t n_max, int k_top, int tile,
@@ -101,12 +113,13 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
                    int pool_block, int nblocks, uint32_t* __restrict__ bkeys, int64_t bkey_stride,
                    int32_t* __restrict__ nb_valid_out, SelectWs blk) {
   static_assert(QT == 1 || (DI == 128 && HB == 1 && H8 && !GATHER && !POOL), "multi-query scan: flat, 8 heads");
+  static_assert(!F4 || DI == 128, "MXFP4 keys: 128 channels");
   constexpr int NW = kScanWavesT<GATHER, HB, QT>;
   constexpr int NT = 64 * NW;
   constexpr int CH = DI / 4;           // bytes of a key row per lane
   constexpr int KS = DI / 32;          // MFMA k-steps
   constexpr int HMAX = QT > 1 ? 8 * QT : 16 * HB;   // MFMA rows (query heads, padded)
-  constexpr int RB = QT > 1 ? QT / 2 : 1;           // 16-row blocks of the whole-line path
+  constexpr int RB = QT > 1 ? QT / 2 : (F4 ? HB : 1);   // 16-row blocks of the whole-line / MXFP4 paths
   // Heads kept per token: 8 per query when the indexer has at most 8 heads,
   // else all 16*HB MFMA rows (padding heads have zero queries and weight 0).
   constexpr int HP = H8 ? 8 * QT : HMAX;
@@ -142,11 +155,12 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     return;
   }
   const int c16 = lane & 15, g = lane >> 4;
-  constexpr bool FULL = (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
+  constexpr bool FULL = !F4 && (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
   const int64_t tile0 = (int64_t)blockIdx.x * tile;
   constexpr int pitch = HP;
   float* my = dots[wave];
   const uint8_t* kb = k_idx + b * k_bstride;
+  const uint8_t* ksb = F4 ? k_scales + b * ks_bstride : nullptr;
   // Each wave owns tile/4 consecutive positions, SG*16 per iteration; the
   // next iteration's key rows are in flight while this one is scored.  Loads
   // are issued unconditionally (positions past the wave's range read the
@@ -177,20 +191,55 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // Flat whole-line scan: buffer loads over exactly the wave's rows (the
   // hardware returns 0 for offsets past the end, without a memory access),
   // so no row clamps; offsets are 32-bit (row strides below 4 MiB).
-  constexpr bool BUF = FULL && !GATHER;
+  constexpr bool BUF = (FULL || F4) && !GATHER;
+  static_assert(!F4 || kScanGroups<HB> == 4, "MXFP4 batches: four groups of 16 keys");
   const uint32_t rs32 = (uint32_t)k_rstride;
-  const uint32_t lane_off = (uint32_t)(c16 >> 1) * rs32 + 16u * (uint32_t)(2 * g + (c16 & 1));
+  const uint32_t ss32 = (uint32_t)ks_rstride;
+  // FP8 whole lines: 8 lanes per key row; MXFP4: lane (c16, g) reads bytes
+  // 16g .. 16g+15 of key c16's code row.
+  const uint32_t lane_off = F4 ? (uint32_t)c16 * rs32 + 16u * (uint32_t)g
+                               : (uint32_t)(c16 >> 1) * rs32 + 16u * (uint32_t)(2 * g + (c16 & 1));
   auto wave_rsrc = [&](int64_t lim) {
     const int64_t n = lim > wbase ? (lim - wbase) * k_rstride : 0;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb + wbase * k_rstride), (short)0,
                                              (int)(n < 0xFFFFFFFFLL ? n : 0xFFFFFFFFLL), 0x00020000);
   };
+  auto wave_srsrc = [&](int64_t lim) {   // MXFP4 scale rows of the wave
+    const int64_t n = lim > wbase ? (lim - wbase) * ks_rstride : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ksb + wbase * ks_rstride), (short)0,
+                                             (int)(n < 0xFFFFFFFFLL ? n : 0xFFFFFFFFLL), 0x00020000);
+  };
   __amdgpu_buffer_rsrc_t krs = wave_rsrc(wend);
+  __amdgpu_buffer_rsrc_t srs = F4 && BUF ? wave_srsrc(wend) : krs;
   // Two fragment buffers used in ping-pong: while one batch of IT tokens is
   // scored, the other batch's loads are in flight.
   Frag<CH> fa[SG], fb[SG];
+  // MXFP4: f[u].w[0..3] = the codes of keys base + 16u + c16 (bytes 16g..),
+  // f[0].w[4] = the 4-byte scale row of key base + lane.
   auto load_batch = [&](Frag<CH>(&f)[SG], int64_t base) {
-    if constexpr (BUF) {
+    if constexpr (F4 && BUF) {
+      const uint32_t boff = (uint32_t)(base - wbase) * rs32;
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        const uint32_t uoff = __builtin_amdgcn_readfirstlane(boff + (uint32_t)(16 * u) * rs32);
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off + uoff, 0, 2 /* non-temporal */);
+        f[u].w[0] = v[0]; f[u].w[1] = v[1]; f[u].w[2] = v[2]; f[u].w[3] = v[3];
+      }
+      const uint32_t soff = (uint32_t)(base - wbase + lane) * ss32;
+      f[0].w[4] = __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 2);
+    } else if constexpr (F4) {
+      auto tok = [&](int64_t pos) -> int64_t {
+        const int64_t p = pos < wend ? pos : wlast;
+        return GATHER ? (int64_t)max(ptok[p - tile0], 0) : p;
+      };
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        const v4u v = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(kb + tok(base + 16 * u + c16) * k_rstride + 16 * g));
+        f[u].w[0] = v[0]; f[u].w[1] = v[1]; f[u].w[2] = v[2]; f[u].w[3] = v[3];
+      }
+      f[0].w[4] = *reinterpret_cast<const uint32_t*>(ksb + tok(base + lane) * ks_rstride);
+    } else if constexpr (BUF) {
       const uint32_t boff = (uint32_t)(base - wbase) * rs32;
 #pragma unroll
       for (int u = 0; u < 2 * SG; ++u) {
@@ -262,7 +311,19 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   long qh[RB][2][2];   // FULL: [row block][parity e][step s] = bytes 32g + 16e + 8s .. +8
   long qa[HB][KS];
   bool hv[RB];
-  if constexpr (FULL) {
+  v8i qa4[F4 ? RB : 1];   // MXFP4: A = E4M3 query rows, bytes 16g.. and 64+16g.. (see the kernel's note)
+  if constexpr (F4) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int R = 16 * rb + c16;
+      const int qt = QT > 1 ? R >> 3 : 0, qhd = QT > 1 ? R & 7 : R;
+      hv[rb] = qt < nq && qhd < H_I;
+      const uint8_t* qp = q_idx + ((row + (hv[rb] ? qt : 0)) * H_I + (hv[rb] ? qhd : 0)) * DI;
+      const v4u lo = *reinterpret_cast<const v4u*>(qp + 16 * g);
+      const v4u hi = *reinterpret_cast<const v4u*>(qp + 64 + 16 * g);
+      qa4[rb] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  } else if constexpr (FULL) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int R = 16 * rb + c16;
@@ -291,6 +352,16 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     load_batch(fa, wbase);
     load_batch(fb, wbase + IT);
     __builtin_amdgcn_sched_barrier(0);   // keep them ahead of the prologue's waits
+  }
+  if constexpr (F4) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!hv[rb]) qa4[rb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      // (per element: the host pass rejects a 256-bit vector operand here and
+      // would silently drop the kernel's host stub)
+      asm volatile("" ::"v"(qa4[rb][0]), "v"(qa4[rb][1]), "v"(qa4[rb][2]), "v"(qa4[rb][3]), "v"(qa4[rb][4]),
+                   "v"(qa4[rb][5]), "v"(qa4[rb][6]), "v"(qa4[rb][7]));
+    }
   }
   if constexpr (FULL) {
 #pragma unroll
@@ -352,9 +423,28 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   if (wend > nv) wend = nv;
   wlast = wend - 1;
   if constexpr (BUF) krs = wave_rsrc(wend);
+  if constexpr (F4 && BUF) srs = wave_srsrc(wend);
 
   auto score_batch = [&](const Frag<CH>(&f)[SG], int64_t it) {
-    if constexpr (FULL) {
+    if constexpr (F4) {
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        // E8M0 scale of this lane's 32 channels: byte g of key 16u + c16's row
+        const uint32_t sw = (uint32_t)__shfl((int)f[0].w[4], 16 * u + c16, 64);
+        const int sb = (int)((sw >> (8 * g)) & 0xFFu);
+        const v8i bk = v8i{(int)f[u].w[0], (int)f[u].w[1], (int)f[u].w[2], (int)f[u].w[3], 0, 0, 0, 0};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa4[rb], bk, acc, 0 /* A E4M3 */, 4 /* B E2M1 */,
+                                                                 0, 127, 0, sb);
+          // acc[r] = dot(A row 16 rb + 4g + r, key 16u + c16)
+          const bool keep = 16 * rb + 4 * g < HP;
+          const int at = keep ? (16 * u + c16) * pitch + 16 * rb + 4 * g : 16 * SG * HP + 4 * lane;
+          *reinterpret_cast<v4f*>(my + at) = acc;
+        }
+      }
+    } else if constexpr (FULL) {
 #pragma unroll
       for (int u = 0; u < 2 * SG; ++u) {
         const uint32_t* w4 = &f[u >> 1].w[4 * (u & 1)];
@@ -521,7 +611,7 @@ static int scan_qt(const ScoreArgs& a) {
   return a.Tq == 2 ? 2 : 4;
 }
 
-template <int QT>
+template <int QT, bool F4>
 static hipError_t launch_scan_mq(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                                  const SelectWs& tok, hipStream_t s) {
   constexpr int NW = kScanWavesT<false, 1, QT>;
@@ -529,14 +619,15 @@ static hipError_t launch_scan_mq(const ScoreArgs& a, uint32_t* keys, int64_t key
   const int tile = scan_tile(groups, a.n_max, NW, QT);
   int64_t tiles = (a.n_max + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("index_score", (index_score_kernel<128, 1, false, false, true, QT>), dim3((unsigned)tiles, (unsigned)groups),
-              dim3(64 * NW), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
+  CSA2_LAUNCH("index_score", (index_score_kernel<128, 1, false, false, true, QT, F4>),
+              dim3((unsigned)tiles, (unsigned)groups), dim3(64 * NW), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride,
+              a.k_rstride, a.k_scales, a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos,
               (const int32_t*)nullptr, (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys,
               key_stride, n_valid, tok, 0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, tok);
   return hipGetLastError();
 }
 
-template <int DI, int HB, bool H8>
+template <int DI, int HB, bool H8, bool F4 = false>
 static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
@@ -548,32 +639,33 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
   SelectWs bw = blk ? *blk : tok;
   dim3 grid((unsigned)tiles, (unsigned)rows);
   if (a.pool_block > 0) {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8, 1>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
-                a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, true, H8, 1, F4>), grid, dim3(64 * NW), 0, s,
+                a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.k_scales, a.ks_bstride, a.ks_rstride, a.ctx_len,
+                a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok,
                 a.pool_block, a.pool_nblocks, bkeys, bkey_stride, nb_valid, bw);
   } else {
-    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8, 1>), grid, dim3(64 * NW), 0, s, a.q_idx, a.w,
-                a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, (const int32_t*)nullptr,
+    CSA2_LAUNCH("index_score", (index_score_kernel<DI, HB, false, false, H8, 1, F4>), grid, dim3(64 * NW), 0, s,
+                a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.k_scales, a.ks_bstride, a.ks_rstride, a.ctx_len,
+                a.q_pos, (const int32_t*)nullptr,
                 (const int32_t*)nullptr, 0, a.Tq, a.H_I, a.n_max, a.k_top, tile, keys, key_stride, n_valid, tok, 0,
                 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, bw);
   }
   return hipGetLastError();
 }
 
-template <int DI, int HB, bool H8>
-static hipError_t launch_pool_t(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                                int64_t k_rstride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
-                                int B, int Tq, int H_I, int k_top, uint32_t* keys, int64_t key_stride,
-                                int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
-  int64_t rows = (int64_t)B * Tq;
+template <int DI, int HB, bool H8, bool F4 = false>
+static hipError_t launch_pool_t(const ScoreArgs& a, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                                uint32_t* keys, int64_t key_stride, int32_t* n_valid, const SelectWs& ws,
+                                hipStream_t s) {
+  int64_t rows = (int64_t)a.B * a.Tq;
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
-  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8, 1>), dim3((unsigned)tiles, (unsigned)rows),
-              dim3(64 * kScanWavesT<true, HB>),
-              0, s, q_idx, w, k_idx, k_bstride, k_rstride, ctx_len, (const int32_t*)nullptr,
-              pool_idx, pool_len, pool_cap, Tq, H_I, (int64_t)pool_cap, k_top, kPoolTile, keys, key_stride, n_valid, ws,
-              0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
+  CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8, 1, F4>),
+              dim3((unsigned)tiles, (unsigned)rows), dim3(64 * kScanWavesT<true, HB>), 0, s, a.q_idx, a.w, a.k_idx,
+              a.k_bstride, a.k_rstride, a.k_scales, a.ks_bstride, a.ks_rstride, a.ctx_len, (const int32_t*)nullptr,
+              pool_idx, pool_len, pool_cap, a.Tq, a.H_I, (int64_t)pool_cap, a.k_top, kPoolTile, keys, key_stride,
+              n_valid, ws, 0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
   return hipGetLastError();
 }
 
@@ -754,18 +846,20 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
 // queries, one MFMA per head.  Lane l then holds, for query l%16, the dots of
 // keys 4g..4g+3 (g = l/16) with every head in its own accumulator, so the
 // head sum stays inside the lane and the four consecutive keys of one query
-// leave in a single 16-byte store.
-template <int PD>
+// leave in a single 16-byte store.  F4: MXFP4 keys (E2M1 codes + E8M0 per 32
+// channels) as the A operand: lane (c16, g) holds bytes 16g .. 16g+15 of key
+// c16's code row (channels 32g .. 32g+31) and passes that block's scale byte.
+template <int PD, bool F4>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                         const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
+                        const uint8_t* __restrict__ k_scales, int64_t ks_bstride, int64_t ks_rstride,
                         const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
                         int Tq, int H_I, int64_t n_max, int key_tile, int qtiles,
                         uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
                         SelectWs tok) {
   constexpr int DI = 128, FW = 8, QW = 16, HP = 8;
   constexpr int NT = 64 * kPrefillWaves;
-  typedef int v8i __attribute__((ext_vector_type(8)));
   __shared__ uint32_t hist[(QW / 2) * 4096 + 1];   // last word: bin of invisible keys
   __shared__ int32_t nvs[QW];
 
@@ -821,6 +915,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   // count the loads in flight instead of draining them all at each chunk.
   const int ik0 = (int)k0, ik1 = (int)k1;
   const uint8_t* kb = k_idx + b * k_bstride;
+  const uint8_t* ksb = F4 ? k_scales + b * ks_bstride : nullptr;
   const int nchunks = (ik1 - ik0 + 15) >> 4;
   uint32_t fk[PD][FW];
   auto load_chunk = [&](uint32_t (&f)[FW], int c) {
@@ -828,17 +923,30 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     j = j < ik1 ? j : ik1 - 1;
     const uint8_t* p = kb + (int64_t)j * k_rstride + 16 * g;
     const v4u lo = *reinterpret_cast<const v4u*>(p);
-    const v4u hi = *reinterpret_cast<const v4u*>(p + 64);
     f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    if constexpr (F4) {
+      f[4] = ksb[(int64_t)j * ks_rstride + g];   // the E8M0 scale of this lane's 32 channels
+    } else {
+      const v4u hi = *reinterpret_cast<const v4u*>(p + 64);
+      f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    }
   };
   auto score_chunk = [&](const uint32_t (&f)[FW], int c) {
-    const v8i ka = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], (int)f[4], (int)f[5], (int)f[6], (int)f[7]};
     v4f acc[HP];
+    if constexpr (F4) {
+      const v8i ka = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], 0, 0, 0, 0};
+      const int sa = (int)f[4];
 #pragma unroll
-    for (int h = 0; h < HP; ++h)
-      acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[h], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127,
-                                                                0, 127);
+      for (int h = 0; h < HP; ++h)
+        acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[h], v4f{0.f, 0.f, 0.f, 0.f}, 4 /* A E2M1 */,
+                                                                  0 /* B E4M3 */, 0, sa, 0, 127);
+    } else {
+      const v8i ka = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], (int)f[4], (int)f[5], (int)f[6], (int)f[7]};
+#pragma unroll
+      for (int h = 0; h < HP; ++h)
+        acc[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[h], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127,
+                                                                  0, 127);
+    }
     // acc[h][r] = dot(key j0 + r, query c16, head h)
     const int j0 = ik0 + 16 * c + 4 * g;
     uint32_t kk[4];
@@ -902,10 +1010,18 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
   int64_t tiles = (a.n_max + key_tile - 1) / key_tile;
   if (tiles < 1) tiles = 1;
   if (qrows > 65535) return hipErrorInvalidValue;
-  if (DI == 128 && HG <= 2) {
-    CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3>), dim3((unsigned)tiles, (unsigned)qrows),
-                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos,
-                a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok);
+  if (DI == 128 && HG <= 2 && a.k_scales) {
+    CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true>), dim3((unsigned)tiles, (unsigned)qrows),
+                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.k_scales,
+                a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys,
+                key_stride, n_valid, tok);
+  } else if (a.k_scales) {
+    return hipErrorInvalidValue;   // (MXFP4 prefill chunks: D_I = 128 and at most 8 heads)
+  } else if (DI == 128 && HG <= 2) {
+    CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false>), dim3((unsigned)tiles, (unsigned)qrows),
+                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride,
+                (const uint8_t*)nullptr, (int64_t)0, (int64_t)0, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile,
+                qtiles, keys, key_stride, n_valid, tok);
   } else {
     CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG>), dim3((unsigned)tiles, (unsigned)qrows),
                 dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len,
@@ -915,6 +1031,7 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
 }
 
 static bool prefill_gemm_applies(const ScoreArgs& a) {
+  if (a.k_scales) return a.Tq >= 16 && a.pool_block == 0 && a.D_I == 128 && a.H_I <= 8;
   return a.Tq >= 16 && a.pool_block == 0 && (a.D_I == 128 || a.D_I == 256) && a.H_I <= 32;
 }
 
@@ -956,10 +1073,21 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
                               const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                               const SelectWs* blk, hipStream_t s) {
   if (prefill_gemm_applies(a)) return launch_prefill(a, keys, key_stride, n_valid, tok, s);
+  const bool f4 = a.k_scales != nullptr;
   switch (scan_qt(a)) {
-    case 2: return launch_scan_mq<2>(a, keys, key_stride, n_valid, tok, s);
-    case 4: return launch_scan_mq<4>(a, keys, key_stride, n_valid, tok, s);
+    case 2: return f4 ? launch_scan_mq<2, true>(a, keys, key_stride, n_valid, tok, s)
+                      : launch_scan_mq<2, false>(a, keys, key_stride, n_valid, tok, s);
+    case 4: return f4 ? launch_scan_mq<4, true>(a, keys, key_stride, n_valid, tok, s)
+                      : launch_scan_mq<4, false>(a, keys, key_stride, n_valid, tok, s);
     default: break;
+  }
+  if (f4) {   // MXFP4 keys: D_I = 128, up to 32 indexer heads
+    if (a.D_I != 128 || a.H_I > 32) return hipErrorInvalidValue;
+    if (a.H_I <= 8) return launch_scan_t<128, 1, true, true>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride,
+                                                             nb_valid, blk, s);
+    if (a.H_I <= 16) return launch_scan_t<128, 1, false, true>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride,
+                                                               nb_valid, blk, s);
+    return launch_scan_t<128, 2, false, true>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s);
   }
 #define CALL_SCAN(D, H, E) launch_scan_t<D, H, E>(a, keys, key_stride, n_valid, tok, bkeys, bkey_stride, nb_valid, blk, s)
   CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_SCAN);
@@ -986,14 +1114,18 @@ int64_t index_score_tiles_bound(int64_t n_max) {
   return tiles < 1 ? 1 : tiles;
 }
 
-hipError_t launch_pool_score(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t k_bstride,
-                             int64_t k_rstride, const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
-                             int B, int Tq, int H_I, int D_I, int k_top, uint32_t* keys, int64_t key_stride,
-                             int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
-#define CALL_POOL(D, H, E) \
-  launch_pool_t<D, H, E>(q_idx, w, k_idx, k_bstride, k_rstride, ctx_len, pool_idx, pool_len, pool_cap, B, Tq, H_I, k_top, keys, \
-                      key_stride, n_valid, ws, s)
-  CSA2_DISPATCH_DI_HB(D_I, H_I, CALL_POOL);
+hipError_t launch_pool_score(const ScoreArgs& a, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,
+                             uint32_t* keys, int64_t key_stride, int32_t* n_valid, const SelectWs& ws, hipStream_t s) {
+  if (a.k_scales) {   // MXFP4 keys
+    if (a.D_I != 128 || a.H_I > 32) return hipErrorInvalidValue;
+    if (a.H_I <= 8) return launch_pool_t<128, 1, true, true>(a, pool_idx, pool_len, pool_cap, keys, key_stride, n_valid,
+                                                             ws, s);
+    if (a.H_I <= 16) return launch_pool_t<128, 1, false, true>(a, pool_idx, pool_len, pool_cap, keys, key_stride,
+                                                               n_valid, ws, s);
+    return launch_pool_t<128, 2, false, true>(a, pool_idx, pool_len, pool_cap, keys, key_stride, n_valid, ws, s);
+  }
+#define CALL_POOL(D, H, E) launch_pool_t<D, H, E>(a, pool_idx, pool_len, pool_cap, keys, key_stride, n_valid, ws, s)
+  CSA2_DISPATCH_DI_HB(a.D_I, a.H_I, CALL_POOL);
 #undef CALL_POOL
 }
 

@@ -11,7 +11,9 @@ Value recipes (the pages' workloads are long-context decode/prefill of the
 DeepSeek-V4.1-Flash CSA2 layers; no dataset is involved):
   * latent KV rows and window rows: float32 N(0, 1), d_qk channels;
   * indexer queries and keys: integers uniform in [-4, 4] stored as E4M3
-    bytes (exact, via torch's float8_e4m3fn cast of small integers);
+    bytes (exact, via torch's float8_e4m3fn cast of small integers); MXFP4
+    indexer keys are float32 N(0, 1) rows written by the library's MXFP4
+    quantiser;
   * indexer head weights: float32 N(0, 1);
   * attention queries: float32 N(0, 1);
   * every sequence has the full context (ctx_len = N) and a full window.
@@ -64,6 +66,7 @@ class Workload:
     softmax_scale: float = 0.0
     page_size: int = 0   # > 0: main rows in a page pool (random page order), window in a ring
     m: int = 1           # tokens per cache entry (2: the encoder layers' compressed entries); N counts entries
+    mxfp4: bool = False  # indexer keys in the pages' MXFP4 format (float32 N(0,1) rows quantised), not E4M3 integers
 
     def __post_init__(self):
         if self.softmax_scale == 0.0:
@@ -96,6 +99,10 @@ WORKLOADS = {
                         "indexer 8x128, top-2048", 8,
                         B=16, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048,
                         layers=["full"] + ["reuse"] * 5, m=2),
+    # The decode64k step with the pages' MXFP4 indexer keys (64 code bytes +
+    # 4 E8M0 scale bytes per token instead of 128 E4M3 bytes).
+    "mxfp4_64k": Workload("MXFP4 indexer keys: B64 x 64K ctx, Full, 64 heads, indexer 8x128, top-2048", 9,
+                          B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048, mxfp4=True),
     # Serving layout: the decode64k step with the main rows in a pool of
     # 64-token pages (random page order) and each window in a 128-row ring.
     "paged64k": Workload("paged decode: B64 x 64K ctx, 64-token pages, ring window, Full, 64 heads, "
@@ -151,6 +158,11 @@ def random_index_lists(B, K, N, seed, layer=0, device="cpu", n_invalid=0):
         bad[:, ::2] = N + 7
         out[:, K - n_invalid:] = bad
     return out
+
+
+def idx_key_rows(shape, seed, device="cpu"):
+    """float32 N(0, 1) indexer key rows (before the MXFP4 write)."""
+    return normal_f32(shape, seed, 0, "k_idx", device=device)
 
 
 def page_order(n_pages, n_used, seed, device="cpu"):

@@ -100,6 +100,22 @@ int swa_fp8_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_st
                      uint8_t* scales, int64_t scales_row_stride, void* stream);
 
 /*
+ * idx_mxfp4_quantize -- indexer K write in the pages' format (fact sheet,
+ * indexer K groups: MXFP4, E2M1 values with one E8M0 scale per 32 channels;
+ * 64 code bytes + 4 scale bytes = 68 bytes per 128-channel entry).
+ * Per row and 32-channel group: shared exponent e = floor(log2 amax) - 2,
+ * E8M0 code clamp(e + 127, 0, 254) (127 when amax == 0); each element is the
+ * E2M1 value nearest x / 2^e, ties to the even code, saturating at 6; the
+ * sign bit only for a negative x with a non-zero magnitude.
+ * x [n_rows][d] float32 (row stride in elements); codes [n_rows][d/2]
+ * (channel 2i in the low nibble of byte i), scales [n_rows][d/32] (row
+ * strides in bytes; code rows 4-byte aligned).  d % 32 == 0.
+ */
+int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_stride,
+                       uint8_t* codes, int64_t codes_row_stride,
+                       uint8_t* scales, int64_t scales_row_stride, void* stream);
+
+/*
  * csa2_index_score_topk -- indexer scoring + exact Top-K for Full and Reindex
  * layers (techniques map, indexer-selected sparse attention; blog, CSA2
  * paragraph), optionally also building the hierarchical candidate pool of
@@ -141,6 +157,33 @@ int csa2_index_score_topk(const uint8_t* q_idx, const float* w,
                           int32_t* topk_idx, float* topk_score,
                           int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx, int32_t* pool_len,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_score_topk_mxfp4 -- csa2_index_score_topk over the pages' MXFP4
+ * indexer keys (fact sheet, indexer K groups: E2M1 values, one E8M0 scale per
+ * 32 channels, 68 bytes per 128-channel entry; idx_mxfp4_quantize writes them).
+ * Same arguments, results, workspace (csa2_index_score_topk_workspace_size)
+ * and pool option, with the key cache given as two arrays:
+ *   k_codes  row j of b at k_codes + b*kc_batch_stride + j*kc_row_stride:
+ *            D_I/2 bytes, channel 2i in the low nibble of byte i (pointer and
+ *            strides multiples of 16; the pages' 68-byte entry therefore
+ *            splits into a code array and a scale array).
+ *   k_scales row j of b at k_scales + b*ks_batch_stride + j*ks_row_stride:
+ *            D_I/32 E8M0 bytes (pointer and strides multiples of 4).
+ *   d_h = q_idx[b][t][h] . dequant(k_j) on the scaled FP4 matrix cores; exact
+ *   (hence bit-identical scores and indices) for integer-valued E4M3 queries
+ *   in [-4, 4] whenever a key's four shared exponents span at most 11 binades.
+ * Supported: D_I = 128, 1 <= H_I <= 32; prefill chunks (Tq >= 16) with
+ * H_I <= 8 run as one dense product, longer head counts row by row.
+ */
+int csa2_index_score_topk_mxfp4(const uint8_t* q_idx, const float* w,
+                                const uint8_t* k_codes, int64_t kc_batch_stride, int64_t kc_row_stride,
+                                const uint8_t* k_scales, int64_t ks_batch_stride, int64_t ks_row_stride,
+                                const int32_t* ctx_len, const int32_t* q_pos,
+                                int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int64_t n_max, int32_t k_top,
+                                int32_t* topk_idx, float* topk_score,
+                                int32_t pool_block, int32_t pool_nblocks, int32_t* pool_idx, int32_t* pool_len,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_index_score_topk_noalloc -- csa2_index_score_topk for callers that
@@ -185,6 +228,18 @@ int csa2_hier_pool_topk(const uint8_t* q_idx, const float* w,
                         int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int32_t k_top,
                         int32_t* topk_idx, float* topk_score,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_hier_pool_topk_mxfp4 -- csa2_hier_pool_topk over MXFP4 indexer keys
+ * (key arrays as in csa2_index_score_topk_mxfp4; workspace
+ * csa2_hier_pool_topk_workspace_size).
+ */
+int csa2_hier_pool_topk_mxfp4(const uint8_t* q_idx, const float* w,
+                              const uint8_t* k_codes, int64_t kc_batch_stride, int64_t kc_row_stride,
+                              const uint8_t* k_scales, int64_t ks_batch_stride, int64_t ks_row_stride,
+                              const int32_t* ctx_len, const int32_t* pool_idx, const int32_t* pool_len,
+                              int32_t pool_cap, int32_t B, int32_t Tq, int32_t H_I, int32_t D_I, int32_t k_top,
+                              int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_sparse_attn_decode -- sparse MLA decode attention over the Top-K FP4

@@ -78,4 +78,17 @@ def pool_topk(q_bytes, w, k_bytes, pool_idx, pool_len, k, ctx_len=None):
     return topk_select(s, len(ids), k, ids=ids)
 
 
-__all__ = ["block_scores", "hier_pool", "pool_topk", "index_scores"]
+def pool_topk_mxfp4(q_bytes, w, k_codes, k_scales, pool_idx, pool_len, k, ctx_len=None):
+    """pool_topk over MXFP4 indexer keys (codes [N][D/2], E8M0 scales [N][D/32])."""
+    from .indexer import head_dots_mxfp4
+    pl = max(0, min(int(pool_len), len(pool_idx)))
+    n = np.asarray(k_codes).shape[0] if ctx_len is None else int(ctx_len)
+    ids = np.asarray(pool_idx[:pl], dtype=np.int64)
+    ids = ids[(ids >= 0) & (ids < n)]
+    if len(ids) == 0:
+        return np.full(k, -1, np.int32), np.full(k, -np.inf, np.float32)
+    s = combine_heads(head_dots_mxfp4(q_bytes, np.asarray(k_codes)[ids], np.asarray(k_scales)[ids]), w)
+    return topk_select(s, len(ids), k, ids=ids)
+
+
+__all__ = ["block_scores", "hier_pool", "pool_topk", "pool_topk_mxfp4", "index_scores"]

@@ -120,3 +120,27 @@ def test_pool_topk_sparse_pool_brute_force():
         want_i, want_s = _brute_pool_topk(q, w, k_bytes, pool, plen, k, ctx)
         assert np.array_equal(got_i, want_i), trial
         assert np.array_equal(got_s, want_s), trial
+
+
+def test_pool_topk_mxfp4_against_flat_selection_and_a_loop():
+    """The MXFP4 pool layer: a pool of all visible tokens gives the flat MXFP4
+    Top-K; a sparse pool equals a loop scoring each pool id's own key row."""
+    from oracle import quant as Q
+    rng = np.random.default_rng(9)
+    n, H, D = 200, 4, 128
+    kc, ks = Q.mxfp4_quantize(rng.standard_normal((n, D)).astype(np.float32))
+    q = _e4m3(rng.integers(-4, 5, (H, D)))
+    w = rng.standard_normal(H).astype(np.float32)
+    nv = 173
+    flat, flat_s = topk_select(I.index_scores_mxfp4(q, w, kc, ks, nv), nv, 30)
+    got, got_s = P.pool_topk_mxfp4(q, w, kc, ks, np.arange(n, dtype=np.int32), n, 30, ctx_len=nv)
+    assert np.array_equal(got, flat) and np.array_equal(got_s, flat_s)
+    ids = np.sort(rng.choice(n, 50, replace=False)).astype(np.int32)
+    got, got_s = P.pool_topk_mxfp4(q, w, kc, ks, ids, len(ids), 12)
+    cand = []
+    for t in ids:
+        sc = I.combine_heads(I.head_dots_mxfp4(q, kc[t:t + 1], ks[t:t + 1]), w)[0]
+        cand.append((float(sc), int(t)))
+    cand.sort(key=lambda c: (-c[0], c[1]))
+    want = sorted(t for _, t in cand[:12])
+    assert got.tolist() == want
