@@ -15,6 +15,8 @@ every cache resident in HBM:
               layers over 16 x 64K entries;
   paged64k    decode64k with the main rows in a page pool and ring windows;
   mxfp4_64k   decode64k with the pages' MXFP4 indexer keys (68 bytes per token);
+  pages64k    the pages' own decode formats: 512-wide K = V rows, MXFP4 keys of
+              32 indexer heads, top-512, RoPE fused around attention;
   mq2_64k     multi-query decode: 2 query tokens per sequence over 64 x 64K
               (one pass over the keys for both, then attention per token).
 Every step is timed by its own pair of HIP events; ms_per_step is their
@@ -198,6 +200,9 @@ class Case:
         else:
             self.k_idx = inputs.int_e4m3((B, N, wl.D_I), wl.seed, 0, "k_idx", device=dev)
         self.ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
+        if wl.rope:   # (cos, sin) of each row's query position for the 32 rotary channel pairs
+            th = inputs.rope_angles(B, wl.seed, device=dev)
+            self.rope_cs = torch.stack([torch.cos(th), torch.sin(th)], dim=-1).reshape(B, 64).contiguous()
         self.swa_len = torch.full((B,), wl.W, dtype=torch.int32, device=dev)
         self.layers = []
         for li, kind in enumerate(wl.layers):
@@ -275,6 +280,11 @@ class Case:
                 csa2.csa2_sparse_attn_prefill(L["q"], self.codes, self.scales, idx, self.ctx, self.q_pos, L["sv"],
                                               L["ss"], self.swa_pos0, wl.W, wl.softmax_scale, d_v=wl.d_v,
                                               workspace=self.ws_attn, out=out)
+            elif wl.rope:
+                out = self.out.view(wl.B, wl.H, wl.d_v)
+                csa2.csa2_sparse_attn_decode_rope(L["q"], self.codes, self.scales, idx[:, 0], self.ctx, L["sv"],
+                                                  L["ss"], self.swa_len, wl.softmax_scale, self.rope_cs,
+                                                  rotate_q=True, workspace=self.ws_attn, out=out)
             else:
                 out = self.out.view(wl.B, wl.H, wl.d_v)
                 csa2.csa2_sparse_attn_decode(L["q"], self.codes, self.scales, idx[:, 0], self.ctx, L["sv"], L["ss"],

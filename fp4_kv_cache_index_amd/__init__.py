@@ -56,6 +56,11 @@ _SIGS = {
                                                c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_int32,
                                                c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                                c_void_p]),
+    "csa2_sparse_attn_decode_rope": (ctypes.c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64,
+                                                    c_int64, c_void_p, c_int32, c_void_p, c_void_p, c_int64, c_int64,
+                                                    c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32,
+                                                    c_int32, c_int32, c_float, c_void_p, c_int32, c_int32, c_void_p,
+                                                    c_void_p, c_void_p, c_size_t, c_void_p]),
     "csa2_sparse_attn_prefill_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "csa2_sparse_attn_prefill": (ctypes.c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64,
                                                 c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int64,
@@ -416,6 +421,42 @@ def csa2_sparse_attn_decode(q, kv_codes, kv_scales, topk_idx, ctx_len, swa_vals,
                                          _ptr(swa_len), W, _ptr(sink), B, H, d_qk, d_v, float(softmax_scale),
                                          _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)),
            "csa2_sparse_attn_decode")
+    return out, lse
+
+
+def csa2_sparse_attn_decode_rope(q, kv_codes, kv_scales, topk_idx, ctx_len, swa_vals, swa_scales, swa_len,
+                                 softmax_scale, rope_cs, rotate_q=False, sink=None, want_lse=False, workspace=None,
+                                 out=None, lse=None):
+    """Decode attention over the pages' 512-wide K = V row with fused RoPE:
+    rope_cs [B][rope_dim] f32 = (cos, sin) per channel pair of the last rope_dim
+    channels; q's rotary channels rotated forward when rotate_q, the output's
+    rotated back.  Other arguments as csa2_sparse_attn_decode.  Returns (out, lse)."""
+    _gpu(q, "q", torch.float32)
+    _gpu(topk_idx, "topk_idx", torch.int32)
+    _gpu(ctx_len, "ctx_len", torch.int32)
+    _gpu(rope_cs, "rope_cs", torch.float32)
+    if not (q.is_contiguous() and topk_idx.is_contiguous() and rope_cs.is_contiguous()):
+        raise ValueError("q, topk_idx and rope_cs must be contiguous")
+    B, H, d = q.shape
+    rope_dim = rope_cs.shape[-1]
+    k_top = topk_idx.shape[-1]
+    W = 0 if swa_vals is None else swa_vals.shape[1]
+    if sink is not None:
+        _gpu(sink, "sink", torch.float32)
+    cb, cr, sb, sr, vb, vr, xb, xr = _attn_caches(kv_codes, kv_scales, swa_vals, swa_scales)
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    need = csa2_sparse_attn_decode_workspace_size(B, H, d, k_top, W)
+    ws, ws_bytes = _workspace(need, dev, workspace)
+    _check(lib().csa2_sparse_attn_decode_rope(_ptr(q), _ptr(kv_codes), cb, cr, _ptr(kv_scales), sb, sr,
+                                              _ptr(topk_idx), k_top, _ptr(ctx_len), _ptr(swa_vals), vb, vr,
+                                              _ptr(swa_scales), xb, xr, _ptr(swa_len), W, _ptr(sink), B, H, d,
+                                              float(softmax_scale), _ptr(rope_cs), rope_dim, int(bool(rotate_q)),
+                                              _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(dev)),
+           "csa2_sparse_attn_decode_rope")
     return out, lse
 
 

@@ -458,6 +458,36 @@ int csa2_sparse_attn_decode(const float* q, const uint8_t* kv_codes, int64_t c_b
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }
 
+int csa2_sparse_attn_decode_rope(const float* q, const uint8_t* kv_codes, int64_t c_batch_stride,
+                                 int64_t c_row_stride, const uint8_t* kv_scales, int64_t s_batch_stride,
+                                 int64_t s_row_stride, const int32_t* topk_idx, int32_t k_top, const int32_t* ctx_len,
+                                 const uint8_t* swa_vals, int64_t sv_batch_stride, int64_t sv_row_stride,
+                                 const uint8_t* swa_scales, int64_t ss_batch_stride, int64_t ss_row_stride,
+                                 const int32_t* swa_len, int32_t W, const float* sink, int32_t B, int32_t H,
+                                 int32_t d, float softmax_scale, const float* rope_cs, int32_t rope_dim,
+                                 int32_t rotate_q, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (B == 0) return CSA2_OK;
+  int st = attn_common_check(q, kv_codes, c_batch_stride, c_row_stride, kv_scales, s_batch_stride, s_row_stride,
+                             topk_idx, k_top, ctx_len, swa_vals, sv_batch_stride, sv_row_stride, swa_scales,
+                             ss_batch_stride, ss_row_stride, W, B, H, d, d, out);
+  if (st != CSA2_OK) return st;
+  if (d != 512) return CSA2_EUNSUPPORTED;   // the pages' K = V row
+  if (!rope_cs || rope_dim <= 0 || rope_dim > d || (rope_dim & 3) || ((uintptr_t)rope_cs & 15)) return CSA2_EINVAL;
+  if (W > 0 && !swa_len) return CSA2_EINVAL;
+  if (k_top + W == 0) return CSA2_EINVAL;
+  if (B > 65535) return CSA2_EUNSUPPORTED;
+  if (!ws || ((uintptr_t)ws & 255u)) return CSA2_EINVAL;
+  if (ws_bytes < csa2_sparse_attn_decode_workspace_size(B, H, d, k_top, W)) return CSA2_EWORKSPACE;
+  AttnArgs a{q, kv_codes, c_batch_stride, c_row_stride, kv_scales, s_batch_stride, s_row_stride, topk_idx, k_top,
+             ctx_len, nullptr, swa_vals, sv_batch_stride, sv_row_stride, swa_scales, ss_batch_stride, ss_row_stride,
+             swa_len, nullptr, 0, W, sink, B, 1, H, d, d, softmax_scale, out, lse};
+  a.rope_cs = rope_cs;
+  a.rope_dim = rope_dim;
+  a.rope_q = rotate_q ? 1 : 0;
+  hipError_t e = launch_sparse_attn(a, false, ws, (hipStream_t)stream);
+  return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
 size_t csa2_sparse_attn_prefill_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d_v, int32_t k_top,
                                                int32_t W) {
   if (B < 0 || Tq < 0 || H <= 0 || d_v <= 0 || k_top < 0 || W < 0) return 0;

@@ -317,11 +317,24 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   // are issued before the wait for q.
   _Float16* qs = kbuf[1];
   if (nch > 0) gather(e_begin, 0);
+  // Rotary channels of q rotated forward by the query position's angles
+  // (fused RoPE of the pages' attention step), pairs (2i, 2i+1), in float32
+  // before the fp16 rounding.
+  const int r0 = DQK - a.rope_dim;
+  const float* cs_row = a.rope_cs ? a.rope_cs + row * (int64_t)a.rope_dim : nullptr;
 #pragma unroll
   for (int u = 0; u < QL; ++u) {
     const int i = (int)threadIdx.x + u * kAttnThreads;
     if (i < n4) {
       const int h = (4 * i) / DQK, d = 4 * i - h * DQK;
+      if (a.rope_q && cs_row && d >= r0) {
+        const float4 cs = *reinterpret_cast<const float4*>(cs_row + (d - r0));   // (cos, sin) of two pairs
+        const float x0 = qv[u].x, y0 = qv[u].y, x1 = qv[u].z, y1 = qv[u].w;
+        qv[u].x = x0 * cs.x - y0 * cs.y;
+        qv[u].y = x0 * cs.y + y0 * cs.x;
+        qv[u].z = x1 * cs.z - y1 * cs.w;
+        qv[u].w = x1 * cs.w + y1 * cs.z;
+      }
       v2h lo = {(_Float16)qv[u].x, (_Float16)qv[u].y}, hi = {(_Float16)qv[u].z, (_Float16)qv[u].w};
       *reinterpret_cast<uint2*>(qs + h * QP + d) =
           uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
@@ -575,7 +588,19 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         const int h = 16 * t + 4 * g + r;
         const float w = pml[0][h], inv = pml[1][h];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) a.out[(row * H + h) * DV + 128 * dq + 16 * n + c16] = (o[t][n][r] * w) * inv;
+        for (int n = 0; n < NT; ++n) {
+          float v = (o[t][n][r] * w) * inv;
+          const int dim = 128 * dq + 16 * n + c16;
+          if (a.rope_cs && 128 * dq + 16 * n >= DV - a.rope_dim) {
+            // inverse rotation of the rotary output channels: the pair's
+            // other half sits in the neighbouring lane
+            const float other = __shfl_xor(v, 1, 64);
+            const int pr = (dim - (DV - a.rope_dim)) & ~1;
+            const float c = a.rope_cs[row * (int64_t)a.rope_dim + pr], sn = a.rope_cs[row * (int64_t)a.rope_dim + pr + 1];
+            v = (c16 & 1) ? v * c - other * sn : v * c + other * sn;
+          }
+          a.out[(row * H + h) * DV + dim] = v;
+        }
       }
     }
     return;
@@ -605,7 +630,8 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 template <int DV, int U, int DPL, int MAXG>
 __global__ void __launch_bounds__(512)
 sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int splits, int H,
-                           const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse) {
+                           const float* __restrict__ sink, float* __restrict__ out, float* __restrict__ lse,
+                           const float* __restrict__ rope_cs, int rope_dim) {
   constexpr int GT = DV / DPL;              // threads per group
   constexpr int NV = DPL / 4;               // float4 per thread and split
   static_assert(DPL % 4 == 0 && GT % 64 == 0, "whole waves of float4 columns");
@@ -674,7 +700,15 @@ sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __rest
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float4* op = reinterpret_cast<float4*>(out + rh * DV) + NV * gl;
 #pragma unroll
-  for (int v = 0; v < NV; ++v) op[v] = float4{acc[v].x * inv, acc[v].y * inv, acc[v].z * inv, acc[v].w * inv};
+  for (int v = 0; v < NV; ++v) {
+    float4 r = float4{acc[v].x * inv, acc[v].y * inv, acc[v].z * inv, acc[v].w * inv};
+    const int d0 = 4 * (NV * gl + v);
+    if (rope_cs && d0 >= DV - rope_dim) {   // inverse rotation of two rotary pairs
+      const float4 cs = *reinterpret_cast<const float4*>(rope_cs + row * (int64_t)rope_dim + (d0 - (DV - rope_dim)));
+      r = float4{r.x * cs.x + r.y * cs.y, r.y * cs.x - r.x * cs.y, r.z * cs.z + r.w * cs.w, r.w * cs.z - r.z * cs.w};
+    }
+    op[v] = r;
+  }
   if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
@@ -716,17 +750,17 @@ static hipError_t launch_attn_t(const AttnArgs& a, bool prefill, void* ws, hipSt
     const dim3 grid((unsigned)(rows * a.H));
     if (real_splits <= 4) {
       CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV, 4, 4, 1>), grid, dim3(DV / 4), 0, s, part_o,
-                  part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+                  part_ml, real_splits, a.H, a.sink, a.out, a.lse, a.rope_cs, a.rope_dim);
     } else {
       const int U = real_splits <= 16 ? 4 : 8;
       int G = (real_splits + U - 1) / U;
       if (G > 8) G = 8;
       if (U == 4)
         CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV, 4, 8, 8>), grid, dim3(64 * G), 0, s, part_o,
-                    part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+                    part_ml, real_splits, a.H, a.sink, a.out, a.lse, a.rope_cs, a.rope_dim);
       else
         CSA2_LAUNCH("sparse_attn_combine", (sparse_attn_combine_kernel<DV, 8, 8, 8>), grid, dim3(64 * G), 0, s, part_o,
-                    part_ml, real_splits, a.H, a.sink, a.out, a.lse);
+                    part_ml, real_splits, a.H, a.sink, a.out, a.lse, a.rope_cs, a.rope_dim);
     }
   }
   return hipGetLastError();

@@ -163,6 +163,10 @@ struct AttnArgs {
   // Ring window (swa_ring > 0): position x at row x % swa_ring; swa_end[b]
   // is one past the newest position written.
   int swa_ring = 0; const int32_t* swa_end = nullptr;
+  // Rotary handling (rope_cs != null): per query row rope_dim floats, (cos,
+  // sin) of each channel pair of the last rope_dim channels; q's rotary
+  // channels rotated forward when rope_q, the output's rotated back.
+  const float* rope_cs = nullptr; int rope_dim = 0; int rope_q = 0;
 };
 int attn_num_splits(int64_t rows, int k_top, int W);
 size_t attn_ws_bytes(int64_t rows, int H, int d_v, int splits);

@@ -67,6 +67,7 @@ class Workload:
     page_size: int = 0   # > 0: main rows in a page pool (random page order), window in a ring
     m: int = 1           # tokens per cache entry (2: the encoder layers' compressed entries); N counts entries
     mxfp4: bool = False  # indexer keys in the pages' MXFP4 format (float32 N(0,1) rows quantised), not E4M3 integers
+    rope: bool = False   # fused RoPE around attention (the pages' K = V row: d_qk = d_v = 512)
 
     def __post_init__(self):
         if self.softmax_scale == 0.0:
@@ -103,6 +104,13 @@ WORKLOADS = {
     # 4 E8M0 scale bytes per token instead of 128 E4M3 bytes).
     "mxfp4_64k": Workload("MXFP4 indexer keys: B64 x 64K ctx, Full, 64 heads, indexer 8x128, top-2048", 9,
                           B=64, N=65536, H=64, d_qk=576, d_v=512, H_I=8, D_I=128, K=2048, mxfp4=True),
+    # The pages' decode step in their own formats: the 512-wide K = V row
+    # (288 bytes), MXFP4 indexer keys of 32 heads x 128 (68 bytes), top-512,
+    # and the fused RoPE around attention.
+    "pages64k": Workload("pages' formats: B64 x 64K ctx, K=V 512 (288 B) + MXFP4 indexer 32x128 (68 B), "
+                         "top-512, fused RoPE", 10,
+                         B=64, N=65536, H=64, d_qk=512, d_v=512, H_I=32, D_I=128, K=512, mxfp4=True, rope=True,
+                         softmax_scale=1.0 / (512.0 ** 0.5)),
     # Serving layout: the decode64k step with the main rows in a pool of
     # 64-token pages (random page order) and each window in a 128-row ring.
     "paged64k": Workload("paged decode: B64 x 64K ctx, 64-token pages, ring window, Full, 64 heads, "
@@ -158,6 +166,12 @@ def random_index_lists(B, K, N, seed, layer=0, device="cpu", n_invalid=0):
         bad[:, ::2] = N + 7
         out[:, K - n_invalid:] = bad
     return out
+
+
+def rope_angles(B, seed, device="cpu"):
+    """Rotary angles of each row's query position for 32 channel pairs (uniform
+    over many turns: the kernel only sees their cosines and sines)."""
+    return normal_f32((B, 32), seed, 0, "sink", device=device) * 100.0
 
 
 def idx_key_rows(shape, seed, device="cpu"):

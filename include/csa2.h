@@ -289,6 +289,34 @@ int csa2_sparse_attn_decode(const float* q,
                             float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_sparse_attn_decode_rope -- csa2_sparse_attn_decode over the pages'
+ * 512-wide K = V row (fact sheet, attention facts: head dim 512 = nope +
+ * rope, one shared K = V entry; partial RoPE on the last 64 dims of Q and KV
+ * with an inverse rotation on the attention output; techniques map, inference
+ * kernel: a fused RoPE-attention-RoPE-cast kernel) with the rotary steps
+ * fused around it.  d_qk = d_v = d = 512.  rope_cs [B][rope_dim] float32
+ * (16-byte aligned): for the query position of row b, the cosine and sine of
+ * the angle of each channel pair (2i, 2i+1) of the last rope_dim channels,
+ * (cos_i, sin_i) at [b][2i], [b][2i+1] (the angles -- RoPE base, YaRN -- are
+ * the caller's).  When rotate_q, q's last rope_dim channels are rotated
+ * forward, (a, b) -> (a cos - b sin, a sin + b cos), before the products
+ * (else q arrives rotated); out's last rope_dim channels are always rotated
+ * back, (a, b) -> (a cos + b sin, b cos - a sin).  The output stays float32.
+ * rope_dim a positive multiple of 4, at most d.  Other arguments as in
+ * csa2_sparse_attn_decode (workspace: csa2_sparse_attn_decode_workspace_size).
+ */
+int csa2_sparse_attn_decode_rope(const float* q,
+                                 const uint8_t* kv_codes, int64_t c_batch_stride, int64_t c_row_stride,
+                                 const uint8_t* kv_scales, int64_t s_batch_stride, int64_t s_row_stride,
+                                 const int32_t* topk_idx, int32_t k_top, const int32_t* ctx_len,
+                                 const uint8_t* swa_vals, int64_t sv_batch_stride, int64_t sv_row_stride,
+                                 const uint8_t* swa_scales, int64_t ss_batch_stride, int64_t ss_row_stride,
+                                 const int32_t* swa_len, int32_t W, const float* sink,
+                                 int32_t B, int32_t H, int32_t d, float softmax_scale,
+                                 const float* rope_cs, int32_t rope_dim, int32_t rotate_q,
+                                 float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * csa2_sparse_attn_prefill -- the same attention for a causal chunk of Tq
  * query tokens per sequence, each with its own Top-K list and its own window:
  * the query at position p = q_pos[b][t] sees window positions

@@ -168,3 +168,42 @@ def sparse_attn_paged_row(q, pool_codes, pool_scales, block_table, page_size, n_
         keys.append(mxfp8_dequantize(ring_vals[wr], ring_scales[wr], d_qk))
     keys = np.concatenate(keys, axis=0) if keys else np.zeros((0, d_qk))
     return attend(q, keys, d_v, scale, sink)
+
+
+def rotate_pairs(x, cs, sign):
+    """Rotate the channel pairs (2i, 2i+1) of x [..., 2n] by sign * theta_i,
+    where cs [n][2] holds (cos theta_i, sin theta_i): (a, b) ->
+    (a cos - sign b sin, sign a sin + b cos)."""
+    x = np.asarray(x, dtype=np.float64)
+    c = np.asarray(cs, dtype=np.float64)[:, 0]
+    s = sign * np.asarray(cs, dtype=np.float64)[:, 1]
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def sparse_attn_decode_rope_row(q, kv_codes, kv_scales, idx, ctx_len, swa_vals, swa_scales, swa_len, d, scale,
+                                rope_cs, rope_dim, rotate_q, sink=None):
+    """Decode attention over the pages' 512-wide K = V row with the rotary part
+    handled around it ([facts] attention: partial RoPE on the last 64 dims of
+    Q and KV, inverse rotation on the attention output; [map] inference
+    kernel: fused RoPE-attention-RoPE-cast).
+
+    The last rope_dim channels of q are rotated forward by the query
+    position's angles when rotate_q (else q arrives rotated), attention runs
+    as sparse_attn_decode_row with d_qk = d_v = d, and the last rope_dim
+    channels of the output are rotated back by the same angles.  rope_cs
+    [rope_dim/2][2] holds (cos, sin) of the query position; channel pairs are
+    adjacent (2i, 2i+1) -- a reading, the pages give no pair convention.
+    """
+    q = np.asarray(q, dtype=np.float64).copy()
+    r0 = d - rope_dim
+    if rotate_q:
+        q[:, r0:] = rotate_pairs(q[:, r0:], rope_cs, +1)
+    out, lse = sparse_attn_decode_row(q, kv_codes, kv_scales, idx, ctx_len, swa_vals, swa_scales, swa_len, d, d,
+                                      scale, sink)
+    out = out.copy()
+    out[:, r0:] = rotate_pairs(out[:, r0:], rope_cs, -1)
+    return out, lse

@@ -306,3 +306,38 @@ def test_window_rows_at_the_ends_of_the_exact_scale_range(code):
     want_o, want_l = _oracle_decode(np_(q), np_(kv_x), np_(idx), np_(ctx), np_(swa_x), np_(swa_len), d_qk, 512,
                                     scale)
     _check(out, lse, want_o, want_l)
+
+
+@gpu
+@pytest.mark.parametrize("B,rotate_q", [(3, True), (3, False), (300, True)])
+def test_pages_row_with_fused_rope(B, rotate_q):
+    """The pages' 512-wide K = V row with the rotary steps fused around the
+    attention: q's last 64 channels rotated forward (or given rotated), the
+    output's last 64 rotated back.  B = 3 runs several splits per row (the
+    rotation in the combine), B = 300 one split per row (in the split kernel)."""
+    require_gpu()
+    announce(f"attn decode rope B={B} rotate_q={rotate_q}")
+    N, d, H, K, W = 3000, 512, 64, 512, 128
+    kv_x, codes, scales, swa_x, sv, ss = _make_caches(B, N, d, W, 101, interleaved=True)
+    q = inputs.normal_f32((B, H, d), 101, 2, "q", device="cuda")
+    idx = inputs.random_index_lists(B, K, N, 101, device="cuda", n_invalid=3)
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    swa_len = torch.full((B,), W, dtype=torch.int32, device="cuda")
+    theta = inputs.normal_f32((B, 32), 101, 3, "q", device="cuda") * 100.0
+    rope_cs = torch.stack([torch.cos(theta), torch.sin(theta)], dim=-1).reshape(B, 64).contiguous()
+    scale = 1 / np.sqrt(512.0)
+    out, lse = csa2.csa2_sparse_attn_decode_rope(q, codes, scales, idx, ctx, sv, ss, swa_len, scale, rope_cs,
+                                                 rotate_q=rotate_q, want_lse=True)
+    torch.cuda.synchronize()
+    qh, kvh, swh, idh, csh = np_(q), np_(kv_x), np_(swa_x), np_(idx), np_(rope_cs).reshape(B, 32, 2)
+    rows = range(B) if B <= 8 else (0, 137, B - 1)
+    want_o, want_l, got_o, got_l = [], [], [], []
+    for b in rows:
+        c_, s_ = Q.fp4_quantize(kvh[b])
+        v8, s8 = Q.mxfp8_quantize(swh[b])
+        o, l = A.sparse_attn_decode_rope_row(qh[b], c_, s_, idh[b], N, v8, s8, W, d, scale, csh[b], 64, rotate_q)
+        want_o.append(o)
+        want_l.append(l)
+        got_o.append(np_(out[b]))
+        got_l.append(np_(lse[b]))
+    _check(torch.from_numpy(np.stack(got_o)), torch.from_numpy(np.stack(got_l)), np.stack(want_o), np.stack(want_l))

@@ -165,3 +165,34 @@ def test_paged_ring_row_equals_the_linear_layout():
     assert A.paged_row([5, -1], 4, 5) == -1 and A.paged_row([5], 4, 4) == -1
     assert A.ring_window_rows(10, 4, 11, 6).tolist() == [7 % 6, 8 % 6, 9 % 6, 10 % 6]
     assert A.ring_window_rows(10, 8, 11, 6).tolist() == [5, 0, 1, 2, 3, 4]   # ring keeps 5..10 only
+
+
+def test_rope_rotation_and_the_inverse_rotation_epilogue():
+    """Pins of the RoPE handling: the pair rotation is orthogonal and its
+    inverse undoes it (closed form for theta = pi/2); zero angles leave plain
+    attention; and with a single entry whose rotary channels were rotated by
+    the query's own angles (a key at the query's position), the epilogue
+    returns that entry's un-rotated channels exactly as V."""
+    rng = np.random.default_rng(31)
+    cs = np.stack([np.cos(t := rng.uniform(-3, 3, 32)), np.sin(t)], axis=1)
+    x = rng.standard_normal((5, 64))
+    y = A.rotate_pairs(x, cs, +1)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    assert np.allclose(A.rotate_pairs(y, cs, -1), x, rtol=1e-13, atol=1e-14)
+    quarter = np.tile([[0.0, 1.0]], (32, 1))                  # theta = pi/2: (a, b) -> (-b, a)
+    z = A.rotate_pairs(x, quarter, +1)
+    assert np.array_equal(z[:, 0::2], -x[:, 1::2]) and np.array_equal(z[:, 1::2], x[:, 0::2])
+    d, n, H = 512, 100, 4
+    codes, scales, kv = _cache(rng, n, d)
+    q = rng.standard_normal((H, d)).astype(np.float32)
+    ident = np.tile([[1.0, 0.0]], (32, 1))
+    o1, l1 = A.sparse_attn_decode_rope_row(q, codes, scales, np.arange(30), n, None, None, 0, d, 0.05, ident, 64,
+                                           True)
+    o2, l2 = A.sparse_attn_decode_row(q, codes, scales, np.arange(30), n, None, None, 0, d, d, 0.05)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # single entry: V's rotary part comes back un-rotated once the row was
+    # rotated by the query's angles (rows are built exactly representable)
+    raw = Q.fp4_dequantize(codes[7:8], scales[7:8], d)[0]
+    o3, _ = A.sparse_attn_decode_rope_row(q, codes, scales, [7], n, None, None, 0, d, 0.05, cs, 64, False)
+    assert np.allclose(A.rotate_pairs(o3[:, 448:], cs, +1), np.broadcast_to(raw[448:], (H, 64)), rtol=1e-12,
+                       atol=1e-13)
