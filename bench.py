@@ -107,12 +107,12 @@ class StepTimer:
 
 # ------------------------------------------------------- counter traffic ---
 
-def counter_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
-    summary, or None when that summary is missing or the kernel's sources
-    have changed since the counters were taken."""
+def counter_traffic(kernel, workload="decode64k"):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when that summary is missing or the
+    kernel's sources have changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_decode64k_hbm_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -451,7 +451,8 @@ def main():
         flops = 2 * wl.H_I * wl.D_I * pairs
         achieved = flops / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                "traffic": counter_traffic(dom, args.workload), "kernel": dom,
                 "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     else:
         # one pass over the keys serves every query row of a sequence
@@ -460,7 +461,7 @@ def main():
         achieved = scan_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": counter_traffic(dom) if args.workload == "decode64k" else None, "kernel": dom,
+                "traffic": counter_traffic(dom, args.workload), "kernel": dom,
                 "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
     cpu = None
     if not args.no_cpu_baseline:
