@@ -110,6 +110,53 @@ def test_select_size_boundary(N):
 
 
 @gpu
+@pytest.mark.parametrize("pool", [False, True])
+@pytest.mark.parametrize("N", [65536, 200_003])
+def test_repeated_calls_give_identical_results(N, pool):
+    """The multi-pass select appends candidates with atomics, so their order in
+    the workspace differs from call to call; the results must not.  Heavy ties
+    at the threshold (scores in a few integer values); five calls, each
+    followed by an unrelated call on the same workspace, all bit-identical to
+    the first, which equals the oracle (Top-K and, with the pool, pool_idx and
+    pool_len)."""
+    require_gpu()
+    announce(f"index_score_topk repeated calls N={N} pool={pool}")
+    B, H_I, D_I, K = 3, 8, 128, 2048
+    pb, nb = (8, 512) if pool else (0, 0)
+    k_idx = inputs.int_e4m3((B, N, D_I), 21, 0, "k_idx", lo=-1, hi=1, device="cuda")
+    q_idx = inputs.int_e4m3((B, 1, H_I, D_I), 21, 1, "q_idx", lo=0, hi=1, device="cuda")
+    w = torch.ones((B, 1, H_I), dtype=torch.float32, device="cuda")
+    ctx = torch.tensor([N, N - 5, N // 3], dtype=torch.int32, device="cuda")
+    need = csa2.csa2_index_score_topk_workspace_size(B, 1, N, K, pb, nb)
+    raw = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + need]
+    other_q = inputs.int_e4m3((B, 1, H_I, D_I), 22, 1, "q_idx", device="cuda")
+    other_w = inputs.normal_f32((B, 1, H_I), 22, 1, "w", device="cuda")
+    runs = []
+    for _ in range(5):
+        r = csa2.csa2_index_score_topk(q_idx, w, k_idx, ctx, K, want_scores=True, pool_block=pb, pool_nblocks=nb,
+                                       workspace=ws)
+        torch.cuda.synchronize()
+        runs.append({key: np_(v).copy() for key, v in r.items() if v is not None})
+        csa2.csa2_index_score_topk(other_q, other_w, k_idx, ctx, K, pool_block=pb, pool_nblocks=nb, workspace=ws)
+    for r in runs[1:]:
+        assert r.keys() == runs[0].keys()
+        for key in runs[0]:
+            assert np.array_equal(r[key], runs[0][key]), key
+    qn, wn, kn, cn = np_(q_idx), np_(w), np_(k_idx), np_(ctx)
+    want_i, want_s = _oracle_rows(qn, wn, kn, cn, K)
+    assert np.array_equal(runs[0]["topk_idx"], want_i)
+    assert np.array_equal(runs[0]["topk_score"], want_s)
+    if pool:
+        for bb in range(B):
+            sc = I.index_scores(qn[bb, 0], wn[bb, 0], kn[bb], int(cn[bb]))
+            pi, pl = P.hier_pool(sc, int(cn[bb]), pb, nb)
+            assert runs[0]["pool_len"][bb, 0] == pl
+            assert np.array_equal(runs[0]["pool_idx"][bb, 0], pi)
+
+
+@gpu
 def test_causal_rows_with_q_pos():
     require_gpu()
     announce("index_score_topk Tq=6 causal rows")
