@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (for counter calibration) and exit")
     p.add_argument("--no-flush", action="store_true",
-                   help="do not write the 512 MB flush buffer between timed steps (MALL left warm)")
+                   help="do not read the 512 MB flush buffer between timed steps (MALL left warm)")
     return p.parse_args()
 
 
