@@ -23,16 +23,17 @@
 
 namespace csa2 {
 
-// Waves per workgroup: 16 for the flat scan with one head block (one large
-// tile per compute unit, so that each workgroup's prologue, histogram flush
-// and key burst are paid once per 16K tokens), 4 for the pool gather and the
-// wide-head variants (their LDS tiles are larger).
-// With QT > 1 query rows of one sequence per workgroup (multi-query decode),
-// 16 / QT waves: the per-wave dot buffers and the staged keys grow with QT.
-template <bool GATHER, int HB, int QT = 1>
-constexpr int kScanWavesT = QT > 1 ? 16 / QT : ((!GATHER && HB == 1) ? 16 : 4);
+// Waves per workgroup of the flat scan: 16 (one large tile per compute unit,
+// so that each workgroup's prologue, histogram flush and key burst are paid
+// once per 16K tokens), 8 for E4M3 keys with 17..32 heads (their key
+// fragments and the two head blocks' results need twice the registers).  4
+// for the pool gather (tiles of 512 pool positions).  With QT > 1 query rows
+// of one sequence per workgroup (multi-query decode), 16 / QT waves: the
+// per-wave dot buffers and the staged keys grow with QT.
+template <bool GATHER, int HB, int QT = 1, bool F4 = false>
+constexpr int kScanWavesT = QT > 1 ? 16 / QT : (GATHER ? 4 : ((HB == 1 || F4) ? 16 : 8));
 constexpr int kScanTileMax = 16384;   // flat-scan tokens per 16-wave workgroup (largest)
-constexpr int kScanTileSmall = 1024;  // flat-scan tokens per 4-wave workgroup
+constexpr int kScanTileSmall = 1024;  // smallest flat-scan tile
 constexpr int kPoolTile = 512;        // pool positions per workgroup (later layers)
 // 16-token MFMA groups per wave iteration (bytes in flight per wave =
 // 2 * 16 * groups * D_I); fewer for 32 indexer heads to bound the LDS tile.
@@ -80,6 +81,30 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
   return (long)(((unsigned long)hi << 32) | lo);
 }
 
+// 4 x 4 transpose across the lane groups g = lane >> 4 (rows of 16 lanes):
+// on entry x[u] of lane (g, c) holds lane group g's value for index u; on
+// exit x[s] holds the value that lane group s had for index g.  Two swap
+// stages: the wave's halves (permlane32 swap: lanes 32..63 of the first
+// operand trade places with lanes 0..31 of the second), then neighbouring
+// rows (permlane16 swap: odd rows of the first with even rows of the
+// second); the lane mapping of both was checked on the device.
+__device__ __forceinline__ void transpose_lane_groups(float (&x)[4]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x[u]),
+                                                    __builtin_bit_cast(unsigned, x[u + 2]), false, false);
+    x[u] = __builtin_bit_cast(float, (unsigned)r[0]);
+    x[u + 2] = __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+#pragma unroll
+  for (int s = 0; s < 4; s += 2) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x[s]),
+                                                    __builtin_bit_cast(unsigned, x[s + 1]), false, false);
+    x[s] = __builtin_bit_cast(float, (unsigned)r[0]);
+    x[s + 1] = __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+}
+
 // GATHER = false: tokens j = tile positions of the row (flat scan).
 // GATHER = true : position p maps to token pool_idx[row][p] (pool layers);
 //                 a pool id outside [0, ctx_len[b]) names no token: the
@@ -101,7 +126,7 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 // products and partial sums stay exact in fp32 while a key's four exponents
 // span at most 11 binades.
 template <int DI, int HB, bool GATHER, bool POOL, bool H8, int QT, bool F4>
-__global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB, QT>))
+__global__ void __launch_bounds__((64 * kScanWavesT<GATHER, HB, QT, F4>))
 index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
                    const uint8_t* __restrict__ k_scales, int64_t ks_bstride, int64_t ks_rstride,
@@ -114,7 +139,7 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
                    int32_t* __restrict__ nb_valid_out, SelectWs blk) {
   static_assert(QT == 1 || (DI == 128 && HB == 1 && H8 && !GATHER && !POOL), "multi-query scan: flat, 8 heads");
   static_assert(!F4 || DI == 128, "MXFP4 keys: 128 channels");
-  constexpr int NW = kScanWavesT<GATHER, HB, QT>;
+  constexpr int NW = kScanWavesT<GATHER, HB, QT, F4>;
   constexpr int NT = 64 * NW;
   constexpr int CH = DI / 4;           // bytes of a key row per lane
   constexpr int KS = DI / 32;          // MFMA k-steps
@@ -131,12 +156,16 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // burst at the end (interleaving small key stores with the key-row stream
   // costs more than the LDS round trip).
   constexpr bool kStage = !GATHER && !POOL;
-  constexpr int kTileCap = QT > 1 ? 1024 * NW : (NW == 16 ? kScanTileMax : kScanTileSmall);
+  constexpr int kTileCap = 1024 * NW;
   __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? QT * kTileCap : 1];
   __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
   __shared__ uint32_t bhist[POOL ? 4096 : 1];
-  // per wave: the batch's dots, then one 4-float trash slot per lane (whole-line path)
-  __shared__ __attribute__((aligned(16))) float dots[NW][16 * kScanGroups<HB> * HP + 256];
+  // Whole-line path: per wave the batch's dots, then one 4-float trash slot
+  // per lane (the other paths move the dots to their token's lane in
+  // registers: RT).
+  constexpr bool FULL = !F4 && (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
+  constexpr bool RT = !FULL;
+  __shared__ __attribute__((aligned(16))) float dots[NW][RT ? 1 : 16 * kScanGroups<HB> * HP + 256];
   __shared__ float wsh[HMAX];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -155,7 +184,6 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
     return;
   }
   const int c16 = lane & 15, g = lane >> 4;
-  constexpr bool FULL = !F4 && (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
   const int64_t tile0 = (int64_t)blockIdx.x * tile;
   constexpr int pitch = HP;
   float* my = dots[wave];
@@ -425,7 +453,14 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   if constexpr (BUF) krs = wave_rsrc(wend);
   if constexpr (F4 && BUF) srs = wave_srsrc(wend);
 
+  // RT: the 16x16 results of a batch stay in registers, x[b][r][u] =
+  // dot(MFMA row 16b + 4g + r, token 16u + c16); one 4x4 transpose across
+  // the lane groups per (b, r) then leaves lane (g, c16) with every row of
+  // token 16g + c16 = lane: x[b][r][s] = dot(row 16b + 4s + r, token lane).
+  constexpr int NRB = F4 ? RB : HB;
+  static_assert(!RT || SG == 4, "register transpose: four groups of 16 tokens per batch");
   auto score_batch = [&](const Frag<CH>(&f)[SG], int64_t it) {
+    float x[RT ? NRB : 1][4][4];
     if constexpr (F4) {
 #pragma unroll
       for (int u = 0; u < SG; ++u) {
@@ -438,10 +473,8 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
           v4f acc = {0.f, 0.f, 0.f, 0.f};
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa4[rb], bk, acc, 0 /* A E4M3 */, 4 /* B E2M1 */,
                                                                  0, 127, 0, sb);
-          // acc[r] = dot(A row 16 rb + 4g + r, key 16u + c16)
-          const bool keep = 16 * rb + 4 * g < HP;
-          const int at = keep ? (16 * u + c16) * pitch + 16 * rb + 4 * g : 16 * SG * HP + 4 * lane;
-          *reinterpret_cast<v4f*>(my + at) = acc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[rb][r][u] = acc[r];
         }
       }
     } else if constexpr (FULL) {
@@ -472,22 +505,29 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
       }
     } else {
 #pragma unroll
-    for (int s = 0; s < SG; ++s) {
+      for (int su = 0; su < SG; ++su) {
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        for (int hb = 0; hb < HB; ++hb) {
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < KS; ++i)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[hb][i], as_long(f[s].w[2 * i], f[s].w[2 * i + 1]),
-                                                           acc, 0, 0, 0);
-        // acc[r] = dot(head 16*hb + 4*g + r, token 16*s + c16)
-        const int h0 = 16 * hb + 4 * g;
-        if (h0 < HP) *reinterpret_cast<v4f*>(my + (16 * s + c16) * pitch + h0) = acc;
+          for (int i = 0; i < KS; ++i)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa[hb][i], as_long(f[su].w[2 * i], f[su].w[2 * i + 1]),
+                                                             acc, 0, 0, 0);
+          // acc[r] = dot(head 16*hb + 4*g + r, token 16*su + c16)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[hb][r][su] = acc[r];
+        }
       }
     }
+    if constexpr (RT) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) transpose_lane_groups(x[rb][r]);
+    } else {
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
     for (int u = 0; u < SG / 4; ++u) {
       // Lane owns token it + 64u + lane.
@@ -502,14 +542,25 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
       for (int t = 0; t < QT; ++t) {
         if (t >= nq) break;   // (uniform)
         float sc = 0.0f;
+        if constexpr (RT) {
 #pragma unroll
-        for (int h4 = 0; h4 < HPQ; h4 += 4) {
-          const v4f d4 = *reinterpret_cast<const v4f*>(src + HPQ * t + h4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int hq = 0; hq < HPQ; ++hq) {
+            // MFMA row of head hq of query t
+            const int R = (QT > 1 ? 8 * t : 0) + hq;
+            const float d = x[R >> 4][R & 3][(R >> 2) & 3];
             // heads past H_I have weight 0: adding +0 leaves the sum unchanged
-            float r = d4[e] > 0.0f ? d4[e] : 0.0f;
-            sc = __fadd_rn(sc, __fmul_rn(wv[HPQ * t + h4 + e], r));
+            const float r = d > 0.0f ? d : 0.0f;
+            sc = __fadd_rn(sc, __fmul_rn(wv[HPQ * t + hq], r));
+          }
+        } else {
+#pragma unroll
+          for (int h4 = 0; h4 < HPQ; h4 += 4) {
+            const v4f d4 = *reinterpret_cast<const v4f*>(src + HPQ * t + h4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float r = d4[e] > 0.0f ? d4[e] : 0.0f;
+              sc = __fadd_rn(sc, __fmul_rn(wv[HPQ * t + h4 + e], r));
+            }
           }
         }
         vis = vis_w && (QT == 1 || j < nvq[t]);
@@ -533,8 +584,10 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (!RT) {
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   };
 
   const int nb = wend > wbase ? (int)((wend - wbase + IT - 1) / IT) : 0;
@@ -593,11 +646,12 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   }
 }
 
-// Flat-scan tile: the largest that still gives every compute unit a
-// workgroup (16-wave workgroups), else kScanTileSmall.
+// Flat-scan tile: 1024 tokens per wave, halved while the grid would leave
+// compute units without a workgroup (down to kScanTileSmall).
 // (`rows` counts workgroup rows: query rows, or groups of them)
 static int scan_tile(int64_t rows, int64_t n_max, int nw, int qt = 1) {
-  int tile = qt > 1 ? 1024 * nw : (nw == 16 ? kScanTileMax : kScanTileSmall);
+  (void)qt;
+  int tile = 1024 * nw;
   while (tile > kScanTileSmall && rows * ((n_max + tile - 1) / tile) < device_cu_count()) tile >>= 1;
   return tile;
 }
@@ -614,7 +668,7 @@ static int scan_qt(const ScoreArgs& a) {
 template <int QT, bool F4>
 static hipError_t launch_scan_mq(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
                                  const SelectWs& tok, hipStream_t s) {
-  constexpr int NW = kScanWavesT<false, 1, QT>;
+  constexpr int NW = kScanWavesT<false, 1, QT, F4>;
   const int64_t groups = (int64_t)a.B * ((a.Tq + QT - 1) / QT);
   const int tile = scan_tile(groups, a.n_max, NW, QT);
   int64_t tiles = (a.n_max + tile - 1) / tile;
@@ -632,7 +686,7 @@ static hipError_t launch_scan_t(const ScoreArgs& a, uint32_t* keys, int64_t key_
                                 const SelectWs& tok, uint32_t* bkeys, int64_t bkey_stride, int32_t* nb_valid,
                                 const SelectWs* blk, hipStream_t s) {
   int64_t rows = (int64_t)a.B * a.Tq;
-  constexpr int NW = kScanWavesT<false, HB>;
+  constexpr int NW = kScanWavesT<false, HB, 1, F4>;
   const int tile = scan_tile(rows, a.n_max, NW);
   int64_t tiles = (a.n_max + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
@@ -662,7 +716,7 @@ static hipError_t launch_pool_t(const ScoreArgs& a, const int32_t* pool_idx, con
   int64_t tiles = (pool_cap + kPoolTile - 1) / kPoolTile;
   if (tiles < 1) tiles = 1;
   CSA2_LAUNCH("pool_score", (index_score_kernel<DI, HB, true, false, H8, 1, F4>),
-              dim3((unsigned)tiles, (unsigned)rows), dim3(64 * kScanWavesT<true, HB>), 0, s, a.q_idx, a.w, a.k_idx,
+              dim3((unsigned)tiles, (unsigned)rows), dim3(64 * kScanWavesT<true, HB, 1, F4>), 0, s, a.q_idx, a.w, a.k_idx,
               a.k_bstride, a.k_rstride, a.k_scales, a.ks_bstride, a.ks_rstride, a.ctx_len, (const int32_t*)nullptr,
               pool_idx, pool_len, pool_cap, a.Tq, a.H_I, (int64_t)pool_cap, a.k_top, kPoolTile, keys, key_stride,
               n_valid, ws, 0, 0, (uint32_t*)nullptr, (int64_t)0, (int32_t*)nullptr, ws);
@@ -1103,7 +1157,9 @@ int64_t index_score_tiles(const ScoreArgs& a) {
   } else if (qt == 4) {
     tile = scan_tile((int64_t)a.B * ((a.Tq + 3) / 4), a.n_max, kScanWavesT<false, 1, 4>, 4);
   } else {
-    tile = scan_tile((int64_t)a.B * a.Tq, a.n_max, a.H_I <= 16 ? kScanWavesT<false, 1> : kScanWavesT<false, 2>);
+    const bool f4 = a.k_scales != nullptr;
+    tile = scan_tile((int64_t)a.B * a.Tq, a.n_max,
+                     a.H_I <= 16 ? kScanWavesT<false, 1> : (f4 ? kScanWavesT<false, 2, 1, true> : kScanWavesT<false, 2>));
   }
   const int64_t tiles = (a.n_max + tile - 1) / tile;
   return tiles < 1 ? 1 : tiles;
