@@ -645,6 +645,22 @@ sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __rest
   const int G = blockDim.x / GT;
   const float sk = sink ? sink[h] * kLog2e : -__builtin_inff();
   const float* mlb = part_ml + (row * splits * (int64_t)H + h) * 2;   // split s at mlb[2 * s * H]
+  const float4* ob = reinterpret_cast<const float4*>(part_o + (row * splits * (int64_t)H + h) * DV) + NV * gl;
+  // The first round's partials are requested before the split maxima are
+  // reduced (their addresses do not depend on them), so that both loads
+  // share one memory round trip.
+  float2 ml[U];
+  float4 ov[U][NV];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + u * G < splits ? s0 + u * G : (s0 < splits ? s0 : 0);
+      ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) ov[u][v] = ob[(int64_t)sp * H * (DV / 4) + v];
+    }
+  };
+  load_round(grp);
   float mx = -__builtin_inff();
   for (int sp = lane; sp < splits; sp += 64) mx = fmaxf(mx, mlb[2 * (int64_t)sp * H]);
 #pragma unroll
@@ -655,17 +671,8 @@ sparse_attn_combine_kernel(const float* __restrict__ part_o, const float* __rest
   for (int v = 0; v < NV; ++v) acc[v] = float4{0.f, 0.f, 0.f, 0.f};
   float L = 0.0f;
   if (M != -__builtin_inff()) {
-    const float4* ob = reinterpret_cast<const float4*>(part_o + (row * splits * (int64_t)H + h) * DV) + NV * gl;
     for (int s0 = grp; s0 < splits; s0 += G * U) {
-      float2 ml[U];
-      float4 ov[U][NV];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sp = s0 + u * G < splits ? s0 + u * G : s0;
-        ml[u] = *reinterpret_cast<const float2*>(mlb + 2 * (int64_t)sp * H);
-#pragma unroll
-        for (int v = 0; v < NV; ++v) ov[u][v] = ob[(int64_t)sp * H * (DV / 4) + v];
-      }
+      if (s0 != grp) load_round(s0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (s0 + u * G >= splits || ml[u].x == -__builtin_inff()) continue;
