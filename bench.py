@@ -56,6 +56,9 @@ def parse():
                    help="run only a plain 1 GiB device copy (for counter calibration) and exit")
     p.add_argument("--no-flush", action="store_true",
                    help="do not read the 512 MB flush buffer between timed steps (MALL left warm)")
+    p.add_argument("--stored-keys", action="store_true",
+                   help="give the indexer its stored-key workspace (prefill chunks then store their score keys "
+                        "and select in one scoring pass instead of by scoring passes)")
     return p.parse_args()
 
 
@@ -161,7 +164,7 @@ def layer_bytes(wl, kind, pool_cap=0):
 class Case:
     """Resident inputs and the step function of one workload."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, stored_keys=False):
         import torch
         import fp4_kv_cache_index_amd as csa2
         from fp4_kv_cache_index_amd import inputs
@@ -224,7 +227,10 @@ class Case:
         # Workspaces and outputs, allocated once.
         rows = B * wl.Tq
         pb, nb = (wl.pool_block, wl.pool_nblocks) if wl.pool_block else (0, 0)
-        self.ws_idx = self._ws(csa2.csa2_index_score_topk_workspace_size(B, wl.Tq, N, wl.K, pb, nb))
+        ws_size = (csa2.csa2_index_score_topk_workspace_size_stored if stored_keys else
+                   csa2.csa2_index_score_topk_workspace_size)
+        self.ws_idx = self._ws(ws_size(B, wl.Tq, N, wl.K, pb, nb))
+        self.ws_idx_bytes = self.ws_idx.numel()
         self.ws_attn = self._ws(csa2.csa2_sparse_attn_prefill_workspace_size(B, wl.Tq, wl.H, wl.d_v, wl.K, wl.W)
                                 if wl.Tq > 1 or wl.page_size else csa2.csa2_sparse_attn_decode_workspace_size(B, wl.H, wl.d_v, wl.K,
                                                                                             wl.W))
@@ -386,7 +392,7 @@ def main():
         return
     wl = inputs.WORKLOADS[args.workload]
     print(f"[bench] building inputs for {wl.name}", file=sys.stderr, flush=True)
-    case = Case(wl, dev)
+    case = Case(wl, dev, args.stored_keys)
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         case.step()
@@ -476,7 +482,7 @@ def main():
                    "heads": wl.H, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.K, "window": wl.W,
                    "layers": wl.layers, "tokens_per_entry": wl.m,
                    "indexer_keys": "MXFP4 (E2M1 + E8M0/32)" if wl.mxfp4 else "E4M3 integers",
-                   "parallelism": "single GPU"},
+                   "indexer_workspace_bytes": case.ws_idx_bytes, "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "step_bytes": step_bytes,
         "step_stats": {"median_ms": round(ms, 5), "mean_ms": round(mean_ms, 5), "min_ms": round(step_ms[0], 5),
                        "max_ms": round(step_ms[-1], 5), "timed_region_ms": round(region_ms, 3),

@@ -30,6 +30,8 @@ _SIGS = {
     "idx_mxfp4_quantize": (ctypes.c_int, [c_void_p, c_int64, c_int32, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                           c_void_p]),
     "csa2_index_score_topk_workspace_size": (c_size_t, [c_int32, c_int32, c_int64, c_int32, c_int32, c_int32]),
+    "csa2_index_score_topk_workspace_size_stored": (c_size_t, [c_int32, c_int32, c_int64, c_int32, c_int32,
+                                                               c_int32]),
     "csa2_index_score_topk": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                              c_int32, c_int32, c_int32, c_int32, c_int64, c_int32, c_void_p,
                                              c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
@@ -204,9 +206,26 @@ def csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block=0, pool
     return lib().csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block, pool_nblocks)
 
 
+def csa2_index_score_topk_workspace_size_stored(B, Tq, n_max, k_top, pool_block=0, pool_nblocks=0):
+    return lib().csa2_index_score_topk_workspace_size_stored(B, Tq, n_max, k_top, pool_block, pool_nblocks)
+
+
+def _index_ws(B, Tq, n_max, k_top, pool_block, pool_nblocks, stored, dev, workspace):
+    """The indexer's workspace: a given one is used when it holds at least
+    the default size (its size then picks the prefill selection)."""
+    need = csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block, pool_nblocks)
+    if stored:
+        need = max(need, csa2_index_score_topk_workspace_size_stored(B, Tq, n_max, k_top, pool_block, pool_nblocks))
+    return _workspace(need, dev, workspace)
+
+
 def csa2_index_score_topk(q_idx, w, k_idx, ctx_len, k_top, q_pos=None, pool_block=0, pool_nblocks=0,
-                          want_scores=False, workspace=None, out=None):
+                          want_scores=False, workspace=None, out=None, stored_keys=False):
     """Indexer scores + exact Top-K (and optionally the hierarchical pool).
+
+    stored_keys: allocate csa2_index_score_topk_workspace_size_stored() bytes
+    (dense prefill chunks then store their score keys and select in one
+    scoring pass instead of selecting by scoring passes).
 
     q_idx [B][Tq][H_I][D_I] u8 (E4M3), w [B][Tq][H_I] f32, k_idx [B][N][D_I] u8
     (any batch/row strides), ctx_len [B] i32, q_pos [B][Tq] i32 or None.
@@ -242,8 +261,7 @@ def csa2_index_score_topk(q_idx, w, k_idx, ctx_len, k_top, q_pos=None, pool_bloc
         pool_len = out.get("pool_len")
         if pool_len is None:
             pool_len = torch.empty(B, Tq, dtype=torch.int32, device=dev)
-    need = csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block, pool_nblocks)
-    ws, ws_bytes = _workspace(need, dev, workspace)
+    ws, ws_bytes = _index_ws(B, Tq, n_max, k_top, pool_block, pool_nblocks, stored_keys, dev, workspace)
     _check(lib().csa2_index_score_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), kb, kr, _ptr(ctx_len), _ptr(q_pos), B, Tq,
                                        H_I, D_I, n_max, k_top, _ptr(topk_idx), _ptr(topk_score), pool_block,
                                        pool_nblocks, _ptr(pool_idx), _ptr(pool_len), _ptr(ws), ws_bytes,
@@ -260,7 +278,8 @@ def _mx_keys(k_codes, k_scales):
 
 
 def csa2_index_score_topk_mxfp4(q_idx, w, k_codes, k_scales, ctx_len, k_top, q_pos=None, pool_block=0,
-                                pool_nblocks=0, want_scores=False, workspace=None, out=None):
+                                pool_nblocks=0, want_scores=False, workspace=None, out=None,
+                                stored_keys=False):
     """csa2_index_score_topk over MXFP4 keys: k_codes [B][N][D_I/2] u8, k_scales [B][N][D_I/32] u8 (E8M0)."""
     _gpu(q_idx, "q_idx", torch.uint8)
     _gpu(w, "w", torch.float32)
@@ -288,8 +307,7 @@ def csa2_index_score_topk_mxfp4(q_idx, w, k_codes, k_scales, ctx_len, k_top, q_p
         pool_len = out.get("pool_len")
         if pool_len is None:
             pool_len = torch.empty(B, Tq, dtype=torch.int32, device=dev)
-    need = csa2_index_score_topk_workspace_size(B, Tq, n_max, k_top, pool_block, pool_nblocks)
-    ws, ws_bytes = _workspace(need, dev, workspace)
+    ws, ws_bytes = _index_ws(B, Tq, n_max, k_top, pool_block, pool_nblocks, stored_keys, dev, workspace)
     _check(lib().csa2_index_score_topk_mxfp4(_ptr(q_idx), _ptr(w), _ptr(k_codes), cb, cr, _ptr(k_scales), sb, sr,
                                              _ptr(ctx_len), _ptr(q_pos), B, Tq, H_I, D_I, n_max, k_top,
                                              _ptr(topk_idx), _ptr(topk_score), pool_block, pool_nblocks,

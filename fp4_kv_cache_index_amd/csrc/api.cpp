@@ -80,6 +80,27 @@ static ScoreLayout score_layout(int64_t B, int64_t Tq, int64_t n_max, int32_t po
   return L;
 }
 
+// Dense prefill chunks given less workspace than the stored score keys need
+// select without storing them (PfRow): the workspace then holds the visible
+// counts of every query row and the state of one block of at most
+// kPfRowsPerBlock rows, or, for chunk shapes that the matrix-core product
+// does not take (row-by-row scans), the keys of up to 15 rows at a time
+// (fewer on long contexts, within 48 MiB).
+static bool prefill_like(int64_t Tq, int32_t pool_block, int32_t k_top) {
+  return Tq >= 16 && pool_block <= 0 && k_top <= kPfMaxK;
+}
+static int prefill_scan_rows(int64_t Tq, int64_t n_max) {
+  int r = Tq < 15 ? (int)Tq : 15;
+  while (r > 1 && score_layout(1, r, n_max, 0).total > ((size_t)48 << 20)) --r;
+  return r;
+}
+static size_t prefill_ws_bytes(int64_t B, int64_t Tq, int64_t n_max) {
+  const int64_t rows = B * Tq;
+  const size_t pf = pf_ws_bytes(rows < kPfRowsPerBlock ? rows : kPfRowsPerBlock);
+  const size_t scan = score_layout(1, prefill_scan_rows(Tq, n_max), n_max, 0).total;
+  return al256(sizeof(int32_t) * rows) + (pf > scan ? pf : scan);
+}
+
 static bool pool_block_ok(int32_t pb) { return pb == 1 || pb == 2 || pb == 4 || pb == 8 || pb == 16; }
 static bool d_idx_ok(int32_t D_I) { return D_I == 32 || D_I == 64 || D_I == 128 || D_I == 256; }
 
@@ -198,17 +219,90 @@ int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_
   return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }
 
-size_t csa2_index_score_topk_workspace_size(int32_t B, int32_t Tq, int64_t n_max, int32_t k_top,
-                                            int32_t pool_block, int32_t pool_nblocks) {
-  (void)k_top;
+size_t csa2_index_score_topk_workspace_size_stored(int32_t B, int32_t Tq, int64_t n_max, int32_t k_top,
+                                                   int32_t pool_block, int32_t pool_nblocks) {
   (void)pool_nblocks;
+  (void)k_top;
   if (B < 0 || Tq < 0 || n_max < 0) return 0;
   return score_layout(B, Tq, n_max, pool_block > 0 ? pool_block : 0).total;
+}
+
+size_t csa2_index_score_topk_workspace_size(int32_t B, int32_t Tq, int64_t n_max, int32_t k_top,
+                                            int32_t pool_block, int32_t pool_nblocks) {
+  if (B < 0 || Tq < 0 || n_max < 0) return 0;
+  const size_t stored = csa2_index_score_topk_workspace_size_stored(B, Tq, n_max, k_top, pool_block, pool_nblocks);
+  if (prefill_like(Tq, pool_block, k_top)) {
+    const size_t bounded = prefill_ws_bytes(B, Tq, n_max);
+    return bounded < stored ? bounded : stored;
+  }
+  return stored;
 }
 
 }  // extern "C"
 
 namespace csa2 {
+
+static int score_topk_impl(ScoreArgs a, int32_t* topk_idx, float* topk_score, int32_t* pool_idx, int32_t* pool_len,
+                           void* ws, size_t ws_bytes, hipStream_t s);
+
+// A dense prefill chunk (Tq >= 16 query rows per sequence, no pool): blocks
+// of query tiles, each selected by kPfPasses scoring passes with a step
+// after each and a final sort (no score keys stored).  Chunk shapes that the
+// matrix-core product does not take are scanned prefill_scan_rows() query
+// rows at a time.
+static int prefill_impl(const ScoreArgs& a, int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                        hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.Tq;
+  if (ws_bytes < prefill_ws_bytes(a.B, a.Tq, a.n_max)) return CSA2_EWORKSPACE;
+  char* base = (char*)ws;
+  int32_t* n_valid = (int32_t*)base;
+  char* rest = base + al256(sizeof(int32_t) * rows);
+  if (!prefill_gemm_applies(a)) {
+    const int SR = prefill_scan_rows(a.Tq, a.n_max);
+    for (int64_t b = 0; b < a.B; ++b)
+      for (int64_t t = 0; t < a.Tq; t += SR) {
+        const int R = (int)(a.Tq - t < SR ? a.Tq - t : SR);
+        const int64_t r0 = b * a.Tq + t;
+        ScoreArgs c = a;
+        c.B = 1;
+        c.Tq = R;
+        c.q_idx = a.q_idx + r0 * (int64_t)a.H_I * a.D_I;
+        c.w = a.w + r0 * a.H_I;
+        c.q_pos = a.q_pos ? a.q_pos + r0 : nullptr;
+        c.k_idx = a.k_idx + b * a.k_bstride;
+        c.k_scales = a.k_scales ? a.k_scales + b * a.ks_bstride : nullptr;
+        c.ctx_len = a.ctx_len + b;
+        const int st = score_topk_impl(c, topk_idx + r0 * a.k_top, topk_score ? topk_score + r0 * a.k_top : nullptr,
+                                       nullptr, nullptr, rest, ws_bytes - (size_t)(rest - base), s);
+        if (st != CSA2_OK) return st;
+      }
+    return CSA2_OK;
+  }
+  const int QW = prefill_rows_per_tile(a);
+  const int64_t qtiles = (a.Tq + QW - 1) / QW;
+  const int64_t ytot = (int64_t)a.B * qtiles;
+  // blocks of equal numbers of query tiles, each within kPfRowsPerBlock rows
+  const int64_t max_tiles = kPfRowsPerBlock / QW, nblk = (ytot + max_tiles - 1) / max_tiles;
+  const int64_t per_block = (ytot + nblk - 1) / nblk;
+  auto row_of = [&](int64_t y) { return y >= ytot ? rows : (y / qtiles) * a.Tq + (y % qtiles) * QW; };
+  for (int64_t y0 = 0; y0 < ytot; y0 += per_block) {
+    const int64_t ny = ytot - y0 < per_block ? ytot - y0 : per_block;
+    PfArgs pf = pf_ws_carve(rest, kPfRowsPerBlock < rows ? kPfRowsPerBlock : rows);
+    pf.row_base = row_of(y0);
+    const int64_t nrows = row_of(y0 + ny) - pf.row_base;
+    pf.out_idx = topk_idx;
+    pf.out_key = reinterpret_cast<uint32_t*>(topk_score);
+    pf.k_top = a.k_top;
+    hipError_t e = pf_clear(pf, nrows, s);
+    for (int p = 0; p < kPfPasses && e == hipSuccess; ++p) {
+      e = launch_prefill_pass(a, pf, p, y0, ny, n_valid, s);
+      if (e == hipSuccess) e = pf_step(pf, nrows, s);
+    }
+    if (e == hipSuccess) e = pf_final(pf, nrows, topk_score, s);
+    if (e != hipSuccess) return CSA2_EHIP;
+  }
+  return CSA2_OK;
+}
 
 // Scoring + Top-K (+ pool) for E4M3 keys (a.k_scales == null) or MXFP4 keys.
 static int score_topk_impl(ScoreArgs a, int32_t* topk_idx, float* topk_score, int32_t* pool_idx, int32_t* pool_len,
@@ -248,6 +342,10 @@ static int score_topk_impl(ScoreArgs a, int32_t* topk_idx, float* topk_score, in
   }
   if (n_max > (int64_t)kSelTile * kMaxSelTiles || (int64_t)B * Tq > 65535) return CSA2_EUNSUPPORTED;
   ScoreLayout L = score_layout(B, Tq, n_max, pool ? a.pool_block : 0);
+  // A prefill chunk with less workspace than its stored score keys take
+  // selects by repeated scoring passes.
+  if (!pool && prefill_like(Tq, 0, k_top) && ws_bytes < L.total)
+    return prefill_impl(a, topk_idx, topk_score, ws, ws_bytes, s);
   if (ws_bytes < L.total) return CSA2_EWORKSPACE;
   char* base = (char*)ws;
   uint32_t* keys = (uint32_t*)(base + L.off_keys);

@@ -119,6 +119,59 @@ hipError_t select_local(const uint32_t* keys, int64_t key_stride, const int32_t*
 hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_stride, const int32_t* n_valid,
                          int64_t rows, int k, const SelectOut& out, hipStream_t s);
 
+// ------------------------------------------------ prefill chunk selection ---
+// A dense prefill chunk (many query rows of one sequence against the same
+// keys) selects without storing its [rows][n] score keys: the scoring
+// product runs again in up to five passes over the chunk's keys, each query
+// row steered by a PfRow.  A pass emits the keys that are selected for
+// certain (above the threshold bucket found so far: their positions go
+// straight to the row's output, unordered) and either histograms the next
+// radix digit (12, 12, then 8 bits) of the keys still undecided, appends
+// them as candidates (when at most kPfCap of them remain), or, once the
+// threshold key itself is known and ties at it outnumber kPfCap, counts the
+// ties per key tile and then emits the lowest-position ones.  A step kernel
+// after each pass resolves the digit and picks the next mode; a last kernel
+// sorts each row's positions.
+constexpr int kPfCap = 4096;            // candidates kept per row
+constexpr int kPfMaxK = 8192;           // largest k_top of this path (LDS sort)
+constexpr int kPfRowsPerBlock = 1920;   // query rows per block of passes (workspace bound)
+constexpr int kPfPasses = 5;            // digit levels 12 + 12 + 8, tie count, tie emission
+
+enum PfMode : uint32_t { PF_DONE = 0, PF_HIST = 1, PF_CAND = 2, PF_EMIT = 3, PF_TIECOUNT = 4, PF_TIEEMIT = 5 };
+
+struct PfRow {                          // 64 bytes per query row
+  uint32_t mode;
+  // Keys selected for certain in the next pass: e_on, key in the previous
+  // bucket (e_ps >= 32: every key; else key >> e_ps == e_pfx) and above the
+  // current bucket (key >> n_ps > n_pfx), or inside it when e_incl.
+  uint32_t e_on, e_ps, e_pfx, e_incl;
+  // The undecided bucket: keys with key >> n_ps == n_pfx (n_ps >= 32: all).
+  uint32_t n_ps, n_pfx;
+  uint32_t need;                        // keys still to take from the bucket
+  uint32_t bcnt;                        // keys in the bucket
+  uint32_t out_cnt;                     // positions emitted so far (atomic)
+  uint32_t cand_cnt;                    // candidates appended (atomic)
+  uint32_t pad[5];
+};
+
+struct PfArgs {
+  PfRow* rows;                          // [block rows]
+  uint32_t* hist;                       // [block rows][4096]: digit histogram, or ties per key tile
+  uint64_t* cand;                       // [block rows][kPfCap]: (key << 32) | ~position
+  int32_t* out_idx;                     // the caller's topk_idx [rows][k_top]
+  uint32_t* out_key;                    // nullable: the caller's topk_score [rows][k_top] (key bits until the end)
+  int64_t row_base;                     // first (global) query row of the block
+  int k_top;
+};
+size_t pf_ws_bytes(int64_t block_rows);
+PfArgs pf_ws_carve(void* base, int64_t block_rows);
+// Initial state of every row of the block (level-1 histogram, zeroed counts).
+hipError_t pf_clear(const PfArgs& pf, int64_t block_rows, hipStream_t s);
+// After a pass: resolve a digit / select candidates / prefix the tie counts.
+hipError_t pf_step(const PfArgs& pf, int64_t block_rows, hipStream_t s);
+// Sort each row's positions ascending, pad with -1 (scores: -inf).
+hipError_t pf_final(const PfArgs& pf, int64_t block_rows, float* topk_score, hipStream_t s);
+
 // ------------------------------------------------------------- scoring ---
 struct ScoreArgs {
   const uint8_t* q_idx; const float* w;
@@ -138,6 +191,14 @@ hipError_t launch_index_score(const ScoreArgs& a, uint32_t* keys, int64_t key_st
 // of it for any device.
 int64_t index_score_tiles(const ScoreArgs& a);
 int64_t index_score_tiles_bound(int64_t n_max);
+// Dense prefill chunks: whether the matrix-core product scores this call,
+// its query rows per workgroup (blocks of passes align with them), and one
+// selection pass over the query tiles [y0, y0 + ny) (flattened (sequence,
+// tile) index) steered by pf.
+bool prefill_gemm_applies(const ScoreArgs& a);
+int prefill_rows_per_tile(const ScoreArgs& a);
+hipError_t launch_prefill_pass(const ScoreArgs& a, const PfArgs& pf, int pass, int64_t y0, int64_t ny,
+                               int32_t* n_valid, hipStream_t s);
 // Pool layers: a.q_idx / a.w / keys / ctx_len / B / Tq / H_I / D_I / k_top
 // (and the MXFP4 scales) as in ScoreArgs.
 hipError_t launch_pool_score(const ScoreArgs& a, const int32_t* pool_idx, const int32_t* pool_len, int pool_cap,

@@ -17,6 +17,8 @@
 // roundings and no FMA.  The epilogue also builds the radix-select
 // histogram of the top 12 key bits in LDS, writes the score keys, and (for
 // the hierarchical pool) the per-block maxima and their histogram.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "select_dev.h"
@@ -740,6 +742,264 @@ static hipError_t launch_pool_t(const ScoreArgs& a, const int32_t* pool_idx, con
 // in LDS, two queries per 32-bit word (counts stay below 2^16 per tile).
 constexpr int kPrefillWaves = 8;
 
+// Per-row state of a prefill selection pass (see PfRow), in registers: the
+// keys emitted now form the range [e_lo, e_hi] (empty: e_lo > e_hi), the
+// undecided bucket [b_lo, b_hi] (empty when the pass takes it whole).
+struct PfLane {
+  uint32_t mode, n_ps, n_pfx, e_lo, e_hi, b_lo, b_hi;
+  // Scores whose keys may lie in either range: [f_lo, f_hi] (a superset in
+  // float order, so that the key need not be formed for every score).
+  float f_lo, f_hi;
+};
+__device__ __forceinline__ PfLane pf_load(const PfArgs& pf, int64_t grow, bool ok) {
+  PfLane L{PF_DONE, 32u, 0u, 1u, 0u, 1u, 0u, __builtin_inff(), -__builtin_inff()};   // (empty ranges)
+  if (ok && pf.rows[grow - pf.row_base].mode != PF_DONE) {
+    const PfRow& r = pf.rows[grow - pf.row_base];
+    L.mode = r.mode;
+    L.n_ps = r.n_ps;
+    L.n_pfx = r.n_pfx;
+    // bucket: keys with key >> n_ps == n_pfx
+    const uint64_t blo = r.n_ps >= 32u ? 0ull : (uint64_t)r.n_pfx << r.n_ps;
+    const uint64_t bhi = r.n_ps >= 32u ? 0xFFFFFFFFull : blo + (1ull << r.n_ps) - 1ull;
+    if (!r.e_incl) {
+      L.b_lo = (uint32_t)blo;
+      L.b_hi = (uint32_t)bhi;
+    }
+    if (r.e_on && r.n_ps < 32u) {
+      // above the bucket (or from its start when it is taken whole), inside
+      // the previous bucket
+      const uint64_t plo = r.e_incl ? blo : bhi + 1ull;
+      const uint64_t phi = r.e_ps >= 32u ? 0xFFFFFFFFull : ((uint64_t)r.e_pfx << r.e_ps) + (1ull << r.e_ps) - 1ull;
+      if (plo <= phi) {
+        L.e_lo = (uint32_t)plo;
+        L.e_hi = (uint32_t)phi;
+      }
+    }
+    // the two ranges are adjacent: their union's bounds as scores (keys at
+    // or below that of -inf, or at or above that of +inf, bound nothing)
+    const uint32_t ulo = L.b_lo <= L.b_hi ? L.b_lo : L.e_lo;
+    const uint32_t uhi = L.e_lo <= L.e_hi ? L.e_hi : L.b_hi;
+    if (ulo <= uhi) {
+      L.f_lo = ulo <= 0x007FFFFFu ? -__builtin_inff() : key_score(ulo);
+      L.f_hi = uhi >= 0xFF800000u ? __builtin_inff() : key_score(uhi);
+    }
+  }
+  return L;
+}
+// 1: selected for certain (emit now); 2: in the undecided bucket; 0: neither.
+__device__ __forceinline__ int pf_class(const PfLane& L, uint32_t k) {
+  return (k >= L.e_lo && k <= L.e_hi) ? 1 : ((k >= L.b_lo && k <= L.b_hi) ? 2 : 0);
+}
+// The next radix digit of a key inside the bucket of n_ps: bits 31..20,
+// 19..8, then 7..0.
+__device__ __forceinline__ uint32_t pf_digit(uint32_t k, uint32_t n_ps) {
+  return n_ps >= 32u ? k >> 20 : (n_ps == 20u ? (k >> 8) & 0xFFFu : k & 0xFFu);
+}
+__device__ __forceinline__ void pf_emit(const PfArgs& pf, int64_t grow, int64_t j, uint32_t k) {
+  const uint32_t slot = atomicAdd(&pf.rows[grow - pf.row_base].out_cnt, 1u);
+  if (slot < (uint32_t)pf.k_top) {   // (never false: the counts are exact)
+    pf.out_idx[grow * pf.k_top + slot] = (int32_t)j;
+    if (pf.out_key) pf.out_key[grow * pf.k_top + slot] = k;
+  }
+}
+__device__ __forceinline__ void pf_cand(const PfArgs& pf, int64_t grow, int64_t j, uint32_t k) {
+  const int64_t lrow = grow - pf.row_base;
+  const uint32_t slot = atomicAdd(&pf.rows[lrow].cand_cnt, 1u);
+  if (slot < (uint32_t)kPfCap) pf.cand[lrow * kPfCap + slot] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+// Selection passes (PFM 2) stage emitted positions and candidates of a
+// workgroup in LDS (in the histogram's space, when no row of the tile
+// histograms) and reserve their slots with one global atomic per row and
+// kind at the end: a global atomic per key kept its wave waiting for the
+// returned slot.  kPfStage entries of (position, key) per row and kind;
+// beyond them a key takes its slot directly.
+constexpr int kPfStage = 512;
+template <int QW>
+__device__ __forceinline__ void pf_stage(const PfArgs& pf, uint32_t* stg, uint32_t* scnt, int kind, int ql,
+                                         int64_t grow, int64_t j, uint32_t k) {
+  const uint32_t sl = atomicAdd(&scnt[kind * QW + ql], 1u);
+  if (sl < (uint32_t)kPfStage) {
+    uint32_t* e = stg + ((ql * 2 + kind) * kPfStage + sl) * 2;
+    e[0] = (uint32_t)j;
+    e[1] = k;
+  } else if (kind == 0) {
+    pf_emit(pf, grow, j, k);
+  } else {
+    pf_cand(pf, grow, j, k);
+  }
+}
+// The transposed product's passes stage per lane instead (no atomics on the
+// key loop): entry i of kind `kind` of workgroup thread tl sits at word
+// ((kind * kPfLane + i) * threads + tl) * 2, its counts stay in registers,
+// and the end of the workgroup reserves one global range per row and kind.
+constexpr int kPfLane = 8;
+// Beyond a lane's kPfLane entries: a shared pool of kPfPool entries
+// (position, key, kind << 4 | row) in LDS; beyond the pool the workgroup
+// sets `spill` and scores its tile again with direct global slots.  Nothing
+// in the key loop then touches global memory (a global atomic there made
+// the compiler drain the key loads in flight).
+constexpr int kPfPool = 4096;
+__device__ __forceinline__ void pf_lane_put2(uint32_t* stg, uint32_t* pool, uint32_t* pool_cnt, uint32_t* spill,
+                                             int kind, int ql, uint32_t& cnt, int64_t j, uint32_t k) {
+  if (cnt < (uint32_t)kPfLane) {
+    // consecutive lanes at consecutive entries (no bank conflicts)
+    uint32_t* e = stg + ((kind * kPfLane + cnt) * (64 * kPrefillWaves) + threadIdx.x) * 2;
+    e[0] = (uint32_t)j;
+    e[1] = k;
+  } else {
+    const uint32_t ps = atomicAdd(pool_cnt, 1u);
+    if (ps < (uint32_t)kPfPool) {
+      pool[3 * ps] = (uint32_t)j;
+      pool[3 * ps + 1] = k;
+      pool[3 * ps + 2] = ((uint32_t)kind << 4) | (uint32_t)ql;
+    } else {
+      *spill = 1u;
+    }
+  }
+  ++cnt;
+}
+// stg: 2*kPfLane*NWV*64*2 words, then 2*NWV*64 count words and 2*NWV*64
+// offset words.  Lane (c16, g) of every wave holds row ql = c16.
+template <int QW, int NWV>
+__device__ void pf_lane_flush(const PfArgs& pf, uint32_t* stg, uint32_t ne, uint32_t nc, uint32_t* sbase,
+                              int64_t row0, int Tq, int t0) {
+  constexpr int NL = NWV * 64;
+  uint32_t* cnts = stg + NL * 2 * kPfLane * 2;   // [kind][lane of the workgroup]
+  uint32_t* offs = cnts + 2 * NL;
+  const int tl = threadIdx.x;
+  cnts[tl] = ne < (uint32_t)kPfLane ? ne : (uint32_t)kPfLane;
+  cnts[NL + tl] = nc < (uint32_t)kPfLane ? nc : (uint32_t)kPfLane;
+  __syncthreads();
+  if (tl < 2 * QW) {
+    const int kind = tl / QW, ql = tl % QW;
+    uint32_t run = 0;
+    for (int wv = 0; wv < NWV; ++wv)
+      for (int gg = 0; gg < 4; ++gg) {
+        const int l = wv * 64 + gg * 16 + ql;
+        offs[kind * NL + l] = run;
+        run += cnts[kind * NL + l];
+      }
+    uint32_t base = 0;
+    if (run && t0 + ql < Tq) {
+      PfRow& r = pf.rows[row0 + ql - pf.row_base];
+      base = atomicAdd(kind ? &r.cand_cnt : &r.out_cnt, run);
+    }
+    sbase[kind * QW + ql] = base;
+  }
+  __syncthreads();
+  const int ql = tl & 15;
+  if (t0 + ql >= Tq) return;
+  const int64_t grow = row0 + ql;
+#pragma unroll
+  for (int kind = 0; kind < 2; ++kind) {
+    const uint32_t n = cnts[kind * NL + tl];
+    const uint32_t b0 = sbase[kind * QW + ql] + offs[kind * NL + tl];
+    for (uint32_t i = 0; i < n; ++i) {
+      const uint32_t* v = stg + ((kind * kPfLane + i) * NL + tl) * 2;
+      const uint32_t slot = b0 + i;
+      if (kind == 0) {
+        if (slot < (uint32_t)pf.k_top) {
+          pf.out_idx[grow * pf.k_top + slot] = (int32_t)v[0];
+          if (pf.out_key) pf.out_key[grow * pf.k_top + slot] = v[1];
+        }
+      } else if (slot < (uint32_t)kPfCap) {
+        pf.cand[(grow - pf.row_base) * kPfCap + slot] = ((uint64_t)v[1] << 32) | (uint64_t)(0xFFFFFFFFu - v[0]);
+      }
+    }
+  }
+}
+
+template <int QW, int NT>
+__device__ void pf_unstage(const PfArgs& pf, const uint32_t* stg, const uint32_t* scnt, uint32_t* sbase, int64_t row0,
+                           int Tq, int t0) {
+  if (threadIdx.x < 2 * QW) {
+    const int kind = threadIdx.x / QW, ql = threadIdx.x % QW;
+    uint32_t n = scnt[kind * QW + ql];
+    n = n < (uint32_t)kPfStage ? n : (uint32_t)kPfStage;
+    uint32_t base = 0;
+    if (n && t0 + ql < Tq) {
+      PfRow& r = pf.rows[row0 + ql - pf.row_base];
+      base = atomicAdd(kind ? &r.cand_cnt : &r.out_cnt, n);
+    }
+    sbase[kind * QW + ql] = base;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * QW * kPfStage; i += NT) {
+    const int kind = i / (QW * kPfStage), rem = i % (QW * kPfStage), ql = rem / kPfStage, e = rem % kPfStage;
+    uint32_t n = scnt[kind * QW + ql];
+    n = n < (uint32_t)kPfStage ? n : (uint32_t)kPfStage;
+    if ((uint32_t)e >= n || t0 + ql >= Tq) continue;
+    const uint32_t* v = stg + ((ql * 2 + kind) * kPfStage + e) * 2;
+    const uint32_t slot = sbase[kind * QW + ql] + e;
+    const int64_t grow = row0 + ql;
+    if (kind == 0) {
+      if (slot < (uint32_t)pf.k_top) {
+        pf.out_idx[grow * pf.k_top + slot] = (int32_t)v[0];
+        if (pf.out_key) pf.out_key[grow * pf.k_top + slot] = v[1];
+      }
+    } else if (slot < (uint32_t)kPfCap) {
+      pf.cand[(grow - pf.row_base) * kPfCap + slot] = ((uint64_t)v[1] << 32) | (uint64_t)(0xFFFFFFFFu - v[0]);
+    }
+  }
+}
+// Level-1 histogram pass (PFM 1: every row of the block histograms the top
+// 12 bits of its visible keys): the tile's LDS histogram into the rows'.
+template <int QW, int NT>
+__device__ void pf_flush_hist(const PfArgs& pf, const uint32_t* hist, int64_t row0, int Tq, int t0) {
+  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
+    const uint32_t v = hist[i];
+    if (!v) continue;
+    const int p = i >> 12, bin = i & 4095;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int ql = 2 * p + hf;
+      const uint32_t c = hf ? v >> 16 : v & 0xFFFFu;
+      if (c && t0 + ql < Tq) atomic_add_agent(pf.hist + (row0 + ql - pf.row_base) * 4096 + bin, c);
+    }
+  }
+}
+
+// End of a pass workgroup: histogram counts and tie counts to global memory,
+// tie emission in position order.  hist holds (QW/2) x 4096 words (two
+// queries per word) or, for tie emission, nchunks x QW masks of 16 bits.
+template <int QW, int NT>
+__device__ void pf_finish(const PfArgs& pf, const PfLane* pfl, uint32_t flags, const uint32_t* hist,
+                          const uint32_t* tcnt, int64_t row0, int Tq, int t0, int64_t k0, int nchunks) {
+  if (flags & (1u << PF_HIST)) {
+    for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
+      const uint32_t v = hist[i];
+      if (!v) continue;
+      const int p = i >> 12, bin = i & 4095;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int ql = 2 * p + hf;
+        const uint32_t c = hf ? v >> 16 : v & 0xFFFFu;
+        if (c && pfl[ql].mode == PF_HIST) atomic_add_agent(pf.hist + (row0 + ql - pf.row_base) * 4096 + bin, c);
+      }
+    }
+  }
+  if (threadIdx.x < QW && t0 + (int)threadIdx.x < Tq) {
+    const int ql = threadIdx.x;
+    const int64_t lrow = row0 + ql - pf.row_base;
+    if (pfl[ql].mode == PF_TIECOUNT && tcnt[ql]) atomic_add_agent(pf.hist + lrow * 4096 + blockIdx.x, tcnt[ql]);
+    if (pfl[ql].mode == PF_TIEEMIT) {
+      // ties of earlier key tiles (exclusive prefix by the step kernel)
+      const uint32_t base = pf.hist[lrow * 4096 + blockIdx.x];
+      const uint32_t need = pf.rows[lrow].need;
+      uint32_t cnt = 0;
+      for (int c = 0; c < nchunks && base + cnt < need; ++c) {
+        uint32_t m = hist[c * QW + ql];
+        while (m && base + cnt < need) {
+          const int bit = __builtin_ctz(m);
+          m &= m - 1u;
+          pf_emit(pf, row0 + ql, k0 + 16 * (int64_t)c + bit, pfl[ql].n_pfx);   // (the tie key T)
+          ++cnt;
+        }
+      }
+    }
+  }
+}
+
 template <int DI>
 __device__ __forceinline__ void load_k128(uint32_t (&f)[DI / 16], const uint8_t* row, int g, bool ok) {
   if (!ok) {
@@ -758,27 +1018,32 @@ __device__ __forceinline__ void load_k128(uint32_t (&f)[DI / 16], const uint8_t*
   }
 }
 
-template <int DI, int HG, int QG>
+template <int DI, int HG, int QG, int PFM>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
                      const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
                      int Tq, int H_I, int64_t n_max, int key_tile, int qtiles,
                      uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
-                     SelectWs tok) {
+                     SelectWs tok, PfArgs pf, int64_t y0) {
   constexpr int KS = DI / 128;          // MFMA k-steps
   constexpr int FW = DI / 16;           // fragment words per lane
   constexpr int QW = 4 * QG;            // queries per workgroup
   constexpr int HP = 4 * HG;            // heads incl. padding
   constexpr int NT = 64 * kPrefillWaves;
   typedef int v8i __attribute__((ext_vector_type(8)));
+  constexpr bool PF = PFM == 2;
   __shared__ uint32_t hist[(QW / 2) * 4096];
   __shared__ int32_t nvs[QW];
+  __shared__ PfLane pfl[PF ? QW : 1];
+  __shared__ uint32_t tcnt[PF ? QW : 1];
+  __shared__ uint32_t scnt[PF ? 2 * QW : 1], sbase[PF ? 2 * QW : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int64_t b = blockIdx.y / qtiles;
-  const int t0 = (int)(blockIdx.y % qtiles) * QW;
+  const int64_t yy = (int64_t)blockIdx.y + y0;
+  const int64_t b = yy / qtiles;
+  const int t0 = (int)(yy % qtiles) * QW;
   const int64_t row0 = b * Tq + t0;
 
   if (threadIdx.x < QW) {
@@ -794,8 +1059,26 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
       if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
     }
     nvs[threadIdx.x] = (int32_t)nv;
+    if constexpr (PF) {
+      pfl[threadIdx.x] = pf_load(pf, row0 + threadIdx.x, t < Tq);
+      tcnt[threadIdx.x] = 0u;
+      scnt[threadIdx.x] = 0u;
+      scnt[QW + threadIdx.x] = 0u;
+    }
   }
-  for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  uint32_t flags = 0;   // PF: bit m set when some row of the tile is in mode m
+  bool stage = false;   // PF: emitted keys and candidates staged in LDS
+  if constexpr (PF) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < QW; ++i) flags |= 1u << pfl[i].mode;
+    if (!(flags & ~1u)) return;   // uniform: every row done
+    stage = !(flags & ((1u << PF_HIST) | (1u << PF_TIEEMIT)));
+    if (!stage)
+      for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  } else {
+    for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  }
   __syncthreads();
   int max_nv = 0;
 #pragma unroll
@@ -830,7 +1113,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
 #pragma unroll
     for (int h = 0; h < HP; ++h) wv[qg][h] = (t < Tq && h < H_I) ? w[(b * Tq + t) * H_I + h] : 0.0f;
     nvq[qg] = nvs[ql];
-    krow[qg] = keys + (row0 + ql) * key_stride;
+    krow[qg] = PFM ? nullptr : keys + (row0 + ql) * key_stride;
   }
 
   const uint8_t* kb = k_idx + b * k_bstride;
@@ -869,9 +1152,29 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
         }
       if (j < nvq[qg]) {
         const uint32_t key = score_key(sc);
-        __builtin_nontemporal_store(key, krow[qg] + j);
         const int ql = 4 * qg + g;
-        atomicAdd(&hist[(ql >> 1) * 4096 + (key >> 20)], 1u << (16 * (ql & 1)));
+        if constexpr (PF) {
+          const PfLane pl = pfl[ql];
+          {
+            const int cls = pf_class(pl, key);
+            if (cls == 1) {
+              if (stage) pf_stage<QW>(pf, hist, scnt, 0, ql, row0 + ql, j, key);
+              else pf_emit(pf, row0 + ql, j, key);
+            } else if (cls == 2) {
+              if (pl.mode == PF_HIST) atomicAdd(&hist[(ql >> 1) * 4096 + pf_digit(key, pl.n_ps)], 1u << (16 * (ql & 1)));
+              else if (pl.mode == PF_CAND) {
+                if (stage) pf_stage<QW>(pf, hist, scnt, 1, ql, row0 + ql, j, key);
+                else pf_cand(pf, row0 + ql, j, key);
+              } else if (pl.mode == PF_TIECOUNT) atomicAdd(&tcnt[ql], 1u);
+              else if (pl.mode == PF_TIEEMIT) atomicOr(&hist[c * QW + ql], 1u << c16);
+            }
+          }
+        } else if constexpr (PFM == 1) {
+          atomicAdd(&hist[(ql >> 1) * 4096 + (key >> 20)], 1u << (16 * (ql & 1)));
+        } else {
+          __builtin_nontemporal_store(key, krow[qg] + j);
+          atomicAdd(&hist[(ql >> 1) * 4096 + (key >> 20)], 1u << (16 * (ql & 1)));
+        }
       }
     }
   };
@@ -885,6 +1188,17 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
     if (cb < nchunks) score_chunk(fb, cb);
   }
   __syncthreads();
+  if constexpr (PF) {
+    // (staging excludes histogram and tie-emission rows; tie counts are
+    // flushed either way)
+    if (stage) pf_unstage<QW, NT>(pf, hist, scnt, sbase, row0, Tq, t0);
+    pf_finish<QW, NT>(pf, pfl, flags, hist, tcnt, row0, Tq, t0, k0, nchunks);
+    return;
+  }
+  if constexpr (PFM == 1) {
+    pf_flush_hist<QW, NT>(pf, hist, row0, Tq, t0);
+    return;
+  }
   if (!tok.hist1) return;
   for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
     const uint32_t v = hist[i];
@@ -903,7 +1217,10 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
 // leave in a single 16-byte store.  F4: MXFP4 keys (E2M1 codes + E8M0 per 32
 // channels) as the A operand: lane (c16, g) holds bytes 16g .. 16g+15 of key
 // c16's code row (channels 32g .. 32g+31) and passes that block's scale byte.
-template <int PD, bool F4>
+// PFM: 0 = score keys stored for the radix select; 1 = the level-1
+// histogram pass of the prefill selection (no keys stored); 2 = a later
+// selection pass steered by each row's PfRow; query tiles y0 + blockIdx.y.
+template <int PD, bool F4, int PFM>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                         const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
@@ -911,16 +1228,25 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
                         const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
                         int Tq, int H_I, int64_t n_max, int key_tile, int qtiles,
                         uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
-                        SelectWs tok) {
+                        SelectWs tok, PfArgs pf, int64_t y0) {
   constexpr int DI = 128, FW = 8, QW = 16, HP = 8;
   constexpr int NT = 64 * kPrefillWaves;
+  constexpr bool PF = PFM == 2;
   __shared__ uint32_t hist[(QW / 2) * 4096 + 1];   // last word: bin of invisible keys
   __shared__ int32_t nvs[QW];
+  __shared__ PfLane pfl[PF ? QW : 1];
+  __shared__ uint32_t tcnt[PF ? QW : 1];
+  __shared__ uint32_t scnt[PF ? 2 * QW : 1], sbase[PF ? 2 * QW : 1];
+  __shared__ uint32_t pool_cnt, spill;
+  // staged entries of the selection passes: per lane, then the pool
+  constexpr int kPoolOff = kPrefillWaves * 64 * 2 * kPfLane * 2 + 4 * kPrefillWaves * 64;
+  static_assert(kPoolOff + 3 * kPfPool <= (QW / 2) * 4096, "staging fits the histogram space");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int64_t b = blockIdx.y / qtiles;
-  const int t0 = (int)(blockIdx.y % qtiles) * QW;
+  const int64_t yy = (int64_t)blockIdx.y + y0;
+  const int64_t b = yy / qtiles;
+  const int t0 = (int)(yy % qtiles) * QW;
   const int64_t row0 = b * Tq + t0;
 
   if (threadIdx.x < QW) {
@@ -936,8 +1262,30 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
     }
     nvs[threadIdx.x] = (int32_t)nv;
+    if constexpr (PF) {
+      pfl[threadIdx.x] = pf_load(pf, row0 + threadIdx.x, t < Tq);
+      tcnt[threadIdx.x] = 0u;
+      scnt[threadIdx.x] = 0u;
+      scnt[QW + threadIdx.x] = 0u;
+      if (threadIdx.x == 0) {
+        pool_cnt = 0u;
+        spill = 0u;
+      }
+    }
   }
-  for (int i = threadIdx.x; i <= (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  uint32_t flags = 0;   // PF: bit m set when some row of the tile is in mode m
+  bool stage = false;   // PF: emitted keys and candidates staged in LDS
+  if constexpr (PF) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < QW; ++i) flags |= 1u << pfl[i].mode;
+    if (!(flags & ~1u)) return;   // uniform: every row done
+    stage = !(flags & ((1u << PF_HIST) | (1u << PF_TIEEMIT)));
+    if (!stage)
+      for (int i = threadIdx.x; i <= (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  } else {
+    for (int i = threadIdx.x; i <= (QW / 2) * 4096; i += NT) hist[i] = 0u;
+  }
   __syncthreads();
   int max_nv = 0;
 #pragma unroll
@@ -946,6 +1294,9 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   int64_t k1 = k0 + key_tile;
   if (k1 > max_nv) k1 = max_nv;
   if (k0 >= k1) return;   // uniform: nothing visible in this tile
+  PfLane pl{};
+  if constexpr (PF) pl = pfl[c16];
+  uint32_t lane_ne = 0u, lane_nc = 0u;   // PF: entries this lane staged (emits, candidates)
 
   // B fragments: column c16 = query t0 + c16, one per head.
   const int t = t0 + c16;
@@ -960,7 +1311,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     wv[h] = (tok_q && h < H_I) ? w[(b * Tq + t) * H_I + h] : 0.0f;
   }
   const int32_t nvq = nvs[c16];
-  uint32_t* krow = keys + (row0 + c16) * key_stride;
+  uint32_t* krow = PFM ? nullptr : keys + (row0 + c16) * key_stride;
   const uint32_t hbase = (uint32_t)(c16 >> 1) * 4096u, add = 1u << (16 * (c16 & 1));
   constexpr uint32_t kTrash = (QW / 2) * 4096;
 
@@ -985,7 +1336,10 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
     }
   };
-  auto score_chunk = [&](const uint32_t (&f)[FW], int c) {
+  // ST (PF): selected keys and candidates staged in LDS, as a compile-time
+  // choice, so that the staged loop holds no global memory operation.
+  auto score_chunk = [&](auto st_tag, const uint32_t (&f)[FW], int c) {
+    constexpr bool ST = decltype(st_tag)::value;
     v4f acc[HP];
     if constexpr (F4) {
       const v8i ka = v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], 0, 0, 0, 0};
@@ -1004,6 +1358,8 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     // acc[h][r] = dot(key j0 + r, query c16, head h)
     const int j0 = ik0 + 16 * c + 4 * g;
     uint32_t kk[4];
+    uint32_t em = 0u, bm = 0u;   // PF: keys to emit / in the undecided bucket
+    uint32_t pm = 0u;            // PF: keys passing the score prefilter
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float sc = 0.0f;
@@ -1019,26 +1375,110 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       const uint32_t u = __float_as_uint(sc);
       const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
       const bool vis = j0 + r < nvq;
-      kk[r] = vis ? key : 0u;
-      atomicAdd(&hist[vis ? hbase + (key >> 20) : kTrash], add);
+      if constexpr (PF) {
+        kk[r] = key;
+        pm |= (vis && sc >= pl.f_lo && sc <= pl.f_hi ? 1u : 0u) << r;
+      } else if constexpr (PFM == 1) {
+        atomicAdd(&hist[vis ? hbase + (key >> 20) : kTrash], add);
+      } else {
+        kk[r] = vis ? key : 0u;
+        atomicAdd(&hist[vis ? hbase + (key >> 20) : kTrash], add);
+      }
     }
     // Positions up to the next multiple of 16 lie inside the row's key
     // stride; entries past the visible count are never read.
-    if (tok_q) *reinterpret_cast<v4u*>(krow + j0) = v4u{kk[0], kk[1], kk[2], kk[3]};
+    if constexpr (PFM == 0) {
+      if (tok_q) *reinterpret_cast<v4u*>(krow + j0) = v4u{kk[0], kk[1], kk[2], kk[3]};
+    }
+    if constexpr (PF) {
+      if (pm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (!(pm & (1u << r))) continue;
+          em |= (kk[r] >= pl.e_lo && kk[r] <= pl.e_hi ? 1u : 0u) << r;
+          bm |= (kk[r] >= pl.b_lo && kk[r] <= pl.b_hi ? 1u : 0u) << r;
+        }
+      }
+      if (em) {
+        if constexpr (ST) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (em & (1u << r)) pf_lane_put2(hist, hist + kPoolOff, &pool_cnt, &spill, 0, c16, lane_ne, j0 + r, kk[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (em & (1u << r)) pf_emit(pf, row0 + c16, j0 + r, kk[r]);
+        }
+      }
+      if (bm) {
+        if (pl.mode == PF_HIST) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (bm & (1u << r)) atomicAdd(&hist[hbase + pf_digit(kk[r], pl.n_ps)], add);
+        } else if (pl.mode == PF_CAND) {
+          if constexpr (ST) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (bm & (1u << r)) pf_lane_put2(hist, hist + kPoolOff, &pool_cnt, &spill, 1, c16, lane_nc, j0 + r, kk[r]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (bm & (1u << r)) pf_cand(pf, row0 + c16, j0 + r, kk[r]);
+          }
+        } else if (pl.mode == PF_TIECOUNT) {
+          atomicAdd(&tcnt[c16], (uint32_t)__builtin_popcount(bm));
+        } else if (pl.mode == PF_TIEEMIT) {
+          atomicOr(&hist[c * QW + c16], bm << (4 * g));
+        }
+      }
+    }
   };
   // Chunks c = wave, wave + 8, ...; PD chunks in flight per wave.
-  int c = wave;
+  auto key_loop = [&](auto st_tag) {
+    int c = wave;
 #pragma unroll
-  for (int d = 0; d < PD; ++d) load_chunk(fk[d], c + d * kPrefillWaves);
-  for (; c < nchunks; c += PD * kPrefillWaves) {
+    for (int d = 0; d < PD; ++d) load_chunk(fk[d], c + d * kPrefillWaves);
+    for (; c < nchunks; c += PD * kPrefillWaves) {
 #pragma unroll
-    for (int d = 0; d < PD; ++d) {
-      const int cd = c + d * kPrefillWaves;
-      if (cd < nchunks) score_chunk(fk[d], cd);
-      load_chunk(fk[d], cd + PD * kPrefillWaves);
+      for (int d = 0; d < PD; ++d) {
+        const int cd = c + d * kPrefillWaves;
+        if (cd < nchunks) score_chunk(st_tag, fk[d], cd);
+        load_chunk(fk[d], cd + PD * kPrefillWaves);
+      }
     }
-  }
+  };
+  if (PF && stage) key_loop(std::true_type{});
+  else key_loop(std::false_type{});
   __syncthreads();
+  if constexpr (PF) {
+    if (stage && spill) {
+      // The staging space overflowed: score the tile again, every selected
+      // key and candidate taking its global slot directly (tie counts start
+      // over; staging excludes histogram and tie-emission rows).
+      stage = false;
+      if (threadIdx.x < QW) tcnt[threadIdx.x] = 0u;
+      __syncthreads();
+      key_loop(std::false_type{});
+      __syncthreads();
+    }
+    if (stage) {
+      pf_lane_flush<QW, kPrefillWaves>(pf, hist, lane_ne, lane_nc, sbase, row0, Tq, t0);
+      const uint32_t np = pool_cnt < (uint32_t)kPfPool ? pool_cnt : (uint32_t)kPfPool;
+      const uint32_t* pool = hist + kPoolOff;
+      for (uint32_t i = threadIdx.x; i < np; i += NT) {
+        const uint32_t tag = pool[3 * i + 2];
+        const int ql = tag & 15;
+        if (tag >> 4) pf_cand(pf, row0 + ql, pool[3 * i], pool[3 * i + 1]);
+        else pf_emit(pf, row0 + ql, pool[3 * i], pool[3 * i + 1]);
+      }
+    }
+    pf_finish<QW, NT>(pf, pfl, flags, hist, tcnt, row0, Tq, t0, k0, nchunks);
+    return;
+  }
+  if constexpr (PFM == 1) {
+    pf_flush_hist<QW, NT>(pf, hist, row0, Tq, t0);
+    return;
+  }
   if (!tok.hist1) return;
   for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
     const uint32_t v = hist[i];
@@ -1050,50 +1490,82 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
 }
 
 template <int DI, int HG>
+constexpr int kPrefillQW = 4 * ((HG * (DI / 128) <= 2) ? 4 : (HG * (DI / 128) <= 4 ? 2 : 1));
+
+// pf == nullptr: the whole chunk, score keys stored for the radix select;
+// else selection pass `pass` over the query tiles [y0, y0 + ny) (pass 0:
+// the level-1 histograms, later ones steered by the rows' states).
+template <int DI, int HG>
 static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
-                                   const SelectWs& tok, hipStream_t s) {
+                                   const SelectWs& tok, const PfArgs* pf, int pass, int64_t y0, int64_t ny,
+                                   hipStream_t s) {
   constexpr int QG = (HG * (DI / 128) <= 2) ? 4 : (HG * (DI / 128) <= 4 ? 2 : 1);
   constexpr int QW = 4 * QG;
+  static_assert(QW == kPrefillQW<DI, HG>, "query tile");
+  const bool kt = DI == 128 && HG <= 2;   // the transposed product (16 queries per workgroup)
   const int qtiles = (a.Tq + QW - 1) / QW;
-  const int64_t qrows = (int64_t)a.B * qtiles;
+  const int64_t qrows = pf ? ny : (int64_t)a.B * qtiles;
   // Key tiles: at most 8192 keys (per-tile counts stay below 2^16), smaller
-  // while the grid would not cover the compute units twice.
+  // while the grid would not cover the compute units twice; for the
+  // selection passes at most 4096 tiles per row (their tie counts).
   int key_tile = 8192;
   const int64_t want = 2LL * device_cu_count();
   while (key_tile > 512 && qrows * ((a.n_max + key_tile - 1) / key_tile) < want) key_tile >>= 1;
+  while (pf && key_tile < 8192 && (a.n_max + key_tile - 1) / key_tile > 4096) key_tile <<= 1;
   int64_t tiles = (a.n_max + key_tile - 1) / key_tile;
   if (tiles < 1) tiles = 1;
-  if (qrows > 65535) return hipErrorInvalidValue;
-  if (DI == 128 && HG <= 2 && a.k_scales) {
-    CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true>), dim3((unsigned)tiles, (unsigned)qrows),
-                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.k_scales,
-                a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys,
-                key_stride, n_valid, tok);
-  } else if (a.k_scales) {
-    return hipErrorInvalidValue;   // (MXFP4 prefill chunks: D_I = 128 and at most 8 heads)
-  } else if (DI == 128 && HG <= 2) {
-    CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false>), dim3((unsigned)tiles, (unsigned)qrows),
-                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride,
-                (const uint8_t*)nullptr, (int64_t)0, (int64_t)0, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile,
-                qtiles, keys, key_stride, n_valid, tok);
+  if (qrows > 65535 || (pf && tiles > 4096)) return hipErrorInvalidValue;
+  if (a.k_scales && !kt) return hipErrorInvalidValue;   // (MXFP4 prefill chunks: D_I = 128 and at most 8 heads)
+  const dim3 grid((unsigned)tiles, (unsigned)qrows), block(64 * kPrefillWaves);
+  const PfArgs pfa = pf ? *pf : PfArgs{};
+  const uint8_t* ks = a.k_scales;
+#define KT_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, ks, a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos, \
+                a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok, pfa, y0
+#define GEN_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, \
+                 qtiles, keys, key_stride, n_valid, tok, pfa, y0
+  const int pfm = !pf ? 0 : (pass == 0 ? 1 : 2);
+  if (kt) {
+    if (a.k_scales) {
+      if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true, 0>), grid, block, 0, s, KT_ARGS);
+      else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true, 1>), grid, block, 0, s, KT_ARGS);
+      else CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true, 2>), grid, block, 0, s, KT_ARGS);
+    } else {
+      if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false, 0>), grid, block, 0, s, KT_ARGS);
+      else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false, 1>), grid, block, 0, s, KT_ARGS);
+      else CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false, 2>), grid, block, 0, s, KT_ARGS);
+    }
   } else {
-    CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG>), dim3((unsigned)tiles, (unsigned)qrows),
-                dim3(64 * kPrefillWaves), 0, s, a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len,
-                a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok);
+    if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 0>), grid, block, 0, s, GEN_ARGS);
+    else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 1>), grid, block, 0, s, GEN_ARGS);
+    else CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 2>), grid, block, 0, s, GEN_ARGS);
   }
+#undef KT_ARGS
+#undef GEN_ARGS
   return hipGetLastError();
 }
 
-static bool prefill_gemm_applies(const ScoreArgs& a) {
+bool prefill_gemm_applies(const ScoreArgs& a) {
   if (a.k_scales) return a.Tq >= 16 && a.pool_block == 0 && a.D_I == 128 && a.H_I <= 8;
   return a.Tq >= 16 && a.pool_block == 0 && (a.D_I == 128 || a.D_I == 256) && a.H_I <= 32;
 }
 
-static hipError_t launch_prefill(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
-                                 const SelectWs& tok, hipStream_t s) {
+static int prefill_hg(const ScoreArgs& a) {
   const int hg = (a.H_I + 3) / 4;
-  const int HGp = hg <= 1 ? 1 : (hg <= 2 ? 2 : (hg <= 4 ? 4 : 8));
-#define CALL_PF(D, H) launch_prefill_t<D, H>(a, keys, key_stride, n_valid, tok, s)
+  return hg <= 1 ? 1 : (hg <= 2 ? 2 : (hg <= 4 ? 4 : 8));
+}
+
+int prefill_rows_per_tile(const ScoreArgs& a) {
+  const int H = prefill_hg(a);
+  if (a.D_I == 128) return H == 1 ? kPrefillQW<128, 1> : H == 2 ? kPrefillQW<128, 2> : H == 4 ? kPrefillQW<128, 4>
+                                                                                       : kPrefillQW<128, 8>;
+  return H == 1 ? kPrefillQW<256, 1> : H == 2 ? kPrefillQW<256, 2> : H == 4 ? kPrefillQW<256, 4> : kPrefillQW<256, 8>;
+}
+
+static hipError_t launch_prefill_any(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                                     const SelectWs& tok, const PfArgs* pf, int pass, int64_t y0, int64_t ny,
+                                     hipStream_t s) {
+  const int HGp = prefill_hg(a);
+#define CALL_PF(D, H) launch_prefill_t<D, H>(a, keys, key_stride, n_valid, tok, pf, pass, y0, ny, s)
   if (a.D_I == 128) {
     switch (HGp) {
       case 1: return CALL_PF(128, 1);
@@ -1109,6 +1581,16 @@ static hipError_t launch_prefill(const ScoreArgs& a, uint32_t* keys, int64_t key
     default: return CALL_PF(256, 8);
   }
 #undef CALL_PF
+}
+
+static hipError_t launch_prefill(const ScoreArgs& a, uint32_t* keys, int64_t key_stride, int32_t* n_valid,
+                                 const SelectWs& tok, hipStream_t s) {
+  return launch_prefill_any(a, keys, key_stride, n_valid, tok, nullptr, 0, 0, 0, s);
+}
+
+hipError_t launch_prefill_pass(const ScoreArgs& a, const PfArgs& pf, int pass, int64_t y0, int64_t ny,
+                               int32_t* n_valid, hipStream_t s) {
+  return launch_prefill_any(a, nullptr, 0, n_valid, SelectWs{}, &pf, pass, y0, ny, s);
 }
 
 #define CSA2_DISPATCH_DI_HB(DI_, HB_, CALL)                                       \

@@ -952,4 +952,216 @@ hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_s
   return hipGetLastError();
 }
 
+
+// ----------------------------------------------- prefill chunk selection ---
+// The states and buffers of a block of query rows (see PfRow): per row its
+// state, a 4096-word histogram (or key-tile tie counts), kPfCap candidates.
+static inline size_t pf_al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t pf_ws_bytes(int64_t block_rows) {
+  return pf_al256(sizeof(PfRow) * block_rows) + pf_al256(sizeof(uint32_t) * 4096 * block_rows) +
+         pf_al256(sizeof(uint64_t) * kPfCap * block_rows);
+}
+
+PfArgs pf_ws_carve(void* base, int64_t block_rows) {
+  char* p = (char*)base;
+  PfArgs a{};
+  a.rows = (PfRow*)p;
+  p += pf_al256(sizeof(PfRow) * block_rows);
+  a.hist = (uint32_t*)p;
+  p += pf_al256(sizeof(uint32_t) * 4096 * block_rows);
+  a.cand = (uint64_t*)p;
+  return a;
+}
+
+__global__ void __launch_bounds__(256) pf_clear_kernel(PfArgs pf) {
+  const int64_t lr = blockIdx.x;
+  if (threadIdx.x == 0) {
+    PfRow r{};
+    r.mode = PF_HIST;
+    r.e_ps = 32u;
+    r.n_ps = 32u;
+    r.need = (uint32_t)pf.k_top;
+    pf.rows[lr] = r;
+  }
+  v4u* h = reinterpret_cast<v4u*>(pf.hist + lr * 4096);
+  for (int i = threadIdx.x; i < 1024; i += 256) h[i] = v4u{0u, 0u, 0u, 0u};
+}
+
+// Bitonic sort of P (a power of two) 64-bit values in LDS by NT threads.
+template <int NT>
+__device__ void pf_bitonic(uint64_t* a, int P, bool descending) {
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += NT) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t x = a[i], y = a[l];
+          const bool up = ((i & k) == 0) != descending;
+          if ((x > y) == up) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// After a pass, per row: resolve the digit of a histogram pass, pick the
+// next mode; select the candidates of a candidate pass; prefix the tie
+// counts of a tie-count pass.
+__global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf) {
+  __shared__ uint32_t red[4];
+  __shared__ uint32_t res[4];
+  __shared__ __align__(16) uint64_t sbuf[kPfCap];
+  const int64_t lr = blockIdx.x;
+  PfRow* st = pf.rows + lr;
+  const uint32_t mode = st->mode;
+  if (mode == PF_DONE) return;
+  uint32_t* h = pf.hist + lr * 4096;
+  const int64_t grow = pf.row_base + lr;
+  const uint32_t K = (uint32_t)pf.k_top;
+  if (mode == PF_HIST) {
+    uint32_t need = st->need;
+    const uint32_t n_ps = st->n_ps, n_pfx = st->n_pfx;
+    if (n_ps >= 32u) {
+      // level 1: every visible key was counted
+      uint32_t sum = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += h[threadIdx.x * 16 + i];
+      const uint32_t incl = block_suffix_sum_256(sum, red);
+      if (threadIdx.x == 0) res[3] = incl;
+      __syncthreads();
+      const uint32_t total = res[3];
+      __syncthreads();
+      if (total <= K) {   // every visible key is selected: the first `total` positions
+        if (!pf.out_key) {
+          for (uint32_t i = threadIdx.x; i < total; i += 256) pf.out_idx[grow * K + i] = (int32_t)i;
+          if (threadIdx.x == 0) {
+            st->out_cnt = total;
+            st->mode = PF_DONE;
+          }
+          return;
+        }
+        if (threadIdx.x == 0) {   // (their scores come from the next pass)
+          st->e_on = 1u; st->e_ps = 32u; st->e_pfx = 0u; st->e_incl = 1u;
+          st->n_ps = 0u; st->n_pfx = 0u; st->need = 0u; st->bcnt = 0u;
+          st->mode = PF_EMIT;
+        }
+        return;
+      }
+      need = K;
+    }
+    const Digit d = resolve_digit<4096>(h, need, red, res);
+    const uint32_t w = n_ps == 8u ? 8u : 12u;
+    const uint32_t new_ps = (n_ps >= 32u ? 32u : n_ps) - w;
+    const uint32_t new_pfx = (n_ps >= 32u ? 0u : (n_pfx << w)) | d.d;
+    const uint32_t need2 = need - d.above;
+    uint32_t nm;
+    if (need2 == d.cnt) nm = PF_EMIT;                 // the whole bucket is taken
+    else if (d.cnt <= (uint32_t)kPfCap) nm = PF_CAND;
+    else nm = new_ps > 0u ? PF_HIST : PF_TIECOUNT;
+    if (threadIdx.x == 0) {
+      st->e_on = 1u; st->e_ps = n_ps; st->e_pfx = n_pfx; st->e_incl = nm == PF_EMIT ? 1u : 0u;
+      st->n_ps = new_ps; st->n_pfx = new_pfx; st->need = need2; st->bcnt = d.cnt; st->cand_cnt = 0u;
+      st->mode = nm;
+    }
+    if (nm == PF_HIST || nm == PF_TIECOUNT) {   // (resolve_digit has read h and synchronised)
+      v4u* h4 = reinterpret_cast<v4u*>(h);
+      for (int i = threadIdx.x; i < 1024; i += 256) h4[i] = v4u{0u, 0u, 0u, 0u};
+    }
+  } else if (mode == PF_CAND) {
+    // The bucket's keys as (key << 32 | ~position): descending order is
+    // (score desc, position asc); the first `need` are taken.
+    uint32_t n = st->cand_cnt;
+    if (n > (uint32_t)kPfCap) n = kPfCap;
+    const uint32_t need = st->need < n ? st->need : n;
+    const uint32_t base = st->out_cnt;
+    int P = 1;
+    while (P < (int)n) P <<= 1;
+    for (int i = threadIdx.x; i < P; i += 256) sbuf[i] = i < (int)n ? pf.cand[lr * kPfCap + i] : 0ull;
+    __syncthreads();
+    pf_bitonic<256>(sbuf, P, true);
+    for (uint32_t i = threadIdx.x; i < need; i += 256) {
+      const uint64_t v = sbuf[i];
+      const uint32_t slot = base + i;
+      if (slot < K) {
+        pf.out_idx[grow * K + slot] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
+        if (pf.out_key) pf.out_key[grow * K + slot] = (uint32_t)(v >> 32);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      st->out_cnt = base + need;
+      st->mode = PF_DONE;
+    }
+  } else if (mode == PF_TIECOUNT) {
+    // exclusive prefix of the ties per key tile, in place
+    uint32_t v[16];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = h[threadIdx.x * 16 + i];
+      sum += v[i];
+    }
+    uint32_t run = block_prefix_sum_256(sum, red) - sum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      h[threadIdx.x * 16 + i] = run;
+      run += v[i];
+    }
+    if (threadIdx.x == 0) {
+      st->e_on = 0u;
+      st->mode = PF_TIEEMIT;
+    }
+  } else {   // PF_EMIT, PF_TIEEMIT: the pass has emitted the rest
+    if (threadIdx.x == 0) st->mode = PF_DONE;
+  }
+}
+
+// Each row's positions ascending (ids unique), scores from their keys, -1 /
+// -inf padding.  PMAX >= k_top.
+template <int PMAX, int NT>
+__global__ void __launch_bounds__(NT) pf_final_kernel(PfArgs pf, float* __restrict__ topk_score) {
+  __shared__ __align__(16) uint64_t sbuf[PMAX];
+  const int64_t lr = blockIdx.x;
+  const int64_t grow = pf.row_base + lr;
+  const int K = pf.k_top;
+  uint32_t n = pf.rows[lr].out_cnt;
+  if (n > (uint32_t)K) n = K;
+  int P = 1;
+  while (P < (int)n) P <<= 1;
+  const int32_t* oi = pf.out_idx + grow * K;
+  const uint32_t* ok = pf.out_key ? pf.out_key + grow * K : nullptr;
+  for (int i = threadIdx.x; i < P; i += NT)
+    sbuf[i] = i < (int)n ? ((uint64_t)(uint32_t)oi[i] << 32) | (ok ? ok[i] : 0u) : ~0ull;
+  __syncthreads();
+  pf_bitonic<NT>(sbuf, P, false);
+  for (int i = threadIdx.x; i < K; i += NT) {
+    const bool v = i < (int)n;
+    pf.out_idx[grow * K + i] = v ? (int32_t)(sbuf[i] >> 32) : -1;
+    if (topk_score) topk_score[grow * K + i] = v ? key_score((uint32_t)sbuf[i]) : -__builtin_inff();
+  }
+}
+
+hipError_t pf_clear(const PfArgs& pf, int64_t block_rows, hipStream_t s) {
+  CSA2_LAUNCH("pf_clear", pf_clear_kernel, dim3((unsigned)block_rows), dim3(256), 0, s, pf);
+  return hipGetLastError();
+}
+
+hipError_t pf_step(const PfArgs& pf, int64_t block_rows, hipStream_t s) {
+  CSA2_LAUNCH("pf_step", pf_step_kernel, dim3((unsigned)block_rows), dim3(256), 0, s, pf);
+  return hipGetLastError();
+}
+
+hipError_t pf_final(const PfArgs& pf, int64_t block_rows, float* topk_score, hipStream_t s) {
+  if (pf.k_top <= 2048)
+    CSA2_LAUNCH("pf_final", (pf_final_kernel<2048, 256>), dim3((unsigned)block_rows), dim3(256), 0, s, pf, topk_score);
+  else
+    CSA2_LAUNCH("pf_final", (pf_final_kernel<kPfMaxK, 512>), dim3((unsigned)block_rows), dim3(512), 0, s, pf,
+                topk_score);
+  return hipGetLastError();
+}
+
 }  // namespace csa2

@@ -147,9 +147,30 @@ int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_
  *   pool_block must be 1, 2, 4, 8 or 16.  The flat Top-K is a subset of the
  *   pool whenever pool_nblocks >= k_top.
  * Supported: D_I in {32, 64, 128, 256}; 1 <= H_I <= 32; k_top >= 1.
+ *
+ * Workspace: ws / ws_bytes, 256-byte aligned, of at least
+ * csa2_index_score_topk_workspace_size() bytes.  Dense prefill chunks
+ * (Tq >= 16, no pool, k_top <= 8192) select in one of two ways, with
+ * identical results:
+ *   - stored score keys, 4 bytes per (query row, visible position) plus
+ *     per-tile histograms (csa2_index_score_topk_workspace_size_stored();
+ *     13.4 GB for 4096 queries on 266,240 tokens), used whenever ws_bytes
+ *     reaches that size: one scoring pass;
+ *   - otherwise no stored keys, as the indexer-selected sparse attention of
+ *     the techniques map expects of a prefill chunk: a scoring pass builds each
+ *     row's histogram of the top 12 key bits, a second one emits the keys
+ *     above the threshold bucket and collects the bucket itself, further
+ *     passes run only for rows whose bucket holds more than 4096 keys (ties
+ *     at one score included).  Query rows go in blocks of at most 1920; the
+ *     workspace stays under 100 MB (10^8 bytes) for chunks up to 65,535
+ *     query rows and 4M positions.
+ * csa2_index_score_topk_workspace_size() is the smaller of the two for such
+ * chunks and the stored size for every other call.
  */
 size_t csa2_index_score_topk_workspace_size(int32_t B, int32_t Tq, int64_t n_max, int32_t k_top,
                                             int32_t pool_block, int32_t pool_nblocks);
+size_t csa2_index_score_topk_workspace_size_stored(int32_t B, int32_t Tq, int64_t n_max, int32_t k_top,
+                                                   int32_t pool_block, int32_t pool_nblocks);
 int csa2_index_score_topk(const uint8_t* q_idx, const float* w,
                           const uint8_t* k_idx, int64_t k_batch_stride, int64_t k_row_stride,
                           const int32_t* ctx_len, const int32_t* q_pos,
@@ -193,11 +214,12 @@ int csa2_index_score_topk_mxfp4(const uint8_t* q_idx, const float* w,
  * 64 MiB (64 << 20 bytes) inside the library, one per GPU, kept until the
  * process ends; the call allocates nothing, and what must start at zero is
  * cleared by a kernel on `stream`.  Inputs whose
- * csa2_index_score_topk_workspace_size() exceeds 64 MiB return CSA2_ESCRATCH
- * with nothing enqueued (e.g. 64 x 64K-token decode rows need 48 MiB, 4 x 1M
- * with the 2048 x 8 pool 55 MiB).  Every call on one GPU uses that GPU's one
- * array: calls that may overlap on one GPU (other streams, other host
- * threads) race and must be ordered by the caller.
+ * csa2_index_score_topk_workspace_size() exceeds 64 MiB return
+ * CSA2_ESCRATCH with nothing enqueued (e.g. 64 x 64K-token decode rows need
+ * 48 MiB, 4 x 1M with the 2048 x 8 pool 55 MiB; a dense prefill chunk whose
+ * stored keys exceed 64 MiB selects by scoring passes).  Every call on one
+ * GPU uses that GPU's one array: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
  */
 int csa2_index_score_topk_noalloc(const uint8_t* q_idx, const float* w,
                                   const uint8_t* k_idx, int64_t k_batch_stride, int64_t k_row_stride,

@@ -95,6 +95,15 @@ int main(void) {
     EXPECT_TRUE(a >= (size_t)64 * 4 * (size_t)n && p >= (size_t)4 * 4 * (size_t)n);
     EXPECT_TRUE(b + 4096 * 64 * 4 >= a);   /* the longer-row layout may drop the per-tile histograms */
   }
+  for (size_t i = 0; i < sizeof(sizes) / sizeof(sizes[0]); ++i) {
+    const int64_t n = sizes[i];
+    const size_t full = csa2_index_score_topk_workspace_size_stored(1, 4096, n, 2048, 0, 0);
+    const size_t bnd = csa2_index_score_topk_workspace_size(1, 4096, n, 2048, 0, 0);
+    EXPECT_TRUE(bnd <= full && bnd < (size_t)100000000);
+    EXPECT_TRUE(csa2_index_score_topk_workspace_size_stored(64, 1, n, 2048, 0, 0) ==
+                csa2_index_score_topk_workspace_size(64, 1, n, 2048, 0, 0));
+  }
+  EXPECT_TRUE(csa2_index_score_topk_workspace_size_stored(-1, 16, 10, 1, 0, 0) == 0);
   EXPECT_TRUE(csa2_index_score_topk_workspace_size(-1, 1, 10, 1, 0, 0) == 0);
   EXPECT_TRUE(csa2_index_score_topk_workspace_size(1, 1, -10, 1, 0, 0) == 0);
   EXPECT_TRUE(csa2_hier_pool_topk_workspace_size(4, 1, 16384, 2048) >= (size_t)4 * 16384 * 4);

@@ -102,3 +102,26 @@ def test_workspace_sizes_are_monotone():
     big = lib.csa2_index_score_topk_workspace_size(64, 1, 65536, 2048, 0, 0)
     assert big >= 64 * 65536 * 4
     assert lib.csa2_hier_pool_topk_workspace_size(4, 1, 16384, 2048) >= 4 * 16384 * 4
+
+
+def test_prefill_chunk_workspace_is_bounded():
+    """Dense prefill chunks (16 or more query rows per sequence) need no
+    [rows][positions] score keys: a 4096-query chunk's default workspace
+    stays under 100 MB on contexts from 266,240 to 4M tokens, against the
+    4 bytes per (query, position) of the stored-key workspace (4.4 GB of keys
+    at 266,240)."""
+    lib = _lib_or_skip()
+    for n in (266240, 1 << 20, 4 << 20):
+        ws = lib.csa2_index_score_topk_workspace_size(1, 4096, n, 2048, 0, 0)
+        assert ws < 100 * 10**6, (n, ws)
+        assert lib.csa2_index_score_topk_workspace_size_stored(1, 4096, n, 2048, 0, 0) >= 4096 * n * 4
+    # the largest chunk the bound is stated for
+    assert lib.csa2_index_score_topk_workspace_size(1, 65535, 4 << 20, 8192, 0, 0) < 100 * 10**6
+    # more than 8192 selected positions per row, decode rows and pooled calls:
+    # the stored keys in either size
+    for args in ((1, 64, 266240, 9000, 0, 0), (64, 1, 65536, 2048, 0, 0), (4, 1, 65536, 2048, 8, 2048)):
+        assert lib.csa2_index_score_topk_workspace_size(*args) == \
+            lib.csa2_index_score_topk_workspace_size_stored(*args)
+    # a short chunk keeps the smaller of the two
+    assert lib.csa2_index_score_topk_workspace_size(1, 16, 256, 64, 0, 0) <= \
+        lib.csa2_index_score_topk_workspace_size_stored(1, 16, 256, 64, 0, 0)

@@ -26,8 +26,9 @@ def _oracle_rows(q_idx, w, k_idx, ctx_len, k_top, q_pos=None):
     return idx, sc
 
 
-def _run_and_check(q_idx, w, k_idx, ctx_len, k_top, q_pos=None):
-    res = csa2.csa2_index_score_topk(q_idx, w, k_idx, ctx_len, k_top, q_pos=q_pos, want_scores=True)
+def _run_and_check(q_idx, w, k_idx, ctx_len, k_top, q_pos=None, stored=False):
+    res = csa2.csa2_index_score_topk(q_idx, w, k_idx, ctx_len, k_top, q_pos=q_pos, want_scores=True,
+                                     stored_keys=stored)
     torch.cuda.synchronize()
     want_i, want_s = _oracle_rows(np_(q_idx), np_(w), np_(k_idx), np_(ctx_len), k_top,
                                   None if q_pos is None else np_(q_pos))
@@ -171,14 +172,17 @@ def test_causal_rows_with_q_pos():
 
 
 @gpu
+@pytest.mark.parametrize("stored", [False, True], ids=["passes", "stored_keys"])
 @pytest.mark.parametrize("H_I,D_I,Tq,K", [(8, 128, 40, 512), (3, 128, 17, 100), (32, 128, 20, 300),
                                          (8, 256, 33, 256), (13, 256, 16, 64), (8, 128, 70, 2048)])
-def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K):
+def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K, stored):
     """Chunks of 16 or more queries per sequence take the matrix-core product
     path; causal positions, a context shorter than some positions, a partial
-    last query tile and K above the visible count all appear."""
+    last query tile and K above the visible count all appear.  The default
+    workspace selects by scoring passes, the stored-key workspace from the
+    stored score keys."""
     require_gpu()
-    announce(f"index_score_topk prefill chunk H_I={H_I} D_I={D_I} Tq={Tq} K={K}")
+    announce(f"index_score_topk prefill chunk H_I={H_I} D_I={D_I} Tq={Tq} K={K} stored={stored}")
     B, N = 3, 2 * 8192 + 1234
     k_idx = inputs.int_e4m3((B, N, D_I), 31, 0, "k_idx", device="cuda")
     q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 31, 1, "q_idx", device="cuda")
@@ -189,7 +193,67 @@ def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K):
     q_pos = (base[:, None] + steps[None, :]).clamp(max=N - 1)
     q_pos[0, :3] = torch.tensor([0, 5, K // 2])          # tiny visible prefixes
     q_pos = q_pos.to(torch.int32).cuda().contiguous()
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos, stored=stored)
+
+
+@gpu
+@pytest.mark.parametrize("qmax,K", [(1, 300), (0, 700), (1, 2500)])
+def test_prefill_selection_passes_under_heavy_ties(qmax, K):
+    """Dense prefill chunks in the default workspace select without storing
+    their score keys, by repeated scoring passes.  Keys in {-1, 0, 1}, queries in {0 .. qmax} and
+    unit weights give a handful of integer scores: the bucket at the
+    threshold holds thousands of keys, so rows go through the second and
+    third digit levels and the tie count / tie emission passes (qmax = 0:
+    every score is 0 and the K lowest positions win).  Early rows see fewer
+    than K positions."""
+    require_gpu()
+    announce(f"index_score_topk prefill heavy ties qmax={qmax} K={K}")
+    B, N, Tq, H_I, D_I = 2, 3 * 8192 + 321, 40, 8, 128
+    k_idx = inputs.int_e4m3((B, N, D_I), 41, 0, "k_idx", lo=-1, hi=1, device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 41, 1, "q_idx", lo=0, hi=qmax, device="cuda")
+    w = torch.ones((B, Tq, H_I), dtype=torch.float32, device="cuda")
+    ctx = torch.tensor([N, N - 4000], dtype=torch.int32, device="cuda")
+    base = torch.tensor([N - Tq, N - 4000 - Tq], dtype=torch.int64)
+    q_pos = base[:, None] + torch.arange(Tq, dtype=torch.int64)[None, :]
+    q_pos[0, :4] = torch.tensor([0, 7, K - 1, K])
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos.to(torch.int32).cuda().contiguous())
+
+
+@gpu
+def test_prefill_selection_takes_a_whole_bucket():
+    """The K-th largest score's bucket is taken whole (the K selected keys are
+    exactly the keys at or above one score value): every row has the same
+    query, so K can be set to such a count from the oracle's scores."""
+    require_gpu()
+    announce("index_score_topk prefill whole threshold bucket")
+    B, N, Tq, H_I, D_I = 1, 20000, 32, 4, 128
+    k_idx = inputs.int_e4m3((B, N, D_I), 43, 0, "k_idx", lo=-1, hi=1, device="cuda")
+    q_one = inputs.int_e4m3((1, 1, H_I, D_I), 43, 1, "q_idx", lo=0, hi=1, device="cuda")
+    q_idx = q_one.expand(B, Tq, H_I, D_I).contiguous()
+    w = torch.ones((B, Tq, H_I), dtype=torch.float32, device="cuda")
+    ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
+    q_pos = torch.full((B, Tq), N - 1, dtype=torch.int32, device="cuda")
+    sc = I.index_scores(np_(q_one)[0, 0], np_(w)[0, 0], np_(k_idx)[0], N)
+    vals = np.unique(sc)[::-1]
+    K = int(np.sum(sc >= vals[3]))
+    assert 0 < K < N
     _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos)
+
+
+@gpu
+@pytest.mark.parametrize("D_I,H_I,Tq", [(64, 8, 20), (32, 4, 33)])
+def test_prefill_chunks_of_row_scans(D_I, H_I, Tq):
+    """Chunk shapes the matrix-core product does not take are scanned a few
+    query rows at a time through the default workspace."""
+    require_gpu()
+    announce(f"index_score_topk prefill as row scans D_I={D_I} H_I={H_I} Tq={Tq}")
+    B, N, K = 2, 9000, 256
+    k_idx = inputs.int_e4m3((B, N, D_I), 44, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 44, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 44, 1, "w", device="cuda")
+    ctx = torch.tensor([N, N - 500], dtype=torch.int32, device="cuda")
+    q_pos = (ctx[:, None].to(torch.int64) - Tq + torch.arange(Tq, device="cuda")[None, :]).to(torch.int32)
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos.contiguous())
 
 
 @gpu

@@ -78,8 +78,9 @@ def _oracle_rows(q_idx, w, kc, ks, ctx, K, q_pos=None):
     return idx, sc
 
 
-def _run(q_idx, w, kc, ks, ctx, K, q_pos=None):
-    res = csa2.csa2_index_score_topk_mxfp4(q_idx, w, kc, ks, ctx, K, q_pos=q_pos, want_scores=True)
+def _run(q_idx, w, kc, ks, ctx, K, q_pos=None, stored=False):
+    res = csa2.csa2_index_score_topk_mxfp4(q_idx, w, kc, ks, ctx, K, q_pos=q_pos, want_scores=True,
+                                           stored_keys=stored)
     torch.cuda.synchronize()
     want_i, want_s = _oracle_rows(np_(q_idx), np_(w), np_(kc), np_(ks), np_(ctx), K,
                                   None if q_pos is None else np_(q_pos))
@@ -127,6 +128,23 @@ def test_mxfp4_prefill_chunk():
     q_pos = (ctx[:, None].to(torch.int64) - Tq + torch.arange(Tq, device="cuda")[None, :] * 1).to(torch.int32)
     q_pos[0, :3] = torch.tensor([5, 700, 2047], dtype=torch.int32, device="cuda")
     _run(q, w, kc, ks, ctx, K, q_pos=q_pos.contiguous())
+    _run(q, w, kc, ks, ctx, K, q_pos=q_pos.contiguous(), stored=True)
+
+
+@gpu
+def test_mxfp4_prefill_chunk_wide_heads():
+    """An MXFP4 prefill chunk with 32 indexer heads (in the default workspace
+    row scans a few query rows at a time; stored keys)."""
+    require_gpu()
+    announce("mxfp4 prefill chunk H_I=32 Tq=20 on 12000 keys")
+    B, N, Tq, H_I, K = 1, 12000, 20, 32, 512
+    kc, ks = _mx_keys(B, N, 95)
+    q = inputs.int_e4m3((B, Tq, H_I, 128), 95, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 95, 1, "w", device="cuda")
+    ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
+    q_pos = (N - Tq + torch.arange(Tq, device="cuda")[None, :]).to(torch.int32).contiguous()
+    _run(q, w, kc, ks, ctx, K, q_pos=q_pos)
+    _run(q, w, kc, ks, ctx, K, q_pos=q_pos, stored=True)
 
 
 @gpu

@@ -172,6 +172,12 @@ def test_prefill256k_sampled_queries():
     swa_pos0 = torch.full((wl.B,), base - wl.W + 1, dtype=torch.int32, device="cuda")
     L = inputs.decode_layer_inputs(wl, 0, device="cuda")
     res = csa2.csa2_index_score_topk(L["q_idx"], L["w"], k_idx, ctx, wl.K, q_pos=q_pos)
+    # the same chunk from its stored score keys (13.4 GB of workspace)
+    # selects the same positions in every row
+    sto = csa2.csa2_index_score_topk(L["q_idx"], L["w"], k_idx, ctx, wl.K, q_pos=q_pos, stored_keys=True)
+    assert torch.equal(sto["topk_idx"], res["topk_idx"])
+    del sto
+    torch.cuda.empty_cache()
     sv, ss = csa2.swa_fp8_quantize(L["swa_x"])
     out, lse = csa2.csa2_sparse_attn_prefill(L["q"], codes, scales, res["topk_idx"], ctx, q_pos, sv, ss, swa_pos0,
                                              wl.W, wl.softmax_scale, want_lse=True)
