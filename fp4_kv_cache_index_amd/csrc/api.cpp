@@ -289,6 +289,7 @@ static int prefill_impl(const ScoreArgs& a, int32_t* topk_idx, float* topk_score
     const int64_t ny = ytot - y0 < per_block ? ytot - y0 : per_block;
     PfArgs pf = pf_ws_carve(rest, kPfRowsPerBlock < rows ? kPfRowsPerBlock : rows);
     pf.row_base = row_of(y0);
+    pf.n_valid = n_valid;
     const int64_t nrows = row_of(y0 + ny) - pf.row_base;
     pf.out_idx = topk_idx;
     pf.out_key = reinterpret_cast<uint32_t*>(topk_score);
@@ -296,7 +297,7 @@ static int prefill_impl(const ScoreArgs& a, int32_t* topk_idx, float* topk_score
     hipError_t e = pf_clear(pf, nrows, s);
     for (int p = 0; p < kPfPasses && e == hipSuccess; ++p) {
       e = launch_prefill_pass(a, pf, p, y0, ny, n_valid, s);
-      if (e == hipSuccess) e = pf_step(pf, nrows, s);
+      if (e == hipSuccess) e = pf_step(pf, nrows, p, s);
     }
     if (e == hipSuccess) e = pf_final(pf, nrows, topk_score, s);
     if (e != hipSuccess) return CSA2_EHIP;

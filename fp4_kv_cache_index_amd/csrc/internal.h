@@ -122,24 +122,41 @@ hipError_t select_finish(const SelectWs& ws, const uint32_t* keys, int64_t key_s
 // ------------------------------------------------ prefill chunk selection ---
 // A dense prefill chunk (many query rows of one sequence against the same
 // keys) selects without storing its [rows][n] score keys: the scoring
-// product runs again in up to five passes over the chunk's keys, each query
-// row steered by a PfRow.  A pass emits the keys that are selected for
-// certain (above the threshold bucket found so far: their positions go
-// straight to the row's output, unordered) and either histograms the next
-// radix digit (12, 12, then 8 bits) of the keys still undecided, appends
-// them as candidates (when at most kPfCap of them remain), or, once the
-// threshold key itself is known and ties at it outnumber kPfCap, counts the
-// ties per key tile and then emits the lowest-position ones.  A step kernel
-// after each pass resolves the digit and picks the next mode; a last kernel
-// sorts each row's positions.
+// product runs again in a few passes over the chunk's keys, each query row
+// steered by a PfRow.
+//   Pass 0 histograms the top 12 key bits of a 1/kPfSample sample of the
+//   keys; from it each row finds the buckets that hold its threshold with a
+//   margin of four standard deviations of the sample count, and pass 1
+//   histograms the same sample again at a finer grain (4096 bins over those
+//   buckets), which narrows the window to a few fine bins.  Pass 2 scores
+//   every key, emits those above the window and appends those inside it as
+//   candidates; the step kernel checks the
+//   counts (emitted at most k_top, emitted + candidates at least k_top,
+//   candidates at most kPfCap) and takes the rest from the sorted
+//   candidates.  A row whose check fails starts over with the exact search:
+//   a pass emits the keys that are selected for certain (above the threshold
+//   bucket found so far: their positions go straight to the row's output,
+//   unordered) and either histograms the next radix digit (12, 12, then 8
+//   bits) of the keys still undecided, appends them as candidates (when at
+//   most kPfCap of them remain), or, once the threshold key itself is known
+//   and ties at it outnumber kPfCap, counts the ties per key tile and then
+//   emits the lowest-position ones.
+// A step kernel after each pass resolves the digit and picks the next mode;
+// a last kernel sorts each row's positions.
 constexpr int kPfCap = 4096;            // candidates kept per row
 constexpr int kPfMaxK = 8192;           // largest k_top of this path (LDS sort)
 constexpr int kPfRowsPerBlock = 1920;   // query rows per block of passes (workspace bound)
-constexpr int kPfPasses = 5;            // digit levels 12 + 12 + 8, tie count, tie emission
+constexpr int kPfSample = 8;            // pass 0 scores one 16-key chunk in kPfSample
+// two sample passes, the guess pass, then (rows whose guess failed) the exact
+// search: digit levels 12 + 12 + 8, tie count, tie emission
+constexpr int kPfPasses = 8;
 
-enum PfMode : uint32_t { PF_DONE = 0, PF_HIST = 1, PF_CAND = 2, PF_EMIT = 3, PF_TIECOUNT = 4, PF_TIEEMIT = 5 };
+enum PfMode : uint32_t {
+  PF_DONE = 0, PF_HIST = 1, PF_CAND = 2, PF_EMIT = 3, PF_TIECOUNT = 4, PF_TIEEMIT = 5,
+  PF_GUESS = 6   // emit keys >= g_emit, append keys in [g_cand, g_emit) as candidates
+};
 
-struct PfRow {                          // 64 bytes per query row
+struct PfRow {                          // 80 bytes per query row
   uint32_t mode;
   // Keys selected for certain in the next pass: e_on, key in the previous
   // bucket (e_ps >= 32: every key; else key >> e_ps == e_pfx) and above the
@@ -151,7 +168,15 @@ struct PfRow {                          // 64 bytes per query row
   uint32_t bcnt;                        // keys in the bucket
   uint32_t out_cnt;                     // positions emitted so far (atomic)
   uint32_t cand_cnt;                    // candidates appended (atomic)
-  uint32_t pad[5];
+  // The histogram counts the sample: 1 coarse (pass 0), 2 fine (pass 1).
+  uint32_t sampled;
+  // PF_GUESS: keys >= g_emit are emitted (none when g_emit_none), keys in
+  // [g_cand, g_emit) become candidates.
+  uint32_t g_emit, g_cand, g_emit_none;
+  // Sample passes: bin min((key - h_base) >> h_shift, 4095) of keys >=
+  // h_base; s_total = sampled visible keys.
+  uint32_t h_base, h_shift, s_total;
+  uint32_t pad;
 };
 
 struct PfArgs {
@@ -160,15 +185,19 @@ struct PfArgs {
   uint64_t* cand;                       // [block rows][kPfCap]: (key << 32) | ~position
   int32_t* out_idx;                     // the caller's topk_idx [rows][k_top]
   uint32_t* out_key;                    // nullable: the caller's topk_score [rows][k_top] (key bits until the end)
+  const int32_t* n_valid;               // [rows]: visible keys per query row (written by every pass)
+  uint32_t* active;                     // [kPfPasses]: 1 when a row of the block is not done after a step
   int64_t row_base;                     // first (global) query row of the block
   int k_top;
+  int pass;                             // the pass a kernel runs (set per launch)
 };
 size_t pf_ws_bytes(int64_t block_rows);
 PfArgs pf_ws_carve(void* base, int64_t block_rows);
 // Initial state of every row of the block (level-1 histogram, zeroed counts).
 hipError_t pf_clear(const PfArgs& pf, int64_t block_rows, hipStream_t s);
-// After a pass: resolve a digit / select candidates / prefix the tie counts.
-hipError_t pf_step(const PfArgs& pf, int64_t block_rows, hipStream_t s);
+// After pass `pass`: resolve a digit / select candidates / prefix the tie
+// counts.
+hipError_t pf_step(const PfArgs& pf, int64_t block_rows, int pass, hipStream_t s);
 // Sort each row's positions ascending, pad with -1 (scores: -inf).
 hipError_t pf_final(const PfArgs& pf, int64_t block_rows, float* topk_score, hipStream_t s);
 

@@ -753,7 +753,26 @@ struct PfLane {
 };
 __device__ __forceinline__ PfLane pf_load(const PfArgs& pf, int64_t grow, bool ok) {
   PfLane L{PF_DONE, 32u, 0u, 1u, 0u, 1u, 0u, __builtin_inff(), -__builtin_inff()};   // (empty ranges)
-  if (ok && pf.rows[grow - pf.row_base].mode != PF_DONE) {
+  if (ok && pf.rows[grow - pf.row_base].mode == PF_GUESS) {
+    // the guessed window: candidates in [g_cand, g_emit), emitted above
+    const PfRow& r = pf.rows[grow - pf.row_base];
+    L.mode = PF_CAND;
+    if (!r.g_emit_none) {
+      L.e_lo = r.g_emit;
+      L.e_hi = 0xFFFFFFFFu;
+    }
+    const uint32_t chi = r.g_emit_none ? 0xFFFFFFFFu : r.g_emit - 1u;
+    if (r.g_emit_none || r.g_emit > r.g_cand) {
+      L.b_lo = r.g_cand;
+      L.b_hi = chi;
+    }
+    const uint32_t ulo = L.b_lo <= L.b_hi ? L.b_lo : L.e_lo;
+    const uint32_t uhi = L.e_lo <= L.e_hi ? L.e_hi : L.b_hi;
+    if (ulo <= uhi) {
+      L.f_lo = ulo <= 0x007FFFFFu ? -__builtin_inff() : key_score(ulo);
+      L.f_hi = uhi >= 0xFF800000u ? __builtin_inff() : key_score(uhi);
+    }
+  } else if (ok && pf.rows[grow - pf.row_base].mode != PF_DONE) {
     const PfRow& r = pf.rows[grow - pf.row_base];
     L.mode = r.mode;
     L.n_ps = r.n_ps;
@@ -942,8 +961,40 @@ __device__ void pf_unstage(const PfArgs& pf, const uint32_t* stg, const uint32_t
     }
   }
 }
-// Level-1 histogram pass (PFM 1: every row of the block histograms the top
-// 12 bits of its visible keys): the tile's LDS histogram into the rows'.
+// Pass 0 of the selection (PFM 1) scores a sample of a tile's 16-key chunks:
+// chunk kPfSample*m + m % kPfSample for m = 0, 1, ... (every part of the
+// tile, and every offset within kPfSample chunks, represented).
+static_assert((kPfSample & (kPfSample - 1)) == 0, "power of two");
+template <int PFM>
+__device__ __forceinline__ int pf_chunk(int m) {
+  return PFM == 1 ? kPfSample * m + (m & (kPfSample - 1)) : m;
+}
+template <int PFM>
+__device__ __forceinline__ int pf_nloop(int nchunks) {
+  return PFM == 1 ? (nchunks + kPfSample - 1) / kPfSample : nchunks;
+}
+// The row's histogram range in a sample pass: (h_base, h_shift), see PfRow.
+__device__ __forceinline__ void pf_sample_range(const PfArgs& pf, int64_t grow, bool ok, uint32_t& base,
+                                                uint32_t& shift) {
+  base = 0xFFFFFFFFu;   // (rows outside the sample: nothing counted)
+  shift = 31u;
+  if (ok) {
+    const PfRow& r = pf.rows[grow - pf.row_base];
+    if (r.sampled != 0u) {
+      base = r.h_base;
+      shift = r.h_shift;
+    }
+  }
+}
+// Sample-pass bin of a key (-1: below the range; the last bin takes every
+// key above it).
+__device__ __forceinline__ int pf_sbin(uint32_t key, uint32_t base, uint32_t shift) {
+  if (key < base) return -1;
+  const uint32_t d = (key - base) >> shift;
+  return d > 4095u ? 4095 : (int)d;
+}
+// Histogram pass (PFM 1: every row of the block histograms the top 12 bits
+// of its sampled visible keys): the tile's LDS histogram into the rows'.
 template <int QW, int NT>
 __device__ void pf_flush_hist(const PfArgs& pf, const uint32_t* hist, int64_t row0, int Tq, int t0) {
   for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
@@ -1035,6 +1086,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
   constexpr bool PF = PFM == 2;
   __shared__ uint32_t hist[(QW / 2) * 4096];
   __shared__ int32_t nvs[QW];
+  __shared__ uint32_t shb[PFM == 1 ? QW : 1], shs[PFM == 1 ? QW : 1];   // sample passes: bin ranges
   __shared__ PfLane pfl[PF ? QW : 1];
   __shared__ uint32_t tcnt[PF ? QW : 1];
   __shared__ uint32_t scnt[PF ? 2 * QW : 1], sbase[PF ? 2 * QW : 1];
@@ -1045,6 +1097,9 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
   const int64_t b = yy / qtiles;
   const int t0 = (int)(yy % qtiles) * QW;
   const int64_t row0 = b * Tq + t0;
+  if constexpr (PF) {
+    if (pf.active[pf.pass - 1] == 0u) return;   // (uniform: every row of the block done)
+  }
 
   if (threadIdx.x < QW) {
     const int t = t0 + threadIdx.x;
@@ -1059,6 +1114,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
       if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
     }
     nvs[threadIdx.x] = (int32_t)nv;
+    if constexpr (PFM == 1) pf_sample_range(pf, row0 + threadIdx.x, t < Tq, shb[threadIdx.x], shs[threadIdx.x]);
     if constexpr (PF) {
       pfl[threadIdx.x] = pf_load(pf, row0 + threadIdx.x, t < Tq);
       tcnt[threadIdx.x] = 0u;
@@ -1170,7 +1226,8 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
             }
           }
         } else if constexpr (PFM == 1) {
-          atomicAdd(&hist[(ql >> 1) * 4096 + (key >> 20)], 1u << (16 * (ql & 1)));
+          const int bin = pf_sbin(key, shb[ql], shs[ql]);
+          if (bin >= 0) atomicAdd(&hist[(ql >> 1) * 4096 + bin], 1u << (16 * (ql & 1)));
         } else {
           __builtin_nontemporal_store(key, krow[qg] + j);
           atomicAdd(&hist[(ql >> 1) * 4096 + (key >> 20)], 1u << (16 * (ql & 1)));
@@ -1178,14 +1235,16 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
       }
     }
   };
+  const int nloop = pf_nloop<PFM>(nchunks);
+  auto live = [&](int m) { return m < nloop && pf_chunk<PFM>(m) < nchunks; };
   int c = wave;
-  if (c < nchunks) load_chunk(fa, c);
-  for (; c < nchunks; c += 2 * kPrefillWaves) {
+  if (live(c)) load_chunk(fa, pf_chunk<PFM>(c));
+  for (; c < nloop; c += 2 * kPrefillWaves) {
     const int cb = c + kPrefillWaves;
-    if (cb < nchunks) load_chunk(fb, cb);
-    score_chunk(fa, c);
-    if (cb + kPrefillWaves < nchunks) load_chunk(fa, cb + kPrefillWaves);
-    if (cb < nchunks) score_chunk(fb, cb);
+    if (live(cb)) load_chunk(fb, pf_chunk<PFM>(cb));
+    if (live(c)) score_chunk(fa, pf_chunk<PFM>(c));
+    if (live(cb + kPrefillWaves)) load_chunk(fa, pf_chunk<PFM>(cb + kPrefillWaves));
+    if (live(cb)) score_chunk(fb, pf_chunk<PFM>(cb));
   }
   __syncthreads();
   if constexpr (PF) {
@@ -1234,6 +1293,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   constexpr bool PF = PFM == 2;
   __shared__ uint32_t hist[(QW / 2) * 4096 + 1];   // last word: bin of invisible keys
   __shared__ int32_t nvs[QW];
+  __shared__ uint32_t shb[PFM == 1 ? QW : 1], shs[PFM == 1 ? QW : 1];   // sample passes: bin ranges
   __shared__ PfLane pfl[PF ? QW : 1];
   __shared__ uint32_t tcnt[PF ? QW : 1];
   __shared__ uint32_t scnt[PF ? 2 * QW : 1], sbase[PF ? 2 * QW : 1];
@@ -1248,6 +1308,9 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   const int64_t b = yy / qtiles;
   const int t0 = (int)(yy % qtiles) * QW;
   const int64_t row0 = b * Tq + t0;
+  if constexpr (PF) {
+    if (pf.active[pf.pass - 1] == 0u) return;   // (uniform: every row of the block done)
+  }
 
   if (threadIdx.x < QW) {
     const int t = t0 + threadIdx.x;
@@ -1262,6 +1325,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
     }
     nvs[threadIdx.x] = (int32_t)nv;
+    if constexpr (PFM == 1) pf_sample_range(pf, row0 + threadIdx.x, t < Tq, shb[threadIdx.x], shs[threadIdx.x]);
     if constexpr (PF) {
       pfl[threadIdx.x] = pf_load(pf, row0 + threadIdx.x, t < Tq);
       tcnt[threadIdx.x] = 0u;
@@ -1296,6 +1360,11 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   if (k0 >= k1) return;   // uniform: nothing visible in this tile
   PfLane pl{};
   if constexpr (PF) pl = pfl[c16];
+  uint32_t s_lo = 0u, s_sh = 20u;   // sample passes: this lane's bin range
+  if constexpr (PFM == 1) {
+    s_lo = shb[c16];
+    s_sh = shs[c16];
+  }
   uint32_t lane_ne = 0u, lane_nc = 0u;   // PF: entries this lane staged (emits, candidates)
 
   // B fragments: column c16 = query t0 + c16, one per head.
@@ -1379,7 +1448,10 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
         kk[r] = key;
         pm |= (vis && sc >= pl.f_lo && sc <= pl.f_hi ? 1u : 0u) << r;
       } else if constexpr (PFM == 1) {
-        atomicAdd(&hist[vis ? hbase + (key >> 20) : kTrash], add);
+        // (most keys of the fine sample pass lie below the range: skipped,
+        // not sent to one shared word)
+        const uint32_t d = (key - s_lo) >> s_sh;
+        if (vis && key >= s_lo) atomicAdd(&hist[hbase + (d > 4095u ? 4095u : d)], add);
       } else {
         kk[r] = vis ? key : 0u;
         atomicAdd(&hist[vis ? hbase + (key >> 20) : kTrash], add);
@@ -1433,17 +1505,19 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       }
     }
   };
-  // Chunks c = wave, wave + 8, ...; PD chunks in flight per wave.
+  // Chunks c = wave, wave + 8, ... (pass 0: of the sampled chunks); PD
+  // chunks in flight per wave (loads past the tile read clamped rows).
   auto key_loop = [&](auto st_tag) {
+    const int nloop = pf_nloop<PFM>(nchunks);
     int c = wave;
 #pragma unroll
-    for (int d = 0; d < PD; ++d) load_chunk(fk[d], c + d * kPrefillWaves);
-    for (; c < nchunks; c += PD * kPrefillWaves) {
+    for (int d = 0; d < PD; ++d) load_chunk(fk[d], pf_chunk<PFM>(c + d * kPrefillWaves));
+    for (; c < nloop; c += PD * kPrefillWaves) {
 #pragma unroll
       for (int d = 0; d < PD; ++d) {
         const int cd = c + d * kPrefillWaves;
-        if (cd < nchunks) score_chunk(st_tag, fk[d], cd);
-        load_chunk(fk[d], cd + PD * kPrefillWaves);
+        if (cd < nloop && pf_chunk<PFM>(cd) < nchunks) score_chunk(st_tag, fk[d], pf_chunk<PFM>(cd));
+        load_chunk(fk[d], pf_chunk<PFM>(cd + PD * kPrefillWaves));
       }
     }
   };
@@ -1505,10 +1579,12 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
   const bool kt = DI == 128 && HG <= 2;   // the transposed product (16 queries per workgroup)
   const int qtiles = (a.Tq + QW - 1) / QW;
   const int64_t qrows = pf ? ny : (int64_t)a.B * qtiles;
-  // Key tiles: at most 8192 keys (per-tile counts stay below 2^16), smaller
+  // Key tiles: at most 8192 keys (per-tile counts stay below 2^16; sample
+  // passes: kPfSample times as many keys, of which they score 8192), smaller
   // while the grid would not cover the compute units twice; for the
   // selection passes at most 4096 tiles per row (their tie counts).
-  int key_tile = 8192;
+  const int pfm = !pf ? 0 : (pass < 2 ? 1 : 2);
+  int key_tile = pfm == 1 ? 8192 * kPfSample : 8192;
   const int64_t want = 2LL * device_cu_count();
   while (key_tile > 512 && qrows * ((a.n_max + key_tile - 1) / key_tile) < want) key_tile >>= 1;
   while (pf && key_tile < 8192 && (a.n_max + key_tile - 1) / key_tile > 4096) key_tile <<= 1;
@@ -1517,13 +1593,13 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
   if (qrows > 65535 || (pf && tiles > 4096)) return hipErrorInvalidValue;
   if (a.k_scales && !kt) return hipErrorInvalidValue;   // (MXFP4 prefill chunks: D_I = 128 and at most 8 heads)
   const dim3 grid((unsigned)tiles, (unsigned)qrows), block(64 * kPrefillWaves);
-  const PfArgs pfa = pf ? *pf : PfArgs{};
+  PfArgs pfa = pf ? *pf : PfArgs{};
+  pfa.pass = pass;
   const uint8_t* ks = a.k_scales;
 #define KT_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, ks, a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos, \
                 a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok, pfa, y0
 #define GEN_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, \
                  qtiles, keys, key_stride, n_valid, tok, pfa, y0
-  const int pfm = !pf ? 0 : (pass == 0 ? 1 : 2);
   if (kt) {
     if (a.k_scales) {
       if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true, 0>), grid, block, 0, s, KT_ARGS);

@@ -960,7 +960,7 @@ static inline size_t pf_al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t pf_ws_bytes(int64_t block_rows) {
   return pf_al256(sizeof(PfRow) * block_rows) + pf_al256(sizeof(uint32_t) * 4096 * block_rows) +
-         pf_al256(sizeof(uint64_t) * kPfCap * block_rows);
+         pf_al256(sizeof(uint64_t) * kPfCap * block_rows) + pf_al256(sizeof(uint32_t) * kPfPasses);
 }
 
 PfArgs pf_ws_carve(void* base, int64_t block_rows) {
@@ -971,6 +971,8 @@ PfArgs pf_ws_carve(void* base, int64_t block_rows) {
   a.hist = (uint32_t*)p;
   p += pf_al256(sizeof(uint32_t) * 4096 * block_rows);
   a.cand = (uint64_t*)p;
+  p += pf_al256(sizeof(uint64_t) * kPfCap * block_rows);
+  a.active = (uint32_t*)p;
   return a;
 }
 
@@ -982,7 +984,12 @@ __global__ void __launch_bounds__(256) pf_clear_kernel(PfArgs pf) {
     r.e_ps = 32u;
     r.n_ps = 32u;
     r.need = (uint32_t)pf.k_top;
+    r.sampled = 1u;
+    r.h_base = 0u;
+    r.h_shift = 20u;   // (the top 12 bits)
     pf.rows[lr] = r;
+    if (lr == 0)
+      for (int i = 0; i < kPfPasses; ++i) pf.active[i] = 0u;
   }
   v4u* h = reinterpret_cast<v4u*>(pf.hist + lr * 4096);
   for (int i = threadIdx.x; i < 1024; i += 256) h[i] = v4u{0u, 0u, 0u, 0u};
@@ -1011,7 +1018,7 @@ __device__ void pf_bitonic(uint64_t* a, int P, bool descending) {
 // After a pass, per row: resolve the digit of a histogram pass, pick the
 // next mode; select the candidates of a candidate pass; prefix the tie
 // counts of a tie-count pass.
-__global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf) {
+__device__ __forceinline__ void pf_step_row(const PfArgs& pf, int pass) {
   __shared__ uint32_t red[4];
   __shared__ uint32_t res[4];
   __shared__ __align__(16) uint64_t sbuf[kPfCap];
@@ -1022,19 +1029,105 @@ __global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf) {
   uint32_t* h = pf.hist + lr * 4096;
   const int64_t grow = pf.row_base + lr;
   const uint32_t K = (uint32_t)pf.k_top;
+  // The exact search from its start (every count cleared; the histogram
+  // zeroed by the caller).
+  auto restart = [&]() {
+    if (threadIdx.x == 0) {
+      st->e_on = 0u; st->e_ps = 32u; st->e_pfx = 0u; st->e_incl = 0u;
+      st->n_ps = 32u; st->n_pfx = 0u; st->need = K; st->bcnt = 0u;
+      st->out_cnt = 0u; st->cand_cnt = 0u; st->sampled = 0u;
+      st->mode = PF_HIST;
+    }
+  };
+  auto zero_hist = [&]() {
+    v4u* h4 = reinterpret_cast<v4u*>(h);
+    for (int i = threadIdx.x; i < 1024; i += 256) h4[i] = v4u{0u, 0u, 0u, 0u};
+  };
+  if (pass == 1 && st->sampled == 0u) {
+    // Pass 1 histograms the sample again: rows already outside it (taking
+    // every key, or searching exactly) wait for the next pass.
+    if (mode == PF_HIST) zero_hist();
+    return;
+  }
   if (mode == PF_HIST) {
     uint32_t need = st->need;
     const uint32_t n_ps = st->n_ps, n_pfx = st->n_pfx;
     if (n_ps >= 32u) {
-      // level 1: every visible key was counted
+      // level 1: every visible key was counted, or (sampled) one chunk in
+      // kPfSample.  (The row's fields are read before the first barrier:
+      // thread 0 rewrites them at the end.)
+      const uint32_t stage = st->sampled, prev_total = st->s_total;
+      const uint64_t hb = st->h_base, hs = st->h_shift;
       uint32_t sum = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sum += h[threadIdx.x * 16 + i];
       const uint32_t incl = block_suffix_sum_256(sum, red);
       if (threadIdx.x == 0) res[3] = incl;
       __syncthreads();
-      const uint32_t total = res[3];
+      const bool sampled = stage != 0u;
+      const uint32_t total = sampled ? (uint32_t)pf.n_valid[grow] : res[3];
+      const uint32_t total_s = res[3];
       __syncthreads();
+      if (sampled && total > K) {
+        const uint32_t s_total = stage == 1u ? total_s : prev_total;
+        if (s_total == 0u) {   // (no sampled key visible: search exactly)
+          restart();
+          zero_hist();
+          return;
+        }
+        // With ks the sample's share of k_top and m four standard deviations
+        // of the sample count (plus four), the window runs from the bin
+        // where ks - m sampled keys are reached from the top (exclusive: the
+        // keys above it are emitted) down to the bin where ks + m are.
+        const float ks = (float)K * (float)s_total / (float)total;
+        const float m = 4.0f * __builtin_sqrtf(ks) + 4.0f;
+        const uint32_t need_e = ks - m >= 1.0f ? (uint32_t)(ks - m) + 1u : 1u;
+        const float fl = __builtin_ceilf(ks + m);
+        const uint32_t need_l = fl > (float)total_s ? total_s + 1u : (uint32_t)fl;
+        // (total_s: the sampled keys inside this histogram's range)
+        Digit de{4095u, 0u, 0u}, dl{0u, 0u, 0u};
+        if (need_e <= total_s) de = resolve_digit<4096>(h, need_e, red, res);
+        const bool has_lo = need_l <= total_s;
+        if (has_lo) dl = resolve_digit<4096>(h, need_l, red, res);
+        // key bounds of bins: bin d covers [hb + (d << hs), hb + ((d + 1) << hs))
+        const uint64_t e_key = hb + ((uint64_t)(de.d + 1u) << hs);
+        const uint64_t c_key = has_lo ? hb + ((uint64_t)dl.d << hs) : (stage == 1u ? 0ull : hb);
+        if (stage == 1u) {
+          // Coarse: histogram the window [c_key, e_key) again at a finer
+          // grain: at most 4095 bins of 2^sh keys cover it, and the last of
+          // the 4096 bins takes the keys above.
+          const uint64_t span = e_key - c_key;
+          uint32_t sh = 8u;
+          while (sh < 20u && ((uint64_t)4095 << sh) < span) ++sh;
+          __syncthreads();   // (every thread has read h)
+          zero_hist();
+          if (threadIdx.x == 0) {
+            st->h_base = (uint32_t)c_key;
+            st->h_shift = sh;
+            st->s_total = s_total;
+            st->sampled = 2u;
+          }
+          return;
+        }
+        // Fine: the guess, unless the window is unusable: its emission
+        // bound in the last bin (which holds every key above the range), no
+        // lower bound, or more candidates expected than kept (heavy ties):
+        // then the row searches exactly from the next pass on.
+        const float in_win = (float)(dl.above + dl.cnt - de.above) * (float)total / (float)s_total;
+        if (de.d >= 4095u || !has_lo || in_win > 0.75f * (float)kPfCap) {
+          restart();
+          zero_hist();
+          return;
+        }
+        if (threadIdx.x == 0) {
+          st->g_emit_none = 0u;
+          st->g_emit = (uint32_t)e_key;
+          st->g_cand = (uint32_t)c_key;
+          st->out_cnt = 0u; st->cand_cnt = 0u; st->sampled = 0u;
+          st->mode = PF_GUESS;
+        }
+        return;
+      }
       if (total <= K) {   // every visible key is selected: the first `total` positions
         if (!pf.out_key) {
           for (uint32_t i = threadIdx.x; i < total; i += 256) pf.out_idx[grow * K + i] = (int32_t)i;
@@ -1046,7 +1139,7 @@ __global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf) {
         }
         if (threadIdx.x == 0) {   // (their scores come from the next pass)
           st->e_on = 1u; st->e_ps = 32u; st->e_pfx = 0u; st->e_incl = 1u;
-          st->n_ps = 0u; st->n_pfx = 0u; st->need = 0u; st->bcnt = 0u;
+          st->n_ps = 0u; st->n_pfx = 0u; st->need = 0u; st->bcnt = 0u; st->sampled = 0u;
           st->mode = PF_EMIT;
         }
         return;
@@ -1067,17 +1160,25 @@ __global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf) {
       st->n_ps = new_ps; st->n_pfx = new_pfx; st->need = need2; st->bcnt = d.cnt; st->cand_cnt = 0u;
       st->mode = nm;
     }
-    if (nm == PF_HIST || nm == PF_TIECOUNT) {   // (resolve_digit has read h and synchronised)
-      v4u* h4 = reinterpret_cast<v4u*>(h);
-      for (int i = threadIdx.x; i < 1024; i += 256) h4[i] = v4u{0u, 0u, 0u, 0u};
-    }
-  } else if (mode == PF_CAND) {
+    if (nm == PF_HIST || nm == PF_TIECOUNT) zero_hist();   // (resolve_digit has read h and synchronised)
+  } else if (mode == PF_CAND || mode == PF_GUESS) {
     // The bucket's keys as (key << 32 | ~position): descending order is
     // (score desc, position asc); the first `need` are taken.
     uint32_t n = st->cand_cnt;
-    if (n > (uint32_t)kPfCap) n = kPfCap;
-    const uint32_t need = st->need < n ? st->need : n;
     const uint32_t base = st->out_cnt;
+    uint32_t need = st->need;
+    if (mode == PF_GUESS) {
+      // The guess holds when the keys above the window are at most k_top,
+      // with the window's keys at least k_top, and every candidate was kept.
+      if (base > K || base + n < K || n > (uint32_t)kPfCap) {
+        restart();
+        zero_hist();
+        return;
+      }
+      need = K - base;
+    }
+    if (n > (uint32_t)kPfCap) n = kPfCap;
+    if (need > n) need = n;
     int P = 1;
     while (P < (int)n) P <<= 1;
     for (int i = threadIdx.x; i < P; i += 256) sbuf[i] = i < (int)n ? pf.cand[lr * kPfCap + i] : 0ull;
@@ -1120,6 +1221,15 @@ __global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf) {
   }
 }
 
+// A step flags whether it leaves a row undone (plain stores of 1: same-address
+// atomics from every workgroup cost more): the next pass and step return at
+// once when none is.
+__global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf, int pass) {
+  if (pass > 0 && pf.active[pass - 1] == 0u) return;   // (uniform)
+  pf_step_row(pf, pass);
+  if (threadIdx.x == 0 && pf.rows[blockIdx.x].mode != PF_DONE) pf.active[pass] = 1u;
+}
+
 // Each row's positions ascending (ids unique), scores from their keys, -1 /
 // -inf padding.  PMAX >= k_top.
 template <int PMAX, int NT>
@@ -1150,8 +1260,8 @@ hipError_t pf_clear(const PfArgs& pf, int64_t block_rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t pf_step(const PfArgs& pf, int64_t block_rows, hipStream_t s) {
-  CSA2_LAUNCH("pf_step", pf_step_kernel, dim3((unsigned)block_rows), dim3(256), 0, s, pf);
+hipError_t pf_step(const PfArgs& pf, int64_t block_rows, int pass, hipStream_t s) {
+  CSA2_LAUNCH("pf_step", pf_step_kernel, dim3((unsigned)block_rows), dim3(256), 0, s, pf, pass);
   return hipGetLastError();
 }
 

@@ -220,6 +220,23 @@ def test_prefill_selection_passes_under_heavy_ties(qmax, K):
 
 
 @gpu
+@pytest.mark.parametrize("D_I,H_I", [(128, 8), (256, 8)])
+def test_prefill_selection_guess_on_small_samples(D_I, H_I):
+    """Rows that see only a little more than K positions: the first pass's
+    sample holds a few dozen keys, the guessed window reaches down to the
+    lowest key, and every visible key not emitted becomes a candidate."""
+    require_gpu()
+    announce(f"index_score_topk prefill guess on small samples D_I={D_I}")
+    B, N, Tq, K = 1, 2000, 32, 512
+    k_idx = inputs.int_e4m3((B, N, D_I), 46, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 46, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 46, 1, "w", device="cuda")
+    ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
+    q_pos = (K + 5 * torch.arange(Tq, dtype=torch.int32, device="cuda"))[None, :].contiguous()
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos)
+
+
+@gpu
 def test_prefill_selection_takes_a_whole_bucket():
     """The K-th largest score's bucket is taken whole (the K selected keys are
     exactly the keys at or above one score value): every row has the same
