@@ -110,10 +110,11 @@ class StepTimer:
 
 # ------------------------------------------------------- counter traffic ---
 
-def counter_traffic(kernel, workload="decode64k"):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    FETCH_SIZE/WRITE_SIZE summary, or None when that summary is missing or the
-    kernel's sources have changed since the counters were taken."""
+def counter_traffic(kernel, workload="decode64k", key="traffic_bytes_per_launch"):
+    """HBM bytes per launch (or, key="traffic_bytes_per_step", per step) of
+    `kernel` on `workload` from the committed FETCH_SIZE/WRITE_SIZE summary,
+    or None when that summary is missing or the kernel's sources have changed
+    since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
@@ -130,7 +131,7 @@ def counter_traffic(kernel, workload="decode64k"):
                 h.update(fh.read())
         if h.hexdigest() != kv["kernel_source_sha256"]:
             return None
-        return int(kv["traffic_bytes_per_launch"])
+        return int(kv[key])
     except (KeyError, OSError, ValueError):
         return None
 
@@ -416,7 +417,10 @@ def main():
     prefill = wl.Tq >= 16         # (2..15 query rows per sequence: the multi-query scan)
     dom = "index_prefill" if prefill else "index_score"
     n_scan_layers = sum(1 for L in case.layers if L["kind"] in ("full", "reindex"))
-    with csa2.KernelTrace(capacity=4 * args.steps * max(1, len(wl.layers)), only=dom) as tr:
+    # (the bounded prefill selection scores in up to 8 passes per block of
+    # query rows: 64 launches per step leave room for them)
+    per_step = 64 if prefill else 4
+    with csa2.KernelTrace(capacity=per_step * args.steps * max(1, len(wl.layers)), only=dom) as tr:
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(args.steps):
@@ -433,15 +437,19 @@ def main():
     ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] +
                                                                    step_ms[len(step_ms) // 2])
     mean_ms = sum(step_ms) / len(step_ms)
+    if tr.count > tr.capacity:
+        raise RuntimeError(f"kernel trace holds {tr.capacity} launches, the timed steps made {tr.count}")
     dom_launches = [t for name, t in tr.durations_ms() if name == dom]
     tr.close()
     dom_ms = sum(dom_launches) / len(dom_launches) if dom_launches else float("nan")
     # Per-kernel breakdown from a separate traced pass (every launch bracketed).
     n_bd = min(args.steps, 5)
-    with csa2.KernelTrace(capacity=64 * n_bd * max(1, len(wl.layers))) as tr:
+    with csa2.KernelTrace(capacity=(256 if prefill else 64) * n_bd * max(1, len(wl.layers))) as tr:
         for _ in range(n_bd):
             case.step()
         torch.cuda.synchronize()
+    if tr.count > tr.capacity:
+        raise RuntimeError(f"kernel trace holds {tr.capacity} launches, the traced steps made {tr.count}")
     per_kernel = {}
     for name, t in tr.durations_ms():
         s = per_kernel.setdefault(name, [0.0, 0])
@@ -452,14 +460,22 @@ def main():
     step_bytes = case.step_bytes()
     gbps = step_bytes / (ms * 1e-3) / 1e9
     if prefill:
+        # The chunk's scoring is one product over its causal (query, key)
+        # pairs, run as one launch with stored keys or as the selection
+        # passes (two sampled, one full, and short ones for rows still open)
+        # with the bounded workspace: its time is the sum of the step's
+        # launches, its work the product counted once.
         base = wl.N - wl.Tq
         pairs = wl.B * (wl.Tq * base + wl.Tq * (wl.Tq + 1) // 2)     # causal (query, key) pairs
         flops = 2 * wl.H_I * wl.D_I * pairs
-        achieved = flops / (dom_ms * 1e-3) / 1e12
+        dom_step_ms = sum(dom_launches) / args.steps if dom_launches else float("nan")
+        achieved = flops / (dom_step_ms * 1e-3) / 1e12
+        wkey = "stored" if args.stored_keys else "passes"
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                "traffic": counter_traffic(dom, args.workload), "kernel": dom,
-                "kernel_ms": round(dom_ms, 5), "launches_per_step": n_scan_layers}
+                "traffic": counter_traffic(dom, f"{args.workload}_{wkey}", "traffic_bytes_per_step"),
+                "kernel": dom, "kernel_ms": round(dom_step_ms, 5),
+                "launches_per_step": round(len(dom_launches) / args.steps, 2), "selection": wkey}
     else:
         # one pass over the keys serves every query row of a sequence
         key = wl.D_I // 2 + wl.D_I // 32 if wl.mxfp4 else wl.D_I
