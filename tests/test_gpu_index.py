@@ -237,6 +237,25 @@ def test_prefill_selection_guess_on_small_samples(D_I, H_I):
 
 
 @gpu
+def test_prefill_selection_blocks_across_sequences():
+    """2,100 query rows select in two blocks of query tiles (at most 1,920
+    rows each), the block boundary inside the second sequence; every
+    sequence ends with a partial query tile, and the third has no visible
+    key at all (every index -1, every score -inf)."""
+    require_gpu()
+    announce("index_score_topk prefill blocks across sequences B=3 Tq=700 N=5000")
+    B, N, Tq, H_I, D_I, K = 3, 5000, 700, 8, 128, 300
+    k_idx = inputs.int_e4m3((B, N, D_I), 47, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 47, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 47, 1, "w", device="cuda")
+    ctx = torch.tensor([N, N - 300, 0], dtype=torch.int32, device="cuda")
+    base = torch.tensor([N - Tq, N - 300 - Tq, 0], dtype=torch.int64)
+    q_pos = (base[:, None] + torch.arange(Tq, dtype=torch.int64)[None, :]).to(torch.int32).cuda().contiguous()
+    res = _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos)
+    assert bool((res["topk_idx"][2] == -1).all())
+
+
+@gpu
 def test_prefill_selection_takes_a_whole_bucket():
     """The K-th largest score's bucket is taken whole (the K selected keys are
     exactly the keys at or above one score value): every row has the same
