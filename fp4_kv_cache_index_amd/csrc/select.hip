@@ -1015,12 +1015,73 @@ __device__ void pf_bitonic(uint64_t* a, int P, bool descending) {
     }
 }
 
+// Ascending bitonic sort of 2048 u64 values held 8 per thread (thread t:
+// elements 8t .. 8t+7) by 256 threads.  Each thread keeps its own elements
+// and takes the min or the max of every compare-exchange itself: partners
+// inside the thread in registers, partners in another lane of the wave
+// (distances 8 .. 256) by lane shuffles, partners in another wave
+// (distances 512 and 1024) through LDS (`lds`: 2048 words of 64 bits).
+__device__ __forceinline__ uint64_t pf_shfl_xor64(uint64_t x, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int J>
+__device__ __forceinline__ void pf_sort_inthread(uint64_t (&v)[8], int k, int t) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e & J) continue;
+    const uint64_t a = v[e], b = v[e | J];
+    const bool up = ((8 * t + e) & k) == 0;
+    const uint64_t lo = a < b ? a : b, hi = a < b ? b : a;
+    v[e] = up ? lo : hi;
+    v[e | J] = up ? hi : lo;
+  }
+}
+__device__ void pf_sort2048(uint64_t (&v)[8], uint64_t* lds) {
+  const int t = threadIdx.x;
+  for (int k = 2; k <= 2048; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 512) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lds[8 * t + e] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * t + e;
+          const uint64_t o = lds[i ^ j];
+          const bool keep_min = (((i & k) == 0) == ((i & j) == 0));
+          v[e] = keep_min ? (v[e] < o ? v[e] : o) : (v[e] < o ? o : v[e]);
+        }
+        __syncthreads();
+      } else if (j >= 8) {
+        const int m = j >> 3;
+        const bool lower = (t & m) == 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint64_t o = pf_shfl_xor64(v[e], m);
+          const bool keep_min = ((((8 * t + e) & k) == 0) == lower);
+          v[e] = keep_min ? (v[e] < o ? v[e] : o) : (v[e] < o ? o : v[e]);
+        }
+      } else if (j == 4) {
+        pf_sort_inthread<4>(v, k, t);
+      } else if (j == 2) {
+        pf_sort_inthread<2>(v, k, t);
+      } else {
+        pf_sort_inthread<1>(v, k, t);
+      }
+    }
+  }
+}
+
 // After a pass, per row: resolve the digit of a histogram pass, pick the
 // next mode; select the candidates of a candidate pass; prefix the tie
 // counts of a tie-count pass.
 __device__ __forceinline__ void pf_step_row(const PfArgs& pf, int pass) {
   __shared__ uint32_t red[4];
   __shared__ uint32_t res[4];
+  // (32 KB: four workgroups per compute unit; with 16 KB and eight the
+  // candidate step measured 1.6 times slower)
   __shared__ __align__(16) uint64_t sbuf[kPfCap];
   const int64_t lr = blockIdx.x;
   PfRow* st = pf.rows + lr;
@@ -1179,18 +1240,30 @@ __device__ __forceinline__ void pf_step_row(const PfArgs& pf, int pass) {
     }
     if (n > (uint32_t)kPfCap) n = kPfCap;
     if (need > n) need = n;
-    int P = 1;
-    while (P < (int)n) P <<= 1;
-    for (int i = threadIdx.x; i < P; i += 256) sbuf[i] = i < (int)n ? pf.cand[lr * kPfCap + i] : 0ull;
-    __syncthreads();
-    pf_bitonic<256>(sbuf, P, true);
-    for (uint32_t i = threadIdx.x; i < need; i += 256) {
-      const uint64_t v = sbuf[i];
+    auto take = [&](uint32_t i, uint64_t v) {   // i-th largest candidate
       const uint32_t slot = base + i;
-      if (slot < K) {
+      if (i < need && slot < K) {
         pf.out_idx[grow * K + slot] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
         if (pf.out_key) pf.out_key[grow * K + slot] = (uint32_t)(v >> 32);
       }
+    };
+    if (n <= 2048u) {
+      // complements sorted ascending: the largest candidates first (padding
+      // ~0 last); loaded in any order (coalesced), sorted into thread order
+      uint64_t v[8];
+      const uint64_t* cp = pf.cand + lr * kPfCap + threadIdx.x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = threadIdx.x + 256u * e < n ? ~cp[256 * e] : ~0ull;
+      pf_sort2048(v, sbuf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) take(8u * threadIdx.x + e, ~v[e]);
+    } else {
+      int P = 1;
+      while (P < (int)n) P <<= 1;
+      for (int i = threadIdx.x; i < P; i += 256) sbuf[i] = i < (int)n ? pf.cand[lr * kPfCap + i] : 0ull;
+      __syncthreads();
+      pf_bitonic<256>(sbuf, P, true);
+      for (uint32_t i = threadIdx.x; i < need; i += 256) take(i, sbuf[i]);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1240,6 +1313,27 @@ __global__ void __launch_bounds__(NT) pf_final_kernel(PfArgs pf, float* __restri
   const int K = pf.k_top;
   uint32_t n = pf.rows[lr].out_cnt;
   if (n > (uint32_t)K) n = K;
+  if constexpr (PMAX == 2048 && NT == 256) {
+    // (position << 32 | key) sorted in registers; padding ~0 last
+    const int32_t* oi = pf.out_idx + grow * K;
+    const uint32_t* ok = pf.out_key ? pf.out_key + grow * K : nullptr;
+    uint64_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {   // (any order in: coalesced loads)
+      const uint32_t i = threadIdx.x + 256u * e;
+      v[e] = i < n ? ((uint64_t)(uint32_t)oi[i] << 32) | (ok ? ok[i] : 0u) : ~0ull;
+    }
+    pf_sort2048(v, sbuf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * (int)threadIdx.x + e;
+      if (i >= K) continue;
+      const bool val = i < (int)n;
+      pf.out_idx[grow * K + i] = val ? (int32_t)(v[e] >> 32) : -1;
+      if (topk_score) topk_score[grow * K + i] = val ? key_score((uint32_t)v[e]) : -__builtin_inff();
+    }
+    return;
+  }
   int P = 1;
   while (P < (int)n) P <<= 1;
   const int32_t* oi = pf.out_idx + grow * K;

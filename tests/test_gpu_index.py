@@ -256,6 +256,26 @@ def test_prefill_selection_blocks_across_sequences():
 
 
 @gpu
+def test_prefill_selection_sorts_many_candidates():
+    """About half of the keys score exactly 0 (keys in {-1, 0, 1}, a query
+    of ones, unit weights) and K falls inside them: the candidates at the
+    threshold number between 2,048 and 4,096, past the register sort, and the
+    lowest positions among the ties are taken."""
+    require_gpu()
+    announce("index_score_topk prefill with 2048..4096 candidates")
+    B, N, Tq, H_I, D_I, K = 1, 6000, 32, 8, 128, 3500
+    k_idx = inputs.int_e4m3((B, N, D_I), 48, 0, "k_idx", lo=-1, hi=1, device="cuda")
+    q_idx = torch.full((B, Tq, H_I, D_I), 0x38, dtype=torch.uint8, device="cuda")   # E4M3 1.0
+    w = torch.ones((B, Tq, H_I), dtype=torch.float32, device="cuda")
+    ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
+    q_pos = torch.full((B, Tq), N - 1, dtype=torch.int32, device="cuda")
+    sc = I.index_scores(np_(q_idx)[0, 0], np_(w)[0, 0], np_(k_idx)[0], N)
+    zeros = int(np.sum(sc == 0.0))
+    assert 2048 < zeros <= 4096 and int(np.sum(sc > 0.0)) < K < int(np.sum(sc >= 0.0))
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos)
+
+
+@gpu
 def test_prefill_selection_takes_a_whole_bucket():
     """The K-th largest score's bucket is taken whole (the K selected keys are
     exactly the keys at or above one score value): every row has the same
