@@ -156,14 +156,15 @@ int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_
  *     per-tile histograms (csa2_index_score_topk_workspace_size_stored();
  *     13.4 GB for 4096 queries on 266,240 tokens), used whenever ws_bytes
  *     reaches that size: one scoring pass;
- *   - otherwise no stored keys, as the indexer-selected sparse attention of
- *     the techniques map expects of a prefill chunk: a scoring pass builds each
- *     row's histogram of the top 12 key bits, a second one emits the keys
- *     above the threshold bucket and collects the bucket itself, further
- *     passes run only for rows whose bucket holds more than 4096 keys (ties
- *     at one score included).  Query rows go in blocks of at most 1920; the
- *     workspace stays under 100 MB (10^8 bytes) for chunks up to 65,535
- *     query rows and 4M positions.
+ *   - otherwise no score matrix at all: two passes over one 16-key chunk
+ *     in eight histogram a sample of the scores and place each
+ *     row's threshold in a narrow window, a full scoring pass emits the keys
+ *     above the window and collects those inside it, and rows whose counts
+ *     do not confirm the window (heavy ties, for instance) search exactly
+ *     in further passes (radix digits of 12, 12 and 8 bits, then tie counts
+ *     and tie emission in position order).  Query rows go in blocks of at
+ *     most 1920; the workspace stays under 100 MB (10^8 bytes) for chunks
+ *     up to 65,535 query rows and 4M positions.
  * csa2_index_score_topk_workspace_size() is the smaller of the two for such
  * chunks and the stored size for every other call.
  */
