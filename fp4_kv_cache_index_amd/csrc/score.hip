@@ -1069,14 +1069,19 @@ __device__ __forceinline__ void load_k128(uint32_t (&f)[DI / 16], const uint8_t*
   }
 }
 
-template <int DI, int HG, int QG, int PFM>
+// F4: MXFP4 keys as the B operand, as in the decode scan: lane (key c16,
+// group g) takes bytes 16g .. 16g+15 of the key's code row (channels 32g ..
+// 32g+31) and scale byte g; the E4M3 query fragments keep their pairing.
+template <int DI, int HG, int QG, int PFM, bool F4>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, int64_t k_bstride, int64_t k_rstride,
+                     const uint8_t* __restrict__ k_scales, int64_t ks_bstride, int64_t ks_rstride,
                      const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos,
                      int Tq, int H_I, int64_t n_max, int key_tile, int qtiles,
                      uint32_t* __restrict__ keys, int64_t key_stride, int32_t* __restrict__ n_valid_out,
                      SelectWs tok, PfArgs pf, int64_t y0) {
+  static_assert(!F4 || DI == 128, "MXFP4 keys: 128 channels");
   constexpr int KS = DI / 128;          // MFMA k-steps
   constexpr int FW = DI / 16;           // fragment words per lane
   constexpr int QW = 4 * QG;            // queries per workgroup
@@ -1173,19 +1178,29 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
   }
 
   const uint8_t* kb = k_idx + b * k_bstride;
+  const uint8_t* ksb = F4 ? k_scales + b * ks_bstride : nullptr;
   const int nchunks = (int)((k1 - k0 + 15) >> 4);
   uint32_t fa[FW], fb[FW];
   auto load_chunk = [&](uint32_t (&f)[FW], int c) {
     const int64_t j = k0 + 16 * (int64_t)c + c16;
-    load_k128<DI>(f, kb + (j < k1 ? j : k0) * k_rstride, g, j < k1);
+    if constexpr (F4) {
+      // (keys past the tile read its first row: their scores are masked)
+      const int64_t jj = j < k1 ? j : k0;
+      const v4u v = *reinterpret_cast<const v4u*>(kb + jj * k_rstride + 16 * g);
+      f[0] = v[0]; f[1] = v[1]; f[2] = v[2]; f[3] = v[3];
+      f[4] = ksb[jj * ks_rstride + g];   // the E8M0 scale of this lane's 32 channels
+    } else {
+      load_k128<DI>(f, kb + (j < k1 ? j : k0) * k_rstride, g, j < k1);
+    }
   };
   auto score_chunk = [&](const uint32_t (&f)[FW], int c) {
     const int64_t j = k0 + 16 * (int64_t)c + c16;
     v8i kf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = v8i{(int)f[8 * ks], (int)f[8 * ks + 1], (int)f[8 * ks + 2], (int)f[8 * ks + 3],
-                   (int)f[8 * ks + 4], (int)f[8 * ks + 5], (int)f[8 * ks + 6], (int)f[8 * ks + 7]};
+      kf[ks] = F4 ? v8i{(int)f[0], (int)f[1], (int)f[2], (int)f[3], 0, 0, 0, 0}
+                  : v8i{(int)f[8 * ks], (int)f[8 * ks + 1], (int)f[8 * ks + 2], (int)f[8 * ks + 3],
+                        (int)f[8 * ks + 4], (int)f[8 * ks + 5], (int)f[8 * ks + 6], (int)f[8 * ks + 7]};
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
       v4f acc[HG];
@@ -1193,9 +1208,14 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
       for (int hg = 0; hg < HG; ++hg) {
         acc[hg] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[qg][hg][ks], kf[ks], acc[hg], 0, 0, 0, 127,
-                                                                     0, 127);
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (F4)
+            acc[hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[qg][hg][ks], kf[ks], acc[hg], 0 /* A E4M3 */,
+                                                                       4 /* B E2M1 */, 0, 127, 0, (int)f[4]);
+          else
+            acc[hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[qg][hg][ks], kf[ks], acc[hg], 0, 0, 0, 127,
+                                                                       0, 127);
+        }
       }
       // acc[hg][i] = dot(query 4qg + g, head 4hg + i; key j)
       float sc = 0.0f;
@@ -1591,15 +1611,15 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
   int64_t tiles = (a.n_max + key_tile - 1) / key_tile;
   if (tiles < 1) tiles = 1;
   if (qrows > 65535 || (pf && tiles > 4096)) return hipErrorInvalidValue;
-  if (a.k_scales && !kt) return hipErrorInvalidValue;   // (MXFP4 prefill chunks: D_I = 128 and at most 8 heads)
+  if (a.k_scales && DI != 128) return hipErrorInvalidValue;   // (MXFP4 keys: 128 channels)
   const dim3 grid((unsigned)tiles, (unsigned)qrows), block(64 * kPrefillWaves);
   PfArgs pfa = pf ? *pf : PfArgs{};
   pfa.pass = pass;
   const uint8_t* ks = a.k_scales;
 #define KT_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, ks, a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos, \
                 a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok, pfa, y0
-#define GEN_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, a.ctx_len, a.q_pos, a.Tq, a.H_I, a.n_max, key_tile, \
-                 qtiles, keys, key_stride, n_valid, tok, pfa, y0
+#define GEN_ARGS a.q_idx, a.w, a.k_idx, a.k_bstride, a.k_rstride, ks, a.ks_bstride, a.ks_rstride, a.ctx_len, a.q_pos, \
+                 a.Tq, a.H_I, a.n_max, key_tile, qtiles, keys, key_stride, n_valid, tok, pfa, y0
   if (kt) {
     if (a.k_scales) {
       if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, true, 0>), grid, block, 0, s, KT_ARGS);
@@ -1610,10 +1630,16 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
       else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false, 1>), grid, block, 0, s, KT_ARGS);
       else CSA2_LAUNCH("index_prefill", (index_prefill_kt_kernel<3, false, 2>), grid, block, 0, s, KT_ARGS);
     }
+  } else if (a.k_scales) {
+    if constexpr (DI == 128) {
+      if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 0, true>), grid, block, 0, s, GEN_ARGS);
+      else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 1, true>), grid, block, 0, s, GEN_ARGS);
+      else CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 2, true>), grid, block, 0, s, GEN_ARGS);
+    }
   } else {
-    if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 0>), grid, block, 0, s, GEN_ARGS);
-    else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 1>), grid, block, 0, s, GEN_ARGS);
-    else CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 2>), grid, block, 0, s, GEN_ARGS);
+    if (pfm == 0) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 0, false>), grid, block, 0, s, GEN_ARGS);
+    else if (pfm == 1) CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 1, false>), grid, block, 0, s, GEN_ARGS);
+    else CSA2_LAUNCH("index_prefill", (index_prefill_kernel<DI, HG, QG, 2, false>), grid, block, 0, s, GEN_ARGS);
   }
 #undef KT_ARGS
 #undef GEN_ARGS
@@ -1621,7 +1647,7 @@ static hipError_t launch_prefill_t(const ScoreArgs& a, uint32_t* keys, int64_t k
 }
 
 bool prefill_gemm_applies(const ScoreArgs& a) {
-  if (a.k_scales) return a.Tq >= 16 && a.pool_block == 0 && a.D_I == 128 && a.H_I <= 8;
+  if (a.k_scales) return a.Tq >= 16 && a.pool_block == 0 && a.D_I == 128 && a.H_I <= 32;
   return a.Tq >= 16 && a.pool_block == 0 && (a.D_I == 128 || a.D_I == 256) && a.H_I <= 32;
 }
 

@@ -132,17 +132,20 @@ def test_mxfp4_prefill_chunk():
 
 
 @gpu
-def test_mxfp4_prefill_chunk_wide_heads():
-    """An MXFP4 prefill chunk with 32 indexer heads (in the default workspace
-    row scans a few query rows at a time; stored keys)."""
+@pytest.mark.parametrize("H_I", [13, 32])
+def test_mxfp4_prefill_chunk_wide_heads(H_I):
+    """MXFP4 prefill chunks with more than 8 indexer heads (the pages' 32 x
+    128 shape; 13: padded head groups) on the query-major matrix-core
+    product, with the selection passes and with stored keys."""
     require_gpu()
-    announce("mxfp4 prefill chunk H_I=32 Tq=20 on 12000 keys")
-    B, N, Tq, H_I, K = 1, 12000, 20, 32, 512
+    announce(f"mxfp4 prefill chunk H_I={H_I} Tq=20 on 12000 keys")
+    B, N, Tq, K = 1, 12000, 20, 512
     kc, ks = _mx_keys(B, N, 95)
     q = inputs.int_e4m3((B, Tq, H_I, 128), 95, 1, "q_idx", device="cuda")
     w = inputs.normal_f32((B, Tq, H_I), 95, 1, "w", device="cuda")
     ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
     q_pos = (N - Tq + torch.arange(Tq, device="cuda")[None, :]).to(torch.int32).contiguous()
+    q_pos[0, :2] = torch.tensor([3, 600], dtype=torch.int32, device="cuda")
     _run(q, w, kc, ks, ctx, K, q_pos=q_pos)
     _run(q, w, kc, ks, ctx, K, q_pos=q_pos, stored=True)
 
