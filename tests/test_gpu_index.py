@@ -174,7 +174,8 @@ def test_causal_rows_with_q_pos():
 @gpu
 @pytest.mark.parametrize("stored", [False, True], ids=["passes", "stored_keys"])
 @pytest.mark.parametrize("H_I,D_I,Tq,K", [(8, 128, 40, 512), (3, 128, 17, 100), (32, 128, 20, 300),
-                                         (8, 256, 33, 256), (13, 256, 16, 64), (8, 128, 70, 2048)])
+                                         (8, 256, 33, 256), (13, 256, 16, 64), (8, 128, 70, 2048),
+                                         (8, 128, 24, 8192)])
 def test_prefill_chunk_dense_scoring(H_I, D_I, Tq, K, stored):
     """Chunks of 16 or more queries per sequence take the matrix-core product
     path; causal positions, a context shorter than some positions, a partial
