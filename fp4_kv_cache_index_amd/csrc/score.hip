@@ -747,12 +747,9 @@ constexpr int kPrefillWaves = 8;
 // undecided bucket [b_lo, b_hi] (empty when the pass takes it whole).
 struct PfLane {
   uint32_t mode, n_ps, n_pfx, e_lo, e_hi, b_lo, b_hi;
-  // Scores whose keys may lie in either range: [f_lo, f_hi] (a superset in
-  // float order, so that the key need not be formed for every score).
-  float f_lo, f_hi;
 };
 __device__ __forceinline__ PfLane pf_load(const PfArgs& pf, int64_t grow, bool ok) {
-  PfLane L{PF_DONE, 32u, 0u, 1u, 0u, 1u, 0u, __builtin_inff(), -__builtin_inff()};   // (empty ranges)
+  PfLane L{PF_DONE, 32u, 0u, 1u, 0u, 1u, 0u};   // (empty ranges)
   if (ok && pf.rows[grow - pf.row_base].mode == PF_GUESS) {
     // the guessed window: candidates in [g_cand, g_emit), emitted above
     const PfRow& r = pf.rows[grow - pf.row_base];
@@ -765,12 +762,6 @@ __device__ __forceinline__ PfLane pf_load(const PfArgs& pf, int64_t grow, bool o
     if (r.g_emit_none || r.g_emit > r.g_cand) {
       L.b_lo = r.g_cand;
       L.b_hi = chi;
-    }
-    const uint32_t ulo = L.b_lo <= L.b_hi ? L.b_lo : L.e_lo;
-    const uint32_t uhi = L.e_lo <= L.e_hi ? L.e_hi : L.b_hi;
-    if (ulo <= uhi) {
-      L.f_lo = ulo <= 0x007FFFFFu ? -__builtin_inff() : key_score(ulo);
-      L.f_hi = uhi >= 0xFF800000u ? __builtin_inff() : key_score(uhi);
     }
   } else if (ok && pf.rows[grow - pf.row_base].mode != PF_DONE) {
     const PfRow& r = pf.rows[grow - pf.row_base];
@@ -793,14 +784,6 @@ __device__ __forceinline__ PfLane pf_load(const PfArgs& pf, int64_t grow, bool o
         L.e_lo = (uint32_t)plo;
         L.e_hi = (uint32_t)phi;
       }
-    }
-    // the two ranges are adjacent: their union's bounds as scores (keys at
-    // or below that of -inf, or at or above that of +inf, bound nothing)
-    const uint32_t ulo = L.b_lo <= L.b_hi ? L.b_lo : L.e_lo;
-    const uint32_t uhi = L.e_lo <= L.e_hi ? L.e_hi : L.b_hi;
-    if (ulo <= uhi) {
-      L.f_lo = ulo <= 0x007FFFFFu ? -__builtin_inff() : key_score(ulo);
-      L.f_hi = uhi >= 0xFF800000u ? __builtin_inff() : key_score(uhi);
     }
   }
   return L;
@@ -1448,7 +1431,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
     const int j0 = ik0 + 16 * c + 4 * g;
     uint32_t kk[4];
     uint32_t em = 0u, bm = 0u;   // PF: keys to emit / in the undecided bucket
-    uint32_t pm = 0u;            // PF: keys passing the score prefilter
+    uint32_t pm = 0u;            // PF: visible keys
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float sc = 0.0f;
@@ -1466,7 +1449,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       const bool vis = j0 + r < nvq;
       if constexpr (PF) {
         kk[r] = key;
-        pm |= (vis && sc >= pl.f_lo && sc <= pl.f_hi ? 1u : 0u) << r;
+        pm |= (vis ? 1u : 0u) << r;
       } else if constexpr (PFM == 1) {
         // (most keys of the fine sample pass lie below the range: skipped,
         // not sent to one shared word)
@@ -1483,44 +1466,51 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
       if (tok_q) *reinterpret_cast<v4u*>(krow + j0) = v4u{kk[0], kk[1], kk[2], kk[3]};
     }
     if constexpr (PF) {
-      if (pm) {
+      // (branch-free: the exact key ranges on every visible key; a score
+      // prefilter that skipped the ranges paid more in branches than it saved)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (!(pm & (1u << r))) continue;
-          em |= (kk[r] >= pl.e_lo && kk[r] <= pl.e_hi ? 1u : 0u) << r;
-          bm |= (kk[r] >= pl.b_lo && kk[r] <= pl.b_hi ? 1u : 0u) << r;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const bool in = (pm >> r) & 1u;
+        em |= (in && kk[r] >= pl.e_lo && kk[r] <= pl.e_hi ? 1u : 0u) << r;
+        bm |= (in && kk[r] >= pl.b_lo && kk[r] <= pl.b_hi ? 1u : 0u) << r;
       }
-      if (em) {
-        if constexpr (ST) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (em & (1u << r)) pf_lane_put2(hist, hist + kPoolOff, &pool_cnt, &spill, 0, c16, lane_ne, j0 + r, kk[r]);
-        } else {
+      if constexpr (ST) {
+        // (a staged tile holds no histogram or tie-emission row) One put
+        // per selected key, in a loop over the lane's set bits: the wave
+        // runs it as often as its busiest lane needs (mostly once), not once
+        // per key slot and kind.
+        if (bm && pl.mode == PF_TIECOUNT) atomicAdd(&tcnt[c16], (uint32_t)__builtin_popcount(bm));
+        uint32_t sel = em | (pl.mode == PF_CAND ? bm : 0u);
+        while (sel) {
+          const int r = __builtin_ctz(sel);
+          sel &= sel - 1u;
+          const uint32_t k = r == 0 ? kk[0] : (r == 1 ? kk[1] : (r == 2 ? kk[2] : kk[3]));
+          const uint32_t kind = (em >> r) & 1u ? 0u : 1u;
+          uint32_t n = kind ? lane_nc : lane_ne;
+          pf_lane_put2(hist, hist + kPoolOff, &pool_cnt, &spill, (int)kind, c16, n, j0 + r, k);
+          if (kind) lane_nc = n;
+          else lane_ne = n;
+        }
+      } else {
+        if (em) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (em & (1u << r)) pf_emit(pf, row0 + c16, j0 + r, kk[r]);
         }
-      }
-      if (bm) {
-        if (pl.mode == PF_HIST) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (bm & (1u << r)) atomicAdd(&hist[hbase + pf_digit(kk[r], pl.n_ps)], add);
-        } else if (pl.mode == PF_CAND) {
-          if constexpr (ST) {
+        if (bm) {
+          if (pl.mode == PF_HIST) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (bm & (1u << r)) pf_lane_put2(hist, hist + kPoolOff, &pool_cnt, &spill, 1, c16, lane_nc, j0 + r, kk[r]);
-          } else {
+              if (bm & (1u << r)) atomicAdd(&hist[hbase + pf_digit(kk[r], pl.n_ps)], add);
+          } else if (pl.mode == PF_CAND) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               if (bm & (1u << r)) pf_cand(pf, row0 + c16, j0 + r, kk[r]);
+          } else if (pl.mode == PF_TIECOUNT) {
+            atomicAdd(&tcnt[c16], (uint32_t)__builtin_popcount(bm));
+          } else if (pl.mode == PF_TIEEMIT) {
+            atomicOr(&hist[c * QW + c16], bm << (4 * g));
           }
-        } else if (pl.mode == PF_TIECOUNT) {
-          atomicAdd(&tcnt[c16], (uint32_t)__builtin_popcount(bm));
-        } else if (pl.mode == PF_TIEEMIT) {
-          atomicOr(&hist[c * QW + c16], bm << (4 * g));
         }
       }
     }
