@@ -238,3 +238,36 @@ def test_enc128k_full_and_five_reuse_layers():
             want_o, want_l = _oracle_decode_attn(wl, b, np_(L["q"][b, 0]), got, np_(L["swa_x"][b]))
             o, l = outs[li]
             _check_attn(np_(o[b]), np_(l[b]), want_o, want_l)
+
+
+@gpu
+def test_pages_prefill_mxfp4_32_heads_sampled_queries():
+    """The pages' indexer shape in a prefill chunk: 32 MXFP4 heads x 128,
+    top-512, 4096 causal queries on 266,240 tokens (the query-major FP4
+    matrix-core product).  Query rows 0, 1, 2047 and 4095 against the
+    oracle; the selection passes and the stored-key selection agree on every
+    row."""
+    require_gpu()
+    announce("pages' prefill: 32 MXFP4 heads, 4096 queries on 266,240 tokens, top-512")
+    B, Tq, N, H_I, K = 1, 4096, 266240, 32, 512
+    dev = torch.device("cuda")
+    codes, scales = csa2.idx_mxfp4_quantize(inputs.idx_key_rows((N, 128), 4242, device=dev))
+    codes, scales = codes[None].contiguous(), scales[None].contiguous()
+    q = inputs.int_e4m3((B, Tq, H_I, 128), 4242, 1, "q_idx", device=dev)
+    w = inputs.normal_f32((B, Tq, H_I), 4242, 1, "w", device=dev)
+    ctx = torch.full((B,), N, dtype=torch.int32, device=dev)
+    q_pos = (torch.arange(Tq, dtype=torch.int32, device=dev) + N - Tq)[None].contiguous()
+    res = csa2.csa2_index_score_topk_mxfp4(q, w, codes, scales, ctx, K, q_pos=q_pos, want_scores=True)
+    sto = csa2.csa2_index_score_topk_mxfp4(q, w, codes, scales, ctx, K, q_pos=q_pos, stored_keys=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sto["topk_idx"], res["topk_idx"])
+    del sto
+    torch.cuda.empty_cache()
+    got_i, got_s = np_(res["topk_idx"])[0], np_(res["topk_score"])[0]
+    ch, sh, qh, wh, ph = np_(codes)[0], np_(scales)[0], np_(q)[0], np_(w)[0], np_(q_pos)[0]
+    for t in (0, 1, Tq // 2 - 1, Tq - 1):
+        nv = I.visible_count(N, int(ph[t]))
+        s = I.index_scores_mxfp4(qh[t], wh[t], ch, sh, nv)
+        want_i, want_s = topk_select(s, nv, K)
+        assert np.array_equal(got_i[t], want_i), t
+        assert np.array_equal(got_s[t], want_s), t
