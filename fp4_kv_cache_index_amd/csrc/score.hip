@@ -998,7 +998,7 @@ __device__ void pf_flush_hist(const PfArgs& pf, const uint32_t* hist, int64_t ro
 // queries per word) or, for tie emission, nchunks x QW masks of 16 bits.
 template <int QW, int NT>
 __device__ void pf_finish(const PfArgs& pf, const PfLane* pfl, uint32_t flags, const uint32_t* hist,
-                          const uint32_t* tcnt, int64_t row0, int Tq, int t0, int64_t k0, int nchunks) {
+                          const uint32_t* tcnt, int64_t row0, int Tq, int t0, int kx, int64_t k0, int nchunks) {
   if (flags & (1u << PF_HIST)) {
     for (int i = threadIdx.x; i < (QW / 2) * 4096; i += NT) {
       const uint32_t v = hist[i];
@@ -1015,10 +1015,10 @@ __device__ void pf_finish(const PfArgs& pf, const PfLane* pfl, uint32_t flags, c
   if (threadIdx.x < QW && t0 + (int)threadIdx.x < Tq) {
     const int ql = threadIdx.x;
     const int64_t lrow = row0 + ql - pf.row_base;
-    if (pfl[ql].mode == PF_TIECOUNT && tcnt[ql]) atomic_add_agent(pf.hist + lrow * 4096 + blockIdx.x, tcnt[ql]);
+    if (pfl[ql].mode == PF_TIECOUNT && tcnt[ql]) atomic_add_agent(pf.hist + lrow * 4096 + kx, tcnt[ql]);
     if (pfl[ql].mode == PF_TIEEMIT) {
       // ties of earlier key tiles (exclusive prefix by the step kernel)
-      const uint32_t base = pf.hist[lrow * 4096 + blockIdx.x];
+      const uint32_t base = pf.hist[lrow * 4096 + kx];
       const uint32_t need = pf.rows[lrow].need;
       uint32_t cnt = 0;
       for (int c = 0; c < nchunks && base + cnt < need; ++c) {
@@ -1031,6 +1031,31 @@ __device__ void pf_finish(const PfArgs& pf, const PfLane* pfl, uint32_t flags, c
         }
       }
     }
+  }
+}
+
+// (key tile, query tile) of a prefill workgroup.  XO: workgroups are dealt
+// round-robin over the 8 XCDs in launch order (workgroup i on XCD i mod 8),
+// and each XCD is given a contiguous run of the pairs, query tile fastest, so
+// that the workgroups resident on one XCD at a time score the same key tile
+// for different queries and find it in that XCD's L2.  Measured: the
+// four-query tiles of wide indexers (which read every key again for each
+// four queries) gain from it on their full passes; the sixteen-query tiles
+// of the transposed product and the sample passes (few, long key tiles,
+// whose short last tile then falls to one XCD) ran slower, and keep the
+// launch order (key tile fastest).
+template <bool XO>
+__device__ __forceinline__ void prefill_tile(int& kx, int64_t& qy) {
+  if constexpr (!XO) {
+    kx = blockIdx.x;
+    qy = blockIdx.y;
+  } else {
+    const uint32_t ny = gridDim.y, nwg = gridDim.x * ny;   // (< 2^28: at most 4096 x 65535)
+    const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const uint32_t x = lin & 7u, per = nwg >> 3, rem = nwg & 7u;
+    const uint32_t pr = x * per + (x < rem ? x : rem) + (lin >> 3);
+    kx = (int)(pr / ny);
+    qy = pr - (uint32_t)kx * ny;
   }
 }
 
@@ -1081,13 +1106,16 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int64_t yy = (int64_t)blockIdx.y + y0;
-  const int64_t b = yy / qtiles;
-  const int t0 = (int)(yy % qtiles) * QW;
-  const int64_t row0 = b * Tq + t0;
   if constexpr (PF) {
     if (pf.active[pf.pass - 1] == 0u) return;   // (uniform: every row of the block done)
   }
+  int kx;
+  int64_t qy;
+  prefill_tile<PFM != 1 && QG == 1>(kx, qy);
+  const int64_t yy = qy + y0;
+  const int64_t b = yy / qtiles;
+  const int t0 = (int)(yy % qtiles) * QW;
+  const int64_t row0 = b * Tq + t0;
 
   if (threadIdx.x < QW) {
     const int t = t0 + threadIdx.x;
@@ -1099,7 +1127,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
         if (qp < nv) nv = qp;
       }
       nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-      if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
+      if (kx == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
     }
     nvs[threadIdx.x] = (int32_t)nv;
     if constexpr (PFM == 1) pf_sample_range(pf, row0 + threadIdx.x, t < Tq, shb[threadIdx.x], shs[threadIdx.x]);
@@ -1127,7 +1155,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
   int max_nv = 0;
 #pragma unroll
   for (int i = 0; i < QW; ++i) max_nv = nvs[i] > max_nv ? nvs[i] : max_nv;
-  const int64_t k0 = (int64_t)blockIdx.x * key_tile;
+  const int64_t k0 = (int64_t)kx * key_tile;
   int64_t k1 = k0 + key_tile;
   if (k1 > max_nv) k1 = max_nv;
   if (k0 >= k1) return;   // uniform: nothing visible in this tile
@@ -1254,7 +1282,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
     // (staging excludes histogram and tie-emission rows; tie counts are
     // flushed either way)
     if (stage) pf_unstage<QW, NT>(pf, hist, scnt, sbase, row0, Tq, t0);
-    pf_finish<QW, NT>(pf, pfl, flags, hist, tcnt, row0, Tq, t0, k0, nchunks);
+    pf_finish<QW, NT>(pf, pfl, flags, hist, tcnt, row0, Tq, t0, kx, k0, nchunks);
     return;
   }
   if constexpr (PFM == 1) {
@@ -1281,7 +1309,7 @@ index_prefill_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict_
 // c16's code row (channels 32g .. 32g+31) and passes that block's scale byte.
 // PFM: 0 = score keys stored for the radix select; 1 = the level-1
 // histogram pass of the prefill selection (no keys stored); 2 = a later
-// selection pass steered by each row's PfRow; query tiles y0 + blockIdx.y.
+// selection pass steered by each row's PfRow; query tiles from y0 on.
 template <int PD, bool F4, int PFM>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -1307,13 +1335,16 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int64_t yy = (int64_t)blockIdx.y + y0;
-  const int64_t b = yy / qtiles;
-  const int t0 = (int)(yy % qtiles) * QW;
-  const int64_t row0 = b * Tq + t0;
   if constexpr (PF) {
     if (pf.active[pf.pass - 1] == 0u) return;   // (uniform: every row of the block done)
   }
+  int kx;
+  int64_t qy;
+  prefill_tile<false>(kx, qy);
+  const int64_t yy = qy + y0;
+  const int64_t b = yy / qtiles;
+  const int t0 = (int)(yy % qtiles) * QW;
+  const int64_t row0 = b * Tq + t0;
 
   if (threadIdx.x < QW) {
     const int t = t0 + threadIdx.x;
@@ -1325,7 +1356,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
         if (qp < nv) nv = qp;
       }
       nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
-      if (blockIdx.x == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
+      if (kx == 0) n_valid_out[row0 + threadIdx.x] = (int32_t)nv;
     }
     nvs[threadIdx.x] = (int32_t)nv;
     if constexpr (PFM == 1) pf_sample_range(pf, row0 + threadIdx.x, t < Tq, shb[threadIdx.x], shs[threadIdx.x]);
@@ -1357,7 +1388,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   int max_nv = 0;
 #pragma unroll
   for (int i = 0; i < QW; ++i) max_nv = nvs[i] > max_nv ? nvs[i] : max_nv;
-  const int64_t k0 = (int64_t)blockIdx.x * key_tile;
+  const int64_t k0 = (int64_t)kx * key_tile;
   int64_t k1 = k0 + key_tile;
   if (k1 > max_nv) k1 = max_nv;
   if (k0 >= k1) return;   // uniform: nothing visible in this tile
@@ -1556,7 +1587,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
         else pf_emit(pf, row0 + ql, pool[3 * i], pool[3 * i + 1]);
       }
     }
-    pf_finish<QW, NT>(pf, pfl, flags, hist, tcnt, row0, Tq, t0, k0, nchunks);
+    pf_finish<QW, NT>(pf, pfl, flags, hist, tcnt, row0, Tq, t0, kx, k0, nchunks);
     return;
   }
   if constexpr (PFM == 1) {
