@@ -1333,7 +1333,7 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   constexpr int kPoolOff = kPrefillWaves * 64 * 2 * kPfLane * 2 + 4 * kPrefillWaves * 64;
   static_assert(kPoolOff + 3 * kPfPool <= (QW / 2) * 4096, "staging fits the histogram space");
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g = lane >> 4;
   if constexpr (PF) {
     if (pf.active[pf.pass - 1] == 0u) return;   // (uniform: every row of the block done)
@@ -1426,17 +1426,31 @@ index_prefill_kt_kernel(const uint8_t* __restrict__ q_idx, const float* __restri
   const uint8_t* ksb = F4 ? k_scales + b * ks_bstride : nullptr;
   const int nchunks = (ik1 - ik0 + 15) >> 4;
   uint32_t fk[PD][FW];
-  auto load_chunk = [&](uint32_t (&f)[FW], int c) {
-    int j = ik0 + 16 * c + c16;
-    j = j < ik1 ? j : ik1 - 1;
-    const uint8_t* p = kb + (int64_t)j * k_rstride + 16 * g;
+  auto load_at = [&](uint32_t (&f)[FW], const uint8_t* p, const uint8_t* ps) {
     const v4u lo = *reinterpret_cast<const v4u*>(p);
     f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
     if constexpr (F4) {
-      f[4] = ksb[(int64_t)j * ks_rstride + g];   // the E8M0 scale of this lane's 32 channels
+      f[4] = *ps;   // the E8M0 scale of this lane's 32 channels
     } else {
       const v4u hi = *reinterpret_cast<const v4u*>(p + 64);
       f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    }
+  };
+  // A chunk wholly inside the tile: this lane's row address plus the chunk's
+  // offset, computed once per wave in scalar registers (the 64-bit vector
+  // multiply per chunk cost about 6% of the pass); the tile's last chunk and
+  // those past it read clamped rows.
+  const uint8_t* lane_k = kb + (int64_t)(ik0 + c16) * k_rstride + 16 * g;
+  const uint8_t* lane_s = F4 ? ksb + (int64_t)(ik0 + c16) * ks_rstride + g : nullptr;
+  auto load_chunk = [&](uint32_t (&f)[FW], int c) {
+    const int cu = __builtin_amdgcn_readfirstlane(c);
+    if (16 * cu + 16 <= ik1 - ik0) {
+      const int64_t r = 16 * (int64_t)cu;
+      load_at(f, lane_k + r * k_rstride, F4 ? lane_s + r * ks_rstride : nullptr);
+    } else {
+      int j = ik0 + 16 * cu + c16;
+      j = j < ik1 ? j : ik1 - 1;
+      load_at(f, kb + (int64_t)j * k_rstride + 16 * g, F4 ? ksb + (int64_t)j * ks_rstride + g : nullptr);
     }
   };
   // ST (PF): selected keys and candidates staged in LDS, as a compile-time
