@@ -1303,17 +1303,94 @@ __global__ void __launch_bounds__(256) pf_step_kernel(PfArgs pf, int pass) {
   if (threadIdx.x == 0 && pf.rows[blockIdx.x].mode != PF_DONE) pf.active[pass] = 1u;
 }
 
+// Rows of up to 32 * kRankWords positions with k_top <= 2048 take their
+// slots by rank in a position bitmap: every position sets its bit, a block
+// scan gives each 32-bit word the number of set bits before it, and a
+// position's slot is that count plus the set bits below it in its word
+// (positions are unique and below the row's visible count).  Thread t owns
+// words t*kRankWpt .. +kRankWpt-1 (odd: a wave's threads hit distinct banks).
+constexpr int kRankWpt = 41;
+constexpr int kRankWords = 256 * kRankWpt;   // 10,496 words: 335,872 positions
+
+__device__ void pf_final_rank(const PfArgs& pf, int64_t lr, int64_t grow, uint32_t n, int nw, uint32_t* bits,
+                              uint16_t* pre, uint32_t* wtot, float* __restrict__ topk_score) {
+  constexpr int NT = 256, EPT = 2048 / NT;
+  const int K = pf.k_top;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int w0 = t * kRankWpt;
+  const bool own = w0 < nw;   // (words past nw in an owned range are zeroed too)
+  if (own) {
+#pragma unroll
+    for (int i = 0; i < kRankWpt; ++i) bits[w0 + i] = 0u;
+  }
+  const int32_t* oi = pf.out_idx + grow * K;
+  const uint32_t* ok = pf.out_key ? pf.out_key + grow * K : nullptr;
+  uint32_t pos[EPT], key[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {   // (all read before any slot is written below)
+    const uint32_t i = (uint32_t)t + NT * e;
+    pos[e] = i < n ? (uint32_t)oi[i] : ~0u;
+    key[e] = i < n && ok ? ok[i] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (pos[e] != ~0u) atomicOr(&bits[pos[e] >> 5], 1u << (pos[e] & 31u));
+  __syncthreads();
+  uint32_t tot = 0;
+  if (own) {
+#pragma unroll
+    for (int i = 0; i < kRankWpt; ++i) tot += (uint32_t)__builtin_popcount(bits[w0 + i]);
+  }
+  const uint32_t incl = wave_prefix_sum(tot);
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  uint32_t run = incl - tot;
+  for (int j = 0; j < wv; ++j) run += wtot[j];
+  if (own) {
+#pragma unroll
+    for (int i = 0; i < kRankWpt; ++i) {
+      const uint32_t b = bits[w0 + i];
+      pre[w0 + i] = (uint16_t)run;
+      run += (uint32_t)__builtin_popcount(b);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (pos[e] == ~0u) continue;
+    const uint32_t w = pos[e] >> 5;
+    const uint32_t r = pre[w] + (uint32_t)__builtin_popcount(bits[w] & ((1u << (pos[e] & 31u)) - 1u));
+    pf.out_idx[grow * K + r] = (int32_t)pos[e];
+    if (topk_score) topk_score[grow * K + r] = key_score(key[e]);
+  }
+  for (int i = (int)n + t; i < K; i += NT) {
+    pf.out_idx[grow * K + i] = -1;
+    if (topk_score) topk_score[grow * K + i] = -__builtin_inff();
+  }
+}
+
 // Each row's positions ascending (ids unique), scores from their keys, -1 /
 // -inf padding.  PMAX >= k_top.
 template <int PMAX, int NT>
 __global__ void __launch_bounds__(NT) pf_final_kernel(PfArgs pf, float* __restrict__ topk_score) {
-  __shared__ __align__(16) uint64_t sbuf[PMAX];
+  constexpr bool RANK = PMAX == 2048 && NT == 256;
+  // (the rank path's bitmap and counts, or the sort's values)
+  __shared__ __align__(16) uint32_t lds[RANK ? kRankWords + kRankWords / 2 + 4 : 2 * PMAX];
+  uint64_t* sbuf = reinterpret_cast<uint64_t*>(lds);
   const int64_t lr = blockIdx.x;
   const int64_t grow = pf.row_base + lr;
   const int K = pf.k_top;
   uint32_t n = pf.rows[lr].out_cnt;
   if (n > (uint32_t)K) n = K;
-  if constexpr (PMAX == 2048 && NT == 256) {
+  if constexpr (RANK) {
+    int64_t nv = pf.n_valid[grow];
+    nv = nv < 0 ? 0 : nv;
+    if (nv <= 32LL * kRankWords) {   // (uniform)
+      pf_final_rank(pf, lr, grow, n, (int)((nv + 31) >> 5), lds, reinterpret_cast<uint16_t*>(lds + kRankWords),
+                    lds + kRankWords + kRankWords / 2, topk_score);
+      return;
+    }
     // (position << 32 | key) sorted in registers; padding ~0 last
     const int32_t* oi = pf.out_idx + grow * K;
     const uint32_t* ok = pf.out_key ? pf.out_key + grow * K : nullptr;

@@ -298,6 +298,27 @@ def test_prefill_selection_takes_a_whole_bucket():
 
 
 @gpu
+def test_prefill_selection_final_order_long_and_short_rows():
+    """The last kernel of the selection puts a row's positions in ascending
+    order by their rank in a position bitmap while the row sees at most
+    335,872 positions, and by a sort beyond that: one chunk with a row on
+    each side of the bound, one exactly at it, and a row with fewer than K
+    positions."""
+    require_gpu()
+    announce("index_score_topk prefill final order, rows of 2K to 340K positions")
+    B, N, Tq, H_I, D_I, K = 1, 340_000, 16, 8, 128, 2048
+    k_idx = inputs.int_e4m3((B, N, D_I), 49, 0, "k_idx", device="cuda")
+    q_idx = inputs.int_e4m3((B, Tq, H_I, D_I), 49, 1, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, Tq, H_I), 49, 1, "w", device="cuda")
+    ctx = torch.tensor([N], dtype=torch.int32, device="cuda")
+    # (one row beyond the bound, one at it, the rest short; the first short
+    # one sees fewer than K positions)
+    pos = [N - 1, 335_871] + [1_900 + 700 * i for i in range(14)]
+    q_pos = torch.tensor([pos], dtype=torch.int32, device="cuda")
+    _run_and_check(q_idx, w, k_idx, ctx, K, q_pos=q_pos)
+
+
+@gpu
 @pytest.mark.parametrize("D_I,H_I,Tq", [(64, 8, 20), (32, 4, 33)])
 def test_prefill_chunks_of_row_scans(D_I, H_I, Tq):
     """Chunk shapes the matrix-core product does not take are scanned a few
