@@ -348,11 +348,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   // the loop, so that each holds only its own state in registers.
   if (s_wave) {
     // ================================================================ S waves
+    // Read by every S wave, active or not (rows past H are staged space,
+    // never used): with the read under a branch, the compiler could not rule
+    // out that these registers still awaited the q loads of the prologue and
+    // made the products wait for every global load in flight, the next
+    // chunk's gather included.
     v8h qf[S::KQ];
-    if (active) {
 #pragma unroll
-      for (int i = 0; i < S::KQ; ++i) qf[i] = *reinterpret_cast<const v8h*>(qs + head_b * QP + 32 * i + 8 * g);
-    }
+    for (int i = 0; i < S::KQ; ++i) qf[i] = *reinterpret_cast<const v8h*>(qs + head_b * QP + 32 * i + 8 * g);
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
     if (nch > 0) store(kbuf[0]);
@@ -410,8 +413,14 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
               z[4 * t + r] = v;
               cmax = fmaxf(cmax, v);
             }
-          cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-          cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+          // The head's maximum over the four lane groups matters only when
+          // some value exceeds the reference by more than kLazy; otherwise
+          // every lane keeps the reference (the same decision either way),
+          // and the two cross-lane exchanges are skipped.
+          if (__any(cmax > m_run + kLazy)) {
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+          }
         }
         float alpha = 1.0f;
         v8h pa;
