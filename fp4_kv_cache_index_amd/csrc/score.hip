@@ -154,20 +154,24 @@ index_score_kernel(const uint8_t* __restrict__ q_idx, const float* __restrict__ 
   // holds at most 16384 positions); the last word takes positions past the
   // visible count.
   __shared__ __attribute__((aligned(16))) uint32_t hist[QT][2052];
-  // Flat scan: the tile's keys are staged here and leave in one coalesced
-  // burst at the end (interleaving small key stores with the key-row stream
-  // costs more than the LDS round trip).
-  constexpr bool kStage = !GATHER && !POOL;
-  constexpr int kTileCap = 1024 * NW;
-  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? QT * kTileCap : 1];
-  __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
-  __shared__ uint32_t bhist[POOL ? 4096 : 1];
   // Whole-line path: per wave the batch's dots, then one 4-float trash slot
   // per lane (the other paths move the dots to their token's lane in
   // registers: RT).
   constexpr bool FULL = !F4 && (DI == 128 && HB == 1 && kScanGroups<HB> == 4);
   constexpr bool RT = !FULL;
-  __shared__ __attribute__((aligned(16))) float dots[NW][RT ? 1 : 16 * kScanGroups<HB> * HP + 256];
+  constexpr int kDots = RT ? 1 : 16 * kScanGroups<HB> * HP + 256;
+  __shared__ __attribute__((aligned(16))) float dots[NW][kDots];
+  // Flat and pool scans: the tile's keys are staged here and leave in one
+  // coalesced burst at the end (interleaving small key stores with the
+  // key-row stream costs more than the LDS round trip); a pool scan whose
+  // staged keys would not fit beside its block histogram stores them
+  // directly.
+  constexpr int kTileCap = 1024 * NW;
+  constexpr bool kStage =
+      !GATHER && (!POOL || 4 * (QT * 2052 + QT * kTileCap + 4096 + NW * kDots + HMAX) <= 150 * 1024);
+  __shared__ __attribute__((aligned(16))) uint32_t kst[kStage ? QT * kTileCap : 1];
+  __shared__ int32_t ptok[GATHER ? kPoolTile : 1];   // pool token ids of this tile
+  __shared__ uint32_t bhist[POOL ? 4096 : 1];
   __shared__ float wsh[HMAX];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
