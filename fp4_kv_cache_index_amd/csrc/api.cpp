@@ -376,8 +376,7 @@ static int score_topk_impl(ScoreArgs a, int32_t* topk_idx, float* topk_score, in
       e = select_local(keys, L.n_stride, n_valid, L.rows, k_top, n_max, th.tile_hist, L.th_stride, tiles, tout, s);
     return e == hipSuccess ? CSA2_OK : CSA2_EHIP;
   }
-  hipError_t e = select_clear(tok, L.rows, s);
-  if (e == hipSuccess && pool) e = select_clear(blk, L.rows, s);
+  hipError_t e = select_clear(tok, L.rows, s, pool ? &blk : nullptr);
   if (e == hipSuccess)
     e = launch_index_score(a, keys, L.n_stride, n_valid, tok, bkeys, L.nb_stride, nb_valid, pool ? &blk : nullptr, s);
   if (e == hipSuccess) e = select_finish(tok, keys, L.n_stride, n_valid, L.rows, k_top, tout, s);

@@ -103,7 +103,7 @@ struct SelectOut {
 };
 
 // Clears the control blocks and first-digit histograms of `rows` rows.
-hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s);
+hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s, const SelectWs* ws2 = nullptr);
 // Rows of at most kLocalSel positions (kLocalSelMap with a map): one
 // workgroup per row does the whole selection from the keys, taking the
 // first radix digit from the producer's per-tile histograms when tile_hist

@@ -67,10 +67,14 @@ SelectWs select_ws_carve(void* base, int64_t rows, int64_t n_max) {
 
 // ------------------------------------------------------------- kernels ---
 
-__global__ void select_clear_kernel(uint32_t* p, int64_t n_words) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+// Zeroes n0 words at p0, then n1 words at p1 (a second region in the same
+// launch: the token and block states of a pool scan).
+__global__ void select_clear_kernel(uint32_t* p0, int64_t n0, uint32_t* p1, int64_t n1) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n0 + n1;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < n0) p0[i] = 0u;
+    else p1[i - n0] = 0u;
+  }
 }
 
 // The 16 keys a thread handles: positions base + 1024*i + 4*tid + j
@@ -925,13 +929,14 @@ hipError_t select_local(const uint32_t* keys, int64_t key_stride, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s) {
+hipError_t select_clear(const SelectWs& ws, int64_t rows, hipStream_t s, const SelectWs* ws2) {
   // ctl and hist1 are carved contiguously.
-  int64_t words = (int64_t)((char*)(ws.hist1 + 4096 * rows) - (char*)ws.ctl) / 4;
-  int64_t grid = (words + 1023) / 1024;
+  auto words = [&](const SelectWs& w) { return (int64_t)((char*)(w.hist1 + 4096 * rows) - (char*)w.ctl) / 4; };
+  const int64_t n0 = words(ws), n1 = ws2 ? words(*ws2) : 0;
+  int64_t grid = (n0 + n1 + 1023) / 1024;
   if (grid > 2048) grid = 2048;
-  CSA2_LAUNCH("select_clear", select_clear_kernel, dim3((unsigned)grid), dim3(256), 0, s, (uint32_t*)ws.ctl,
-              words);
+  CSA2_LAUNCH("select_clear", select_clear_kernel, dim3((unsigned)grid), dim3(256), 0, s, (uint32_t*)ws.ctl, n0,
+              ws2 ? (uint32_t*)ws2->ctl : (uint32_t*)nullptr, n1);
   return hipGetLastError();
 }
 
