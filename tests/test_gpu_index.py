@@ -388,6 +388,42 @@ def test_decode64k_full_size_sampled_rows():
     assert np.all(np.diff(got, axis=1) > 0) and got.min() >= 0 and got.max() < wl.N
 
 
+@gpu
+def test_maximum_context_with_a_huge_zero_tie_bucket():
+    """Rows at the documented limit of 4,194,304 positions (one whole, one
+    ragged by 777), every key row zero except 3,000 random ones per sequence.
+    A zero key row scores +0 under the oracle's definition, so the positive
+    scores (about half of the 3,000) are taken first and the rest of the
+    Top-2048 is the lowest-index ties at +0, out of a bucket of some four
+    million equal keys (the crowded-bucket path of the long-row select);
+    negative scores rank below the ties."""
+    require_gpu()
+    B, N, H_I, D_I, K, S = 2, 1 << 22, 8, 128, 2048, 3000
+    announce(f"index_score_topk at the row limit: B={B} N={N} ctx N and N-777, {S} nonzero keys per row, K={K}")
+    g = torch.Generator().manual_seed(4_194_304)
+    pos = [torch.randperm(N - 777, generator=g)[:S].sort().values for _ in range(B)]
+    rows = inputs.int_e4m3((B, S, D_I), 9, 11, "k_idx", device="cuda")
+    k_idx = torch.zeros((B, N, D_I), dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        k_idx[b, pos[b].cuda()] = rows[b]
+    q_idx = inputs.int_e4m3((B, 1, H_I, D_I), 9, 11, "q_idx", device="cuda")
+    w = inputs.normal_f32((B, 1, H_I), 9, 11, "w", device="cuda")
+    ctx = torch.tensor([N, N - 777], dtype=torch.int32, device="cuda")
+    res = csa2.csa2_index_score_topk(q_idx, w, k_idx, ctx, K, want_scores=True)
+    torch.cuda.synchronize()
+    zero = I.index_scores(np_(q_idx[0, 0]), np_(w[0, 0]), np.zeros((4, D_I), np.uint8), 4)
+    assert np.all(zero == 0) and not np.any(np.signbit(zero))
+    for b in range(B):
+        nv = int(ctx[b])
+        s = np.zeros(N, dtype=np.float32)
+        s[nv:] = -np.inf
+        s[np_(pos[b])] = I.index_scores(np_(q_idx[b, 0]), np_(w[b, 0]), np_(rows[b]), S)
+        want_i, want_s = topk_select(s, nv, K)
+        assert 0 < int((want_s > 0).sum()) < K and int((want_s == 0).sum()) > 0   # both kinds are taken
+        assert np.array_equal(np_(res["topk_idx"][b, 0]), want_i)
+        assert np.array_equal(np_(res["topk_score"][b, 0]), want_s)
+
+
 def _dot_rows(dots, D_I=128):
     """E4M3 key rows whose dot with an all-ones query row is the given integer
     (the first `dot` bytes are 1.0, the rest 0)."""
