@@ -146,7 +146,8 @@ int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_
  *   -1 padded; pool_len [B][Tq] int32 = number of valid entries.
  *   pool_block must be 1, 2, 4, 8 or 16.  The flat Top-K is a subset of the
  *   pool whenever pool_nblocks >= k_top.
- * Supported: D_I in {32, 64, 128, 256}; 1 <= H_I <= 32; k_top >= 1.
+ * Supported: D_I in {32, 64, 128, 256}; 1 <= H_I <= 32; k_top >= 1;
+ * n_max <= 4,194,304 positions; B*Tq <= 65,535; k_row_stride < 4 MiB.
  *
  * Workspace: ws / ws_bytes, 256-byte aligned, of at least
  * csa2_index_score_topk_workspace_size() bytes.  Dense prefill chunks
@@ -156,8 +157,8 @@ int idx_mxfp4_quantize(const float* x, int64_t n_rows, int32_t d, int64_t x_row_
  *     per-tile histograms (csa2_index_score_topk_workspace_size_stored();
  *     13.4 GB for 4096 queries on 266,240 tokens), used whenever ws_bytes
  *     reaches that size: one scoring pass;
- *   - otherwise no score matrix at all: two passes over one 16-key chunk
- *     in eight histogram a sample of the scores and place each
+ *   - otherwise no score matrix at all: two passes that score one 16-key
+ *     chunk in every eight build histograms of that sample and place each
  *     row's threshold in a narrow window, a full scoring pass emits the keys
  *     above the window and collects those inside it, and rows whose counts
  *     do not confirm the window (heavy ties, for instance) search exactly
