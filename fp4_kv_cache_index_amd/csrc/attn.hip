@@ -103,6 +103,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   __shared__ __attribute__((aligned(16))) int32_t eidc[4][kChunk];
   __shared__ __attribute__((aligned(16))) v8h pex[2][4][64];   // P fragments of the 4 S waves, 2 chunks
   __shared__ __attribute__((aligned(16))) float alf[2][64];     // per-head rescale factor, 2 chunks
+  __shared__ __attribute__((aligned(16))) uint32_t mvf[2][4];   // per S wave: some factor is not 1, 2 chunks
   __shared__ float pml[2][64];                                  // epilogue: per-head (w, 1/L)
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -446,6 +447,10 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         }
         pex[pb][hg][lane] = pa;
         if (g == 0) alf[pb][16 * hg + c16] = alpha;
+        // One flag per S wave tells the PV waves whether any of its heads'
+        // reference maxima moved (the factors are then read and applied).
+        const bool moved = __any(alpha != 1.0f);
+        if (lane == 0) mvf[pb][hg] = moved ? 1u : 0u;
       }
       advance(it, c0, kb_next);
       __syncthreads();
@@ -564,14 +569,11 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       v8h pf[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) pf[t] = pex[pb ^ 1][t][lane];
-      float4 al[4];
+      const uint4 mv = *reinterpret_cast<const uint4*>(&mvf[pb ^ 1][0]);
+      if (__builtin_amdgcn_readfirstlane(mv.x | mv.y | mv.z | mv.w) != 0u) {
+        float4 al[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const float4*>(&alf[pb ^ 1][16 * t + 4 * g]);
-      bool ones = true;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        ones = ones && al[t].x == 1.0f && al[t].y == 1.0f && al[t].z == 1.0f && al[t].w == 1.0f;
-      if (!__all(ones)) {
+        for (int t = 0; t < 4; ++t) al[t] = *reinterpret_cast<const float4*>(&alf[pb ^ 1][16 * t + 4 * g]);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
