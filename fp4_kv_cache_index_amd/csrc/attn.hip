@@ -219,7 +219,11 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
+      // A skipped task stages zero words: the main-row conversion turns
+      // them into +0 halves, so the dequantisation has no third path.
       raw[u].kind = 0;
+      raw[u].w[0] = 0u; raw[u].w[1] = 0u; raw[u].w[2] = 0u; raw[u].w[3] = 0u;
+      raw[u].sc = 0u;
       if (task < NTASK) {
         const int e = task / NB;
         // The block's byte offsets are recomputed every chunk (an opaque j):
@@ -261,7 +265,18 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       if (task >= NTASK) break;
       const int e = task / NB, j = task - (task / NB) * NB;
       uint32_t hv[16];
-      if (raw[u].kind == 1u) {
+      if (raw[u].kind == 2u) {
+        // E4M3 -> fp16 scaled by the E8M0 power of two, in one instruction.
+        const float sc = e8m0_to_f32(raw[u].sc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t word = raw[u].w[i >> 1];
+          v2h v = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, true)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, false);
+          hv[i] = __builtin_bit_cast(uint32_t, v);
+        }
+      } else {
+        // A main row, or a skipped task (zero words: +0 halves).
         // E2M1 -> fp16 in hardware (scale 1), then the E4M3 scale of each
         // 16-channel group (converted to fp16 by the fp8 convert) as an fp16
         // multiply; every step is exact (at most 6 significant bits).
@@ -283,19 +298,6 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
             hv[8 * hgp + i] = __builtin_bit_cast(uint32_t, v);
           }
         }
-      } else if (raw[u].kind == 2u) {
-        // E4M3 -> fp16 scaled by the E8M0 power of two, in one instruction.
-        const float sc = e8m0_to_f32(raw[u].sc);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t word = raw[u].w[i >> 1];
-          v2h v = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, true)
-                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, sc, false);
-          hv[i] = __builtin_bit_cast(uint32_t, v);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) hv[i] = 0u;
       }
       uint4* dst = reinterpret_cast<uint4*>(kt + e * S::PITCH + 32 * j);
 #pragma unroll
