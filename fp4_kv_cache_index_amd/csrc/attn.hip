@@ -215,7 +215,19 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   // ---- gather: task = (entry e, 32-channel block j), j fastest, so that
   // consecutive lanes read consecutive 16-byte pieces of one row.
   RawTask raw[TPT];
-  auto gather = [&](int c0, int slot) {
+  // Entry ids of this thread's tasks in chunk c0 (ring slot `slot`; -1 past
+  // the split).  Read apart from the gather, at the top of an iteration, so
+  // that the LDS round trip passes under that iteration's other work.
+  auto task_ids = [&](int c0, int slot, int32_t(&idv)[TPT]) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int task = threadIdx.x + u * kAttnThreads;
+      const int e = task < NTASK ? task / NB : 0;
+      const int32_t v = eidc[slot][e];
+      idv[u] = task < NTASK && c0 + e < e_end ? v : -1;
+    }
+  };
+  auto gather_ids = [&](int c0, const int32_t(&idv)[TPT]) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int task = threadIdx.x + u * kAttnThreads;
@@ -232,7 +244,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         int j = task - (task / NB) * NB;
         asm volatile("" : "+v"(j));
         const int ce = c0 + e;
-        const int32_t id = ce < e_end ? eidc[slot][e] : -1;
+        const int32_t id = idv[u];
         if (id >= 0 && ce < K) {
           const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes_b + (int64_t)id * a.c_rstride + 16 * j);
           raw[u].w[0] = cp[0]; raw[u].w[1] = cp[1]; raw[u].w[2] = cp[2]; raw[u].w[3] = cp[3];
@@ -248,6 +260,11 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         }
       }
     }
+  };
+  auto gather = [&](int c0, int slot) {
+    int32_t idv[TPT];
+    task_ids(c0, slot, idv);
+    gather_ids(c0, idv);
   };
   // ---- dequantise the staged bytes into fp16 K rows.
   auto store = [&](_Float16* kt) {
@@ -308,10 +325,10 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   const int nch = e_end > e_begin ? (e_end - e_begin + kChunk - 1) / kChunk : 0;
   // Dequantise chunk it+1 into the buffer last read as V one iteration ago,
   // then issue the loads of chunk it+2 (every wave takes a share).
-  auto advance = [&](int it, int c0, int kb_next) {
+  auto advance = [&](int it, int c0, int kb_next, const int32_t(&idn)[TPT]) {
     if (it + 1 < nch) {
       store(kbuf[kb_next]);
-      if (it + 2 < nch) gather(c0 + 2 * kChunk, (it + 2) & 3);
+      if (it + 2 < nch) gather_ids(c0 + 2 * kChunk, idn);
     }
   };
 
@@ -369,6 +386,8 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
       const int c0 = e_begin + it * kChunk;
       const int pb = it & 1;
       const int kb_next = kb == 2 ? 0 : kb + 1;
+      int32_t idn[TPT];
+      if (it + 2 < nch) task_ids(c0 + 2 * kChunk, (it + 2) & 3, idn);
       if (it < nch) {
         const _Float16* kt = kbuf[kb];
         float z[8];
@@ -454,7 +473,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
         const bool moved = __any(alpha != 1.0f);
         if (lane == 0) mvf[pb][hg] = moved ? 1u : 0u;
       }
-      advance(it, c0, kb_next);
+      advance(it, c0, kb_next, idn);
       __syncthreads();
       kb = kb_next;
     }
@@ -527,6 +546,8 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
     const int c0 = e_begin + it * kChunk;
     const int pb = it & 1;
     const int kb_prev = kb == 0 ? 2 : kb - 1, kb_next = kb == 2 ? 0 : kb + 1;
+    int32_t idn[TPT];
+    if (it + 2 < nch) task_ids(c0 + 2 * kChunk, (it + 2) & 3, idn);
     // The dequantisation comes first here (the S waves end with it), so
     // that one role's VALU work overlaps the other's products.
     if (it + 1 < nch) {
@@ -546,7 +567,7 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           ldn = idx_row[cn < K ? cn : K - 1];
         }
       }
-      if (it + 2 < nch) gather(c0 + 2 * kChunk, (it + 2) & 3);
+      if (it + 2 < nch) gather_ids(c0 + 2 * kChunk, idn);
     }
     if (it >= 1) {
       // O += P V for chunk it-1; k index: entries {4g..4g+3, 16+4g..16+4g+3},
