@@ -112,7 +112,8 @@ static int attn_common_check(const float* q, const uint8_t* kv_codes, int64_t c_
                              const uint8_t* swa_vals, int64_t sv_bstride, int64_t sv_rstride,
                              const uint8_t* swa_scales, int64_t ss_bstride, int64_t ss_rstride, int32_t W,
                              int32_t B, int32_t H, int32_t d_qk, int32_t d_v, float* out) {
-  if (!q || !kv_codes || !kv_scales || !topk_idx || !ctx_len || !out) return CSA2_EINVAL;
+  // (topk_idx may be NULL when k_top == 0: attention over the window alone)
+  if (!q || !kv_codes || !kv_scales || (!topk_idx && k_top > 0) || !ctx_len || !out) return CSA2_EINVAL;
   if (B < 0 || k_top < 0 || W < 0 || H <= 0 || d_qk <= 0 || d_v <= 0) return CSA2_EINVAL;
   if (d_qk % 16 != 0 || d_v > d_qk || d_v % 16 != 0) return CSA2_EINVAL;
   // Code rows are read as 32-bit words; scale bytes are read one at a time.

@@ -524,18 +524,22 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
   // and no wait for the gather is needed anywhere else in the loop.
   // Paged: the raw ids are loaded two chunks ahead, validated and their
   // block-table entries loaded one chunk ahead, and the pool rows staged.
-  const bool id_lane = wave == 4 && lane < kChunk && K > 0;
+  // (With no Top-K entries, k_top = 0, the window rows are still staged by
+  // this lane; its raw id loads then read ctx_len[b], a valid address whose
+  // value no window entry uses.)
+  const bool id_lane = wave == 4 && lane < kChunk;
+  auto raw_id = [&](int c) -> const int32_t* { return K > 0 ? idx_row + (c < K ? c : K - 1) : a.ctx_len + b; };
   int32_t ldn = 0, vn = -1, pgn = 0;
   if (id_lane) {
     const int ce = e_begin + 3 * kChunk + lane;
     if constexpr (PAGED) {
-      const int32_t r3 = idx_row[ce < K ? ce : K - 1];
+      const int32_t r3 = *raw_id(ce);
       const int c4 = ce + kChunk;
-      ldn = idx_row[c4 < K ? c4 : K - 1];
+      ldn = *raw_id(c4);
       vn = entry_id(ce, r3);
       pgn = page_of(ce, vn);
     } else {
-      ldn = idx_row[ce < K ? ce : K - 1];
+      ldn = *raw_id(ce);
     }
   }
   if (nch > 0) store(kbuf[0]);
@@ -560,11 +564,11 @@ sparse_attn_split_kernel(AttnArgs a, int prefill, int splits, int span,
           vn = entry_id(c4, ldn);
           pgn = page_of(c4, vn);
           const int c5 = c4 + kChunk;
-          ldn = idx_row[c5 < K ? c5 : K - 1];
+          ldn = *raw_id(c5);
         } else {
           if (it + 3 < nch) eidc[(it + 3) & 3][lane] = entry_id(ce, ldn);
           const int cn = ce + kChunk;
-          ldn = idx_row[cn < K ? cn : K - 1];
+          ldn = *raw_id(cn);
         }
       }
       if (it + 2 < nch) gather_ids(c0 + 2 * kChunk, idn);

@@ -281,7 +281,7 @@ int csa2_hier_pool_topk_mxfp4(const uint8_t* q_idx, const float* w,
  * q        [B][H][d_qk] float32.
  * kv_codes row j of b at kv_codes + b*c_batch_stride + j*c_row_stride (d_qk/2 bytes);
  * kv_scales row j of b at kv_scales + b*s_batch_stride + j*s_row_stride (d_qk/16 bytes).
- * topk_idx [B][k_top] int32.  ctx_len [B].
+ * topk_idx [B][k_top] int32 (NULL allowed when k_top = 0: the window alone).  ctx_len [B].
  * swa_vals  row w of b at swa_vals + b*sv_batch_stride + w*sv_row_stride (d_qk bytes E4M3);
  * swa_scales row w of b at swa_scales + b*ss_batch_stride + w*ss_row_stride (d_qk/32 bytes E8M0);
  * swa_len  [B] int32 (clamped to [0, W]); swa pointers may be NULL when W == 0.

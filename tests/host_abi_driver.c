@@ -234,6 +234,11 @@ int main(void) {
              d, dv, 0.04f, out, lse, aws, dsz, NULL), CSA2_EINVAL);
   EXPECT(DEC(qa, cache, cb, 324, cache + 288, cb, 324, idx, 0, ctx, sv, W * d, d, ss, W * 18, 18, swl, 0, NULL, B, H,
              d, dv, 0.04f, out, lse, aws, dsz, NULL), CSA2_EINVAL);   /* no entries at all */
+  EXPECT(DEC(qa, cache, cb, 324, cache + 288, cb, 324, NULL, Ka, ctx, sv, W * d, d, ss, W * 18, 18, swl, W, NULL, B,
+             H, d, dv, 0.04f, out, lse, aws, dsz, NULL), CSA2_EINVAL);   /* Top-K entries without ids */
+  if (no_device)   /* the window alone: no Top-K ids needed */
+    EXPECT(DEC(qa, cache, cb, 324, cache + 288, cb, 324, NULL, 0, ctx, sv, W * d, d, ss, W * 18, 18, swl, W, NULL, B,
+               H, d, dv, 0.04f, out, lse, aws, dsz, NULL), launch);
   EXPECT(DEC(qa, cache, cb, 324, cache + 288, cb, 324, idx, Ka, ctx, sv, W * d, d, ss, W * 18, 18, swl, W, NULL, B, H,
              d, dv, 0.04f, out, lse, (char*)aws + 64, dsz, NULL), CSA2_EINVAL);
   EXPECT(DEC(qa, cache, cb, 324, cache + 288, cb, 324, idx, Ka, ctx, sv, W * d, d, ss, W * 18, 18, swl, W, NULL, B, H,

@@ -82,7 +82,8 @@ def test_tiny_config_decode_attention():
 @gpu
 @pytest.mark.parametrize("d_qk,H,K,W,n_invalid", [(576, 64, 2048, 128, 0), (576, 64, 300, 50, 40),
                                                   (512, 64, 512, 128, 7), (576, 32, 64, 0, 3),
-                                                  (576, 48, 200, 17, 5), (512, 16, 33, 1, 0)])
+                                                  (576, 48, 200, 17, 5), (512, 16, 33, 1, 0),
+                                                  (576, 64, 0, 128, 0), (512, 32, 0, 128, 0)])
 def test_decode_shapes_invalid_entries_and_ragged_windows(d_qk, H, K, W, n_invalid):
     require_gpu()
     announce(f"attn decode d_qk={d_qk} H={H} K={K} W={W} invalid={n_invalid}")
@@ -189,17 +190,21 @@ def test_empty_entry_sets():
 
 
 @gpu
-def test_prefill_attention_causal_windows():
+@pytest.mark.parametrize("K", [256, 0])
+def test_prefill_attention_causal_windows(K):
+    """Causal windows of nine consecutive queries, with Top-K rows and with
+    the window alone (k_top = 0: up to 128 window rows, four chunks)."""
     require_gpu()
-    announce("attn prefill B2 Tq=9 K=256 W=128")
-    B, Tq, N0, d_qk, H, K, W = 2, 9, 3000, 576, 64, 256, 128
+    announce(f"attn prefill B2 Tq=9 K={K} W=128")
+    B, Tq, N0, d_qk, H, W = 2, 9, 3000, 576, 64, 128
     N = N0 + Tq
     kv_x, codes, scales, _, _, _ = _make_caches(B, N, d_qk, 0, 24)
     S = W - 1 + Tq
     swa_x = inputs.normal_f32((B, S, d_qk), 24, 1, "swa", device="cuda")
     sv, ss = csa2.swa_fp8_quantize(swa_x)
     q = inputs.normal_f32((B, Tq, H, d_qk), 24, 2, "q", device="cuda")
-    idx = inputs.random_index_lists(B * Tq, K, N0, 24, device="cuda", n_invalid=5).reshape(B, Tq, K).contiguous()
+    idx = inputs.random_index_lists(B * Tq, K, N0, 24, device="cuda", n_invalid=5 if K else 0).reshape(B, Tq, K)
+    idx = idx.contiguous()
     ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
     q_pos = (torch.arange(Tq, dtype=torch.int32, device="cuda") + N0).repeat(B, 1).contiguous()
     swa_pos0 = torch.tensor([N0 - W + 1, N0 - W + 1], dtype=torch.int32, device="cuda")

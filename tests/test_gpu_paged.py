@@ -59,16 +59,16 @@ def _oracle(c, q, idx, ctx, q_pos, page, n_pages, R, W, d_qk, scale):
 
 
 @gpu
-@pytest.mark.parametrize("Tq,page,R", [(1, 64, 128), (1, 16, 200), (3, 64, 131)])
-def test_paged_attention_against_the_oracle(Tq, page, R):
+@pytest.mark.parametrize("Tq,page,R,K", [(1, 64, 128, 700), (1, 16, 200, 700), (3, 64, 131, 700), (2, 64, 128, 0)])
+def test_paged_attention_against_the_oracle(Tq, page, R, K):
     require_gpu()
-    announce(f"paged attention Tq={Tq} page={page} ring={R}")
-    B, N, d_qk, H, K, W = 3, 3000, 576, 64, 700, 128
+    announce(f"paged attention Tq={Tq} page={page} ring={R} K={K}")
+    B, N, d_qk, H, W = 3, 3000, 576, 64, 128
     n_pages = 3 * ((N + page - 1) // page) + 11
     swa_end = [N, N - 40, 97]                     # a wrapped ring, a partial one
     c = _paged_case(B, N, d_qk, page, n_pages, R, swa_end, 71 + page)
     ctx = torch.tensor([N, N - 40, 2000], dtype=torch.int32, device="cuda")
-    idx = torch.stack([inputs.random_index_lists(B, K, N, 71, layer=t, device="cuda", n_invalid=9)
+    idx = torch.stack([inputs.random_index_lists(B, K, N, 71, layer=t, device="cuda", n_invalid=9 if K else 0)
                        for t in range(Tq)], dim=1).contiguous()
     c["bt"][1, 5] = -1                            # a missing page
     c["bt"][2, 7] = n_pages + 3                   # an entry outside the pool
